@@ -1,0 +1,312 @@
+/*
+ * Oracle for the tiled dense GEMM and the weight-only 4-bit dequant GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library calls, links or includes
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark load it.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes is the plain definition, not the tiled algorithm:
+ *   - "TileLang: 用Python DSL简化GPU算子开发" (gtnt.cn), section 2.2, writes the
+ *     GEMM as C[i, j] = sum over k of A[i, k] * B[k, j] on row-major operands;
+ *   - "TileLang ... 一个高效 GEMM 内核" (mhpq.cn), sections 2.1 and 3.2, state the
+ *     same product C = A x B for an M x K and a K x N matrix, and section 4.3
+ *     says tiling only changes the fp32 summation order.
+ * So every result here is the exact sum in fp64 (exact for the integer and
+ * dyadic test inputs; within K * 2^-52 * sum|a||b| otherwise), followed by an
+ * optional ReLU (the blog.hotdry.top page's post-processing loop) and, for
+ * bitwise checks, ONE round-to-nearest-even from fp64 to the output type.
+ *
+ * Number formats are decoded and encoded from their field definitions
+ * (sign / biased exponent / fraction), never through a hardware cast:
+ *   IEEE-754 binary32 and binary16, bfloat16 (binary32 with a 7-bit fraction),
+ *   and the OCP Microscaling (MX) v1.0 element type E2M1 and scale type E8M0.
+ * The 4-bit weight format is not on the pages; it follows the workload text:
+ * two E2M1 codes per byte (even k in bits 3:0, odd k in bits 7:4), one E8M0
+ * scale per 32 consecutive k of a weight row, C = A * W^T with W stored [N][K].
+ *
+ * dtype codes: 0 = fp32, 1 = fp16, 2 = bf16 (operands and output share it).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+
+/* ---------------------------------------------------------------------- */
+/* Field-level decoding.                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Decode a binary floating-point code with `ebits` exponent bits and `fbits`
+ * fraction bits.  has_special: top exponent encodes Inf/NaN (IEEE); E2M1 has
+ * no special values, so its top exponent is an ordinary binade. */
+static double decode_bits(uint64_t bits, int ebits, int fbits, int has_special)
+{
+    const uint64_t fmask = (1ull << fbits) - 1ull;
+    const uint64_t emask = (1ull << ebits) - 1ull;
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int sign = (int)((bits >> (ebits + fbits)) & 1ull);
+    const uint64_t e = (bits >> fbits) & emask;
+    const uint64_t f = bits & fmask;
+    double v;
+    if (has_special && e == emask) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else if (e == 0) {
+        /* subnormal: f * 2^(1 - bias - fbits) */
+        v = ldexp((double)f, 1 - bias - fbits);
+    } else {
+        /* normal: (2^fbits + f) * 2^(e - bias - fbits) */
+        v = ldexp((double)((1ull << fbits) + f), (int)e - bias - fbits);
+    }
+    return sign ? -v : v;
+}
+
+double orc_decode_f32(uint32_t b) { return decode_bits(b, 8, 23, 1); }
+double orc_decode_f16(uint16_t b) { return decode_bits(b, 5, 10, 1); }
+double orc_decode_bf16(uint16_t b) { return decode_bits(b, 8, 7, 1); }
+
+/* OCP MX E2M1: bit 3 sign, bits 2:1 exponent (bias 1), bit 0 fraction. */
+double orc_decode_e2m1(uint8_t code) { return decode_bits(code & 0xFu, 2, 1, 0); }
+
+/* OCP MX E8M0: 2^(E - 127); E = 255 is NaN. */
+double orc_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* ---------------------------------------------------------------------- */
+/* Field-level encoding: one round-to-nearest-even from a double.          */
+/* ---------------------------------------------------------------------- */
+
+static uint64_t encode_rne(double x, int ebits, int fbits)
+{
+    const int bias = (1 << (ebits - 1)) - 1;
+    const uint64_t emax_field = (1ull << ebits) - 1ull;
+    const uint64_t sign = signbit(x) ? 1ull : 0ull;
+    const uint64_t sbit = sign << (ebits + fbits);
+    if (isnan(x))
+        return sbit | (emax_field << fbits) | (1ull << (fbits - 1)); /* quiet NaN */
+    double a = fabs(x);
+    if (isinf(a))
+        return sbit | (emax_field << fbits);
+    if (a == 0.0)
+        return sbit;
+
+    /* a = m * 2^(ex - 53), m a 53-bit integer (exact). */
+    int ex;
+    double fr = frexp(a, &ex);            /* a = fr * 2^ex, fr in [0.5, 1) */
+    uint64_t m = (uint64_t)ldexp(fr, 53); /* exact */
+    int ue = ex - 1;                      /* a in [2^ue, 2^(ue+1)) */
+    int emin = 1 - bias;                  /* smallest normal exponent */
+    /* quantum of the target grid around a: 2^q */
+    int q = (ue > emin ? ue : emin) - fbits;
+    int s = q - (ex - 53); /* right shift applied to m; always > 0 here */
+    uint64_t n;
+    if (s >= 64) {
+        n = 0; /* a < 2^(q-11): rounds to zero */
+    } else {
+        n = m >> s;
+        uint64_t rem = m & ((1ull << s) - 1ull);
+        uint64_t half = 1ull << (s - 1);
+        if (rem > half || (rem == half && (n & 1ull)))
+            n += 1;
+    }
+    /* value = n * 2^q.  n < 2^fbits only in the subnormal binade. */
+    uint64_t efield, ffield;
+    if (n < (1ull << fbits)) {
+        efield = 0; /* subnormal (q == emin - fbits) or zero */
+        ffield = n;
+    } else {
+        if (n == (2ull << fbits)) { /* carry into the next binade */
+            n >>= 1;
+            q += 1;
+        }
+        efield = (uint64_t)(q + fbits + bias);
+        ffield = n - (1ull << fbits);
+    }
+    if (efield >= emax_field) /* overflow: RNE rounds to infinity */
+        return sbit | (emax_field << fbits);
+    return sbit | (efield << fbits) | ffield;
+}
+
+uint32_t orc_encode_f32(double x) { return (uint32_t)encode_rne(x, 8, 23); }
+uint16_t orc_encode_f16(double x) { return (uint16_t)encode_rne(x, 5, 10); }
+uint16_t orc_encode_bf16(double x) { return (uint16_t)encode_rne(x, 8, 7); }
+
+/* Bulk helpers used by the Python side. */
+void orc_decode_array(int dtype, int64_t n, const void* src, double* dst)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (dtype == ORC_F32)
+            dst[i] = orc_decode_f32(((const uint32_t*)src)[i]);
+        else if (dtype == ORC_F16)
+            dst[i] = orc_decode_f16(((const uint16_t*)src)[i]);
+        else
+            dst[i] = orc_decode_bf16(((const uint16_t*)src)[i]);
+    }
+}
+
+void orc_encode_array(int dtype, int64_t n, const double* src, void* dst)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (dtype == ORC_F32)
+            ((uint32_t*)dst)[i] = orc_encode_f32(src[i]);
+        else if (dtype == ORC_F16)
+            ((uint16_t*)dst)[i] = orc_encode_f16(src[i]);
+        else
+            ((uint16_t*)dst)[i] = orc_encode_bf16(src[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* GEMM: Y = epi(A * B), A [M][K], B [K][N] row-major, Y [M][N] fp64.      */
+/* ---------------------------------------------------------------------- */
+
+static double relu_f64(double y) { return y > 0.0 ? y : 0.0; /* x <= 0 -> +0 */ }
+
+/* Returns 0 on success, -1 on allocation failure. */
+int orc_gemm_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* A, const void* B,
+                 int relu, double* Y)
+{
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -1;
+    }
+    orc_decode_array(dtype, M * K, A, Ad);
+    orc_decode_array(dtype, K * N, B, Bd);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double* yi = Y + i * N;
+        for (int64_t j = 0; j < N; ++j)
+            yi[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = Ad[i * K + k];
+            const double* bk = Bd + k * N;
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] += a * bk[j];
+        }
+        if (relu)
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] = relu_f64(yi[j]);
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* Selected entries only: out[t] = epi(sum_k A[rows[t]][k] * B[k][cols[t]]).
+ * For checking large outputs one element at a time. */
+void orc_gemm_entries_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* A,
+                          const void* B, int relu, int64_t count, const int64_t* rows,
+                          const int64_t* cols, double* out)
+{
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a, b;
+            if (dtype == ORC_F32) {
+                a = orc_decode_f32(((const uint32_t*)A)[i * K + k]);
+                b = orc_decode_f32(((const uint32_t*)B)[k * N + j]);
+            } else if (dtype == ORC_F16) {
+                a = orc_decode_f16(((const uint16_t*)A)[i * K + k]);
+                b = orc_decode_f16(((const uint16_t*)B)[k * N + j]);
+            } else {
+                a = orc_decode_bf16(((const uint16_t*)A)[i * K + k]);
+                b = orc_decode_bf16(((const uint16_t*)B)[k * N + j]);
+            }
+            s += a * b;
+        }
+        out[t] = relu ? relu_f64(s) : s;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Weight-only 4-bit dequant GEMM.                                         */
+/*   W[n][k] = E2M1(code(n, k)) * E8M0(Ws[n][k / 32])                      */
+/*   code(n, k) = (Wq[n][k / 2] >> (4 * (k % 2))) & 0xF                    */
+/*   Y[m][n] = epi(sum_k A[m][k] * W[n][k]),  A bf16 [M][K]                */
+/* K must be a multiple of 32 (one scale per 32 consecutive k).            */
+/* ---------------------------------------------------------------------- */
+
+static double w4_value(const uint8_t* Wq, const uint8_t* Ws, int64_t K, int64_t n, int64_t k)
+{
+    const uint8_t byte = Wq[n * (K / 2) + k / 2];
+    const uint8_t code = (uint8_t)((byte >> (4 * (k % 2))) & 0xF);
+    return orc_decode_e2m1(code) * orc_decode_e8m0(Ws[n * (K / 32) + k / 32]);
+}
+
+/* Decode the whole weight matrix to fp64 [N][K]. */
+void orc_w4_decode(int64_t N, int64_t K, const uint8_t* Wq, const uint8_t* Ws, double* W)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[n * K + k] = w4_value(Wq, Ws, K, n, k);
+}
+
+int orc_dequant_w4_f64(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint8_t* Wq,
+                       const uint8_t* Ws, int relu, double* Y)
+{
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -1;
+    }
+    orc_decode_array(ORC_BF16, M * K, A, Ad);
+    /* B[k][n] := W[n][k] */
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Bd[k * N + n] = w4_value(Wq, Ws, K, n, k);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double* yi = Y + i * N;
+        for (int64_t j = 0; j < N; ++j)
+            yi[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = Ad[i * K + k];
+            const double* bk = Bd + k * N;
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] += a * bk[j];
+        }
+        if (relu)
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] = relu_f64(yi[j]);
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+void orc_dequant_w4_entries_f64(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                const uint8_t* Wq, const uint8_t* Ws, int relu, int64_t count,
+                                const int64_t* rows, const int64_t* cols, double* out)
+{
+    (void)M;
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += orc_decode_bf16(A[i * K + k]) * w4_value(Wq, Ws, K, j, k);
+        out[t] = relu ? relu_f64(s) : s;
+    }
+}
+
+/* Number of OpenMP threads the oracle runs with (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,472 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each check takes an ``oracle.Oracle`` so the same checks can also be run
+against deliberately broken copies of the oracle (tests/test_oracle_mutants.py)
+to show that a plausible mistake in it is caught.
+
+What pins what:
+  * number codecs: exhaustive comparison with numpy / torch CPU casts, and an
+    exact-rational (fractions.Fraction) round-to-nearest-even written here
+    from the definition of a binary floating-point grid;
+  * E2M1 / E8M0: the OCP MX v1.0 tables under tests/golden/, and torch's
+    float8_e8m0fnu encoding;
+  * GEMM: closed forms (identity, permutation, all ones, rank one, the 2 x 2
+    textbook product) and brute force in exact rational arithmetic;
+  * ReLU: y = max(sum, 0) with +0 for non-positive sums;
+  * dequant GEMM: reductions to row sums, one-hot weights (nibble order and
+    the k/32 scale index), per-group scales, and a weight decode done here from
+    the golden table.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Independent helpers (written here, not taken from the oracle).
+# ---------------------------------------------------------------------------
+
+def rne_fraction(x: Fraction, ebits: int, fbits: int):
+    """Nearest value of a binary floating-point grid, ties to even (exact).
+
+    Returns a Fraction, or +-inf on overflow.
+    """
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    bias = 2 ** (ebits - 1) - 1
+    emin = 1 - bias
+    emax = (2 ** ebits - 2) - bias
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = max(e, emin) - fbits
+    scaled = a / (Fraction(2) ** q)
+    n = math.floor(scaled)
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * Fraction(2) ** q
+    maxval = (2 - Fraction(1, 2 ** fbits)) * Fraction(2) ** emax
+    if val > maxval:
+        return sign * math.inf
+    return sign * val
+
+
+def storage_of(values, dtype: int) -> np.ndarray:
+    """Exactly representable float values -> storage words via numpy / torch casts."""
+    v = np.asarray(values, dtype=np.float64)
+    if dtype == F32:
+        f = v.astype(np.float32)
+        assert np.array_equal(f.astype(np.float64), v), "value not exact in fp32"
+        return f.view(np.uint32)
+    if dtype == F16:
+        h = v.astype(np.float16)
+        assert np.array_equal(h.astype(np.float64), v), "value not exact in fp16"
+        return h.view(np.uint16)
+    import torch
+
+    t = torch.from_numpy(v).to(torch.bfloat16)
+    assert np.array_equal(t.to(torch.float64).numpy(), v), "value not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def exact_product(A, B):
+    """Exact rational A @ B for small float64 matrices."""
+    M, K = A.shape
+    _, N = B.shape
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                s += Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+            out[i][j] = s
+    return out
+
+
+def load_e2m1_golden():
+    tab = {}
+    with open(os.path.join(GOLDEN, "e2m1_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code, val = line.split()
+            tab[int(code)] = float(val)
+    assert sorted(tab) == list(range(16))
+    return tab
+
+
+def load_e8m0_golden():
+    pts = {}
+    with open(os.path.join(GOLDEN, "e8m0_points.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            e, lg = line.split()
+            pts[int(e)] = None if lg == "nan" else int(lg)
+    return pts
+
+
+def decode_w4_here(Wq, Ws):
+    """Test-side weight decode from the golden tables (independent of the oracle)."""
+    tab = load_e2m1_golden()
+    lut = np.array([tab[c] for c in range(16)], dtype=np.float64)
+    Wq = np.asarray(Wq, dtype=np.uint8)
+    N, half = Wq.shape
+    K = 2 * half
+    codes = np.empty((N, K), dtype=np.uint8)
+    codes[:, 0::2] = Wq & 0xF
+    codes[:, 1::2] = Wq >> 4
+    scale = np.ldexp(1.0, np.asarray(Ws, dtype=np.int64) - 127)
+    return lut[codes] * np.repeat(scale, 32, axis=1)
+
+
+def _gemm_both(orc, A, B, dtype, relu=False):
+    """Full-matrix and entry-by-entry oracle results (both must pass every pin)."""
+    Y = orc.gemm_f64(A, B, dtype, relu)
+    M, N = Y.shape
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Ye = orc.gemm_entries_f64(A, B, dtype, rr.ravel(), cc.ravel(), relu).reshape(M, N)
+    return Y, Ye
+
+
+def _dq_both(orc, A, Wq, Ws, relu=False):
+    Y = orc.dequant_w4_f64(A, Wq, Ws, relu)
+    M, N = Y.shape
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Ye = orc.dequant_w4_entries_f64(A, Wq, Ws, rr.ravel(), cc.ravel(), relu).reshape(M, N)
+    return Y, Ye
+
+
+def _same(x, y):
+    """Bitwise equality of float64 arrays (distinguishes +0 and -0)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    return x.shape == y.shape and np.array_equal(x.view(np.uint64), y.view(np.uint64))
+
+
+# ---------------------------------------------------------------------------
+# Codec pins.
+# ---------------------------------------------------------------------------
+
+def check_decode_f16_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.decode(F16, bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert _same(got[~nan], ref[~nan])
+
+
+def check_decode_bf16_exhaustive(orc):
+    import torch
+
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.decode(BF16, bits)
+    # bf16 is the upper half of a binary32 word
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref_t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert _same(got[~nan], ref[~nan])
+    assert _same(ref_t[~nan], ref[~nan])
+
+
+def check_decode_f32_sample(orc):
+    r = np.random.Generator(np.random.PCG64(11))
+    bits = r.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    bits[:8] = [0, 0x80000000, 1, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0x7F800000, 0xFF800000]
+    got = orc.decode(F32, bits)
+    ref = bits.view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert _same(got[~nan], ref[~nan])
+
+
+def _random_doubles(seed, n):
+    r = np.random.Generator(np.random.PCG64(seed))
+    x = r.standard_normal(n) * np.exp2(r.integers(-40, 40, size=n))
+    return x
+
+
+def check_encode_f16(orc):
+    x = np.concatenate([
+        _random_doubles(1, 100000) * 1e-3,
+        np.random.Generator(np.random.PCG64(2)).standard_normal(100000) * 3e4,  # overflow side
+        np.random.Generator(np.random.PCG64(3)).standard_normal(100000) * 1e-6,  # subnormals
+    ])
+    # constructed ties: midpoints between neighbouring fp16 values
+    h = np.arange(0, 0x7BFF, 7, dtype=np.uint16).view(np.float16).astype(np.float64)
+    h2 = (np.arange(0, 0x7BFF, 7, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
+    x = np.concatenate([x, (h + h2) / 2, -(h + h2) / 2, [65504.0, 65519.99, 65520.0, 1e9, -1e9]])
+    got = orc.encode(F16, x).view(np.float16).astype(np.float64)
+    ref = x.astype(np.float16).astype(np.float64)  # numpy rounds float64 -> float16 once
+    assert _same(got, ref)
+
+
+def check_encode_f32(orc):
+    x = np.concatenate([_random_doubles(4, 200000),
+                        np.random.Generator(np.random.PCG64(5)).standard_normal(1000) * 1e-40,
+                        [3.5e38, 3.4028235677973366e38, 1e39, -1e39]])
+    got = orc.encode(F32, x).view(np.float32).astype(np.float64)
+    ref = x.astype(np.float32).astype(np.float64)
+    assert _same(got, ref)
+
+
+def check_encode_bf16_from_f32(orc):
+    import torch
+
+    r = np.random.Generator(np.random.PCG64(6))
+    f = r.standard_normal(200000).astype(np.float32)
+    # constructed ties: exactly halfway between two bf16 neighbours
+    hi = r.integers(0, 0x7F00, size=20000).astype(np.uint32) << 16
+    ties = (hi | 0x8000).view(np.float32)
+    f = np.concatenate([f, ties, -ties, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8], np.float32)])
+    got = orc.encode(BF16, f.astype(np.float64))
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    # worked ties: 1 + 2^-8 -> 1.0 (even), 1 + 3*2^-8 -> 1 + 2^-6
+    assert got[-2] == 0x3F80 and got[-1] == 0x3F82
+
+
+def check_encode_exact_rational(orc):
+    """Direct fp64 -> fp16 / bf16 / fp32 rounding against Fraction RNE (single rounding)."""
+    x = _random_doubles(7, 1500)
+    x = np.concatenate([x, [0.0, -0.0, 2.0 ** -140, 6e-8, -6e-8, 2.0 ** -25, 2.0 ** -24 * 1.5]])
+    for dtype, eb, fb in ((F16, 5, 10), (BF16, 8, 7), (F32, 8, 23)):
+        got = orc.decode(dtype, orc.encode(dtype, x))
+        for xi, gi in zip(x, got):
+            ref = rne_fraction(Fraction(float(xi)), eb, fb)
+            if isinstance(ref, float):  # inf
+                assert gi == ref, (dtype, xi, gi)
+            else:
+                assert Fraction(float(gi)) == ref, (dtype, xi, gi, ref)
+
+
+def check_e2m1_table(orc):
+    tab = load_e2m1_golden()
+    for code, val in tab.items():
+        got = orc.decode_e2m1(code)
+        assert got == val and math.copysign(1.0, got) == math.copysign(1.0, val), (code, got)
+
+
+def check_e8m0(orc):
+    import torch
+
+    for e, lg in load_e8m0_golden().items():
+        got = orc.decode_e8m0(e)
+        if lg is None:
+            assert math.isnan(got)
+        else:
+            assert got == math.ldexp(1.0, lg), (e, got)
+    # torch's float8_e8m0fnu encodes powers of two to the same byte
+    for e in range(0, 255):
+        v = orc.decode_e8m0(e)
+        b = torch.tensor([v], dtype=torch.float32).to(torch.float8_e8m0fnu).view(torch.uint8)
+        assert int(b.item()) == e, (e, v)
+
+
+# ---------------------------------------------------------------------------
+# GEMM pins.
+# ---------------------------------------------------------------------------
+
+def check_textbook_2x2(orc):
+    for dtype in (F32, F16, BF16):
+        A = storage_of([[1, 2], [3, 4]], dtype)
+        B = storage_of([[5, 6], [7, 8]], dtype)
+        for Y in _gemm_both(orc, A, B, dtype):
+            assert _same(Y, [[19, 22], [43, 50]])
+
+
+def check_identity(orc):
+    r = np.random.Generator(np.random.PCG64(21))
+    for dtype in (F32, F16, BF16):
+        K, N = 24, 17
+        Bv = r.integers(-100, 101, size=(K, N)) / 8.0
+        B = storage_of(Bv, dtype)
+        A = storage_of(np.eye(K), dtype)
+        for Y in _gemm_both(orc, A, B, dtype):
+            assert _same(Y + 0.0, Bv + 0.0)
+
+
+def check_permutation(orc):
+    r = np.random.Generator(np.random.PCG64(22))
+    for dtype in (F32, BF16):
+        K, N = 19, 13
+        perm = r.permutation(K)
+        P = np.zeros((K, K))
+        P[np.arange(K), perm] = 1.0
+        Bv = r.integers(-50, 51, size=(K, N)).astype(np.float64)
+        for Y in _gemm_both(orc, storage_of(P, dtype), storage_of(Bv, dtype), dtype):
+            assert _same(Y + 0.0, Bv[perm] + 0.0)
+
+
+def check_all_ones(orc):
+    for dtype in (F32, F16, BF16):
+        for (M, N, K) in ((3, 5, 7), (1, 1, 1), (9, 4, 33)):
+            A = storage_of(np.ones((M, K)), dtype)
+            B = storage_of(np.ones((K, N)), dtype)
+            for Y in _gemm_both(orc, A, B, dtype):
+                assert _same(Y, np.full((M, N), float(K)))
+
+
+def check_rank_one(orc):
+    # A[m, k] = u_m * a_k, B[k, n] = b_k * v_n  ->  C = (a . b) u_m v_n.
+    # Non-symmetric vectors: a transposed operand or a wrong index changes it.
+    u = np.array([1, -2, 3, 0, 5, -1, 2], dtype=np.float64)
+    a = np.array([2, 1, -3, 4, 1, -1, 3, 2, -2, 1, 1], dtype=np.float64)
+    b = np.array([1, 3, 2, -1, 2, 2, -3, 1, 1, -2, 4], dtype=np.float64)
+    v = np.array([3, -1, 2, 1, -2, 4, 1, 1, 2], dtype=np.float64)
+    ab = float(a @ b)
+    ref = ab * np.outer(u, v)
+    for dtype in (F32, F16, BF16):
+        A = storage_of(np.outer(u, a), dtype)
+        B = storage_of(np.outer(b, v), dtype)
+        for Y in _gemm_both(orc, A, B, dtype):
+            assert _same(Y + 0.0, ref + 0.0)
+
+
+def check_brute_force_dyadic(orc):
+    r = np.random.Generator(np.random.PCG64(23))
+    for trial in range(60):
+        M, N, K = (int(x) for x in r.integers(1, 9, size=3))
+        dtype = (F32, F16, BF16)[trial % 3]
+        Av = r.integers(-64, 65, size=(M, K)) * np.exp2(r.integers(-6, 1, size=(M, K)))
+        Bv = r.integers(-64, 65, size=(K, N)) * np.exp2(r.integers(-6, 1, size=(K, N)))
+        ex = exact_product(Av, Bv)
+        for relu in (False, True):
+            for Y in _gemm_both(orc, storage_of(Av, dtype), storage_of(Bv, dtype), dtype, relu):
+                for i in range(M):
+                    for j in range(N):
+                        want = ex[i][j]
+                        if relu:
+                            want = max(want, Fraction(0))
+                        assert Fraction(float(Y[i, j])) == want, (M, N, K, i, j)
+
+
+def check_brute_force_general(orc):
+    """General fp32 inputs: the fp64 sum is within the standard accumulation bound."""
+    r = np.random.Generator(np.random.PCG64(24))
+    for _ in range(20):
+        M, N, K = (int(x) for x in r.integers(1, 9, size=3))
+        Af = r.standard_normal((M, K)).astype(np.float32)
+        Bf = r.standard_normal((K, N)).astype(np.float32)
+        ex = exact_product(Af.astype(np.float64), Bf.astype(np.float64))
+        for Y in _gemm_both(orc, Af.view(np.uint32), Bf.view(np.uint32), F32):
+            for i in range(M):
+                for j in range(N):
+                    mag = sum(abs(float(Af[i, k]) * float(Bf[k, j])) for k in range(K))
+                    err = abs(Fraction(float(Y[i, j])) - ex[i][j])
+                    assert err <= Fraction(K + 1) * Fraction(1, 2 ** 52) * Fraction(mag)
+
+
+def check_relu(orc):
+    r = np.random.Generator(np.random.PCG64(25))
+    M, N, K = 7, 9, 5
+    Av = r.integers(-4, 5, size=(M, K)).astype(np.float64)
+    Bv = r.integers(-4, 5, size=(K, N)).astype(np.float64)
+    for dtype in (F32, BF16):
+        A, B = storage_of(Av, dtype), storage_of(Bv, dtype)
+        Y0 = orc.gemm_f64(A, B, dtype, False)
+        for Y in _gemm_both(orc, A, B, dtype, True):
+            assert np.all(Y >= 0) and not np.any(np.signbit(Y))
+            assert _same(Y, np.where(Y0 > 0, Y0, 0.0))
+        assert np.any(Y0 < 0) and np.any(Y0 > 0)
+
+
+def check_round_outputs(orc):
+    """Integer sums below 2^24 encode exactly; fp16 overflow goes to inf."""
+    y = np.array([0.0, 1.0, -3.0, 16384.0, 65504.0, 65520.0, 2.0 ** 23 + 1, -(2.0 ** 24)])
+    assert np.array_equal(orc.decode(F32, orc.encode(F32, y)), y)
+    f16 = orc.decode(F16, orc.encode(F16, y))
+    assert f16[4] == 65504.0 and math.isinf(f16[5])
+    assert np.array_equal(f16[:4], y[:4])
+
+
+# ---------------------------------------------------------------------------
+# Dequant GEMM pins.
+# ---------------------------------------------------------------------------
+
+def _bf16_ints(r, shape, lo=-4, hi=4):
+    v = r.integers(lo, hi + 1, size=shape).astype(np.float64)
+    return v, storage_of(v, BF16)
+
+
+def check_dequant_row_sums(orc):
+    r = np.random.Generator(np.random.PCG64(31))
+    M, N, K = 5, 6, 64
+    Av, A = _bf16_ints(r, (M, K))
+    Wq = np.full((N, K // 2), 0x22, dtype=np.uint8)  # every code is 2 -> 1.0
+    Ws = np.full((N, K // 32), 127, dtype=np.uint8)  # every scale 2^0
+    for Y in _dq_both(orc, A, Wq, Ws):
+        assert _same(Y + 0.0, np.repeat(Av.sum(axis=1, keepdims=True), N, axis=1) + 0.0)
+
+
+def check_dequant_one_hot(orc):
+    r = np.random.Generator(np.random.PCG64(32))
+    tab = load_e2m1_golden()
+    M, N, K = 4, 5, 96
+    Av, A = _bf16_ints(r, (M, K))
+    for (n0, k0, code, e) in ((0, 0, 7, 127), (1, 1, 3, 125), (2, 33, 13, 126),
+                              (4, 95, 5, 123), (3, 64, 9, 130), (2, 62, 15, 124)):
+        Wq = np.zeros((N, K // 2), dtype=np.uint8)
+        Wq[n0, k0 // 2] = code << (4 * (k0 % 2))
+        Ws = np.full((N, K // 32), 127, dtype=np.uint8)
+        Ws[n0, k0 // 32] = e
+        want = np.zeros((M, N))
+        want[:, n0] = Av[:, k0] * tab[code] * 2.0 ** (e - 127)
+        for Y in _dq_both(orc, A, Wq, Ws):
+            assert _same(Y + 0.0, want + 0.0), (n0, k0, code, e)
+
+
+def check_dequant_group_scales(orc):
+    r = np.random.Generator(np.random.PCG64(33))
+    M, N, K = 3, 4, 128
+    Av, A = _bf16_ints(r, (M, K))
+    Wq = np.full((N, K // 2), 0x44, dtype=np.uint8)  # every code 4 -> 2.0
+    Ws = r.integers(120, 131, size=(N, K // 32)).astype(np.uint8)
+    gsum = Av.reshape(M, K // 32, 32).sum(axis=2)  # [M, groups]
+    want = 2.0 * gsum @ np.ldexp(1.0, Ws.astype(np.int64) - 127).T
+    for Y in _dq_both(orc, A, Wq, Ws):
+        assert _same(Y + 0.0, want + 0.0)
+
+
+def check_dequant_random_vs_decoded(orc):
+    r = np.random.Generator(np.random.PCG64(34))
+    M, N, K = 6, 10, 96
+    Av, A = _bf16_ints(r, (M, K))
+    Wq = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    Ws = (127 + r.integers(-4, 1, size=(N, K // 32))).astype(np.uint8)
+    W = decode_w4_here(Wq, Ws)
+    assert _same(orc.w4_decode(Wq, Ws) + 0.0, W + 0.0)
+    ex = exact_product(Av, W.T)
+    for relu in (False, True):
+        for Y in _dq_both(orc, A, Wq, Ws, relu):
+            for i in range(M):
+                for j in range(N):
+                    want = max(ex[i][j], Fraction(0)) if relu else ex[i][j]
+                    assert Fraction(float(Y[i, j])) == want
+
+
+ALL_CHECKS = [
+    check_decode_f16_exhaustive, check_decode_bf16_exhaustive, check_decode_f32_sample,
+    check_encode_f16, check_encode_f32, check_encode_bf16_from_f32, check_encode_exact_rational,
+    check_e2m1_table, check_e8m0, check_textbook_2x2, check_identity, check_permutation,
+    check_all_ones, check_rank_one, check_brute_force_dyadic, check_brute_force_general,
+    check_relu, check_round_outputs, check_dequant_row_sums, check_dequant_one_hot,
+    check_dequant_group_scales, check_dequant_random_vs_decoded,
+]

@@ -1,0 +1,59 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one: a dropped term, a wrong sign, a transposed operand, a
+wrong index, a swapped nibble order, a wrong scale index, ties rounded away from
+even, a lost ReLU or its sign of zero, and wrong special-value handling."""
+
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (name, exact text in oracle.c, replacement, which occurrence (0-based))
+MUTANTS = [
+    ("gemm_drops_last_k", "yi[j] += a * bk[j];", "yi[j] += a * bk[j] * (k + 1 < K);", 0),
+    ("gemm_wrong_sign", "yi[j] += a * bk[j];", "yi[j] -= a * bk[j];", 0),
+    ("gemm_transposed_a", "const double a = Ad[i * K + k];", "const double a = Ad[k * M + i];", 0),
+    ("dequant_transposed_a", "const double a = Ad[i * K + k];", "const double a = Ad[k * M + i];", 1),
+    ("entries_drop_first_k", "s += a * b;", "s += a * b * (k > 0);", 0),
+    ("entries_wrong_col_bf16", "b = orc_decode_bf16(((const uint16_t*)B)[k * N + j]);",
+     "b = orc_decode_bf16(((const uint16_t*)B)[k * N + (N - 1 - j)]);", 0),
+    ("gemm_relu_lost", "yi[j] = relu_f64(yi[j]);", "yi[j] = yi[j];", 0),
+    ("relu_negative_zero", "return y > 0.0 ? y : 0.0;", "return y > 0.0 ? y : -0.0;", 0),
+    ("dequant_drops_last_k", "yi[j] += a * bk[j];", "yi[j] += a * bk[j] * (k + 1 < K);", 1),
+    ("nibble_order_swapped", "(4 * (k % 2))", "(4 * (1 - k % 2))", 1),
+    ("scale_index_wrong", "Ws[n * (K / 32) + k / 32]", "Ws[n * (K / 32) + (k / 32 + 1) % (K / 32)]", 0),
+    ("ties_away_from_even", "(rem == half && (n & 1ull))", "(rem == half)", 0),
+    ("overflow_off_by_one", "if (efield >= emax_field)", "if (efield > emax_field)", 0),
+    ("e2m1_has_specials", "decode_bits(code & 0xFu, 2, 1, 0)", "decode_bits(code & 0xFu, 2, 1, 1)", 0),
+    ("subnormal_exponent", "v = ldexp((double)f, 1 - bias - fbits);", "v = ldexp((double)f, -bias - fbits);", 0),
+    ("e8m0_bias", "ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)", 0),
+]
+
+
+def _mutate(text, old, new, occurrence):
+    pos = -1
+    for _ in range(occurrence + 1):
+        pos = text.find(old, pos + 1)
+        assert pos >= 0, "mutation target not found: %r" % old
+    return text[:pos] + new + text[pos + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new, occ):
+    src = open(oracle.SRC).read()
+    bad = _mutate(src, old, new, occ)
+    assert bad != src
+    csrc = tmp_path / "oracle_mutant.c"
+    csrc.write_text(bad)
+    lib = oracle.build(force=True, src=str(csrc), out=str(tmp_path / "liboracle_mutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, "no pin caught mutant %s" % name

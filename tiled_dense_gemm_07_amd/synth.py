@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the GEMM and dequant-GEMM workloads.
+
+This module only draws random numbers and stores them in the operand formats.
+It holds none of the GEMM arithmetic: the tests and the benchmark feed the same
+arrays to the HIP library and to the CPU oracle, and neither side imports the
+other.
+
+The pages benchmark on random matrices only (``torch.randn`` inputs in the
+mhpq.cn page, section 3.2; ``assert_close`` checks in the blog.hotdry.top
+page), so every workload here is synthetic:
+
+* floating inputs: numpy ``Generator(PCG64(seed)).standard_normal`` in float64,
+  rounded to float32, then rounded (nearest-even) to the operand type;
+* integer inputs: uniform on {-4, ..., 4}, exact in every operand type;
+* 4-bit weights: uniform bytes (so both nibbles are uniform on 0..15),
+  E8M0 scale bytes 127 + uniform{-4..0}, i.e. scales 2^-4 .. 2^0.
+
+Seeds: ``20260000 + 100 * workload_index + {0: A, 1: B, 2: codes, 3: scales}``,
+plus 50 for the integer-valued run.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+STORAGE = {F32: np.uint32, F16: np.uint16, BF16: np.uint16}
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal_f32(shape, seed: int) -> np.ndarray:
+    """N(0, 1) draws rounded to float32."""
+    return rng(seed).standard_normal(shape).astype(np.float32)
+
+
+def integers_f32(shape, seed: int, lo: int = -4, hi: int = 4) -> np.ndarray:
+    """Uniform integers in [lo, hi] stored as float32 (exact)."""
+    return rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
+    """float32 values -> raw storage words of the operand type (round to nearest even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F32:
+        return x.view(np.uint32).copy()
+    if dtype == F16:
+        return x.astype(np.float16).view(np.uint16).copy()
+    if dtype == BF16:
+        import torch  # CPU cast only
+
+        t = torch.from_numpy(x).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError("unknown dtype %r" % (dtype,))
+
+
+def w4_codes(N: int, K: int, seed: int) -> np.ndarray:
+    """Packed E2M1 codes [N, K/2]: two uniform 4-bit codes per byte."""
+    return rng(seed).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+
+
+def w4_scales(N: int, K: int, seed: int, emin: int = -4, emax: int = 0) -> np.ndarray:
+    """E8M0 scale bytes [N, K/32] for scales 2^emin .. 2^emax (uniform exponent)."""
+    e = rng(seed).integers(emin, emax + 1, size=(N, K // 32))
+    return (127 + e).astype(np.uint8)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One of the workload shapes; `index` keys the seeds."""
+
+    name: str
+    index: int
+    op: str  # "gemm" or "dequant_w4"
+    dtype: int
+    M: int
+    N: int
+    K: int
+    relu: bool
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self) -> int:
+        """Read every operand once and write C once."""
+        if self.op == "gemm":
+            es = 4 if self.dtype == F32 else 2
+            return es * (self.M * self.K + self.K * self.N + self.M * self.N)
+        return 2 * self.M * self.K + self.N * self.K // 2 + self.N * self.K // 32 + 2 * self.M * self.N
+
+
+WORKLOADS = {
+    "f32_512": Workload("f32_512", 1, "gemm", F32, 512, 512, 512, False),
+    "f16_1024": Workload("f16_1024", 2, "gemm", F16, 1024, 1024, 1024, False),
+    "f32_4096": Workload("f32_4096", 3, "gemm", F32, 4096, 4096, 4096, False),
+    "bf16_4096_relu": Workload("bf16_4096_relu", 4, "gemm", BF16, 4096, 4096, 4096, True),
+    "bf16_4000x4032x4096_relu": Workload("bf16_4000x4032x4096_relu", 4, "gemm", BF16,
+                                         4000, 4032, 4096, True),
+    "w4_256x8192x8192": Workload("w4_256x8192x8192", 5, "dequant_w4", BF16, 256, 8192, 8192,
+                                 False),
+    # memory-bound probes of the same dequant entry (decode-like M)
+    "w4_1x8192x8192": Workload("w4_1x8192x8192", 6, "dequant_w4", BF16, 1, 8192, 8192, False),
+    "w4_16x8192x8192": Workload("w4_16x8192x8192", 7, "dequant_w4", BF16, 16, 8192, 8192, False),
+}
+
+
+def seeds(w: Workload, integer: bool = False) -> dict:
+    base = 20260000 + 100 * w.index + (50 if integer else 0)
+    return {"A": base + 0, "B": base + 1, "codes": base + 2, "scales": base + 3}
+
+
+def gemm_inputs(M: int, N: int, K: int, dtype: int, seed_a: int, seed_b: int,
+                integer: bool = False):
+    """Row-major A [M, K] and B [K, N] as storage words."""
+    draw = integers_f32 if integer else normal_f32
+    A = to_storage(draw((M, K), seed_a), dtype)
+    B = to_storage(draw((K, N), seed_b), dtype)
+    return A, B
+
+
+def dequant_inputs(M: int, N: int, K: int, seed_a: int, seed_codes: int, seed_scales: int,
+                   integer: bool = False):
+    """bf16 activations [M, K], packed codes [N, K/2], scale bytes [N, K/32]."""
+    draw = integers_f32 if integer else normal_f32
+    A = to_storage(draw((M, K), seed_a), BF16)
+    return A, w4_codes(N, K, seed_codes), w4_scales(N, K, seed_scales)
+
+
+def make_inputs(w: Workload, integer: bool = False) -> dict:
+    s = seeds(w, integer)
+    if w.op == "gemm":
+        A, B = gemm_inputs(w.M, w.N, w.K, w.dtype, s["A"], s["B"], integer)
+        return {"A": A, "B": B, "seeds": s}
+    A, Wq, Ws = dequant_inputs(w.M, w.N, w.K, s["A"], s["codes"], s["scales"], integer)
+    return {"A": A, "Wq": Wq, "Ws": Ws, "seeds": s}
