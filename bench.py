@@ -1,0 +1,244 @@
+"""Benchmark: tiled GEMM TFLOP/s on one MI355X, with roofline and CPU baseline.
+
+A step is one call of the library's GEMM on the bf16 4096 x 4096 x 4096 workload
+with the fused ReLU epilogue (row-major A and B, N(0,1) entries cast to bf16,
+fp32 accumulation, bf16 output), inputs already resident in HBM.  W untimed
+warm-up steps, then K timed steps between a synchronize on each side.
+
+Printed: ONE JSON line (rank 0) with
+  value       whole-job TFLOP/s = 2 M N K * K_steps / elapsed,
+  roofline    the kernel's average duration from HIP events recorded on the
+              stream it runs on, against the bf16 dense MFMA peak,
+  cpu_baseline the C oracle timed on host cores on a bounded row sample,
+  workloads   the other workload shapes (fp32 / fp16 GEMMs, the non-divisible
+              bf16 GEMM, the 4-bit dequant GEMM and its decode-like probes),
+              each timed the same way.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (4096³ bf16/fp32, 1 GPU)"
+# MI355X dense matrix peaks (256 CUs at 2.4 GHz): bf16/fp16 4096 FLOP/clk/CU,
+# fp32 256 FLOP/clk/CU; HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "bf16_4096_relu"
+OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x8192x8192",
+         "w4_16x8192x8192", "w4_1x8192x8192"]
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: counter files are valid only for this kernel code."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "tiled_dense_gemm_07_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec
+
+
+def make_device_inputs(w, dev):
+    import numpy as np
+    import torch
+
+    from tiled_dense_gemm_07_amd import synth
+
+    inp = synth.make_inputs(w, integer=False)
+    tdt = {synth.F32: torch.float32, synth.F16: torch.float16, synth.BF16: torch.bfloat16}
+    if w.op == "gemm":
+        view = np.int32 if w.dtype == synth.F32 else np.int16
+        A = torch.from_numpy(inp["A"].view(view)).view(tdt[w.dtype]).to(dev)
+        B = torch.from_numpy(inp["B"].view(view)).view(tdt[w.dtype]).to(dev)
+        C = torch.empty((w.M, w.N), dtype=tdt[w.dtype], device=dev)
+        return inp, (A, B, C)
+    A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+    Wq = torch.from_numpy(inp["Wq"]).to(dev)
+    Ws = torch.from_numpy(inp["Ws"]).to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    return inp, (A, Wq, Ws, C)
+
+
+def launcher(w, tensors, stream):
+    from tiled_dense_gemm_07_amd import binding
+
+    epi = "relu" if w.relu else None
+    if w.op == "gemm":
+        A, B, C = tensors
+        return lambda: binding.gemm(A, B, C=C, epilogue=epi, stream=stream)
+    A, Wq, Ws, C = tensors
+    return lambda: binding.dequant_gemm_w4(A, Wq, Ws, C=C, epilogue=epi, stream=stream)
+
+
+def time_kernel(fn, stream, launches: int, warmup: int):
+    """Average kernel duration (ms) from HIP event pairs around each launch,
+    recorded on the stream the kernel runs on."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    stream.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    stream.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0],
+            "max_ms": ts[-1]}
+
+
+def dtype_name(w):
+    from tiled_dense_gemm_07_amd import synth
+
+    return {synth.F32: "f32", synth.F16: "f16", synth.BF16: "bf16"}[w.dtype]
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0):
+    """The oracle, as it stands, on the first R rows of C; R grows until one
+    call takes a good part of the budget."""
+    import numpy as np
+
+    import oracle
+
+    A, B = inp["A"], inp["B"]
+    rows = 4
+    elapsed = 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_f64(np.ascontiguousarray(A[:rows]), B, w.dtype, w.relu)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s / 4 or rows >= w.M:
+            break
+        rows = min(w.M, max(rows * 2, int(rows * (budget_s / 4) / max(elapsed, 1e-3))))
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "rows 0..%d of C = A @ B for the %s workload (%d x %d x %d fp64 sums, "
+                      "%.1f s)" % (rows - 1, w.name, rows, w.N, w.K, elapsed),
+            "seconds": elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tiled_dense_gemm_07_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    w = synth.WORKLOADS[HEADLINE]
+    inp, tensors = make_device_inputs(w, dev)
+    fn = launcher(w, tensors, stream)
+
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    # timed region: exactly K steps
+    t0 = time.perf_counter()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    end_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record(stream)
+    for _ in range(args.steps):
+        fn()
+    end_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops * args.steps / wall / 1e12
+
+    # per-launch kernel duration from HIP events on the kernel's stream
+    kt = time_kernel(fn, stream, launches=args.steps, warmup=2)
+    achieved = w.flops / (kt["mean_ms"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype_name(w)]
+    traffic = load_traffic(HEADLINE)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                "kernel_ms": round(kt["mean_ms"], 5),
+                "events_span_ms_per_step": round(start_ev.elapsed_time(end_ev) / args.steps, 5),
+                "algorithmic_flops_per_launch": w.flops,
+                "algorithmic_bytes_per_launch": w.algorithmic_bytes()}
+
+    workloads = {}
+    if not args.no_workloads:
+        for name in OTHER:
+            ow = synth.WORKLOADS[name]
+            _, t = make_device_inputs(ow, dev)
+            r = time_kernel(launcher(ow, t, stream), stream, launches=30, warmup=5)
+            tf = ow.flops / (r["mean_ms"] * 1e-3) / 1e12
+            gbs = ow.algorithmic_bytes() / (r["mean_ms"] * 1e-3) / 1e9
+            dn = dtype_name(ow)
+            workloads[name] = {
+                "kernel_ms": round(r["mean_ms"], 5), "tflops": round(tf, 2),
+                "frac_mfma_peak": round(tf / PEAK_TFLOPS[dn], 4),
+                "gbs_algorithmic": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "config": binding.query_config(0 if ow.op == "gemm" else 1, ow.M, ow.N, ow.K,
+                                               ow.dtype)}
+            del t
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "M": w.M, "N": w.N, "K": w.K, "epilogue": "relu",
+                   "layout": "row-major A[M,K], B[K,N]",
+                   "kernel": binding.query_config(0, w.M, w.N, w.K, w.dtype)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

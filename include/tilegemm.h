@@ -1,0 +1,147 @@
+/*
+ * tilegemm — tiled dense GEMM and weight-only 4-bit dequant GEMM for one
+ * AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ *
+ * The operation follows the pages' problem statement:
+ *   - "TileLang ... 一个高效 GEMM 内核" (mhpq.cn), section 3.2: the caller
+ *     allocates A (M x K), B (K x N) and C (M x N) on the device and launches
+ *     kernel(A, B, C); the result is C = A x B.  Section 3.4 checks that the
+ *     inner dimensions agree before launching.
+ *   - "TileLang：用Python DSL简化GPU算子开发" (gtnt.cn), section 4.3: operands
+ *     are row-major unless stated otherwise; mixed precision needs an explicit
+ *     cast.
+ *   - "使用 Tilelang DSL 开发 GPU/CPU/加速器高性能内核" (blog.hotdry.top): an
+ *     elementwise post-processing loop (ReLU) on the output tile, and the
+ *     weight-only low-bit "Dequant GEMM" as a target workload.
+ *
+ * Conventions shared by every entry point:
+ *   - All matrix pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises, and keeps no per-call state.
+ *   - Dense row-major storage with implied leading dimensions
+ *     (lda = K, ldb = N, ldc = N; packed weights: K/2 bytes per row).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream): they return
+ *     once the kernel is enqueued.  Thread-safe.
+ *   - Arguments are validated before any HIP call; on a non-OK status nothing
+ *     has been launched and C is untouched.
+ *   - M == 0 or N == 0: TG_OK, nothing launched (all pointers may be NULL).
+ *     K == 0: C = epilogue(0) = 0; the operand pointers may be NULL then.
+ *   - Accumulation is always fp32; the output is rounded to its type once,
+ *     round-to-nearest-even (fp32 -> fp16 overflow gives +-inf).
+ *   - Each operand must fit a 31-bit byte offset per tile row band: the library
+ *     returns TG_ERR_BAD_SHAPE when 256 * K * element_size or
+ *     64 * N * element_size exceeds 2^31 - 1 (and for M, N, K above 2^31 - 1).
+ */
+#ifndef TILEGEMM_H
+#define TILEGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* tg_stream_t; /* same object as hipStream_t */
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
+    TG_ERR_BAD_SHAPE = 2,    /* negative / too large size, or dequant K % 32 != 0 */
+    TG_ERR_BAD_DTYPE = 3,    /* dtype not one of tg_dtype                         */
+    TG_ERR_BAD_EPILOGUE = 4, /* epilogue not one of tg_epilogue                   */
+    TG_ERR_ALIAS = 5,        /* C overlaps an input                               */
+    TG_ERR_NO_CONFIG = 6,    /* forced config index out of range / wrong op       */
+    TG_ERR_HIP = 7           /* the HIP runtime reported an error at launch       */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
+
+typedef enum { TG_EPI_NONE = 0, TG_EPI_RELU = 1 } tg_epilogue;
+
+typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1 } tg_op;
+
+/*
+ * C = epilogue(A x B).
+ *   A: [M][K] row-major, B: [K][N] row-major, C: [M][N] row-major, all of
+ *   `dtype` (fp32, fp16 or bf16); products accumulate in fp32 on the matrix
+ *   cores; TG_EPI_RELU maps every accumulated value v to (v > 0 ? v : +0)
+ *   before the single rounding to `dtype`.
+ *   Non-multiple-of-tile shapes are handled inside the kernel (out-of-range
+ *   rows and columns are never read into the sum nor written).
+ * Errors: TG_ERR_NULL_POINTER (C NULL with M, N > 0, or A or B NULL with
+ *   M, N, K > 0), TG_ERR_BAD_SHAPE,
+ *   TG_ERR_BAD_DTYPE, TG_ERR_BAD_EPILOGUE, TG_ERR_ALIAS (C's bytes overlap A's
+ *   or B's), TG_ERR_HIP.
+ */
+tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, const void* B,
+                  void* C, tg_epilogue epi, tg_stream_t stream);
+
+/*
+ * Weight-only 4-bit dequant GEMM: C = epilogue(A x W^T).
+ *   A : bf16 [M][K] row-major activations.
+ *   Wq: uint8 [N][K/2]: weight row n holds its K E2M1 codes (OCP MX v1.0 FP4:
+ *       sign, 2-bit exponent with bias 1, 1-bit mantissa) two per byte, even k
+ *       in bits 3:0 and odd k in bits 7:4.
+ *   Ws: uint8 [N][K/32]: one E8M0 scale byte E per 32 consecutive k of a row,
+ *       scale 2^(E - 127).
+ *   W[n][k] = e2m1(code(n, k)) * 2^(Ws[n][k/32] - 127); C[m][n] = sum_k A[m][k] * W[n][k].
+ *   C : bf16 [M][N].  The weights are expanded to bf16 on chip (exact for
+ *       E in [2, 252]; other scale bytes follow the hardware conversion) and
+ *       multiplied on the bf16 matrix cores with fp32 accumulation.
+ *   The pages name this workload ("WFP4" GEMM, "Dequant GEMM") but not its
+ *   format; the format above is the workload statement's.
+ * Errors: as tg_gemm; TG_ERR_BAD_SHAPE also when K % 32 != 0.
+ */
+tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, const uint8_t* Wq,
+                             const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* tg_status_str(tg_status s);
+
+/*
+ * Which compiled kernel configuration the library would launch for this call.
+ * Writes a NUL-terminated description (tile sizes, waves, stages, swizzle
+ * group, launch grid) into buf[0 .. len-1], truncating if needed.
+ * op: TG_OP_GEMM or TG_OP_DEQUANT_W4 (dtype is ignored for the latter).
+ * Errors: TG_ERR_NULL_POINTER (buf NULL or len 0), TG_ERR_BAD_SHAPE,
+ *   TG_ERR_BAD_DTYPE, TG_ERR_NO_CONFIG (op unknown).
+ */
+tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
+                          size_t len);
+
+/*
+ * Offline sweep support: the compiled configurations, listed per (op, dtype),
+ * can be launched by index instead of by the built-in selection table.
+ *   tg_config_count: number of configurations for (op, dtype); 0 if none.
+ *   tg_config_name : description of configuration `index` (as tg_query_config).
+ *   tg_gemm_config / tg_dequant_gemm_w4_config: same contract as tg_gemm /
+ *     tg_dequant_gemm_w4, launching configuration `index`;
+ *     TG_ERR_NO_CONFIG if `index` is out of range.
+ */
+int tg_config_count(int op, tg_dtype dtype);
+tg_status tg_config_name(int op, tg_dtype dtype, int index, char* buf, size_t len);
+tg_status tg_gemm_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                         const void* A, const void* B, void* C, tg_epilogue epi,
+                         tg_stream_t stream);
+tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, const void* A,
+                                    const uint8_t* Wq, const uint8_t* Ws, void* C,
+                                    tg_epilogue epi, tg_stream_t stream);
+
+/*
+ * The block-swizzled tile order, for host-side checking.  For a grid of
+ * tiles_m x tiles_n output tiles and a swizzle group of `group_m` tile rows,
+ * writes for every workgroup id w in [0, tiles_m * tiles_n) the tile it
+ * computes: out_m[w], out_n[w].  Workgroup ids are first regrouped so that
+ * the ids the hardware dispatches to one XCD (w mod 8) form a contiguous run,
+ * then walked in groups of `group_m` tile rows, column by column.
+ * Pure host function; touches no device.  Errors: TG_ERR_NULL_POINTER,
+ * TG_ERR_BAD_SHAPE (tiles_m, tiles_n < 1, product above 2^31 - 1, group_m < 1).
+ */
+tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,
+                      int32_t* out_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEGEMM_H */

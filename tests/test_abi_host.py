@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* the library loads and exports every entry point include/tilegemm.h declares;
+* every invalid-argument path returns its status before any HIP call;
+* the block-swizzled tile order is a bijection and keeps each XCD's tiles
+  in one contiguous run of the grouped raster order.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tiled_dense_gemm_07_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP = range(8)
+
+# fake, well-separated device addresses: validation never dereferences them
+PA, PB, PC, PS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tilegemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    declared = declared_functions()
+    assert declared == sorted(binding.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        text = binding.status_str(s)
+        assert text.startswith("TG_")
+    assert "unknown" in binding.status_str(99)
+
+
+def test_gemm_argument_errors(lib):
+    g = lib.tg_gemm
+    assert g(-1, 4, 4, 2, PA, PB, PC, 0, None) == SHAPE
+    assert g(4, -1, 4, 2, PA, PB, PC, 0, None) == SHAPE
+    assert g(4, 4, -1, 2, PA, PB, PC, 0, None) == SHAPE
+    assert g(4, 4, 1 << 31, 2, PA, PB, PC, 0, None) == SHAPE
+    assert g(4, 4, 1 << 23, 2, PA, PB, PC, 0, None) == SHAPE  # 256*K*2 > 2^31
+    assert g(4, 4, 4, 3, PA, PB, PC, 0, None) == DTYPE
+    assert g(4, 4, 4, -1, PA, PB, PC, 0, None) == DTYPE
+    assert g(4, 4, 4, 2, PA, PB, PC, 2, None) == EPI
+    assert g(4, 4, 4, 2, None, PB, PC, 0, None) == NULLP
+    assert g(4, 4, 4, 2, PA, None, PC, 0, None) == NULLP
+    assert g(4, 4, 4, 2, PA, PB, None, 0, None) == NULLP
+    # C overlapping A or B
+    assert g(4, 4, 4, 2, PA, PB, PA + 8, 0, None) == ALIAS
+    assert g(4, 4, 4, 0, PA, PB, PB - 8, 0, None) == ALIAS
+    # empty outputs are a no-op, even with NULL pointers
+    assert g(0, 4, 4, 2, None, None, None, 0, None) == OK
+    assert g(4, 0, 4, 2, None, None, None, 0, None) == OK
+    # K == 0 needs only C
+    assert g(4, 4, 0, 2, None, None, None, 0, None) == NULLP
+
+
+def test_dequant_argument_errors(lib):
+    d = lib.tg_dequant_gemm_w4
+    assert d(4, 4, 48, PA, PB, PS, PC, 0, None) == SHAPE  # K % 32
+    assert d(4, 4, -32, PA, PB, PS, PC, 0, None) == SHAPE
+    assert d(4, 4, 64, PA, PB, PS, PC, 7, None) == EPI
+    assert d(4, 4, 64, PA, PB, None, PC, 0, None) == NULLP
+    assert d(4, 4, 64, PA, PB, PS, PB + 4, 0, None) == ALIAS
+    assert d(4, 4, 64, PA, PB, PS, PS, 0, None) == ALIAS
+    assert d(0, 4, 64, None, None, None, None, 0, None) == OK
+
+
+def test_forced_config_errors(lib):
+    n = lib.tg_config_count(0, 2)
+    assert n > 0
+    assert lib.tg_gemm_config(n, 4, 4, 4, 2, PA, PB, PC, 0, None) == NOCFG
+    assert lib.tg_gemm_config(-1, 4, 4, 4, 2, PA, PB, PC, 0, None) == NOCFG
+    nw = lib.tg_config_count(1, 2)
+    assert nw > 0
+    assert lib.tg_dequant_gemm_w4_config(nw, 4, 4, 64, PA, PB, PS, PC, 0, None) == NOCFG
+    # a 16-byte-load configuration refuses operands that are not 16-byte aligned
+    names = binding.list_configs(0, 2)
+    wide = names.index("gemm_bf16_256x256x64_w2x2_s2_g4")
+    assert lib.tg_gemm_config(wide, 4, 4, 4, 2, PA + 2, PB, PC, 0, None) == NOCFG
+
+
+def test_launch_failure_is_reported(lib, monkeypatch):
+    # TG_FAULT=launch makes the launcher report a HIP failure after validation
+    # and before any HIP call.
+    monkeypatch.setenv("TG_FAULT", "launch")
+    assert lib.tg_gemm(4, 4, 4, 2, PA, PB, PC, 0, None) == HIP
+    assert lib.tg_dequant_gemm_w4(4, 4, 64, PA, PB, PS, PC, 0, None) == HIP
+    with pytest.raises(binding.TileGemmError) as ei:
+        binding._check(HIP)
+    assert ei.value.status == HIP
+
+
+def test_query_config(lib):
+    s = binding.query_config(0, 4096, 4096, 4096, binding.TG_BF16)
+    assert s.startswith("gemm_bf16_") and "grid=" in s
+    s = binding.query_config(1, 256, 8192, 8192)
+    assert s.startswith("w4_bf16_")
+    s = binding.query_config(0, 17, 31, 33, binding.TG_F16)
+    assert s.endswith("threads=256") and "_narrow" in s
+    buf = ctypes.create_string_buffer(8)
+    assert lib.tg_query_config(0, 64, 64, 64, 2, buf, 8) == OK  # truncates
+    assert len(buf.value) == 7
+    assert lib.tg_query_config(5, 64, 64, 64, 2, buf, 8) == NOCFG
+    assert lib.tg_query_config(0, 64, 64, 64, 2, None, 8) == NULLP
+    assert lib.tg_query_config(1, 64, 64, 40, 2, buf, 8) == SHAPE
+
+
+def test_config_lists(lib):
+    for op, dt in ((0, 0), (0, 1), (0, 2), (1, 2)):
+        names = binding.list_configs(op, dt)
+        assert len(names) == len(set(names)) and names
+        # each list has a narrow (element-load) configuration for unaligned operands
+        assert any(n.endswith("_narrow") for n in names)
+
+
+def _raster_reference(tiles_m, tiles_n, group_m, logical):
+    """Grouped raster order written out directly: groups of group_m tile rows,
+    each walked column by column, top to bottom within a column."""
+    order = []
+    for first in range(0, tiles_m, group_m):
+        rows = range(first, min(first + group_m, tiles_m))
+        for n in range(tiles_n):
+            for m in rows:
+                order.append((m, n))
+    return order[logical]
+
+
+@pytest.mark.parametrize("tm,tn,gm", [(1, 1, 1), (3, 5, 2), (16, 16, 4), (16, 16, 8), (7, 9, 4),
+                                      (4, 64, 4), (64, 2, 8), (17, 16, 16), (1, 37, 4), (33, 1, 8)])
+def test_tile_map_bijection_and_xcd_runs(tm, tn, gm):
+    om, on = binding.tile_map(tm, tn, gm)
+    total = tm * tn
+    pairs = set(zip(om.tolist(), on.tolist()))
+    assert len(pairs) == total
+    assert all(0 <= m < tm and 0 <= n < tn for m, n in pairs)
+    # ids dealt to one XCD (w mod 8) take one contiguous run of the raster order
+    q, r = divmod(total, 8)
+    start = 0
+    for x in range(8):
+        ids = list(range(x, total, 8))
+        assert len(ids) == q + (1 if x < r else 0)
+        for j, w in enumerate(ids):
+            assert (int(om[w]), int(on[w])) == _raster_reference(tm, tn, gm, start + j)
+        start += len(ids)
+
+
+def test_tile_map_errors(lib):
+    a = np.empty(4, dtype=np.int32)
+    p = a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.tg_tile_map(0, 4, 1, p, p) == SHAPE
+    assert lib.tg_tile_map(2, 2, 0, p, p) == SHAPE
+    assert lib.tg_tile_map(2, 2, 1, None, p) == NULLP

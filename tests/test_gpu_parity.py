@@ -1,0 +1,272 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bars (from the workload statement):
+  * integer-valued inputs: bit-exact with one round-to-nearest-even of the
+    exact sum (every partial sum is exactly representable in fp32 there);
+  * random inputs, fp16 / bf16 / 4-bit paths: |C - Y| <= 1e-2 + 1e-2 |Y|
+    elementwise against the unrounded fp64 result Y;
+  * random inputs, fp32 path: relative Frobenius error <= 1e-5.
+Small shapes are compared in full; the full-size workloads, in the launch
+configuration the benchmark uses, on sampled entries the oracle sums one by
+one, plus properties that hold everywhere (ReLU sign, guard bands).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (BF16, F16, F32, assert_close_16, assert_fro_32, bits_to_f64, say,
+                         sample_entries, to_device, to_host_bits)
+from tiled_dense_gemm_07_amd import binding, synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = [F32, F16, BF16]
+DNAME = {F32: "f32", F16: "f16", BF16: "bf16"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def run_gemm(A, B, dtype, relu, config=None, C=None, stream=None):
+    At, Bt = to_device(A, dtype, DEV), to_device(B, dtype, DEV)
+    epi = "relu" if relu else None
+    if config is None:
+        Ct = binding.gemm(At, Bt, C=C, epilogue=epi, stream=stream)
+    else:
+        Ct = binding.gemm_with_config(config, At, Bt, C=C, epilogue=epi, stream=stream)
+    torch.cuda.synchronize()
+    return to_host_bits(Ct, dtype)
+
+
+def run_w4(A, Wq, Ws, relu=False, config=None):
+    At = to_device(A, BF16, DEV)
+    Wqt = torch.from_numpy(Wq).to(DEV)
+    Wst = torch.from_numpy(Ws).to(DEV)
+    epi = "relu" if relu else None
+    if config is None:
+        Ct = binding.dequant_gemm_w4(At, Wqt, Wst, epilogue=epi)
+    else:
+        Ct = binding.dequant_gemm_w4_with_config(config, At, Wqt, Wst, epilogue=epi)
+    torch.cuda.synchronize()
+    return to_host_bits(Ct, BF16)
+
+
+def check_full(got_bits, Y, dtype, integer):
+    if integer:
+        want = oracle.encode(dtype, Y)
+        diff = got_bits != want
+        assert not diff.any(), "%d of %d entries differ bitwise (first at %s)" % (
+            int(diff.sum()), diff.size, np.argwhere(diff)[0].tolist())
+    else:
+        got = bits_to_f64(got_bits, dtype)
+        if dtype == F32:
+            assert_fro_32(got, Y)
+        else:
+            assert_close_16(got, Y)
+
+
+SMALL = [(1, 1, 1), (3, 5, 7), (17, 31, 33), (64, 64, 64), (65, 72, 40), (129, 257, 65),
+         (200, 136, 96), (256, 256, 64), (300, 520, 136)]
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+@pytest.mark.parametrize("relu", [False, True], ids=["none", "relu"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_small_shapes(dtype, shape, relu, integer):
+    M, N, K = shape
+    A, B = synth.gemm_inputs(M, N, K, dtype, 101 + M, 202 + N, integer)
+    say("small %s %s relu=%s int=%s" % (DNAME[dtype], shape, relu, integer))
+    got = run_gemm(A, B, dtype, relu)
+    check_full(got, oracle.gemm_f64(A, B, dtype, relu), dtype, integer)
+
+
+def _configs(op, dtype):
+    return list(enumerate(binding.list_configs(op, dtype)))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_every_gemm_config(dtype):
+    """Each compiled configuration, forced, on a ragged shape: bit-exact."""
+    M, N, K = 300, 264, 200
+    A, B = synth.gemm_inputs(M, N, K, dtype, 303, 404, integer=True)
+    want = oracle.encode(dtype, oracle.gemm_f64(A, B, dtype, relu=True))
+    for idx, name in _configs(0, dtype):
+        say("config %d %s" % (idx, name))
+        got = run_gemm(A, B, dtype, True, config=idx)
+        assert np.array_equal(got, want), name
+
+
+def test_every_w4_config():
+    M, N, K = 300, 264, 256
+    A, Wq, Ws = synth.dequant_inputs(M, N, K, 505, 606, 707, integer=True)
+    want = oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws))
+    for idx, name in _configs(1, BF16):
+        say("config %d %s" % (idx, name))
+        got = run_w4(A, Wq, Ws, config=idx)
+        assert np.array_equal(got, want), name
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+@pytest.mark.parametrize("shape", [(1, 8, 32), (5, 24, 64), (33, 100, 96), (130, 72, 320),
+                                   (257, 264, 128)], ids=lambda s: "x".join(map(str, s)))
+def test_dequant_small(shape, integer):
+    M, N, K = shape
+    A, Wq, Ws = synth.dequant_inputs(M, N, K, 808 + M, 909 + N, 1010 + K, integer)
+    say("w4 small %s int=%s" % (shape, integer))
+    got = run_w4(A, Wq, Ws)
+    check_full(got, oracle.dequant_w4_f64(A, Wq, Ws), BF16, integer)
+
+
+def test_dequant_scale_range():
+    """Scale bytes across [2, 200] with integer activations: still bit-exact.
+
+    One scale per weight row keeps every partial sum a multiple of half that
+    scale and below 2^24 of them, so the fp32 accumulation is exact."""
+    M, N, K = 64, 96, 256
+    r = np.random.Generator(np.random.PCG64(77))
+    A = synth.to_storage(r.integers(-4, 5, size=(M, K)).astype(np.float32), BF16)
+    Wq = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    e_row = r.integers(2, 201, size=N)
+    e_row[0], e_row[1] = 2, 200
+    Ws = np.repeat(e_row[:, None], K // 32, axis=1).astype(np.uint8)
+    say("w4 scale range")
+    got = run_w4(A, Wq, Ws)
+    assert np.array_equal(got, oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws)))
+
+
+WORKLOADS = ["f32_512", "f16_1024", "f32_4096", "bf16_4096_relu", "bf16_4000x4032x4096_relu",
+             "w4_256x8192x8192", "w4_1x8192x8192", "w4_16x8192x8192"]
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload(name, integer):
+    """Full-size workloads in the benchmark's launch configuration."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, integer)
+    say("workload %s int=%s seeds=%s" % (name, integer, inp["seeds"]))
+    if w.op == "gemm":
+        got = run_gemm(inp["A"], inp["B"], w.dtype, w.relu)
+    else:
+        got = run_w4(inp["A"], inp["Wq"], inp["Ws"], w.relu)
+    got = got.reshape(w.M, w.N)
+    small = w.flops <= 2 * 1024 ** 3
+    if small and w.op == "gemm":
+        check_full(got, oracle.gemm_f64(inp["A"], inp["B"], w.dtype, w.relu), w.dtype, integer)
+    else:
+        rows, cols = sample_entries(w.M, w.N, 3000, seed=w.index * 7 + integer)
+        if w.op == "gemm":
+            Y = oracle.gemm_entries_f64(inp["A"], inp["B"], w.dtype, rows, cols, w.relu)
+        else:
+            Y = oracle.dequant_w4_entries_f64(inp["A"], inp["Wq"], inp["Ws"], rows, cols, w.relu)
+        check_full(got[rows, cols], Y, w.dtype, integer)
+    if w.relu:
+        vals = bits_to_f64(got, w.dtype)
+        assert (vals >= 0).all() and not np.signbit(vals).any()
+    assert np.isfinite(bits_to_f64(got, w.dtype)).all()
+
+
+def test_deterministic_bf16():
+    """Same inputs, same bits: ten launches of the benchmark's bf16 kernel."""
+    w = synth.WORKLOADS["bf16_4000x4032x4096_relu"]
+    inp = synth.make_inputs(w, integer=False)
+    A, B = to_device(inp["A"], BF16, DEV), to_device(inp["B"], BF16, DEV)
+    say("determinism bf16 %dx%dx%d" % (w.M, w.N, w.K))
+    first = binding.gemm(A, B, epilogue="relu").clone()
+    for _ in range(9):
+        again = binding.gemm(A, B, epilogue="relu")
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("shape", [(129, 257, 65), (300, 264, 200), (1000, 1032, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_guard_bands(dtype, shape):
+    """C inside a sentinel-filled buffer: nothing outside [M, N] is written."""
+    M, N, K = shape
+    A, B = synth.gemm_inputs(M, N, K, dtype, 11, 12, integer=True)
+    pad = 4096
+    if dtype == F32:
+        buf = torch.full((pad + M * N + pad,), float("nan"), dtype=torch.float32, device=DEV)
+        sentinel = buf[:1].view(torch.int32).item()
+        view_int = torch.int32
+    else:
+        buf = torch.empty((pad + M * N + pad,), dtype=torch.int16, device=DEV).fill_(0x7FC1)
+        buf = buf.view(binding_dtype(dtype))
+        sentinel = 0x7FC1
+        view_int = torch.int16
+    C = buf[pad:pad + M * N].view(M, N)
+    say("guard bands %s %s" % (DNAME[dtype], shape))
+    got = run_gemm(A, B, dtype, False, C=C)
+    raw = buf.view(view_int).cpu().numpy()
+    assert (raw[:pad] == sentinel).all() and (raw[pad + M * N:] == sentinel).all()
+    assert np.array_equal(got, oracle.encode(dtype, oracle.gemm_f64(A, B, dtype)))
+
+
+def binding_dtype(dtype):
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_k_zero_and_empty(dtype):
+    say("degenerate shapes %s" % DNAME[dtype])
+    td = binding_dtype(dtype)
+    A = torch.empty((7, 0), dtype=td, device=DEV)
+    B = torch.empty((0, 9), dtype=td, device=DEV)
+    C = torch.full((7, 9), 3.0, dtype=td, device=DEV)
+    binding.gemm(A, B, C=C)
+    torch.cuda.synchronize()
+    assert (C == 0).all()
+    C2 = torch.full((0, 9), 3.0, dtype=td, device=DEV)
+    binding.gemm(torch.empty((0, 5), dtype=td, device=DEV), torch.ones((5, 9), dtype=td, device=DEV),
+                 C=C2)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("K", [1, 16])
+def test_single_rounding(dtype, K):
+    """Only one product per output (column 0 of A): the output is the exact
+    product rounded once, so the cast itself is checked bit for bit."""
+    M, N = 96, 136
+    r = np.random.Generator(np.random.PCG64(5 + K))
+    Af = np.zeros((M, K), dtype=np.float32)
+    Af[:, 0] = r.standard_normal(M)
+    Bf = r.standard_normal((K, N)).astype(np.float32)
+    A, B = synth.to_storage(Af, dtype), synth.to_storage(Bf, dtype)
+    say("single rounding %s K=%d" % (DNAME[dtype], K))
+    got = run_gemm(A, B, dtype, False)
+    Y = oracle.gemm_f64(A, B, dtype)
+    if dtype == F32:
+        # the fp32 product is itself rounded once by the matrix unit: within half an ulp
+        g = bits_to_f64(got, F32)
+        ulp = np.spacing(np.abs(Y).astype(np.float32)).astype(np.float64)
+        assert (np.abs(g - Y) <= 0.5 * ulp).all()
+    else:
+        assert np.array_equal(got, oracle.encode(dtype, Y))
+
+
+def test_side_stream():
+    """A call on a non-default stream is ordered on that stream."""
+    M, N, K = 512, 512, 512
+    A, B = synth.gemm_inputs(M, N, K, BF16, 21, 22, integer=True)
+    s = torch.cuda.Stream()
+    say("side stream")
+    with torch.cuda.stream(s):
+        At, Bt = to_device(A, BF16, DEV), to_device(B, BF16, DEV)
+        Ct = binding.gemm(At, Bt)
+    s.synchronize()
+    got = to_host_bits(Ct, BF16)
+    assert np.array_equal(got, oracle.encode(BF16, oracle.gemm_f64(A, B, BF16)))

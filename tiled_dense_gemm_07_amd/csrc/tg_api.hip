@@ -1,0 +1,365 @@
+// C ABI of tilegemm: argument validation, kernel-configuration choice and launch.
+//
+// The call shape follows the pages' problem statement (the mhpq.cn page,
+// section 3.2: the caller allocates A, B and C and launches kernel(A, B, C);
+// section 3.4 checks the inner dimensions first) and the blog.hotdry.top page's
+// per-shape kernels (matmul(M, N, K, ...)).  Shapes arrive at run time here;
+// tile sizes, wave layout, stage count and swizzle group are compile-time
+// constants of each compiled configuration, chosen per call from a table that
+// the offline sweep (tiled_dense_gemm_07_amd/sweep.py) writes.
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/tilegemm.h"
+#include "tg_configs.h"
+#include "tg_kernel.h"
+
+namespace {
+
+using tg::Config;
+using tg::ConfigList;
+
+struct TunedEntry {
+    int op;
+    int dtype;
+    int64_t M, N, K;
+    const char* config;  // configuration name, as config_name() prints it
+};
+
+#include "tg_tuned.inc"
+
+ConfigList list_for(int op, int dtype)
+{
+    if (op == TG_OP_GEMM) {
+        if (dtype == TG_F32)
+            return tg::configs_gemm_f32();
+        if (dtype == TG_F16)
+            return tg::configs_gemm_f16();
+        if (dtype == TG_BF16)
+            return tg::configs_gemm_bf16();
+    } else if (op == TG_OP_DEQUANT_W4) {
+        return tg::configs_dequant_w4();
+    }
+    return ConfigList{nullptr, 0};
+}
+
+void config_name(const Config& c, char* buf, size_t len)
+{
+    static const char* dn[] = {"f32", "f16", "bf16"};
+    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s", c.op == 0 ? "gemm" : "w4",
+             dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
+             c.wide ? "" : "_narrow");
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Elements per 16-byte chunk for the operand type.
+int vec_of(int dtype) { return dtype == TG_F32 ? 4 : 8; }
+int esize_of(int dtype) { return dtype == TG_F32 ? 4 : 2; }
+
+int64_t tiles(int64_t x, int t) { return (x + t - 1) / t; }
+
+// Built-in choice when no tuned entry matches: the largest tile that still
+// gives about one workgroup per compute unit (256 on MI355X).
+const Config* heuristic(int op, int dtype, int64_t M, int64_t N, bool wide)
+{
+    ConfigList L = list_for(op, dtype);
+    const Config* best = nullptr;
+    int64_t best_area = -1;
+    const Config* fallback = nullptr;
+    for (int i = 0; i < L.count; ++i) {
+        const Config& c = L.items[i];
+        if (c.wide != wide)
+            continue;
+        if (!fallback || (int64_t)c.bm * c.bn < (int64_t)fallback->bm * fallback->bn)
+            fallback = &c;  // smallest tile of this width
+        const int64_t grid = tiles(M, c.bm) * tiles(N, c.bn);
+        const int64_t area = (int64_t)c.bm * c.bn;
+        // prefer 2 stages unless the tile is tiny; prefer 256-thread blocks at equal area
+        if (grid >= 192 && c.stages == 2 && (c.wgm * c.wgn == 4) && area > best_area) {
+            best = &c;
+            best_area = area;
+        }
+    }
+    return best ? best : fallback;
+}
+
+const Config* find_by_name(int op, int dtype, const char* name)
+{
+    ConfigList L = list_for(op, dtype);
+    char buf[96];
+    for (int i = 0; i < L.count; ++i) {
+        config_name(L.items[i], buf, sizeof buf);
+        if (strcmp(buf, name) == 0)
+            return &L.items[i];
+    }
+    return nullptr;
+}
+
+const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide)
+{
+    for (size_t i = 0; i < sizeof(kTuned) / sizeof(kTuned[0]); ++i) {
+        const TunedEntry& e = kTuned[i];
+        if (e.config == nullptr)
+            continue;
+        if (e.op == op && (op == TG_OP_DEQUANT_W4 || e.dtype == dtype) && e.M == M && e.N == N &&
+            e.K == K) {
+            const Config* c = find_by_name(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, e.config);
+            if (c && c->wide == wide)
+                return c;
+        }
+    }
+    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, wide);
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+// Shape limits that keep every per-tile byte offset inside 31 bits.
+tg_status check_shape(int64_t M, int64_t N, int64_t K, int esize)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return TG_ERR_BAD_SHAPE;
+    if (256 * K * esize > kMaxDim || 64 * N * esize > kMaxDim)
+        return TG_ERR_BAD_SHAPE;
+    if (tiles(M, 32) * tiles(N, 32) > kMaxDim)
+        return TG_ERR_BAD_SHAPE;
+    return TG_OK;
+}
+
+tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream)
+{
+    tg::GemmParams p = base;
+    p.tiles_m = (int)tiles(p.M, c.bm);
+    p.tiles_n = (int)tiles(p.N, c.bn);
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    if (grid > kMaxDim)
+        return TG_ERR_BAD_SHAPE;
+    const char* fault = getenv("TG_FAULT");
+    if (fault && strcmp(fault, "launch") == 0)
+        return TG_ERR_HIP;  // forced failure, for testing error reporting
+    if (getenv("TG_LOG")) {
+        char name[96];
+        config_name(c, name, sizeof name);
+        fprintf(stderr, "[tilegemm] M=%d N=%d K=%d -> %s grid=%lld\n", p.M, p.N, p.K, name,
+                (long long)grid);
+    }
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(c.kernel, dim3((unsigned)grid), dim3(c.wgm * c.wgn * 64), args,
+                                   0, stream);
+    if (e != hipSuccess)
+        return TG_ERR_HIP;
+    if (hipPeekAtLastError() != hipSuccess)
+        return TG_ERR_HIP;
+    return TG_OK;
+}
+
+tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
+                    tg_dtype dtype, const void* A, const void* B, void* C, tg_epilogue epi,
+                    tg_stream_t stream)
+{
+    if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    if (epi != TG_EPI_NONE && epi != TG_EPI_RELU)
+        return TG_ERR_BAD_EPILOGUE;
+    const int es = esize_of(dtype);
+    tg_status s = check_shape(M, N, K, es);
+    if (s != TG_OK)
+        return s;
+    if (forced_index >= 0 && !forced)
+        return TG_ERR_NO_CONFIG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    // with K == 0 the operands hold no elements and are never read
+    if (!C || (K > 0 && (!A || !B)))
+        return TG_ERR_NULL_POINTER;
+    const size_t cbytes = (size_t)(M * N * es);
+    if (overlaps(C, cbytes, A, (size_t)(M * K * es)) || overlaps(C, cbytes, B, (size_t)(K * N * es)))
+        return TG_ERR_ALIAS;
+    const int v = vec_of(dtype);
+    const bool wide = aligned16(A) && aligned16(B) && (K % v == 0) && (N % v == 0);  // NULL is aligned
+    const Config* c = forced ? forced : select_config(TG_OP_GEMM, dtype, M, N, K, wide);
+    if (!c)
+        return TG_ERR_NO_CONFIG;
+    if (c->wide && !wide)
+        return TG_ERR_NO_CONFIG;  // a forced 16-byte-load config on unaligned operands
+    tg::GemmParams p{};
+    p.A = A;
+    p.B = B;
+    p.Bs = nullptr;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.relu = epi == TG_EPI_RELU;
+    p.c_vec = (N % 4 == 0) && ((uintptr_t)C % (dtype == TG_F32 ? 16 : 8) == 0);
+    return launch(*c, p, (hipStream_t)stream);
+}
+
+tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
+                  const void* A, const uint8_t* Wq, const uint8_t* Ws, void* C, tg_epilogue epi,
+                  tg_stream_t stream)
+{
+    if (epi != TG_EPI_NONE && epi != TG_EPI_RELU)
+        return TG_ERR_BAD_EPILOGUE;
+    tg_status s = check_shape(M, N, K, 2);
+    if (s != TG_OK)
+        return s;
+    if (K % 32 != 0)
+        return TG_ERR_BAD_SHAPE;
+    if (forced_index >= 0 && !forced)
+        return TG_ERR_NO_CONFIG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (!C || (K > 0 && (!A || !Wq || !Ws)))
+        return TG_ERR_NULL_POINTER;
+    const size_t cbytes = (size_t)(M * N * 2);
+    if (overlaps(C, cbytes, A, (size_t)(M * K * 2)) || overlaps(C, cbytes, Wq, (size_t)(N * K / 2)) ||
+        overlaps(C, cbytes, Ws, (size_t)(N * K / 32)))
+        return TG_ERR_ALIAS;
+    const bool wide = aligned16(A) && aligned16(Wq);
+    const Config* c = forced ? forced : select_config(TG_OP_DEQUANT_W4, TG_BF16, M, N, K, wide);
+    if (!c)
+        return TG_ERR_NO_CONFIG;
+    if (c->wide && !wide)
+        return TG_ERR_NO_CONFIG;
+    tg::GemmParams p{};
+    p.A = A;
+    p.B = Wq;
+    p.Bs = Ws;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.relu = epi == TG_EPI_RELU;
+    p.c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    return launch(*c, p, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, const void* B,
+                  void* C, tg_epilogue epi, tg_stream_t stream)
+{
+    return gemm_impl(nullptr, -1, M, N, K, dtype, A, B, C, epi, stream);
+}
+
+tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, const uint8_t* Wq,
+                             const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream)
+{
+    return w4_impl(nullptr, -1, M, N, K, A, Wq, Ws, C, epi, stream);
+}
+
+const char* tg_status_str(tg_status s)
+{
+    switch (s) {
+    case TG_OK:
+        return "TG_OK: success";
+    case TG_ERR_NULL_POINTER:
+        return "TG_ERR_NULL_POINTER: a required pointer is NULL";
+    case TG_ERR_BAD_SHAPE:
+        return "TG_ERR_BAD_SHAPE: negative or too large size, or dequant K not a multiple of 32";
+    case TG_ERR_BAD_DTYPE:
+        return "TG_ERR_BAD_DTYPE: dtype must be TG_F32, TG_F16 or TG_BF16";
+    case TG_ERR_BAD_EPILOGUE:
+        return "TG_ERR_BAD_EPILOGUE: epilogue must be TG_EPI_NONE or TG_EPI_RELU";
+    case TG_ERR_ALIAS:
+        return "TG_ERR_ALIAS: the output overlaps an input";
+    case TG_ERR_NO_CONFIG:
+        return "TG_ERR_NO_CONFIG: no such kernel configuration for this call";
+    case TG_ERR_HIP:
+        return "TG_ERR_HIP: the HIP runtime reported an error at launch";
+    }
+    return "unknown tg_status";
+}
+
+tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
+                          size_t len)
+{
+    if (!buf || len == 0)
+        return TG_ERR_NULL_POINTER;
+    if (op != TG_OP_GEMM && op != TG_OP_DEQUANT_W4)
+        return TG_ERR_NO_CONFIG;
+    if (op == TG_OP_GEMM && dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    const int dt = op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype;
+    tg_status s = check_shape(M, N, K, esize_of(dt));
+    if (s != TG_OK)
+        return s;
+    if (op == TG_OP_DEQUANT_W4 && K % 32 != 0)
+        return TG_ERR_BAD_SHAPE;
+    // assume aligned operands (what torch allocations give)
+    const bool wide = op == TG_OP_DEQUANT_W4 || (K % vec_of(dt) == 0 && N % vec_of(dt) == 0);
+    const Config* c = select_config(op, dt, M, N, K, wide);
+    if (!c)
+        return TG_ERR_NO_CONFIG;
+    char name[96];
+    config_name(*c, name, sizeof name);
+    snprintf(buf, len, "%s grid=%lld threads=%d", name,
+             (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * 64);
+    return TG_OK;
+}
+
+int tg_config_count(int op, tg_dtype dtype)
+{
+    return list_for(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype).count;
+}
+
+tg_status tg_config_name(int op, tg_dtype dtype, int index, char* buf, size_t len)
+{
+    if (!buf || len == 0)
+        return TG_ERR_NULL_POINTER;
+    ConfigList L = list_for(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype);
+    if (index < 0 || index >= L.count)
+        return TG_ERR_NO_CONFIG;
+    config_name(L.items[index], buf, len);
+    return TG_OK;
+}
+
+tg_status tg_gemm_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                         const void* A, const void* B, void* C, tg_epilogue epi,
+                         tg_stream_t stream)
+{
+    if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    ConfigList L = list_for(TG_OP_GEMM, dtype);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    return gemm_impl(c, index < 0 ? 0 : index, M, N, K, dtype, A, B, C, epi, stream);
+}
+
+tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, const void* A,
+                                    const uint8_t* Wq, const uint8_t* Ws, void* C,
+                                    tg_epilogue epi, tg_stream_t stream)
+{
+    ConfigList L = list_for(TG_OP_DEQUANT_W4, TG_BF16);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    return w4_impl(c, index < 0 ? 0 : index, M, N, K, A, Wq, Ws, C, epi, stream);
+}
+
+tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,
+                      int32_t* out_n)
+{
+    if (!out_m || !out_n)
+        return TG_ERR_NULL_POINTER;
+    if (tiles_m < 1 || tiles_n < 1 || group_m < 1 || tiles_m * tiles_n > kMaxDim)
+        return TG_ERR_BAD_SHAPE;
+    const int total = (int)(tiles_m * tiles_n);
+    for (int w = 0; w < total; ++w) {
+        tg::TileCoord t = tg::tile_of(w, (int)tiles_m, (int)tiles_n, group_m);
+        out_m[w] = t.m;
+        out_n[w] = t.n;
+    }
+    return TG_OK;
+}
+
+}  // extern "C"

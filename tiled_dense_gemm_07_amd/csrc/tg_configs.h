@@ -1,0 +1,37 @@
+// Compiled kernel configurations and the launch table shared by the
+// per-dtype translation units and the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace tg {
+
+struct Config {
+    int op;     // 0 = GEMM, 1 = 4-bit dequant GEMM
+    int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
+    int bm, bn, bk;
+    int wgm, wgn;  // waves along M and N (64 threads each)
+    int stages;    // LDS ring depth
+    int group_m;   // swizzle group (tile rows)
+    bool wide;     // 16-byte global loads (aligned operands) vs element loads
+    const void* kernel;
+};
+
+struct ConfigList {
+    const Config* items;
+    int count;
+};
+
+ConfigList configs_gemm_f32();
+ConfigList configs_gemm_f16();
+ConfigList configs_gemm_bf16();
+ConfigList configs_dequant_w4();
+
+}  // namespace tg
+
+#define TG_CONFIG(OP, DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE)                            \
+    tg::Config                                                                                 \
+    {                                                                                          \
+        OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE,                                            \
+            (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE>       \
+    }

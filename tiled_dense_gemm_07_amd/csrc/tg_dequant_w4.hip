@@ -1,0 +1,21 @@
+// Weight-only 4-bit dequant GEMM configurations: the bf16 tiled kernel with its
+// B strip read as packed E2M1 codes + E8M0 scales and expanded to bf16 in LDS.
+#include "tg_configs.h"
+#include "tg_kernel.h"
+
+namespace tg {
+
+static const Config kCfg[] = {
+    TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 128, 64, 128, 2, 2, 2, 4, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 32, 128, 128, 1, 4, 2, 8, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 32, 64, 128, 1, 2, 2, 8, true),
+    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, false),
+};
+
+ConfigList configs_dequant_w4() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }
+
+}  // namespace tg

@@ -1,0 +1,19 @@
+// fp32 GEMM kernel configurations (instantiations of the tiled kernel template).
+// The first one is the pages' own tile: 128 x 128 x 32 (mhpq.cn, section 3.2).
+#include "tg_configs.h"
+#include "tg_kernel.h"
+
+namespace tg {
+
+static const Config kCfg[] = {
+    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true),
+    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 3, 8, true),
+    TG_CONFIG(0, DT_F32, B_KN, 256, 128, 32, 2, 2, 2, 4, true),
+    TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true),
+    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true),
+    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, false),
+};
+
+ConfigList configs_gemm_f32() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }
+
+}  // namespace tg

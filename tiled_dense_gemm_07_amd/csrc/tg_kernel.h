@@ -1,0 +1,540 @@
+// Tiled GEMM kernel template for CDNA4 (gfx950).
+//
+// One workgroup owns a BM x BN tile of C and walks K in BK-deep strips, as in
+// the mhpq.cn page's GEMM ("TileLang ... 一个高效 GEMM 内核", sections 2.1, 2.3,
+// 3.2): the A strip (BM x BK) and the B strip (BK x BN) are staged in on-chip
+// memory (LDS), an fp32 accumulator lives in registers (here the AccVGPRs fed
+// by MFMA), and copies of the next strips overlap the math on the current one
+// (section 3.3; the blog.hotdry.top page's num_stages = 3, 2-4 to start).
+//
+// MI355X-specific choices (not from the pages):
+//  * LDS holds both operands "K-contiguous": A as [BM][BK], B as [BN][BK]
+//    (row-major B is transposed in registers on its way into LDS; the 4-bit
+//    weights [N][K] are K-contiguous already and are expanded to bf16 there).
+//    Every MFMA operand fragment is then one 16-byte ds_read_b128 per lane.
+//  * 16-byte chunks of each LDS row are XOR-swizzled by the row index, so the
+//    global->LDS writes and the MFMA fragment reads are both free of bank
+//    conflicts without padding (the pages pad a column instead, mhpq.cn 4.2).
+//  * The MFMA is issued with the B fragment as its first operand, so each lane
+//    ends up owning 4 consecutive columns of one row of C: the epilogue
+//    (ReLU, one rounding to the output type, edge mask) stores 8 or 16 bytes.
+//  * Global reads go through buffer instructions whose range check returns 0
+//    past the end of the tile band, plus explicit masks for the ragged K and N
+//    edges, so partial tiles need no second code path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tg_sched.h"
+
+namespace tg {
+
+typedef uint32_t u32;
+typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+typedef __attribute__((ext_vector_type(4))) u32 u32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum BMode { B_KN = 0, B_W4 = 1 };
+
+template <int DT>
+struct DtTraits;
+template <>
+struct DtTraits<DT_F32> {
+    static constexpr int ES = 4;   // bytes per element
+    static constexpr int VEC = 4;  // elements per 16-byte chunk
+};
+template <>
+struct DtTraits<DT_F16> {
+    static constexpr int ES = 2;
+    static constexpr int VEC = 8;
+};
+template <>
+struct DtTraits<DT_BF16> {
+    static constexpr int ES = 2;
+    static constexpr int VEC = 8;
+};
+
+struct GemmParams {
+    const void* A;   // [M][K] row-major
+    const void* B;   // B_KN: [K][N] row-major; B_W4: packed codes [N][K/2]
+    const void* Bs;  // B_W4: scale bytes [N][K/32]; unused otherwise
+    void* C;         // [M][N] row-major
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int relu;
+    int c_vec;  // 1 if C rows allow 4-element vector stores
+};
+
+// --------------------------------------------------------------------------
+// Buffer resources (range-checked global access).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes)
+{
+    // 4th dword 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr u32 kOob = 0x80000000u;  // any offset >= num_records reads as 0
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, u32 off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32 buf_load4(__amdgpu_buffer_rsrc_t r, u32 off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32 buf_load2(__amdgpu_buffer_rsrc_t r, u32 off)
+{
+    return (u32)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32 buf_load1(__amdgpu_buffer_rsrc_t r, u32 off)
+{
+    return (u32)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ u32 clamp_bytes(int64_t b)
+{
+    return b <= 0 ? 0u : (b >= 0x7FFFFFFF ? 0x7FFFFFFFu : (u32)b);
+}
+
+// XOR swizzle of the 16-byte chunk index within an LDS row.  Rows are at
+// least 128 bytes (8 chunks), so a group of 8 lanes that reads 8 consecutive
+// rows at one logical chunk, or writes rows 8c + j for c = 0..7, touches 8
+// different 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// --------------------------------------------------------------------------
+// Output conversion (one rounding, nearest-even).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ u32 pack2(float a, float b, int dt)
+{
+    if (dt == DT_BF16) {
+        bf16x2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(u32, v);
+    }
+    _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (u32)__builtin_bit_cast(uint16_t, ha) | ((u32)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ uint16_t cvt1(float a, int dt)
+{
+    if (dt == DT_BF16)
+        return __builtin_bit_cast(uint16_t, (__bf16)a);
+    return __builtin_bit_cast(uint16_t, (_Float16)a);
+}
+
+// E8M0 scale byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127; 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(u32 e)
+{
+    u32 bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
+    return __builtin_bit_cast(float, bits);
+}
+
+// --------------------------------------------------------------------------
+// The kernel.
+// --------------------------------------------------------------------------
+template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
+          bool WIDE>
+struct GemmKernel {
+    using TR = DtTraits<DT>;
+    static constexpr int ES = TR::ES;
+    static constexpr int VEC = TR::VEC;
+    static constexpr int NT = WGM * WGN * 64;
+    static constexpr int WTM = BM / WGM;
+    static constexpr int WTN = BN / WGN;
+    static constexpr int FM = WTM / 32;
+    static constexpr int FN = WTN / 32;
+    static constexpr int CPR = BK / VEC;         // 16-byte chunks per LDS row
+    static constexpr int NSLAB = BK / (2 * VEC);  // MFMA k-slabs per strip
+    static constexpr int ROWB = BK * ES;          // bytes per LDS row
+    static constexpr int A_STAGE = BM * ROWB;
+    static constexpr int B_STAGE = BN * ROWB;
+    static constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // A: 16-byte chunks per thread
+    static constexpr int ACH = BM * CPR / NT;
+    // B (row-major KN): units of VEC k-rows by UW n-columns (UW <= VEC), so
+    // that every thread owns a whole number of units; a unit is UW*ES-byte
+    // loads of VEC rows, transposed into UW LDS rows of one 16-byte chunk.
+    static constexpr int UW_RAW = (BK / VEC) * BN / NT;
+    static constexpr int UW = UW_RAW >= VEC ? VEC : UW_RAW;
+    static constexpr int BU_KN = (BK / VEC) * (BN / (UW > 0 ? UW : 1)) / NT;
+    // B (4-bit weights): units of CU codes (CU/2 bytes) of one weight row,
+    // CU in {8, 16, 32}, all under one scale byte
+    static constexpr int CU_RAW = BN * BK / NT;
+    static constexpr int CU = CU_RAW >= 32 ? 32 : CU_RAW;
+    static constexpr int BU_W4 = BN * BK / (CU > 0 ? CU : 1) / NT;
+
+    static_assert(DT != DT_F32 || BMODE == B_KN, "4-bit weights feed the bf16 path only");
+    static_assert(BMODE == B_KN || DT == DT_BF16, "4-bit weights feed the bf16 path only");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "LDS rows must be >= 128 B, power of 2");
+    static_assert(BK % (2 * VEC) == 0, "BK must hold whole MFMA k-slabs");
+    static_assert(BM * CPR % NT == 0, "A strip must split evenly over threads");
+    static_assert(BMODE != B_KN || (UW >= 1 && (UW & (UW - 1)) == 0 &&
+                                    ((BK / VEC) * (BN / UW)) % NT == 0 && BU_KN >= 1),
+                  "B units must split evenly");
+    static_assert(BMODE != B_KN || UW * ES >= 4, "B loads of at least 4 bytes");
+    static_assert(BMODE != B_W4 || (CU >= 8 && (CU & (CU - 1)) == 0 && BU_W4 >= 1 &&
+                                    (BN * BK / CU) % NT == 0),
+                  "W4 units must split evenly");
+    static_assert(BMODE != B_W4 || BK % 32 == 0, "W4 strips hold whole scale groups");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 2, "at least double buffering");
+
+    struct Regs {
+        u32x4 a[ACH];
+        u32x4 b[BMODE == B_KN ? BU_KN * VEC : BU_W4];
+        u32 s[BMODE == B_W4 ? BU_W4 : 1];
+    };
+
+    // ---- global -> registers --------------------------------------------
+    static __device__ __forceinline__ void load_a(Regs& R, const GemmParams& p, int m0, int k0,
+                                                  int tid)
+    {
+        const char* base = (const char*)p.A + ((int64_t)m0 * p.K + k0) * ES;
+        const int rows_valid = p.M - m0;
+        const int64_t bytes = ((int64_t)(rows_valid - 1) * p.K + (p.K - k0)) * ES;
+        const auto rs = make_rsrc(base, clamp_bytes(bytes));
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int q = tid + NT * i;
+            const int row = q / CPR;
+            const int c = q % CPR;
+            const int kk = c * VEC;  // k offset within the strip
+            const bool rv = row < rows_valid;
+            const u32 off = (u32)(row * p.K + kk) * ES;
+            if (WIDE) {
+                const bool v = rv && (k0 + kk < p.K);
+                R.a[i] = buf_load16(rs, v ? off : kOob);
+            } else {
+                u32 w[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const bool v = rv && (k0 + kk + e < p.K);
+                    const u32 o = v ? off + e * ES : kOob;
+                    if (ES == 4)
+                        w[e] = buf_load4(rs, o);
+                    else
+                        w[e / 2] |= buf_load2(rs, o) << (16 * (e & 1));
+                }
+                R.a[i] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void load_b(Regs& R, const GemmParams& p, int n0, int k0,
+                                                  int tid)
+    {
+        if constexpr (BMODE == B_KN) {
+            const char* base = (const char*)p.B + ((int64_t)k0 * p.N + n0) * ES;
+            const int64_t bytes = ((int64_t)(p.K - k0 - 1) * p.N + (p.N - n0)) * ES;
+            const auto rs = make_rsrc(base, clamp_bytes(bytes));
+#pragma unroll
+            for (int i = 0; i < BU_KN; ++i) {
+                const int u = tid + NT * i;
+                const int nc = u % (BN / UW);
+                const int kg = u / (BN / UW);
+                const int nn = nc * UW;
+#pragma unroll
+                for (int r = 0; r < VEC; ++r) {
+                    const int kr = kg * VEC + r;  // k row within the strip
+                    const bool kv = k0 + kr < p.K;
+                    const u32 off = (u32)(kr * p.N + nn) * ES;
+                    u32x4 w = {0, 0, 0, 0};
+                    if (WIDE) {
+                        const u32 o = (kv && n0 + nn < p.N) ? off : kOob;
+                        if constexpr (UW * ES == 16) {
+                            w = buf_load16(rs, o);
+                        } else if constexpr (UW * ES == 8) {
+                            const u32x2 h = __builtin_bit_cast(
+                                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0));
+                            w[0] = h[0];
+                            w[1] = h[1];
+                        } else {
+                            w[0] = buf_load4(rs, o);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < UW; ++e) {
+                            const bool v = kv && (n0 + nn + e < p.N);
+                            const u32 o = v ? off + e * ES : kOob;
+                            if (ES == 4)
+                                w[e] = buf_load4(rs, o);
+                            else
+                                w[e / 2] |= buf_load2(rs, o) << (16 * (e & 1));
+                        }
+                    }
+                    R.b[i * VEC + r] = w;
+                }
+            }
+        } else {
+            // packed codes: row n has K/2 bytes; this strip covers bytes k0/2 .. (k0+BK)/2
+            const int rows_valid = p.N - n0;
+            const int rowb = p.K / 2;
+            const char* base = (const char*)p.B + (int64_t)n0 * rowb + k0 / 2;
+            const int64_t bytes = (int64_t)(rows_valid - 1) * rowb + (rowb - k0 / 2);
+            const auto rs = make_rsrc(base, clamp_bytes(bytes));
+            const int srow = p.K / 32;
+            const char* sbase = (const char*)p.Bs + (int64_t)n0 * srow + k0 / 32;
+            const int64_t sbytes = (int64_t)(rows_valid - 1) * srow + (srow - k0 / 32);
+            const auto ss = make_rsrc(sbase, clamp_bytes(sbytes));
+            constexpr int UPR = BK / CU;  // units per row
+#pragma unroll
+            for (int i = 0; i < BU_W4; ++i) {
+                const int u = tid + NT * i;
+                const int row = u / UPR;
+                const int g = u % UPR;
+                const int kk = g * CU;  // first code of this unit within the strip
+                const bool v = row < rows_valid && (k0 + kk < p.K);
+                const u32 off = (u32)(row * rowb + kk / 2);
+                u32x4 w = {0, 0, 0, 0};
+                if (WIDE) {
+                    const u32 o = v ? off : kOob;
+                    if constexpr (CU == 32) {
+                        w = buf_load16(rs, o);
+                    } else if constexpr (CU == 16) {
+                        const u32x2 h = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0));
+                        w[0] = h[0];
+                        w[1] = h[1];
+                    } else {
+                        w[0] = buf_load4(rs, o);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < CU / 2; ++e)
+                        w[e / 4] |= buf_load1(rs, v ? off + e : kOob) << (8 * (e & 3));
+                }
+                R.b[i] = w;
+                R.s[i] = buf_load1(ss, v ? (u32)(row * srow + kk / 32) : kOob);
+            }
+        }
+    }
+
+    // ---- registers -> LDS ---------------------------------------------------
+    static __device__ __forceinline__ void store_lds(const Regs& R, char* stage, int tid)
+    {
+        char* As = stage;
+        char* Bs = stage + A_STAGE;
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int q = tid + NT * i;
+            const int row = q / CPR;
+            const int c = q % CPR;
+            *(u32x4*)(As + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
+        }
+        if constexpr (BMODE == B_KN) {
+#pragma unroll
+            for (int i = 0; i < BU_KN; ++i) {
+                const int u = tid + NT * i;
+                const int nc = u % (BN / UW);
+                const int kg = u / (BN / UW);
+                const u32x4* L = &R.b[i * VEC];
+#pragma unroll
+                for (int j = 0; j < UW; ++j) {
+                    u32x4 o;
+                    if (ES == 4) {
+                        // 4 k-rows of fp32: column j
+                        o = u32x4{L[0][j], L[1][j], L[2][j], L[3][j]};
+                    } else {
+                        // 8 k-rows of 16-bit values: column j, k pairs packed low-to-high
+                        const u32 sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                        const int d = j >> 1;
+                        o = u32x4{__builtin_amdgcn_perm(L[1][d], L[0][d], sel),
+                                  __builtin_amdgcn_perm(L[3][d], L[2][d], sel),
+                                  __builtin_amdgcn_perm(L[5][d], L[4][d], sel),
+                                  __builtin_amdgcn_perm(L[7][d], L[6][d], sel)};
+                    }
+                    const int n = nc * UW + j;
+                    *(u32x4*)(Bs + n * ROWB + ((kg ^ swz(n)) << 4)) = o;
+                }
+            }
+        } else {
+            constexpr int UPR = BK / CU;
+#pragma unroll
+            for (int i = 0; i < BU_W4; ++i) {
+                const int u = tid + NT * i;
+                const int row = u / UPR;
+                const int g = u % UPR;
+                const float sc = e8m0_to_f32(R.s[i]);
+#pragma unroll
+                for (int cc = 0; cc < CU / 8; ++cc) {
+                    const u32 packed = R.b[i][cc];  // 8 codes: k = 8cc .. 8cc+7 of this unit
+                    u32x4 o;
+                    o[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0));
+                    o[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1));
+                    o[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 2));
+                    o[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 3));
+                    const int chunk = g * (CU / 8) + cc;
+                    *(u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4)) = o;
+                }
+            }
+        }
+    }
+
+    // ---- LDS -> MFMA ---------------------------------------------------------
+    static __device__ __forceinline__ void compute(f32x16 (&acc)[FM][FN], const char* stage,
+                                                   int wm, int wn, int lane)
+    {
+        const char* As = stage;
+        const char* Bs = stage + A_STAGE;
+        const int lr = lane & 31;
+        const int g = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < NSLAB; ++s) {
+            const int chunk = 2 * s + g;
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = wm * WTM + fm * 32 + lr;
+                af[fm] = *(const u32x4*)(As + row * ROWB + ((chunk ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int row = wn * WTN + fn * 32 + lr;
+                bf[fn] = *(const u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    if constexpr (DT == DT_F32) {
+                        // cast whole vectors: clang reads element 0 when
+                        // __builtin_bit_cast is applied to a vector element
+                        const f32x4 bv = __builtin_bit_cast(f32x4, bf[fn]);
+                        const f32x4 av = __builtin_bit_cast(f32x4, af[fm]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                bv[e], av[e], acc[fm][fn], 0, 0, 0);
+                    } else if constexpr (DT == DT_F16) {
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, bf[fn]), __builtin_bit_cast(f16x8, af[fm]),
+                            acc[fm][fn], 0, 0, 0);
+                    } else {
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, bf[fn]), __builtin_bit_cast(bf16x8, af[fm]),
+                            acc[fm][fn], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: ReLU, one rounding, edge-masked stores -----------------------
+    static __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN],
+                                                    const GemmParams& p, int m0, int n0, int wm,
+                                                    int wn, int lane)
+    {
+        const int lr = lane & 31;
+        const int g = lane >> 5;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * WTM + fm * 32 + lr;
+            if (m >= p.M)
+                continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * WTN + fn * 32 + 8 * q + 4 * g;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = acc[fm][fn][4 * q + e];
+                        v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
+                    }
+                    const int64_t idx = (int64_t)m * p.N + n;
+                    if (DT == DT_F32) {
+                        float* C = (float*)p.C;
+                        if (p.c_vec && n + 3 < p.N) {
+                            *(f32x4*)(C + idx) = f32x4{v[0], v[1], v[2], v[3]};
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    C[idx + e] = v[e];
+                        }
+                    } else {
+                        uint16_t* C = (uint16_t*)p.C;
+                        if (p.c_vec && n + 3 < p.N) {
+                            *(u32x2*)(C + idx) = u32x2{pack2(v[0], v[1], DT), pack2(v[2], v[3], DT)};
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    C[idx + e] = cvt1(v[e], DT);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void run(const GemmParams& p)
+    {
+        __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int wm = wave / WGN;
+        const int wn = wave % WGN;
+        const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const int m0 = t.m * BM;
+        const int n0 = t.n * BN;
+        const int KT = (p.K + BK - 1) / BK;
+
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[fm][fn][r] = 0.0f;
+
+        Regs R;
+        // prologue: fill STAGES-1 strips
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) {
+            if (s < KT) {
+                load_a(R, p, m0, s * BK, tid);
+                load_b(R, p, n0, s * BK, tid);
+                store_lds(R, smem + s * STAGE_BYTES, tid);
+            }
+        }
+        __syncthreads();
+
+        for (int it = 0; it < KT; ++it) {
+            const int nxt = it + STAGES - 1;
+            if (nxt < KT) {
+                load_a(R, p, m0, nxt * BK, tid);
+                load_b(R, p, n0, nxt * BK, tid);
+            }
+            compute(acc, smem + (it % STAGES) * STAGE_BYTES, wm, wn, lane);
+            if (nxt < KT)
+                store_lds(R, smem + (nxt % STAGES) * STAGE_BYTES, tid);
+            __syncthreads();
+        }
+
+        epilogue(acc, p, m0, n0, wm, wn, lane);
+    }
+};
+
+template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
+          bool WIDE>
+__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64))) void
+gemm_kernel(GemmParams p)
+{
+    GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE>::run(p);
+}
+
+}  // namespace tg
