@@ -18,8 +18,6 @@ Printed: ONE JSON line (rank 0) with
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -39,16 +37,6 @@ OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x
          "w4_16x8192x8192", "w4_1x8192x8192"]
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources: counter files are valid only for this kernel code."""
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "tiled_dense_gemm_07_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -57,6 +45,8 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from tiled_dense_gemm_07_amd.traffic import source_hash
+
     if rec.get("source_hash") != source_hash():
         return None
     return rec

@@ -49,9 +49,9 @@ ConfigList list_for(int op, int dtype)
 void config_name(const Config& c, char* buf, size_t len)
 {
     static const char* dn[] = {"f32", "f16", "bf16"};
-    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s", c.op == 0 ? "gemm" : "w4",
+    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s", c.op == 0 ? "gemm" : "w4",
              dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
-             c.wide ? "" : "_narrow");
+             c.pipe ? "_deep" : "", c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -62,29 +62,60 @@ int esize_of(int dtype) { return dtype == TG_F32 ? 4 : 2; }
 
 int64_t tiles(int64_t x, int t) { return (x + t - 1) / t; }
 
-// Built-in choice when no tuned entry matches: the largest tile that still
-// gives about one workgroup per compute unit (256 on MI355X).
+// Built-in choice when no tuned entry matches.  Each (op, dtype) has a list
+// of compiled configurations from the largest tile down; the first whose
+// grid reaches about one workgroup per compute unit (256 CUs on MI355X) wins,
+// else the last.  The lists follow the sweep's measurements on MI355X.
+struct Pref {
+    int op, dtype;
+    const char* names[4];
+};
+const Pref kPrefs[] = {
+    {0, 2, {"gemm_bf16_256x256x64_w2x4_s2_g4", "gemm_bf16_128x128x64_w2x2_s2_g8_deep",
+            "gemm_bf16_64x64x64_w2x2_s2_g8_deep", nullptr}},
+    {0, 1, {"gemm_f16_256x256x64_w2x4_s2_g4", "gemm_f16_128x128x64_w2x2_s2_g8_deep",
+            "gemm_f16_64x64x64_w2x2_s2_g8_deep", nullptr}},
+    {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x32_w2x2_s2_g8_deep", nullptr,
+            nullptr}},
+    {1, 2, {"w4_bf16_128x64x128_w2x2_s2_g4_deep", "w4_bf16_64x64x128_w2x2_s2_g8_deep",
+            "w4_bf16_32x64x128_w1x2_s2_g8_deep", nullptr}},
+};
+
+const Config* find_by_name(int op, int dtype, const char* name);
+
 const Config* heuristic(int op, int dtype, int64_t M, int64_t N, bool wide)
 {
     ConfigList L = list_for(op, dtype);
-    const Config* best = nullptr;
-    int64_t best_area = -1;
-    const Config* fallback = nullptr;
-    for (int i = 0; i < L.count; ++i) {
-        const Config& c = L.items[i];
-        if (c.wide != wide)
-            continue;
-        if (!fallback || (int64_t)c.bm * c.bn < (int64_t)fallback->bm * fallback->bn)
-            fallback = &c;  // smallest tile of this width
-        const int64_t grid = tiles(M, c.bm) * tiles(N, c.bn);
-        const int64_t area = (int64_t)c.bm * c.bn;
-        // prefer 2 stages unless the tile is tiny; prefer 256-thread blocks at equal area
-        if (grid >= 192 && c.stages == 2 && (c.wgm * c.wgn == 4) && area > best_area) {
-            best = &c;
-            best_area = area;
-        }
+    if (!wide) {
+        for (int i = 0; i < L.count; ++i)
+            if (!L.items[i].wide)
+                return &L.items[i];
+        return nullptr;
     }
-    return best ? best : fallback;
+    for (const Pref& pr : kPrefs) {
+        if (pr.op != op || pr.dtype != dtype)
+            continue;
+        const Config* last = nullptr;
+        for (const char* name : pr.names) {
+            if (!name)
+                break;
+            const Config* c = find_by_name(op, dtype, name);
+            if (!c)
+                continue;
+            last = c;
+            // small M: a tile taller than M wastes matrix-core work
+            if (op == 1 && M <= c->bm / 2)
+                continue;
+            if (tiles(M, c->bm) * tiles(N, c->bn) >= 200)
+                return c;
+        }
+        if (last)
+            return last;
+    }
+    for (int i = 0; i < L.count; ++i)
+        if (L.items[i].wide)
+            return &L.items[i];
+    return nullptr;
 }
 
 const Config* find_by_name(int op, int dtype, const char* name)

@@ -14,6 +14,7 @@ struct Config {
     int stages;    // LDS ring depth
     int group_m;   // swizzle group (tile rows)
     bool wide;     // 16-byte global loads (aligned operands) vs element loads
+    int pipe;      // 0: single staging set; 1: deep pipeline
     const void* kernel;
 };
 
@@ -29,9 +30,9 @@ ConfigList configs_dequant_w4();
 
 }  // namespace tg
 
-#define TG_CONFIG(OP, DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE)                            \
+#define TG_CONFIG(OP, DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE)                      \
     tg::Config                                                                                 \
     {                                                                                          \
-        OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE,                                            \
-            (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE>       \
+        OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE,                                      \
+            (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE> \
     }

@@ -6,14 +6,17 @@
 namespace tg {
 
 static const Config kCfg[] = {
-    TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 128, 64, 128, 2, 2, 2, 4, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 32, 128, 128, 1, 4, 2, 8, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 32, 64, 128, 1, 2, 2, 8, true),
-    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, false),
+    TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 128, 64, 128, 2, 2, 2, 4, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 32, 128, 128, 1, 4, 2, 8, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 32, 64, 128, 1, 2, 2, 8, true, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, false, 0),
+    TG_CONFIG(1, DT_BF16, B_W4, 128, 64, 128, 2, 2, 2, 4, true, 1),
+    TG_CONFIG(1, DT_BF16, B_W4, 64, 64, 128, 2, 2, 2, 8, true, 1),
+    TG_CONFIG(1, DT_BF16, B_W4, 32, 64, 128, 1, 2, 2, 8, true, 1),
 };
 
 ConfigList configs_dequant_w4() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }

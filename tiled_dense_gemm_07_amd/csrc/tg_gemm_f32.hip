@@ -6,12 +6,15 @@
 namespace tg {
 
 static const Config kCfg[] = {
-    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true),
-    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 3, 8, true),
-    TG_CONFIG(0, DT_F32, B_KN, 256, 128, 32, 2, 2, 2, 4, true),
-    TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true),
-    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true),
-    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, false),
+    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 3, 8, true, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 256, 128, 32, 2, 2, 2, 4, true, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, false, 0),
+    TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true, 1),
+    TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true, 1),
+    TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true, 1),
 };
 
 ConfigList configs_gemm_f32() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }

@@ -141,7 +141,7 @@ __device__ __forceinline__ float e8m0_to_f32(u32 e)
 // The kernel.
 // --------------------------------------------------------------------------
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE>
+          bool WIDE, int PIPE>
 struct GemmKernel {
     using TR = DtTraits<DT>;
     static constexpr int ES = TR::ES;
@@ -381,51 +381,68 @@ struct GemmKernel {
     }
 
     // ---- LDS -> MFMA ---------------------------------------------------------
-    static __device__ __forceinline__ void compute(f32x16 (&acc)[FM][FN], const char* stage,
-                                                   int wm, int wn, int lane)
+    // Fragments of one k-slab (two 16-byte chunks deep): lane l reads chunk
+    // 2s + l/32 of LDS row (fragment base + l%32), for FM A-blocks and FN B-blocks.
+    struct Frags {
+        u32x4 a[FM];
+        u32x4 b[FN];
+    };
+
+    static __device__ __forceinline__ void read_frags(Frags& F, const char* stage, int s, int wm,
+                                                      int wn, int lane)
     {
         const char* As = stage;
         const char* Bs = stage + A_STAGE;
         const int lr = lane & 31;
-        const int g = lane >> 5;
+        const int chunk = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < NSLAB; ++s) {
-            const int chunk = 2 * s + g;
-            u32x4 af[FM], bf[FN];
+        for (int fm = 0; fm < FM; ++fm) {
+            const int row = wm * WTM + fm * 32 + lr;
+            F.a[fm] = *(const u32x4*)(As + row * ROWB + ((chunk ^ swz(row)) << 4));
+        }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int row = wm * WTM + fm * 32 + lr;
-                af[fm] = *(const u32x4*)(As + row * ROWB + ((chunk ^ swz(row)) << 4));
-            }
+        for (int fn = 0; fn < FN; ++fn) {
+            const int row = wn * WTN + fn * 32 + lr;
+            F.b[fn] = *(const u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4));
+        }
+    }
+
+    static __device__ __forceinline__ void mfma_slab(f32x16 (&acc)[FM][FN], const Frags& F)
+    {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int row = wn * WTN + fn * 32 + lr;
-                bf[fn] = *(const u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4));
-            }
+                if constexpr (DT == DT_F32) {
+                    // cast whole vectors: clang reads element 0 when
+                    // __builtin_bit_cast is applied to a vector element
+                    const f32x4 bv = __builtin_bit_cast(f32x4, F.b[fn]);
+                    const f32x4 av = __builtin_bit_cast(f32x4, F.a[fm]);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    if constexpr (DT == DT_F32) {
-                        // cast whole vectors: clang reads element 0 when
-                        // __builtin_bit_cast is applied to a vector element
-                        const f32x4 bv = __builtin_bit_cast(f32x4, bf[fn]);
-                        const f32x4 av = __builtin_bit_cast(f32x4, af[fm]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                bv[e], av[e], acc[fm][fn], 0, 0, 0);
-                    } else if constexpr (DT == DT_F16) {
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, bf[fn]), __builtin_bit_cast(f16x8, af[fm]),
-                            acc[fm][fn], 0, 0, 0);
-                    } else {
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, bf[fn]), __builtin_bit_cast(bf16x8, af[fm]),
-                            acc[fm][fn], 0, 0, 0);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[e], av[e],
+                                                                           acc[fm][fn], 0, 0, 0);
+                } else if constexpr (DT == DT_F16) {
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(f16x8, F.b[fn]), __builtin_bit_cast(f16x8, F.a[fm]),
+                        acc[fm][fn], 0, 0, 0);
+                } else {
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, F.b[fn]), __builtin_bit_cast(bf16x8, F.a[fm]),
+                        acc[fm][fn], 0, 0, 0);
                 }
             }
+        }
+    }
+
+    static __device__ __forceinline__ void compute(f32x16 (&acc)[FM][FN], const char* stage,
+                                                   int wm, int wn, int lane)
+    {
+#pragma unroll
+        for (int s = 0; s < NSLAB; ++s) {
+            Frags F;
+            read_frags(F, stage, s, wm, wn, lane);
+            mfma_slab(acc, F);
         }
     }
 
@@ -527,14 +544,100 @@ struct GemmKernel {
 
         epilogue(acc, p, m0, n0, wm, wn, lane);
     }
+
+    // Deep pipeline (two LDS stages, two register staging sets): the global
+    // loads for strip t+3 are issued while strip t is multiplied, so each load
+    // has about two strips of MFMA work to land; strip t+1 is written from
+    // registers into the free LDS stage two slabs before the end of strip t;
+    // and the fragments of slab s+1 are read while slab s is multiplied, the
+    // first slab of the next strip right after the one barrier per strip.
+    static __device__ __forceinline__ void strip_deep(f32x16 (&acc)[FM][FN], Regs& R,
+                                                      Frags& Fa, Frags& Fb, char* smem,
+                                                      const GemmParams& p, int it, int KT,
+                                                      int m0, int n0, int wm, int wn, int tid,
+                                                      int lane)
+    {
+        static_assert(NSLAB % 2 == 0 && NSLAB >= 2, "slab fragments alternate in pairs");
+        char* cur = smem + (it & 1) * STAGE_BYTES;
+        char* nxt = smem + ((it + 1) & 1) * STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < NSLAB; ++s) {
+            Frags& F = (s & 1) ? Fb : Fa;    // slab s
+            Frags& G = (s & 1) ? Fa : Fb;    // slab s + 1 (or slab 0 of the next strip)
+            if (s + 1 < NSLAB)
+                read_frags(G, cur, s + 1, wm, wn, lane);
+            // No branches in the steady state: a strip past the end of K loads as
+            // out-of-range zeros and is written to (or read from) an LDS stage
+            // nothing uses, which keeps the wait counters exact.
+            if (s == NSLAB - 2) {
+                store_lds(R, nxt, tid);
+                load_a(R, p, m0, (it + 3) * BK, tid);
+                load_b(R, p, n0, (it + 3) * BK, tid);
+            }
+            if (s == NSLAB - 1) {
+                __syncthreads();
+                read_frags(G, nxt, 0, wm, wn, lane);
+            }
+            mfma_slab(acc, F);
+        }
+    }
+
+    static __device__ __forceinline__ void run_deep(const GemmParams& p)
+    {
+        static_assert(STAGES == 2, "the deep pipeline uses two LDS stages");
+        __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int wm = wave / WGN;
+        const int wn = wave % WGN;
+        const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const int m0 = t.m * BM;
+        const int n0 = t.n * BN;
+        const int KT = (p.K + BK - 1) / BK;
+
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[fm][fn][r] = 0.0f;
+
+        Regs X, Y;
+        Frags Fa, Fb;
+        // strips at or past KT load as zeros (all offsets out of range)
+        load_a(X, p, m0, 0, tid);
+        load_b(X, p, n0, 0, tid);
+        store_lds(X, smem, tid);
+        load_a(X, p, m0, BK, tid);
+        load_b(X, p, n0, BK, tid);
+        load_a(Y, p, m0, 2 * BK, tid);
+        load_b(Y, p, n0, 2 * BK, tid);
+        __syncthreads();
+        read_frags(Fa, smem, 0, wm, wn, lane);
+        // an even number of strips: a trailing all-zero strip adds nothing
+        for (int it = 0; it < KT; it += 2) {
+            strip_deep(acc, X, Fa, Fb, smem, p, it, KT, m0, n0, wm, wn, tid, lane);
+            strip_deep(acc, Y, Fa, Fb, smem, p, it + 1, KT, m0, n0, wm, wn, tid, lane);
+        }
+        epilogue(acc, p, m0, n0, wm, wn, lane);
+    }
 };
 
+// PIPE 0: one register staging set, STAGES-deep LDS ring.
+// PIPE 1: the deep pipeline above (two register sets, two LDS stages).
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE>
+          bool WIDE, int PIPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64))) void
 gemm_kernel(GemmParams p)
 {
-    GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE>::run(p);
+    using Kern = GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE>;
+    if constexpr (PIPE == 1)
+        Kern::run_deep(p);
+    else
+        Kern::run(p);
 }
 
 }  // namespace tg

@@ -1,0 +1,153 @@
+"""Measured HBM traffic of one kernel launch, from rocprofv3 counters.
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) count traffic between the L2s
+and the memory fabric (MALL hits included, data still in L2 from the previous
+launch excluded).  Their scale is calibrated with one plain elementwise kernel
+that reads and writes a known number of bytes in the same process:
+factor = true bytes / counter bytes.  Two separate counter passes are needed (FETCH_SIZE, then WRITE_SIZE):
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/f -o f -- \\
+        python -m tiled_dense_gemm_07_amd.traffic run --workload bf16_4096_relu
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/w -o w -- \\
+        python -m tiled_dense_gemm_07_amd.traffic run --workload bf16_4096_relu
+    python -m tiled_dense_gemm_07_amd.traffic summarize --workload bf16_4096_relu \\
+        --fetch OUT/f/f_counter_collection.csv --write OUT/w/w_counter_collection.csv \\
+        --out profiles/traffic_bf16_4096_relu.json
+
+The summary records a hash of the HIP sources; the benchmark reports the
+traffic only while the kernels are unchanged since the counters were taken.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written by the calibration copy
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources the kernels are built from."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def run(workload: str, launches: int) -> None:
+    """The program profiled: one calibration copy, then the workload's kernel."""
+    import numpy as np
+    import torch
+
+    from . import binding, synth
+
+    dev = torch.device("cuda:0")
+    # calibration: one elementwise kernel that reads COPY_BYTES and writes
+    # COPY_BYTES (the runtime's own copy engine path is not seen by FETCH_SIZE)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    dst = torch.mul(src, 1.0)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+    w = synth.WORKLOADS[workload]
+    inp = synth.make_inputs(w, integer=False)
+    epi = "relu" if w.relu else None
+    if w.op == "gemm":
+        tdt = {synth.F32: torch.float32, synth.F16: torch.float16, synth.BF16: torch.bfloat16}
+        view = np.int32 if w.dtype == synth.F32 else np.int16
+        A = torch.from_numpy(inp["A"].view(view)).view(tdt[w.dtype]).to(dev)
+        B = torch.from_numpy(inp["B"].view(view)).view(tdt[w.dtype]).to(dev)
+        for _ in range(launches):
+            binding.gemm(A, B, epilogue=epi)
+    else:
+        A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+        Wq = torch.from_numpy(inp["Wq"]).to(dev)
+        Ws = torch.from_numpy(inp["Ws"]).to(dev)
+        for _ in range(launches):
+            binding.dequant_gemm_w4(A, Wq, Ws, epilogue=epi)
+    torch.cuda.synchronize()
+    print("traffic run done: %s x%d" % (workload, launches))
+
+
+def _read(path: str, counter: str):
+    """(calibration KiB, [kernel KiB per launch]) from a counter_collection CSV.
+    The calibration kernel is the only other kernel the profiled program runs."""
+    other, kern = [], []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "gemm_kernel" in r["Kernel_Name"]:
+                kern.append(v)
+            else:
+                other.append((r["Kernel_Name"], v))
+    if len(other) != 1:
+        raise SystemExit("expected exactly one calibration kernel, found: %s" % other)
+    return other[0][1], kern
+
+
+def summarize(workload: str, fetch_csv: str, write_csv: str, out: str) -> dict:
+    from . import synth
+
+    w = synth.WORKLOADS[workload]
+    f_copy, f_k = _read(fetch_csv, "FETCH_SIZE")
+    w_copy, w_k = _read(write_csv, "WRITE_SIZE")
+    if not f_k or not w_k or f_copy is None or w_copy is None:
+        raise SystemExit("counter files lack the copy or the kernel rows")
+    f_factor = COPY_BYTES / (f_copy * 1024.0)
+    w_factor = COPY_BYTES / (w_copy * 1024.0)
+    fetch = f_factor * 1024.0 * sum(f_k) / len(f_k)
+    write = w_factor * 1024.0 * sum(w_k) / len(w_k)
+    rec = {
+        "workload": workload,
+        "source_hash": source_hash(),
+        "copy_bytes": COPY_BYTES,
+        "fetch_size_kib_copy": f_copy, "write_size_kib_copy": w_copy,
+        "fetch_factor": f_factor, "write_factor": w_factor,
+        "fetch_size_kib_per_launch": sum(f_k) / len(f_k),
+        "write_size_kib_per_launch": sum(w_k) / len(w_k),
+        "hbm_fetch_bytes_per_launch": fetch,
+        "hbm_write_bytes_per_launch": write,
+        "hbm_bytes_per_launch": fetch + write,
+        "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
+        "traffic_over_algorithmic": (fetch + write) / w.algorithmic_bytes(),
+        "launches": len(f_k),
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--launches", type=int, default=3)
+    s = sub.add_parser("summarize")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "run":
+        run(args.workload, args.launches)
+    else:
+        print(json.dumps(summarize(args.workload, args.fetch, args.write, args.out), indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
