@@ -51,7 +51,7 @@ void config_name(const Config& c, char* buf, size_t len)
     static const char* dn[] = {"f32", "f16", "bf16"};
     snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s", c.op == 0 ? "gemm" : "w4",
              dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
-             c.pipe ? "_deep" : "", c.wide ? "" : "_narrow");
+             c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : ""), c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -71,9 +71,9 @@ struct Pref {
     const char* names[4];
 };
 const Pref kPrefs[] = {
-    {0, 2, {"gemm_bf16_256x256x64_w2x4_s2_g4", "gemm_bf16_128x128x64_w2x2_s2_g8_deep",
+    {0, 2, {"gemm_bf16_256x256x32_w2x2_s4_g4_dma", "gemm_bf16_128x128x32_w2x2_s4_g8_dma",
             "gemm_bf16_64x64x64_w2x2_s2_g8_deep", nullptr}},
-    {0, 1, {"gemm_f16_256x256x64_w2x4_s2_g4", "gemm_f16_128x128x64_w2x2_s2_g8_deep",
+    {0, 1, {"gemm_f16_256x256x32_w2x2_s4_g4_dma", "gemm_f16_128x128x32_w2x2_s4_g8_dma",
             "gemm_f16_64x64x64_w2x2_s2_g8_deep", nullptr}},
     {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x32_w2x2_s2_g8_deep", nullptr,
             nullptr}},

@@ -14,7 +14,7 @@ struct Config {
     int stages;    // LDS ring depth
     int group_m;   // swizzle group (tile rows)
     bool wide;     // 16-byte global loads (aligned operands) vs element loads
-    int pipe;      // 0: single staging set; 1: deep pipeline
+    int pipe;      // 0: single staging set; 1: deep pipeline; 2: LDS-DMA pipeline
     const void* kernel;
 };
 
@@ -35,4 +35,12 @@ ConfigList configs_dequant_w4();
     {                                                                                          \
         OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE,                                      \
             (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE> \
+    }
+
+// Configurations of the LDS-DMA kernel (16-bit operands, BK = 32, NS stages).
+#define TG_CONFIG_DMA(DT, BM, BN, WGM, WGN, NS, GM)                                         \
+    tg::Config                                                                             \
+    {                                                                                      \
+        0, DT, BM, BN, 32, WGM, WGN, NS, GM, true, 2,                                      \
+            (const void*)&tg::gemm_dma_kernel<DT, BM, BN, WGM, WGN, NS, GM>                \
     }

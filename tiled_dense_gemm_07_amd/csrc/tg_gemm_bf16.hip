@@ -1,20 +1,22 @@
 // bf16 GEMM kernel configurations (instantiations of the tiled kernel template).
 #include "tg_configs.h"
 #include "tg_kernel.h"
+#include "tg_kernel_dma.h"
 
 namespace tg {
 
 static const Config kCfg[] = {
-    TG_CONFIG(0, DT_BF16, B_KN, 256, 256, 64, 2, 2, 2, 4, true, 0),
+    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 4, 4),
+    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 3, 4),
+    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 5, 4),
+    TG_CONFIG_DMA(DT_BF16, 256, 128, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, 128, 128, 2, 2, 4, 8),
     TG_CONFIG(0, DT_BF16, B_KN, 256, 256, 64, 2, 4, 2, 4, true, 0),
-    TG_CONFIG(0, DT_BF16, B_KN, 256, 128, 64, 2, 2, 2, 4, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 128, 128, 64, 2, 2, 2, 8, true, 0),
-    TG_CONFIG(0, DT_BF16, B_KN, 128, 128, 64, 2, 2, 3, 8, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 128, 64, 64, 2, 2, 2, 8, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 64, 64, 64, 2, 2, 2, 8, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 64, 64, 64, 2, 2, 2, 8, false, 0),
-    TG_CONFIG(0, DT_BF16, B_KN, 256, 256, 64, 2, 2, 2, 4, true, 1),
-    TG_CONFIG(0, DT_BF16, B_KN, 256, 256, 64, 2, 4, 2, 4, true, 1),
     TG_CONFIG(0, DT_BF16, B_KN, 128, 128, 64, 2, 2, 2, 8, true, 1),
     TG_CONFIG(0, DT_BF16, B_KN, 64, 64, 64, 2, 2, 2, 8, true, 1),
 };
