@@ -92,8 +92,11 @@ def test_forced_config_errors(lib):
     assert lib.tg_dequant_gemm_w4_config(nw, 4, 4, 64, PA, PB, PS, PC, 0, None) == NOCFG
     # a 16-byte-load configuration refuses operands that are not 16-byte aligned
     names = binding.list_configs(0, 2)
-    wide = names.index("gemm_bf16_256x256x64_w2x2_s2_g4")
-    assert lib.tg_gemm_config(wide, 4, 4, 4, 2, PA + 2, PB, PC, 0, None) == NOCFG
+    for name in ("gemm_bf16_256x256x32_w2x2_s4_g4_dma", "gemm_bf16_128x128x64_w2x2_s2_g8"):
+        wide = names.index(name)
+        assert lib.tg_gemm_config(wide, 4, 4, 4, 2, PA + 2, PB, PC, 0, None) == NOCFG
+        # rows that are not whole 16-byte chunks (K % 8 != 0) are refused too
+        assert lib.tg_gemm_config(wide, 4, 4, 12, 2, PA, PB, PC, 0, None) == NOCFG
 
 
 def test_launch_failure_is_reported(lib, monkeypatch):

@@ -88,7 +88,7 @@ def _read(path: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if "gemm_kernel" in r["Kernel_Name"]:
+            if "tg::gemm" in r["Kernel_Name"]:
                 kern.append(v)
             else:
                 other.append((r["Kernel_Name"], v))
