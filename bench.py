@@ -166,31 +166,41 @@ def main():
     for _ in range(args.warmup):
         fn()
     torch.cuda.synchronize()
-    # timed region: exactly K steps
+    # timed region: exactly K steps; an event pair on the kernel's stream around
+    # each launch gives the kernel's own duration in the same (thermal) state
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    end_ev = torch.cuda.Event(enable_timing=True)
-    start_ev.record(stream)
-    for _ in range(args.steps):
+    for a, b in evs:
+        a.record(stream)
         fn()
-    end_ev.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops * args.steps / wall / 1e12
+    kt = sorted(a.elapsed_time(b) for a, b in evs)
+    kernel_ms = sum(kt) / len(kt)
 
-    # per-launch kernel duration from HIP events on the kernel's stream
-    kt = time_kernel(fn, stream, launches=args.steps, warmup=2)
-    achieved = w.flops / (kt["mean_ms"] * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype_name(w)]
     traffic = load_traffic(HEADLINE)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
-                "kernel_ms": round(kt["mean_ms"], 5),
-                "events_span_ms_per_step": round(start_ev.elapsed_time(end_ev) / args.steps, 5),
+                "kernel_ms": round(kernel_ms, 5),
+                "kernel_ms_min": round(kt[0], 5), "kernel_ms_median": round(kt[len(kt) // 2], 5),
                 "algorithmic_flops_per_launch": w.flops,
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes()}
+    # the matrix cores' own ceiling on this card: the same MFMA work on
+    # register operands, no memory traffic (power-limited clock)
+    try:
+        from tiled_dense_gemm_07_amd import clockprobe
+
+        roofline["mfma_ceiling"] = [clockprobe.measure("random"), clockprobe.measure("zeros")]
+    except Exception as e:  # the probe is context only
+        roofline["mfma_ceiling"] = "unavailable: %s" % e
 
     workloads = {}
     if not args.no_workloads:

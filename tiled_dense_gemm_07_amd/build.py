@@ -17,6 +17,9 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilegemm.so")
 SOURCES = ["tg_api.hip", "tg_gemm_f32.hip", "tg_gemm_f16.hip", "tg_gemm_bf16.hip",
            "tg_dequant_w4.hip"]
+# measurement-only probe (sustained clock of the matrix cores); its own library
+PROBE_LIB = os.path.join(HERE, "libtgprobe.so")
+PROBE_SOURCES = ["tg_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -24,10 +27,16 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 
 def build(verbose: bool = False) -> str:
+    lib = _build_lib(SOURCES, LIB, verbose)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    return lib
+
+
+def _build_lib(sources, lib_path: str, verbose: bool) -> str:
     os.makedirs(BUILD, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-c",
@@ -47,11 +56,11 @@ def build(verbose: bool = False) -> str:
         for src, text in failed:
             sys.stderr.write("---- %s ----\n%s\n" % (src, text))
         raise RuntimeError("hipcc failed for: " + ", ".join(s for s, _ in failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib_path + ".tmp%d" % os.getpid()
     subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs,
                    check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

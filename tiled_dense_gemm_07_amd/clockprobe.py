@@ -1,0 +1,86 @@
+"""Sustained matrix-core clock and the bf16 MFMA ceiling on this card.
+
+Runs the probe kernel of csrc/tg_probe.hip (the bf16 GEMM's 256-workgroup
+grid and exact MFMA count at 4096^3, on register operands, with no memory
+traffic in the loop) once on random N(0, 1) bf16 operands and once on zeros,
+and reports TFLOP/s (HIP events on the launch stream) and the average shader
+clock that workgroup 0 measured (s_memtime ticks over 100 MHz s_memrealtime
+ticks).  This is the throughput the chip sustains for the GEMM's MFMA work
+alone under its power limit; the GEMM kernel cannot exceed it.
+
+    python -m tiled_dense_gemm_07_amd.clockprobe
+"""
+
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROBE_LIB = os.path.join(HERE, "libtgprobe.so")
+GRID = 256          # tiles of the 4096^3 bf16 GEMM at 256 x 256
+STRIPS = 128        # 4096 / 32
+FLOPS = 2.0 * 4096 ** 3
+
+
+def load():
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError("libtgprobe.so is missing: run python -m tiled_dense_gemm_07_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tgp_operand_words.argtypes = [ctypes.c_int]
+    lib.tgp_operand_words.restype = ctypes.c_int
+    lib.tgp_mfma_ceiling.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int,
+                                                             ctypes.c_void_p]
+    lib.tgp_mfma_ceiling.restype = ctypes.c_int
+    return lib
+
+
+def measure(data: str = "random", launches: int = 20, warmup: int = 3) -> dict:
+    import torch
+
+    lib = load()
+    dev = torch.device("cuda:0")
+    words = lib.tgp_operand_words(GRID)
+    g = torch.Generator(device=dev).manual_seed(20260001)
+    if data == "random":
+        src = torch.randn((words * 8,), generator=g, device=dev).to(torch.bfloat16)
+    else:
+        src = torch.zeros((words * 8,), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((GRID * 256,), dtype=torch.float32, device=dev)
+    clk = torch.zeros((2,), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch():
+        rc = lib.tgp_mfma_ceiling(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(clk.data_ptr()), GRID, STRIPS, s)
+        if rc != 0:
+            raise RuntimeError("probe launch failed (%d)" % rc)
+
+    for _ in range(warmup):
+        launch()
+    stream.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for a, b in evs:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    stream.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ts[len(ts) // 2]
+    ticks, real = clk.cpu().tolist()
+    return {"data": data, "median_ms": round(med, 5), "tflops": round(FLOPS / med / 1e9, 1),
+            "clock_ghz": round(ticks / (real * 10.0), 3) if real > 0 else None}
+
+
+def main():
+    for data in ("random", "zeros"):
+        print(json.dumps(measure(data)), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

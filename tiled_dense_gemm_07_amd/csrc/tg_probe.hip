@@ -1,0 +1,96 @@
+// Power / clock ceiling probe for the bf16 roofline (measurement only; not
+// part of the GEMM path and not exported by libtilegemm).
+//
+// One workgroup of 4 waves per tile of the 4096^3 bf16 GEMM's 256-tile grid,
+// each wave issuing exactly the MFMA work of the GEMM kernel (128 strips x 32
+// v_mfma_f32_32x32x16_bf16 into 16 accumulators of 32x32), but on register
+// operands loaded once: no LDS, no global traffic in the loop.  The operands
+// come from the caller's buffer (random or zero bit patterns), so the run shows
+// how the sustained clock depends on the data the matrix cores multiply.
+// Workgroup 0 reads the shader clock counter (s_memtime) and the fixed
+// 100 MHz counter (s_memrealtime) around its loop: their ratio is the average
+// shader clock during the kernel.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kFrag = 8;  // operand fragments per wave (16 bytes per lane each)
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+mfma_ceiling(const u32x4* __restrict__ src, float* __restrict__ out, uint64_t* __restrict__ clk,
+             int strips)
+{
+    const int tid = threadIdx.x;
+    uint64_t c0 = 0, r0 = 0;
+    if (blockIdx.x == 0 && tid == 0) {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    const u32x4* s = src + (size_t)(blockIdx.x * 256 + tid) * 2 * kFrag;
+    u32x4 a[kFrag], b[kFrag];
+#pragma unroll
+    for (int i = 0; i < kFrag; ++i) {
+        a[i] = s[i];
+        b[i] = s[kFrag + i];
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+    for (int t = 0; t < strips; ++t) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, b[(j + 4 * sl) % kFrag]),
+                        __builtin_bit_cast(bf16x8, a[(i + 4 * sl + t) % kFrag]), acc[i][j], 0, 0,
+                        0);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sum += acc[i][j][r];
+    out[blockIdx.x * 256 + tid] = sum;
+    if (blockIdx.x == 0 && tid == 0) {
+        clk[0] = __builtin_amdgcn_s_memtime() - c0;
+        clk[1] = __builtin_amdgcn_s_memrealtime() - r0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Operand buffer: grid * 256 * 2 * kFrag 16-byte words.  out: grid * 256
+// floats.  clk: 2 words (shader-clock ticks, 100 MHz ticks).  Returns 0 on a
+// successful launch.
+int tgp_operand_words(int grid) { return grid * 256 * 2 * kFrag; }
+
+int tgp_mfma_ceiling(const void* src, void* out, void* clk, int grid, int strips,
+                     hipStream_t stream)
+{
+    if (!src || !out || !clk || grid < 1 || strips < 1)
+        return 1;
+    hipLaunchKernelGGL(mfma_ceiling, dim3(grid), dim3(256), 0, stream, (const u32x4*)src,
+                       (float*)out, (uint64_t*)clk, strips);
+    return hipPeekAtLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

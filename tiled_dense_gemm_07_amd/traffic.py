@@ -33,9 +33,14 @@ COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written by the calibration copy
 
 
 def source_hash() -> str:
-    """Hash of the HIP sources the kernels are built from."""
+    """Hash of the HIP sources the library's kernels are built from (the
+    measurement-only probe source is not one of them)."""
+    from .build import PROBE_SOURCES
+
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        if os.path.basename(p) in PROBE_SOURCES:
+            continue
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
