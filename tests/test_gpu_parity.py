@@ -119,7 +119,12 @@ def test_every_w4_config():
 
 @pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
 @pytest.mark.parametrize("shape", [(1, 8, 32), (5, 24, 64), (33, 100, 96), (130, 72, 320),
-                                   (257, 264, 128)], ids=lambda s: "x".join(map(str, s)))
+                                   (257, 264, 128),
+                                   # few rows (weight-streaming kernel): K not a multiple of
+                                   # 128 (byte scale loads), partial 512-wide rounds, ragged N
+                                   (16, 100, 1056), (7, 264, 1152), (1, 33, 4096),
+                                   (16, 8200, 2048), (3, 40, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_dequant_small(shape, integer):
     M, N, K = shape
     A, Wq, Ws = synth.dequant_inputs(M, N, K, 808 + M, 909 + N, 1010 + K, integer)
@@ -143,6 +148,30 @@ def test_dequant_scale_range():
     say("w4 scale range")
     got = run_w4(A, Wq, Ws)
     assert np.array_equal(got, oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws)))
+
+
+def test_dequant_scale_range_few_rows():
+    """As above, through the weight-streaming kernel (M <= 16)."""
+    M, N, K = 16, 96, 1024
+    r = np.random.Generator(np.random.PCG64(78))
+    A = synth.to_storage(r.integers(-4, 5, size=(M, K)).astype(np.float32), BF16)
+    Wq = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    e_row = r.integers(2, 201, size=N)
+    e_row[0], e_row[1] = 2, 200
+    Ws = np.repeat(e_row[:, None], K // 32, axis=1).astype(np.uint8)
+    say("w4 scale range, few rows")
+    got = run_w4(A, Wq, Ws)
+    assert np.array_equal(got, oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws)))
+
+
+def test_dequant_few_rows_deterministic():
+    """The weight-streaming kernel adds its per-wave partial sums in a fixed order."""
+    w = synth.WORKLOADS["w4_16x8192x8192"]
+    inp = synth.make_inputs(w, integer=False)
+    say("w4 determinism M=16")
+    first = run_w4(inp["A"], inp["Wq"], inp["Ws"])
+    for _ in range(3):
+        assert np.array_equal(run_w4(inp["A"], inp["Wq"], inp["Ws"]), first)
 
 
 WORKLOADS = ["f32_512", "f16_1024", "f32_4096", "bf16_4096_relu", "bf16_4000x4032x4096_relu",

@@ -51,7 +51,8 @@ void config_name(const Config& c, char* buf, size_t len)
     static const char* dn[] = {"f32", "f16", "bf16"};
     snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s", c.op == 0 ? "gemm" : "w4",
              dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
-             c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : ""), c.wide ? "" : "_narrow");
+             c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
+             c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -83,7 +84,18 @@ const Pref kPrefs[] = {
 
 const Config* find_by_name(int op, int dtype, const char* name);
 
-const Config* heuristic(int op, int dtype, int64_t M, int64_t N, bool wide)
+// The weight-streaming dequant kernel for this K (the variant with dword
+// scale loads needs K % 128 == 0), or nullptr.
+const Config* gemv_for(int64_t K)
+{
+    ConfigList L = list_for(TG_OP_DEQUANT_W4, TG_BF16);
+    for (int i = 0; i < L.count; ++i)
+        if (L.items[i].pipe == 3 && K % L.items[i].bk == 0)
+            return &L.items[i];
+    return nullptr;
+}
+
+const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide)
 {
     ConfigList L = list_for(op, dtype);
     if (!wide) {
@@ -91,6 +103,11 @@ const Config* heuristic(int op, int dtype, int64_t M, int64_t N, bool wide)
             if (!L.items[i].wide)
                 return &L.items[i];
         return nullptr;
+    }
+    // few activation rows: the run time is the weight stream from HBM
+    if (op == TG_OP_DEQUANT_W4 && M <= 16) {
+        if (const Config* c = gemv_for(K))
+            return c;
     }
     for (const Pref& pr : kPrefs) {
         if (pr.op != op || pr.dtype != dtype)
@@ -139,11 +156,11 @@ const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, 
         if (e.op == op && (op == TG_OP_DEQUANT_W4 || e.dtype == dtype) && e.M == M && e.N == N &&
             e.K == K) {
             const Config* c = find_by_name(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, e.config);
-            if (c && c->wide == wide)
+            if (c && c->wide == wide && K % c->bk == 0)
                 return c;
         }
     }
-    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, wide);
+    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, K, wide);
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
@@ -262,6 +279,8 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
         return TG_ERR_NO_CONFIG;
     if (c->wide && !wide)
         return TG_ERR_NO_CONFIG;
+    if (c->pipe == 3 && K % c->bk != 0)
+        return TG_ERR_NO_CONFIG;  // a forced weight-streaming config needs K % bk == 0
     tg::GemmParams p{};
     p.A = A;
     p.B = Wq;

@@ -14,7 +14,8 @@ struct Config {
     int stages;    // LDS ring depth
     int group_m;   // swizzle group (tile rows)
     bool wide;     // 16-byte global loads (aligned operands) vs element loads
-    int pipe;      // 0: single staging set; 1: deep pipeline; 2: LDS-DMA pipeline
+    int pipe;      // 0: single staging set; 1: deep pipeline; 2: LDS-DMA pipeline;
+                   // 3: weight-streaming dequant kernel for few rows (K % bk == 0)
     const void* kernel;
 };
 

@@ -2,10 +2,14 @@
 // B strip read as packed E2M1 codes + E8M0 scales and expanded to bf16 in LDS.
 #include "tg_configs.h"
 #include "tg_kernel.h"
+#include "tg_kernel_gemv_w4.h"
 
 namespace tg {
 
 static const Config kCfg[] = {
+    // few activation rows: weight-streaming kernel (bk = the K multiple it needs)
+    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, 3, (const void*)&gemv_w4_kernel<true>},
+    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, 3, (const void*)&gemv_w4_kernel<false>},
     TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true, 0),
