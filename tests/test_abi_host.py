@@ -99,6 +99,20 @@ def test_forced_config_errors(lib):
         assert lib.tg_gemm_config(wide, 4, 4, 12, 2, PA, PB, PC, 0, None) == NOCFG
 
 
+def test_forced_dequant_config_requirements(lib):
+    """The DMA dequant kernel needs whole 128-wide strips and 4-byte aligned
+    scale bytes; the weight-streaming kernel needs K % bk == 0.  A forced
+    configuration that cannot run the call is refused before any HIP call."""
+    names = binding.list_configs(1, 2)
+    d = lib.tg_dequant_gemm_w4_config
+    for name in names:
+        idx = names.index(name)
+        if name.endswith("_dma") or name.startswith("w4_bf16_16x32x128_"):
+            assert d(idx, 64, 64, 96, PA, PB, PS, PC, 0, None) == NOCFG, name
+        if name.endswith("_dma"):
+            assert d(idx, 64, 64, 256, PA, PB, PS + 2, PC, 0, None) == NOCFG, name
+
+
 def test_launch_failure_is_reported(lib, monkeypatch):
     # TG_FAULT=launch makes the launcher report a HIP failure after validation
     # and before any HIP call.

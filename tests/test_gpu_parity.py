@@ -133,6 +133,26 @@ def test_dequant_small(shape, integer):
     check_full(got, oracle.dequant_w4_f64(A, Wq, Ws), BF16, integer)
 
 
+@pytest.mark.parametrize("shape", [(300, 264, 256), (70, 130, 384), (64, 128, 128),
+                                   (256, 8192, 1024), (1, 200, 640)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_every_w4_config_ragged(shape):
+    """Every dequant configuration this shape allows, forced, with integer
+    activations: bit-exact (ragged M and N, several strip counts)."""
+    M, N, K = shape
+    A, Wq, Ws = synth.dequant_inputs(M, N, K, 515 + M, 616 + N, 717 + K, integer=True)
+    want = oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws, relu=True))
+    for idx, name in _configs(1, BF16):
+        if name.endswith("_narrow"):
+            continue
+        bk = int(name.split("_")[2].split("x")[2])
+        if (name.endswith("_dma") or name.endswith("_gemv")) and K % bk:
+            continue
+        say("w4 config %d %s %s" % (idx, name, shape))
+        got = run_w4(A, Wq, Ws, relu=True, config=idx)
+        assert np.array_equal(got, want), name
+
+
 def test_dequant_scale_range():
     """Scale bytes across [2, 200] with integer activations: still bit-exact.
 

@@ -78,8 +78,8 @@ const Pref kPrefs[] = {
             "gemm_f16_64x64x64_w2x2_s2_g8_deep", nullptr}},
     {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x32_w2x2_s2_g8_deep", nullptr,
             nullptr}},
-    {1, 2, {"w4_bf16_128x64x128_w2x2_s2_g4_deep", "w4_bf16_64x64x128_w2x2_s2_g8_deep",
-            "w4_bf16_32x64x128_w1x2_s2_g8_deep", nullptr}},
+    {1, 2, {"w4_bf16_64x128x128_w2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
+            "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
 };
 
 const Config* find_by_name(int op, int dtype, const char* name);
@@ -95,7 +95,20 @@ const Config* gemv_for(int64_t K)
     return nullptr;
 }
 
-const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide)
+// Whether configuration c can run this call.  wide: 16-byte aligned operands
+// with whole 16-byte rows; ws4: the scale bytes start 4-byte aligned.
+bool usable(const Config& c, int64_t K, bool wide, bool ws4)
+{
+    if (c.wide && !wide)
+        return false;
+    if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && K % c.bk != 0)
+        return false;  // whole strips / rounds of bk
+    if (c.op == TG_OP_DEQUANT_W4 && c.pipe == 2 && !ws4)
+        return false;  // scale bytes are copied as dwords
+    return true;
+}
+
+const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide, bool ws4)
 {
     ConfigList L = list_for(op, dtype);
     if (!wide) {
@@ -117,7 +130,7 @@ const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool
             if (!name)
                 break;
             const Config* c = find_by_name(op, dtype, name);
-            if (!c)
+            if (!c || !usable(*c, K, wide, ws4))
                 continue;
             last = c;
             // small M: a tile taller than M wastes matrix-core work
@@ -130,7 +143,7 @@ const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool
             return last;
     }
     for (int i = 0; i < L.count; ++i)
-        if (L.items[i].wide)
+        if (L.items[i].wide && usable(L.items[i], K, wide, ws4))
             return &L.items[i];
     return nullptr;
 }
@@ -147,7 +160,8 @@ const Config* find_by_name(int op, int dtype, const char* name)
     return nullptr;
 }
 
-const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide)
+const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide,
+                            bool ws4)
 {
     for (size_t i = 0; i < sizeof(kTuned) / sizeof(kTuned[0]); ++i) {
         const TunedEntry& e = kTuned[i];
@@ -156,11 +170,11 @@ const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, 
         if (e.op == op && (op == TG_OP_DEQUANT_W4 || e.dtype == dtype) && e.M == M && e.N == N &&
             e.K == K) {
             const Config* c = find_by_name(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, e.config);
-            if (c && c->wide == wide && K % c->bk == 0)
+            if (c && c->wide == wide && usable(*c, K, wide, ws4))
                 return c;
         }
     }
-    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, K, wide);
+    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, K, wide, ws4);
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
@@ -234,7 +248,7 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         return TG_ERR_ALIAS;
     const int v = vec_of(dtype);
     const bool wide = aligned16(A) && aligned16(B) && (K % v == 0) && (N % v == 0);  // NULL is aligned
-    const Config* c = forced ? forced : select_config(TG_OP_GEMM, dtype, M, N, K, wide);
+    const Config* c = forced ? forced : select_config(TG_OP_GEMM, dtype, M, N, K, wide, false);
     if (!c)
         return TG_ERR_NO_CONFIG;
     if (c->wide && !wide)
@@ -274,13 +288,13 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
         overlaps(C, cbytes, Ws, (size_t)(N * K / 32)))
         return TG_ERR_ALIAS;
     const bool wide = aligned16(A) && aligned16(Wq);
-    const Config* c = forced ? forced : select_config(TG_OP_DEQUANT_W4, TG_BF16, M, N, K, wide);
+    const bool ws4 = ((uintptr_t)Ws & 3u) == 0;
+    const Config* c =
+        forced ? forced : select_config(TG_OP_DEQUANT_W4, TG_BF16, M, N, K, wide, ws4);
     if (!c)
         return TG_ERR_NO_CONFIG;
-    if (c->wide && !wide)
-        return TG_ERR_NO_CONFIG;
-    if (c->pipe == 3 && K % c->bk != 0)
-        return TG_ERR_NO_CONFIG;  // a forced weight-streaming config needs K % bk == 0
+    if (!usable(*c, K, wide, ws4))
+        return TG_ERR_NO_CONFIG;  // a forced configuration this call cannot use
     tg::GemmParams p{};
     p.A = A;
     p.B = Wq;
@@ -350,7 +364,7 @@ tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
         return TG_ERR_BAD_SHAPE;
     // assume aligned operands (what torch allocations give)
     const bool wide = op == TG_OP_DEQUANT_W4 || (K % vec_of(dt) == 0 && N % vec_of(dt) == 0);
-    const Config* c = select_config(op, dt, M, N, K, wide);
+    const Config* c = select_config(op, dt, M, N, K, wide, true);
     if (!c)
         return TG_ERR_NO_CONFIG;
     char name[96];
