@@ -39,15 +39,17 @@ OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x
 
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken with the configuration the library launches now and on that
+    kernel's current sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    from tiled_dense_gemm_07_amd.traffic import source_hash
+    from tiled_dense_gemm_07_amd.traffic import source_hash, workload_config
 
-    if rec.get("source_hash") != source_hash():
+    config = workload_config(workload)
+    if rec.get("config") != config or rec.get("source_hash") != source_hash(config):
         return None
     return rec
 
@@ -102,6 +104,42 @@ def time_kernel(fn, stream, launches: int, warmup: int):
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0],
             "max_ms": ts[-1]}
+
+
+# Workloads whose run time is the operand stream from HBM: also timed with
+# the operands rotated over copies larger than the caches (256 MB MALL,
+# 8 x 4 MB L2), so every launch reads its bytes from HBM.
+MEMORY_BOUND = ("w4_1x8192x8192", "w4_16x8192x8192")
+COLD_BYTES = 1 << 30
+
+
+def time_cold(w, tensors, stream, launches: int = 40):
+    """Kernel duration with each launch on a different copy of the inputs
+    (together COLD_BYTES or more), so nothing is cache-resident."""
+    import torch
+
+    from tiled_dense_gemm_07_amd import binding
+
+    per = sum(x.numel() * x.element_size() for x in tensors)
+    copies = max(4, -(-COLD_BYTES // per))
+    sets = [tuple(x.clone() for x in tensors) for _ in range(copies)]
+    fns = [launcher(w, s_, stream) for s_ in sets]
+    for f in fns[:4]:
+        f()
+    stream.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fns[i % copies]()
+        b.record(stream)
+    stream.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    mean = sum(ts) / len(ts)
+    gbs = w.algorithmic_bytes() / (mean * 1e-3) / 1e9
+    del sets, fns
+    return {"copies": copies, "kernel_ms": round(mean, 5), "kernel_ms_min": round(ts[0], 5),
+            "gbs_algorithmic": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def dtype_name(w):
@@ -218,6 +256,8 @@ def main():
                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                 "config": binding.query_config(0 if ow.op == "gemm" else 1, ow.M, ow.N, ow.K,
                                                ow.dtype)}
+            if name in MEMORY_BOUND:
+                workloads[name]["cold"] = time_cold(ow, t, stream)
             del t
             torch.cuda.empty_cache()
 

@@ -14,8 +14,9 @@ factor = true bytes / counter bytes.  Two separate counter passes are needed (FE
         --fetch OUT/f/f_counter_collection.csv --write OUT/w/w_counter_collection.csv \\
         --out profiles/traffic_bf16_4096_relu.json
 
-The summary records a hash of the HIP sources; the benchmark reports the
-traffic only while the kernels are unchanged since the counters were taken.
+The summary records which compiled configuration ran and a hash of the
+sources that kernel is built from; the benchmark reports the traffic only
+while both still match.
 """
 
 from __future__ import annotations
@@ -32,19 +33,42 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written by the calibration copy
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources the library's kernels are built from (the
-    measurement-only probe source is not one of them)."""
-    from .build import PROBE_SOURCES
+# Sources each kernel family is built from (its header, the shared helpers and
+# the scheduler); a change to any of them invalidates a stored traffic record.
+_FAMILY_SOURCES = {
+    "dma": ["tg_kernel_dma.h", "tg_kernel.h", "tg_sched.h"],
+    "dma_w4": ["tg_kernel_dma_w4.h", "tg_kernel_dma.h", "tg_kernel.h", "tg_sched.h"],
+    "gemv": ["tg_kernel_gemv_w4.h", "tg_kernel.h"],
+    "tiled": ["tg_kernel.h", "tg_sched.h"],
+}
 
+
+def kernel_family(config: str) -> str:
+    if config.startswith("w4_") and "_dma" in config:
+        return "dma_w4"
+    if "_dma" in config:
+        return "dma"
+    if "_gemv" in config:
+        return "gemv"
+    return "tiled"
+
+
+def source_hash(config: str) -> str:
+    """Hash of the HIP sources the kernel of `config` is built from."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        if os.path.basename(p) in PROBE_SOURCES:
-            continue
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in _FAMILY_SOURCES[kernel_family(config)]:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def workload_config(workload: str) -> str:
+    """The configuration the library launches for the workload (aligned operands)."""
+    from . import binding, synth
+
+    w = synth.WORKLOADS[workload]
+    return binding.query_config(0 if w.op == "gemm" else 1, w.M, w.N, w.K, w.dtype).split()[0]
 
 
 def run(workload: str, launches: int) -> None:
@@ -93,7 +117,7 @@ def _read(path: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if "tg::gemm" in r["Kernel_Name"]:
+            if "tg::" in r["Kernel_Name"]:
                 kern.append(v)
             else:
                 other.append((r["Kernel_Name"], v))
@@ -114,9 +138,11 @@ def summarize(workload: str, fetch_csv: str, write_csv: str, out: str) -> dict:
     w_factor = COPY_BYTES / (w_copy * 1024.0)
     fetch = f_factor * 1024.0 * sum(f_k) / len(f_k)
     write = w_factor * 1024.0 * sum(w_k) / len(w_k)
+    config = workload_config(workload)
     rec = {
         "workload": workload,
-        "source_hash": source_hash(),
+        "config": config,
+        "source_hash": source_hash(config),
         "copy_bytes": COPY_BYTES,
         "fetch_size_kib_copy": f_copy, "write_size_kib_copy": w_copy,
         "fetch_factor": f_factor, "write_factor": w_factor,
