@@ -51,7 +51,8 @@ typedef enum {
     TG_ERR_BAD_EPILOGUE = 4, /* epilogue not one of tg_epilogue                   */
     TG_ERR_ALIAS = 5,        /* C overlaps an input                               */
     TG_ERR_NO_CONFIG = 6,    /* forced config index out of range / wrong op       */
-    TG_ERR_HIP = 7           /* the HIP runtime reported an error at launch       */
+    TG_ERR_HIP = 7,          /* the HIP runtime reported an error at launch       */
+    TG_ERR_BAD_LAYOUT = 8    /* trans_a / trans_b not 0 or 1                      */
 } tg_status;
 
 typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
@@ -75,6 +76,28 @@ typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1 } tg_op;
  */
 tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, const void* B,
                   void* C, tg_epilogue epi, tg_stream_t stream);
+
+/*
+ * C = epilogue(op(A) x op(B)) with either operand stored transposed: the
+ * operand layouts of the backward products of the mhpq.cn page's autograd
+ * wrapper (section 3.4: dA = dC x B^T, dB = A^T x dC) and the column-major
+ * option the gtnt.cn page names (section 4.3).
+ *   trans_a = 0: A is [M][K] row-major (as tg_gemm); 1: A is stored [K][M]
+ *                row-major, i.e. op(A) = (stored A)^T, M x K.
+ *   trans_b = 0: B is [K][N] row-major (as tg_gemm); 1: B is stored [N][K]
+ *                row-major, i.e. op(B) = (stored B)^T, K x N.
+ *   C: [M][N] row-major.  Same arithmetic, epilogue and rounding as tg_gemm;
+ *   tg_gemm_ex(..., A, 0, B, 0, ...) is tg_gemm.
+ * Transposed layouts are compiled for 16-bit operands (fp16, bf16) whose
+ * pointers are 16-byte aligned and whose stored rows are whole 16-byte chunks
+ * (leading dimension a multiple of 8); other transposed calls return
+ * TG_ERR_NO_CONFIG before any HIP call.
+ * Errors: as tg_gemm; TG_ERR_BAD_LAYOUT (trans_a or trans_b not 0 or 1),
+ *   TG_ERR_NO_CONFIG (see above), TG_ERR_BAD_SHAPE also when trans_a and
+ *   64 * M * element_size exceeds 2^31 - 1.
+ */
+tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, int trans_a,
+                     const void* B, int trans_b, void* C, tg_epilogue epi, tg_stream_t stream);
 
 /*
  * Weight-only 4-bit dequant GEMM: C = epilogue(A x W^T).
@@ -109,20 +132,30 @@ const char* tg_status_str(tg_status s);
 tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
                           size_t len);
 
+/* As tg_query_config, for the operand layouts of tg_gemm_ex (dequant: 0, 0;
+ * TG_ERR_BAD_LAYOUT otherwise). */
+tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, int trans_a,
+                             int trans_b, char* buf, size_t len);
+
 /*
  * Offline sweep support: the compiled configurations, listed per (op, dtype),
  * can be launched by index instead of by the built-in selection table.
  *   tg_config_count: number of configurations for (op, dtype); 0 if none.
  *   tg_config_name : description of configuration `index` (as tg_query_config).
- *   tg_gemm_config / tg_dequant_gemm_w4_config: same contract as tg_gemm /
- *     tg_dequant_gemm_w4, launching configuration `index`;
- *     TG_ERR_NO_CONFIG if `index` is out of range.
+ *   tg_gemm_config / tg_gemm_ex_config / tg_dequant_gemm_w4_config: same
+ *     contract as tg_gemm / tg_gemm_ex / tg_dequant_gemm_w4, launching
+ *     configuration `index`; TG_ERR_NO_CONFIG if `index` is out of range or
+ *     the configuration cannot run the call (operand layout, alignment, or a
+ *     K multiple it needs).
  */
 int tg_config_count(int op, tg_dtype dtype);
 tg_status tg_config_name(int op, tg_dtype dtype, int index, char* buf, size_t len);
 tg_status tg_gemm_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                          const void* A, const void* B, void* C, tg_epilogue epi,
                          tg_stream_t stream);
+tg_status tg_gemm_ex_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                            const void* A, int trans_a, const void* B, int trans_b, void* C,
+                            tg_epilogue epi, tg_stream_t stream);
 tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, const void* A,
                                     const uint8_t* Wq, const uint8_t* Ws, void* C,
                                     tg_epilogue epi, tg_stream_t stream);

@@ -60,6 +60,10 @@ def _bind(lib):
         "orc_gemm_f64": ([i64, i64, i64, ctypes.c_int, p, p, ctypes.c_int, p], ctypes.c_int),
         "orc_gemm_entries_f64": ([i64, i64, i64, ctypes.c_int, p, p, ctypes.c_int, i64, p, p,
                                   p], None),
+        "orc_gemm_layout_f64": ([i64, i64, i64, ctypes.c_int, p, ctypes.c_int, p, ctypes.c_int,
+                                 ctypes.c_int, p], ctypes.c_int),
+        "orc_gemm_layout_entries_f64": ([i64, i64, i64, ctypes.c_int, p, ctypes.c_int, p,
+                                         ctypes.c_int, ctypes.c_int, i64, p, p, p], None),
         "orc_w4_decode": ([i64, i64, p, p, p], None),
         "orc_dequant_w4_f64": ([i64, i64, i64, p, p, p, ctypes.c_int, p], ctypes.c_int),
         "orc_dequant_w4_entries_f64": ([i64, i64, i64, p, p, p, ctypes.c_int, i64, p, p, p],
@@ -153,6 +157,44 @@ class Oracle:
                                       r.size, _ptr(r), _ptr(c), _ptr(out))
         return out
 
+    # -- operands stored transposed -------------------------------------------
+    @staticmethod
+    def _layout_dims(a, ta, b, tb):
+        K, M = a.shape if ta else (a.shape[1], a.shape[0])
+        N, K2 = b.shape if tb else (b.shape[1], b.shape[0])
+        if K != K2:
+            raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+        return M, N, K
+
+    def gemm_layout_f64(self, A, trans_a, B, trans_b, dtype: int, relu: bool = False) -> np.ndarray:
+        """Y = epi(op(A) @ op(B)) in fp64: A stored [M, K] or (trans_a) [K, M],
+        B stored [K, N] or (trans_b) [N, K], as storage words."""
+        a, b = _bits(A, dtype), _bits(B, dtype)
+        M, N, K = self._layout_dims(a, trans_a, b, trans_b)
+        Y = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.orc_gemm_layout_f64(M, N, K, dtype, _ptr(a), int(bool(trans_a)), _ptr(b),
+                                          int(bool(trans_b)), int(bool(relu)), _ptr(Y))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+        return Y
+
+    def gemm_layout_entries_f64(self, A, trans_a, B, trans_b, dtype: int, rows, cols,
+                                relu: bool = False) -> np.ndarray:
+        """Selected entries of epi(op(A) @ op(B)), each summed one by one in fp64."""
+        a, b = _bits(A, dtype), _bits(B, dtype)
+        M, N, K = self._layout_dims(a, trans_a, b, trans_b)
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        if r.shape != c.shape:
+            raise ValueError("rows and cols differ in length")
+        if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+            raise IndexError("entry outside the output")
+        out = np.empty(r.shape, dtype=np.float64)
+        self.lib.orc_gemm_layout_entries_f64(M, N, K, dtype, _ptr(a), int(bool(trans_a)), _ptr(b),
+                                             int(bool(trans_b)), int(bool(relu)), r.size, _ptr(r),
+                                             _ptr(c), _ptr(out))
+        return out
+
     # -- weight-only 4-bit dequant GEMM ---------------------------------------
     @staticmethod
     def _w4_check(A, Wq, Ws):
@@ -244,6 +286,14 @@ def gemm_f64(A, B, dtype, relu=False):
 
 def gemm_entries_f64(A, B, dtype, rows, cols, relu=False):
     return default().gemm_entries_f64(A, B, dtype, rows, cols, relu)
+
+
+def gemm_layout_f64(A, trans_a, B, trans_b, dtype, relu=False):
+    return default().gemm_layout_f64(A, trans_a, B, trans_b, dtype, relu)
+
+
+def gemm_layout_entries_f64(A, trans_a, B, trans_b, dtype, rows, cols, relu=False):
+    return default().gemm_layout_entries_f64(A, trans_a, B, trans_b, dtype, rows, cols, relu)
 
 
 def w4_decode(Wq, Ws):

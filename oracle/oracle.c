@@ -227,6 +227,80 @@ void orc_gemm_entries_f64(int64_t M, int64_t N, int64_t K, int dtype, const void
 }
 
 /* ---------------------------------------------------------------------- */
+/* Operands stored transposed.                                             */
+/*   Y[i][j] = epi(sum_k opA[i][k] * opB[k][j]) with                       */
+/*   opA[i][k] = A[i][k] (A stored [M][K]) or A[k][i] (A stored [K][M]),   */
+/*   opB[k][j] = B[k][j] (B stored [K][N]) or B[j][k] (B stored [N][K]).   */
+/* The same plain sum; only the element each (i, k) / (k, j) names moves.  */
+/* ---------------------------------------------------------------------- */
+
+static double op_a(const double* Ad, int trans_a, int64_t M, int64_t K, int64_t i, int64_t k)
+{
+    return trans_a ? Ad[k * M + i] : Ad[i * K + k];
+}
+
+static double op_b(const double* Bd, int trans_b, int64_t N, int64_t K, int64_t k, int64_t j)
+{
+    return trans_b ? Bd[j * K + k] : Bd[k * N + j];
+}
+
+int orc_gemm_layout_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* A, int trans_a,
+                        const void* B, int trans_b, int relu, double* Y)
+{
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -1;
+    }
+    orc_decode_array(dtype, M * K, A, Ad);
+    orc_decode_array(dtype, K * N, B, Bd);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += op_a(Ad, trans_a, M, K, i, k) * op_b(Bd, trans_b, N, K, k, j);
+            Y[i * N + j] = relu ? relu_f64(s) : s;
+        }
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* Selected entries of the above, one element at a time. */
+void orc_gemm_layout_entries_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* A,
+                                 int trans_a, const void* B, int trans_b, int relu, int64_t count,
+                                 const int64_t* rows, const int64_t* cols, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t ia = trans_a ? k * M + i : i * K + k;
+            const int64_t ib = trans_b ? j * K + k : k * N + j;
+            double a, b;
+            if (dtype == ORC_F32) {
+                a = orc_decode_f32(((const uint32_t*)A)[ia]);
+                b = orc_decode_f32(((const uint32_t*)B)[ib]);
+            } else if (dtype == ORC_F16) {
+                a = orc_decode_f16(((const uint16_t*)A)[ia]);
+                b = orc_decode_f16(((const uint16_t*)B)[ib]);
+            } else {
+                a = orc_decode_bf16(((const uint16_t*)A)[ia]);
+                b = orc_decode_bf16(((const uint16_t*)B)[ib]);
+            }
+            s += a * b;
+        }
+        out[t] = relu ? relu_f64(s) : s;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Weight-only 4-bit dequant GEMM.                                         */
 /*   W[n][k] = E2M1(code(n, k)) * E8M0(Ws[n][k / 32])                      */
 /*   code(n, k) = (Wq[n][k / 2] >> (4 * (k % 2))) & 0xF                    */

@@ -462,11 +462,73 @@ def check_dequant_random_vs_decoded(orc):
                     assert Fraction(float(Y[i, j])) == want
 
 
+# ---------------------------------------------------------------------------
+# Operands stored transposed (C = op(A) op(B)).
+# ---------------------------------------------------------------------------
+
+LAYOUTS = ((0, 0), (0, 1), (1, 0), (1, 1))
+
+
+def _stored(X, trans):
+    """Storage of a logical matrix X: as is, or its transpose."""
+    X = np.asarray(X, dtype=np.float64)
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def check_layout_textbook_2x2(orc):
+    for dtype in (F32, F16, BF16):
+        for ta, tb in LAYOUTS:
+            A = storage_of(_stored([[1, 2], [3, 4]], ta), dtype)
+            B = storage_of(_stored([[5, 6], [7, 8]], tb), dtype)
+            Y = orc.gemm_layout_f64(A, ta, B, tb, dtype)
+            assert _same(Y, [[19, 22], [43, 50]]), (ta, tb)
+            e = orc.gemm_layout_entries_f64(A, ta, B, tb, dtype, [0, 0, 1, 1], [0, 1, 0, 1])
+            assert _same(e, [19, 22, 43, 50]), (ta, tb)
+
+
+def check_layout_brute_force(orc):
+    """Random dyadic operands in every layout, against the exact rational
+    product of the logical matrices (the stored arrays transposed here)."""
+    r = np.random.Generator(np.random.PCG64(31))
+    for trial in range(24):
+        M, N, K = (int(x) for x in r.integers(1, 9, size=3))
+        ta, tb = LAYOUTS[trial % 4]
+        dtype = (F32, F16, BF16)[trial % 3]
+        Av = r.integers(-64, 65, size=(M, K)) / 16.0
+        Bv = r.integers(-64, 65, size=(K, N)) / 16.0
+        A = storage_of(_stored(Av, ta), dtype)
+        B = storage_of(_stored(Bv, tb), dtype)
+        # dyadic inputs with small sums: the exact product is an fp64 value
+        want = np.array([[float(x) for x in row] for row in exact_product(Av, Bv)])
+        Y = orc.gemm_layout_f64(A, ta, B, tb, dtype)
+        assert _same(Y + 0.0, want + 0.0), (M, N, K, ta, tb)
+        rows = np.repeat(np.arange(M), N)
+        cols = np.tile(np.arange(N), M)
+        e = orc.gemm_layout_entries_f64(A, ta, B, tb, dtype, rows, cols)
+        assert _same(e.reshape(M, N) + 0.0, want + 0.0), (M, N, K, ta, tb)
+
+
+def check_layout_rank_one(orc):
+    # Non-square, non-symmetric: a stride or index mix-up changes the result.
+    u = np.array([1, -2, 3, 0, 5], dtype=np.float64)
+    a = np.array([2, 1, -1, 3, 0, 1, -2], dtype=np.float64)
+    b = np.array([1, 0, 2, -1, 1, 3, 1], dtype=np.float64)
+    v = np.array([3, -1, 2], dtype=np.float64)
+    Av, Bv = np.outer(u, a), np.outer(b, v)
+    want = float(a @ b) * np.outer(u, v)
+    for ta, tb in LAYOUTS:
+        A = storage_of(_stored(Av, ta), BF16)
+        B = storage_of(_stored(Bv, tb), BF16)
+        assert _same(orc.gemm_layout_f64(A, ta, B, tb, BF16, relu=True) + 0.0,
+                     np.maximum(want, 0.0) + 0.0), (ta, tb)
+
+
 ALL_CHECKS = [
     check_decode_f16_exhaustive, check_decode_bf16_exhaustive, check_decode_f32_sample,
     check_encode_f16, check_encode_f32, check_encode_bf16_from_f32, check_encode_exact_rational,
     check_e2m1_table, check_e8m0, check_textbook_2x2, check_identity, check_permutation,
     check_all_ones, check_rank_one, check_brute_force_dyadic, check_brute_force_general,
     check_relu, check_round_outputs, check_dequant_row_sums, check_dequant_one_hot,
-    check_dequant_group_scales, check_dequant_random_vs_decoded,
+    check_dequant_group_scales, check_dequant_random_vs_decoded, check_layout_textbook_2x2,
+    check_layout_brute_force, check_layout_rank_one,
 ]

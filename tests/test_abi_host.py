@@ -17,7 +17,7 @@ from tiled_dense_gemm_07_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP = range(8)
+OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP, BADL = range(9)
 
 # fake, well-separated device addresses: validation never dereferences them
 PA, PB, PC, PS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -42,7 +42,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         text = binding.status_str(s)
         assert text.startswith("TG_")
     assert "unknown" in binding.status_str(99)
@@ -111,6 +111,26 @@ def test_forced_dequant_config_requirements(lib):
             assert d(idx, 64, 64, 96, PA, PB, PS, PC, 0, None) == NOCFG, name
         if name.endswith("_dma"):
             assert d(idx, 64, 64, 256, PA, PB, PS + 2, PC, 0, None) == NOCFG, name
+
+
+def test_gemm_ex_argument_errors(lib):
+    g = lib.tg_gemm_ex
+    BADL = 8
+    assert g(4, 4, 4, 2, PA, 2, PB, 0, PC, 0, None) == BADL
+    assert g(4, 4, 4, 2, PA, 0, PB, -1, PC, 0, None) == BADL
+    assert g(-1, 4, 4, 2, PA, 1, PB, 1, PC, 0, None) == SHAPE
+    assert g(1 << 25, 4, 8, 2, PA, 1, PB, 0, PC, 0, None) == SHAPE  # 64 * M * 2 > 2^31
+    assert g(4, 4, 4, 2, None, 1, PB, 0, PC, 0, None) == NULLP
+    assert g(4, 4, 4, 2, PA, 1, PB, 0, PA + 4, 0, None) == ALIAS
+    assert g(0, 4, 4, 2, None, 1, None, 1, None, 0, None) == OK
+    # transposed fp32, or transposed rows that are not whole 16-byte chunks
+    assert g(64, 64, 64, 0, PA, 1, PB, 0, PC, 0, None) == NOCFG
+    assert g(36, 64, 64, 2, PA, 1, PB, 0, PC, 0, None) == NOCFG
+    assert g(64, 64, 36, 2, PA, 0, PB, 1, PC, 0, None) == NOCFG
+    buf = ctypes.create_string_buffer(128)
+    assert lib.tg_query_config_ex(1, 4, 64, 64, 2, 1, 0, buf, 128) == BADL
+    assert lib.tg_query_config_ex(0, 4096, 4096, 4096, 2, 1, 1, buf, 128) == OK
+    assert buf.value.decode().startswith("gemm_bf16_256x256x32_w2x2_s4_g4_dma_tt")
 
 
 def test_launch_failure_is_reported(lib, monkeypatch):

@@ -102,6 +102,8 @@ def test_every_gemm_config(dtype):
     A, B = synth.gemm_inputs(M, N, K, dtype, 303, 404, integer=True)
     want = oracle.encode(dtype, oracle.gemm_f64(A, B, dtype, relu=True))
     for idx, name in _configs(0, dtype):
+        if name.endswith(("_nt", "_tn", "_tt")):
+            continue  # transposed layouts: test_every_transposed_config
         say("config %d %s" % (idx, name))
         got = run_gemm(A, B, dtype, True, config=idx)
         assert np.array_equal(got, want), name
@@ -305,6 +307,91 @@ def test_single_rounding(dtype, K):
         assert (np.abs(g - Y) <= 0.5 * ulp).all()
     else:
         assert np.array_equal(got, oracle.encode(dtype, Y))
+
+
+# ---------------------------------------------------------------------------
+# Operands stored transposed (tg_gemm_ex).
+# ---------------------------------------------------------------------------
+
+LAYOUTS = [(0, 1), (1, 0), (1, 1)]
+LAYOUT_IDS = ["nt", "tn", "tt"]
+
+
+def _store(X, trans):
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def run_gemm_ex(A_st, ta, B_st, tb, dtype, relu, config=None):
+    At, Bt = to_device(A_st, dtype, DEV), to_device(B_st, dtype, DEV)
+    Ct = binding.gemm_ex(At, Bt, trans_a=ta, trans_b=tb, epilogue="relu" if relu else None,
+                         config=config)
+    torch.cuda.synchronize()
+    return to_host_bits(Ct, dtype)
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
+@pytest.mark.parametrize("shape", [(128, 128, 32), (200, 136, 96), (296, 264, 200),
+                                   (1000, 1032, 264), (64, 8, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=lambda d: DNAME[d])
+def test_transposed_layouts(dtype, shape, layout, integer):
+    """op(A) x op(B) with A stored [K][M] and/or B stored [N][K] against the oracle."""
+    M, N, K = shape
+    ta, tb = layout
+    A, B = synth.gemm_inputs(M, N, K, dtype, 1101 + M, 1202 + N, integer)
+    A_st, B_st = _store(A, ta), _store(B, tb)
+    say("layout %s %s %s int=%s" % (LAYOUT_IDS[LAYOUTS.index(layout)], DNAME[dtype], shape, integer))
+    got = run_gemm_ex(A_st, ta, B_st, tb, dtype, relu=True)
+    check_full(got, oracle.gemm_layout_f64(A_st, ta, B_st, tb, dtype, relu=True), dtype, integer)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=lambda d: DNAME[d])
+def test_every_transposed_config(dtype):
+    """Each compiled transposed-layout configuration, forced, on a ragged shape."""
+    M, N, K = 296, 264, 200
+    A, B = synth.gemm_inputs(M, N, K, dtype, 1303, 1404, integer=True)
+    names = binding.list_configs(0, dtype)
+    ran = 0
+    for idx, name in enumerate(names):
+        for code, (ta, tb) in zip(LAYOUT_IDS, LAYOUTS):
+            if not name.endswith("_" + code):
+                continue
+            say("config %d %s" % (idx, name))
+            A_st, B_st = _store(A, ta), _store(B, tb)
+            got = run_gemm_ex(A_st, ta, B_st, tb, dtype, relu=False, config=idx)
+            want = oracle.encode(dtype, oracle.gemm_layout_f64(A_st, ta, B_st, tb, dtype))
+            assert np.array_equal(got, want), name
+            ran += 1
+    assert ran >= 6
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
+def test_transposed_full_size(layout):
+    """bf16 4096^3 + ReLU in each transposed layout: sampled entries vs the oracle."""
+    M = N = K = 4096
+    ta, tb = layout
+    w = synth.WORKLOADS["bf16_4096_relu"]
+    inp = synth.make_inputs(w, integer=False)
+    A_st, B_st = _store(inp["A"], ta), _store(inp["B"], tb)
+    say("layout %s bf16 4096^3" % LAYOUT_IDS[LAYOUTS.index(layout)])
+    got = run_gemm_ex(A_st, ta, B_st, tb, BF16, relu=True).reshape(M, N)
+    rows, cols = sample_entries(M, N, 2000, seed=91 + ta + 2 * tb)
+    Y = oracle.gemm_layout_entries_f64(A_st, ta, B_st, tb, BF16, rows, cols, relu=True)
+    check_full(got[rows, cols], Y, BF16, integer=False)
+
+
+def test_transposed_unsupported():
+    """fp32 and non-16-byte rows have no transposed configuration: refused."""
+    A = torch.zeros((64, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.TileGemmError) as ei:
+        binding.gemm_ex(A, A, trans_a=True)
+    assert ei.value.status == 6
+    A = torch.zeros((20, 36), dtype=torch.bfloat16, device=DEV)  # stored [K=20][M=36]
+    B = torch.zeros((20, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(binding.TileGemmError) as ei:
+        binding.gemm_ex(A, B, trans_a=True)
+    assert ei.value.status == 6
 
 
 def test_side_stream():

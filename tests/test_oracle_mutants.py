@@ -30,6 +30,15 @@ MUTANTS = [
     ("e2m1_has_specials", "decode_bits(code & 0xFu, 2, 1, 0)", "decode_bits(code & 0xFu, 2, 1, 1)", 0),
     ("subnormal_exponent", "v = ldexp((double)f, 1 - bias - fbits);", "v = ldexp((double)f, -bias - fbits);", 0),
     ("e8m0_bias", "ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 128)", 0),
+    ("layout_a_stride", "return trans_a ? Ad[k * M + i] : Ad[i * K + k];",
+     "return trans_a ? Ad[i * M + k] : Ad[i * K + k];", 0),
+    ("layout_b_stride", "return trans_b ? Bd[j * K + k] : Bd[k * N + j];",
+     "return trans_b ? Bd[k * K + j] : Bd[k * N + j];", 0),
+    ("layout_entries_a", "const int64_t ia = trans_a ? k * M + i : i * K + k;",
+     "const int64_t ia = trans_a ? i * K + k : i * K + k;", 0),
+    ("layout_entries_b", "const int64_t ib = trans_b ? j * K + k : k * N + j;",
+     "const int64_t ib = trans_b ? k * N + j : k * N + j;", 0),
+    ("layout_relu_lost", "Y[i * N + j] = relu ? relu_f64(s) : s;", "Y[i * N + j] = s;", 0),
 ]
 
 

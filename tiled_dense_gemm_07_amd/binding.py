@@ -24,9 +24,9 @@ TG_EPI_NONE, TG_EPI_RELU = 0, 1
 TG_OP_GEMM, TG_OP_DEQUANT_W4 = 0, 1
 
 # exported symbols, as declared in include/tilegemm.h
-EXPORTS = ("tg_gemm", "tg_dequant_gemm_w4", "tg_status_str", "tg_query_config",
-           "tg_config_count", "tg_config_name", "tg_gemm_config", "tg_dequant_gemm_w4_config",
-           "tg_tile_map")
+EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_query_config",
+           "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
+           "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map")
 
 _lib = None
 
@@ -55,6 +55,13 @@ def load_library():
     i64, p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.tg_gemm.argtypes = [i64, i64, i64, c_int, p, p, p, c_int, p]
     lib.tg_gemm.restype = c_int
+    lib.tg_gemm_ex.argtypes = [i64, i64, i64, c_int, p, c_int, p, c_int, p, c_int, p]
+    lib.tg_gemm_ex.restype = c_int
+    lib.tg_gemm_ex_config.argtypes = [c_int, i64, i64, i64, c_int, p, c_int, p, c_int, p, c_int, p]
+    lib.tg_gemm_ex_config.restype = c_int
+    lib.tg_query_config_ex.argtypes = [c_int, i64, i64, i64, c_int, c_int, c_int, ctypes.c_char_p,
+                                       ctypes.c_size_t]
+    lib.tg_query_config_ex.restype = c_int
     lib.tg_dequant_gemm_w4.argtypes = [i64, i64, i64, p, p, p, p, c_int, p]
     lib.tg_dequant_gemm_w4.restype = c_int
     lib.tg_status_str.argtypes = [c_int]
@@ -158,6 +165,42 @@ def gemm_with_config(index: int, A, B, C=None, epilogue=None, stream=None):
     return C
 
 
+def _gemm_ex_args(A, B, trans_a, trans_b, C):
+    _require_gpu_tensor("A", A)
+    _require_gpu_tensor("B", B)
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    K, M = A.shape if trans_a else (A.shape[1], A.shape[0])
+    N, K2 = B.shape if trans_b else (B.shape[1], B.shape[0])
+    if K != K2:
+        raise ValueError("inner dimensions differ: A is %s (trans_a=%d), B is %s (trans_b=%d)"
+                         % (tuple(A.shape), trans_a, tuple(B.shape), trans_b))
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    if C is not None:
+        _require_gpu_tensor("C", C)
+        if tuple(C.shape) != (M, N) or C.dtype != A.dtype:
+            raise ValueError("C must be [M, N] of the operand dtype")
+    return M, N, K
+
+
+def gemm_ex(A, B, trans_a=False, trans_b=False, C=None, epilogue=None, stream=None, config=None):
+    """C = epilogue(op(A) @ op(B)): A stored [M, K] (or [K, M] with trans_a),
+    B stored [K, N] (or [N, K] with trans_b).  config: force a compiled
+    configuration by index (for the sweep and tests)."""
+    import torch
+
+    ta, tb = int(bool(trans_a)), int(bool(trans_b))
+    M, N, K = _gemm_ex_args(A, B, ta, tb, C)
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    lib = load_library()
+    args = (M, N, K, _dtype_code(A), A.data_ptr(), ta, B.data_ptr(), tb, C.data_ptr(),
+            _epi_code(epilogue), _stream_ptr(A.device, stream))
+    _check(lib.tg_gemm_ex(*args) if config is None else lib.tg_gemm_ex_config(config, *args))
+    return C
+
+
 def _w4_args(A, Wq, Ws, C):
     import torch
 
@@ -204,9 +247,11 @@ def dequant_gemm_w4_with_config(index: int, A, Wq, Ws, C=None, epilogue=None, st
     return C
 
 
-def query_config(op: int, M: int, N: int, K: int, dtype: int = TG_BF16) -> str:
+def query_config(op: int, M: int, N: int, K: int, dtype: int = TG_BF16, trans_a: bool = False,
+                 trans_b: bool = False) -> str:
     buf = ctypes.create_string_buffer(256)
-    _check(load_library().tg_query_config(op, M, N, K, dtype, buf, len(buf)))
+    _check(load_library().tg_query_config_ex(op, M, N, K, dtype, int(trans_a), int(trans_b), buf,
+                                             len(buf)))
     return buf.value.decode()
 
 

@@ -49,10 +49,11 @@ ConfigList list_for(int op, int dtype)
 void config_name(const Config& c, char* buf, size_t len)
 {
     static const char* dn[] = {"f32", "f16", "bf16"};
-    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s", c.op == 0 ? "gemm" : "w4",
+    static const char* lay[] = {"", "_nt", "_tn", "_tt"};  // A^T-stored / B^T-stored
+    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s", c.op == 0 ? "gemm" : "w4",
              dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
-             c.wide ? "" : "_narrow");
+             lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)], c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -95,57 +96,76 @@ const Config* gemv_for(int64_t K)
     return nullptr;
 }
 
-// Whether configuration c can run this call.  wide: 16-byte aligned operands
-// with whole 16-byte rows; ws4: the scale bytes start 4-byte aligned.
-bool usable(const Config& c, int64_t K, bool wide, bool ws4)
+// What a call needs from a configuration.
+struct Call {
+    int op, dtype;
+    int64_t M, N, K;
+    bool wide;    // 16-byte aligned operands whose rows are whole 16-byte chunks
+    bool ws4;     // dequant scale bytes start 4-byte aligned
+    bool ta, tb;  // A stored [K][M], B stored [N][K]
+};
+
+// Whether configuration c can run call q.
+bool usable(const Config& c, const Call& q)
 {
-    if (c.wide && !wide)
+    if (c.wide && !q.wide)
         return false;
-    if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && K % c.bk != 0)
+    if (c.ta != q.ta || c.tb != q.tb)
+        return false;  // operand layouts are compiled in
+    if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
         return false;  // whole strips / rounds of bk
-    if (c.op == TG_OP_DEQUANT_W4 && c.pipe == 2 && !ws4)
+    if (c.op == TG_OP_DEQUANT_W4 && c.pipe == 2 && !q.ws4)
         return false;  // scale bytes are copied as dwords
     return true;
 }
 
-const Config* heuristic(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide, bool ws4)
+const Config* heuristic(const Call& q)
 {
-    ConfigList L = list_for(op, dtype);
-    if (!wide) {
+    ConfigList L = list_for(q.op, q.dtype);
+    if (!q.wide) {
         for (int i = 0; i < L.count; ++i)
-            if (!L.items[i].wide)
+            if (usable(L.items[i], q))
                 return &L.items[i];
         return nullptr;
     }
     // few activation rows: the run time is the weight stream from HBM
-    if (op == TG_OP_DEQUANT_W4 && M <= 16) {
-        if (const Config* c = gemv_for(K))
+    if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16) {
+        if (const Config* c = gemv_for(q.K))
             return c;
     }
     for (const Pref& pr : kPrefs) {
-        if (pr.op != op || pr.dtype != dtype)
+        if (pr.op != q.op || pr.dtype != q.dtype || q.ta || q.tb)
             continue;
         const Config* last = nullptr;
         for (const char* name : pr.names) {
             if (!name)
                 break;
-            const Config* c = find_by_name(op, dtype, name);
-            if (!c || !usable(*c, K, wide, ws4))
+            const Config* c = find_by_name(q.op, q.dtype, name);
+            if (!c || !usable(*c, q))
                 continue;
             last = c;
             // small M: a tile taller than M wastes matrix-core work
-            if (op == 1 && M <= c->bm / 2)
+            if (q.op == 1 && q.M <= c->bm / 2)
                 continue;
-            if (tiles(M, c->bm) * tiles(N, c->bn) >= 200)
+            if (tiles(q.M, c->bm) * tiles(q.N, c->bn) >= 200)
                 return c;
         }
         if (last)
             return last;
     }
-    for (int i = 0; i < L.count; ++i)
-        if (L.items[i].wide && usable(L.items[i], K, wide, ws4))
-            return &L.items[i];
-    return nullptr;
+    // transposed layouts (and anything the preference lists miss): the first
+    // usable configuration, largest tile first, whose grid reaches about one
+    // workgroup per compute unit, else the last usable one
+    const Config* last = nullptr;
+    for (int i = 0; i < L.count; ++i) {
+        const Config& c = L.items[i];
+        if (!c.wide || !usable(c, q))
+            continue;
+        last = &c;
+        if (tiles(q.M, c.bm) * tiles(q.N, c.bn) >= 200)
+            return &c;
+    }
+    return last;
 }
 
 const Config* find_by_name(int op, int dtype, const char* name)
@@ -160,21 +180,19 @@ const Config* find_by_name(int op, int dtype, const char* name)
     return nullptr;
 }
 
-const Config* select_config(int op, int dtype, int64_t M, int64_t N, int64_t K, bool wide,
-                            bool ws4)
+const Config* select_config(const Call& q)
 {
     for (size_t i = 0; i < sizeof(kTuned) / sizeof(kTuned[0]); ++i) {
         const TunedEntry& e = kTuned[i];
         if (e.config == nullptr)
             continue;
-        if (e.op == op && (op == TG_OP_DEQUANT_W4 || e.dtype == dtype) && e.M == M && e.N == N &&
-            e.K == K) {
-            const Config* c = find_by_name(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, e.config);
-            if (c && c->wide == wide && usable(*c, K, wide, ws4))
+        if (e.op == q.op && e.dtype == q.dtype && e.M == q.M && e.N == q.N && e.K == q.K) {
+            const Config* c = find_by_name(q.op, q.dtype, e.config);
+            if (c && c->wide == q.wide && usable(*c, q))
                 return c;
         }
     }
-    return heuristic(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype, M, N, K, wide, ws4);
+    return heuristic(q);
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
@@ -225,17 +243,21 @@ tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream
 }
 
 tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
-                    tg_dtype dtype, const void* A, const void* B, void* C, tg_epilogue epi,
-                    tg_stream_t stream)
+                    tg_dtype dtype, const void* A, int trans_a, const void* B, int trans_b,
+                    void* C, tg_epilogue epi, tg_stream_t stream)
 {
     if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
         return TG_ERR_BAD_DTYPE;
     if (epi != TG_EPI_NONE && epi != TG_EPI_RELU)
         return TG_ERR_BAD_EPILOGUE;
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return TG_ERR_BAD_LAYOUT;
     const int es = esize_of(dtype);
     tg_status s = check_shape(M, N, K, es);
     if (s != TG_OK)
         return s;
+    if (trans_a && 64 * M * es > kMaxDim)
+        return TG_ERR_BAD_SHAPE;  // per-strip offsets of a [K][M] operand
     if (forced_index >= 0 && !forced)
         return TG_ERR_NO_CONFIG;
     if (M == 0 || N == 0)
@@ -247,12 +269,13 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     if (overlaps(C, cbytes, A, (size_t)(M * K * es)) || overlaps(C, cbytes, B, (size_t)(K * N * es)))
         return TG_ERR_ALIAS;
     const int v = vec_of(dtype);
-    const bool wide = aligned16(A) && aligned16(B) && (K % v == 0) && (N % v == 0);  // NULL is aligned
-    const Config* c = forced ? forced : select_config(TG_OP_GEMM, dtype, M, N, K, wide, false);
-    if (!c)
-        return TG_ERR_NO_CONFIG;
-    if (c->wide && !wide)
-        return TG_ERR_NO_CONFIG;  // a forced 16-byte-load config on unaligned operands
+    const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
+    Call q{TG_OP_GEMM, dtype, M, N, K, false, false, trans_a != 0, trans_b != 0};
+    // NULL is aligned
+    q.wide = aligned16(A) && aligned16(B) && (lda % v == 0) && (ldb % v == 0);
+    const Config* c = forced ? forced : select_config(q);
+    if (!c || !usable(*c, q))
+        return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     tg::GemmParams p{};
     p.A = A;
     p.B = B;
@@ -287,14 +310,11 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     if (overlaps(C, cbytes, A, (size_t)(M * K * 2)) || overlaps(C, cbytes, Wq, (size_t)(N * K / 2)) ||
         overlaps(C, cbytes, Ws, (size_t)(N * K / 32)))
         return TG_ERR_ALIAS;
-    const bool wide = aligned16(A) && aligned16(Wq);
-    const bool ws4 = ((uintptr_t)Ws & 3u) == 0;
-    const Config* c =
-        forced ? forced : select_config(TG_OP_DEQUANT_W4, TG_BF16, M, N, K, wide, ws4);
-    if (!c)
-        return TG_ERR_NO_CONFIG;
-    if (!usable(*c, K, wide, ws4))
-        return TG_ERR_NO_CONFIG;  // a forced configuration this call cannot use
+    Call q{TG_OP_DEQUANT_W4, TG_BF16, M, N, K, aligned16(A) && aligned16(Wq),
+           ((uintptr_t)Ws & 3u) == 0, false, false};
+    const Config* c = forced ? forced : select_config(q);
+    if (!c || !usable(*c, q))
+        return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     tg::GemmParams p{};
     p.A = A;
     p.B = Wq;
@@ -315,7 +335,13 @@ extern "C" {
 tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, const void* B,
                   void* C, tg_epilogue epi, tg_stream_t stream)
 {
-    return gemm_impl(nullptr, -1, M, N, K, dtype, A, B, C, epi, stream);
+    return gemm_impl(nullptr, -1, M, N, K, dtype, A, 0, B, 0, C, epi, stream);
+}
+
+tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, int trans_a,
+                     const void* B, int trans_b, void* C, tg_epilogue epi, tg_stream_t stream)
+{
+    return gemm_impl(nullptr, -1, M, N, K, dtype, A, trans_a, B, trans_b, C, epi, stream);
 }
 
 tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, const uint8_t* Wq,
@@ -343,12 +369,14 @@ const char* tg_status_str(tg_status s)
         return "TG_ERR_NO_CONFIG: no such kernel configuration for this call";
     case TG_ERR_HIP:
         return "TG_ERR_HIP: the HIP runtime reported an error at launch";
+    case TG_ERR_BAD_LAYOUT:
+        return "TG_ERR_BAD_LAYOUT: trans_a and trans_b must be 0 or 1";
     }
     return "unknown tg_status";
 }
 
-tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
-                          size_t len)
+tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, int trans_a,
+                             int trans_b, char* buf, size_t len)
 {
     if (!buf || len == 0)
         return TG_ERR_NULL_POINTER;
@@ -356,6 +384,9 @@ tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
         return TG_ERR_NO_CONFIG;
     if (op == TG_OP_GEMM && dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
         return TG_ERR_BAD_DTYPE;
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1) ||
+        (op == TG_OP_DEQUANT_W4 && (trans_a || trans_b)))
+        return TG_ERR_BAD_LAYOUT;
     const int dt = op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype;
     tg_status s = check_shape(M, N, K, esize_of(dt));
     if (s != TG_OK)
@@ -363,8 +394,10 @@ tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
     if (op == TG_OP_DEQUANT_W4 && K % 32 != 0)
         return TG_ERR_BAD_SHAPE;
     // assume aligned operands (what torch allocations give)
-    const bool wide = op == TG_OP_DEQUANT_W4 || (K % vec_of(dt) == 0 && N % vec_of(dt) == 0);
-    const Config* c = select_config(op, dt, M, N, K, wide, true);
+    const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
+    Call q{op, dt, M, N, K, false, true, trans_a != 0, trans_b != 0};
+    q.wide = op == TG_OP_DEQUANT_W4 || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0);
+    const Config* c = select_config(q);
     if (!c)
         return TG_ERR_NO_CONFIG;
     char name[96];
@@ -372,6 +405,12 @@ tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
     snprintf(buf, len, "%s grid=%lld threads=%d", name,
              (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * 64);
     return TG_OK;
+}
+
+tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
+                          size_t len)
+{
+    return tg_query_config_ex(op, M, N, K, dtype, 0, 0, buf, len);
 }
 
 int tg_config_count(int op, tg_dtype dtype)
@@ -398,7 +437,19 @@ tg_status tg_gemm_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dt
         return TG_ERR_BAD_DTYPE;
     ConfigList L = list_for(TG_OP_GEMM, dtype);
     const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
-    return gemm_impl(c, index < 0 ? 0 : index, M, N, K, dtype, A, B, C, epi, stream);
+    return gemm_impl(c, index < 0 ? 0 : index, M, N, K, dtype, A, 0, B, 0, C, epi, stream);
+}
+
+tg_status tg_gemm_ex_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                            const void* A, int trans_a, const void* B, int trans_b, void* C,
+                            tg_epilogue epi, tg_stream_t stream)
+{
+    if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    ConfigList L = list_for(TG_OP_GEMM, dtype);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    return gemm_impl(c, index < 0 ? 0 : index, M, N, K, dtype, A, trans_a, B, trans_b, C, epi,
+                     stream);
 }
 
 tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, const void* A,

@@ -14,6 +14,7 @@ struct Config {
     int stages;    // LDS ring depth
     int group_m;   // swizzle group (tile rows)
     bool wide;     // 16-byte global loads (aligned operands) vs element loads
+    bool ta, tb;   // operand layouts: A stored [K][M] / B stored [N][K] (else [M][K] / [K][N])
     int pipe;      // 0: single staging set; 1: deep pipeline; 2: LDS-DMA pipeline;
                    // 3: weight-streaming dequant kernel for few rows (K % bk == 0)
     const void* kernel;
@@ -34,14 +35,14 @@ ConfigList configs_dequant_w4();
 #define TG_CONFIG(OP, DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE)                      \
     tg::Config                                                                                 \
     {                                                                                          \
-        OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE,                                      \
+        OP, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, false, false, PIPE,                        \
             (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE> \
     }
 
 // Configurations of the LDS-DMA kernel (16-bit operands, BK = 32, NS stages).
-#define TG_CONFIG_DMA(DT, BM, BN, WGM, WGN, NS, GM)                                         \
+#define TG_CONFIG_DMA(DT, TA, TB, BM, BN, WGM, WGN, NS, GM)                                 \
     tg::Config                                                                             \
     {                                                                                      \
-        0, DT, BM, BN, 32, WGM, WGN, NS, GM, true, 2,                                      \
-            (const void*)&tg::gemm_dma_kernel<DT, BM, BN, WGM, WGN, NS, GM>                \
+        0, DT, BM, BN, 32, WGM, WGN, NS, GM, true, TA, TB, 2,                              \
+            (const void*)&tg::gemm_dma_kernel<DT, TA, TB, BM, BN, WGM, WGN, NS, GM>        \
     }

@@ -9,12 +9,12 @@ namespace tg {
 
 static const Config kCfg[] = {
     // few activation rows: weight-streaming kernel (bk = the K multiple it needs)
-    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, 3, (const void*)&gemv_w4_kernel<true>},
-    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, 3, (const void*)&gemv_w4_kernel<false>},
+    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, false, false, 3, (const void*)&gemv_w4_kernel<true>},
+    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, false, false, 3, (const void*)&gemv_w4_kernel<false>},
     // many rows: LDS-DMA pipeline, codes dequantised in registers (K % 128 == 0)
-    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4>},
-    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 8, true, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 8>},
-    tg::Config{1, DT_BF16, 64, 256, 128, 2, 2, 4, 4, true, 2, (const void*)&dma_w4_kernel<64, 256, 2, 2, 4, 4>},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4>},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 8, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 8>},
+    tg::Config{1, DT_BF16, 64, 256, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 256, 2, 2, 4, 4>},
     TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true, 0),

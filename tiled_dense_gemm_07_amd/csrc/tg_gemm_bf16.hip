@@ -6,12 +6,19 @@
 namespace tg {
 
 static const Config kCfg[] = {
-    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 4, 4),
-    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 4, 8),
-    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 3, 4),
-    TG_CONFIG_DMA(DT_BF16, 256, 256, 2, 2, 5, 4),
-    TG_CONFIG_DMA(DT_BF16, 256, 128, 2, 2, 4, 8),
-    TG_CONFIG_DMA(DT_BF16, 128, 128, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 4, 4),
+    TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 3, 4),
+    TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 5, 4),
+    TG_CONFIG_DMA(DT_BF16, false, false, 256, 128, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, false, false, 128, 128, 2, 2, 4, 8),
+    // transposed-operand layouts (A stored [K][M] and/or B stored [N][K])
+    TG_CONFIG_DMA(DT_BF16, false, true, 256, 256, 2, 2, 4, 4),
+    TG_CONFIG_DMA(DT_BF16, true, false, 256, 256, 2, 2, 4, 4),
+    TG_CONFIG_DMA(DT_BF16, true, true, 256, 256, 2, 2, 4, 4),
+    TG_CONFIG_DMA(DT_BF16, false, true, 128, 128, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, true, false, 128, 128, 2, 2, 4, 8),
+    TG_CONFIG_DMA(DT_BF16, true, true, 128, 128, 2, 2, 4, 8),
     TG_CONFIG(0, DT_BF16, B_KN, 256, 256, 64, 2, 4, 2, 4, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 128, 128, 64, 2, 2, 2, 8, true, 0),
     TG_CONFIG(0, DT_BF16, B_KN, 128, 64, 64, 2, 2, 2, 8, true, 0),

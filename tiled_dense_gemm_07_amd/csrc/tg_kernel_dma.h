@@ -76,7 +76,120 @@ __device__ __forceinline__ void wait_copies_barrier()
 __device__ __forceinline__ int swz_a(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 1) * 6) ^ ((k & 2) * 5); }
 
-template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+// One operand of the 16-bit DMA kernel: X (BM or BN) output rows/columns by
+// BK = 32 k per strip.  In global memory the operand is either k-contiguous
+// (KMAJ: each of its X rows holds consecutive k; leading dimension K) or
+// x-contiguous (each k row holds consecutive x; leading dimension = the
+// operand's full extent).  The LDS stage keeps the global orientation:
+//  * KMAJ: [X][32 k], 64-byte rows, chunk swizzle swz_a; an MFMA fragment
+//    (8 consecutive k of one row per lane) is one ds_read_b128;
+//  * x-contiguous: [32 k][X], chunk swizzle swz_b; a fragment is two
+//    ds_read_b64_tr_b16 (4 consecutive k of one column each).
+// Both give the MFMA the same operand layout: lane l holds 8 consecutive k of
+// index l % 32 of a 32-wide block, starting at k = 8 (l / 32).
+template <bool KMAJ, int X, int WX, int FX, int NW>
+struct DmaOperand {
+    static constexpr int BK = 32;
+    static constexpr int STAGE = X * BK * 2;      // bytes per LDS stage
+    static constexpr int J = STAGE / 1024 / NW;   // 1 KiB copies per wave per strip
+    static constexpr int LPR = KMAJ ? 4 : X / 8;  // 16-byte chunks per LDS row
+    static constexpr int RPB = 64 / LPR;          // LDS rows per 1 KiB copy
+    static constexpr int NRD = KMAJ ? FX : 2 * FX;  // LDS reads per slab
+    static_assert(J >= 1 && STAGE % (1024 * NW) == 0, "strips split into whole 1 KiB copies per wave");
+    static_assert(KMAJ || (LPR >= 16 && LPR <= 64), "x-contiguous rows of 256 to 1024 bytes");
+
+    struct Lane {
+        u32 off[J];   // copy offsets within a strip (out of range past the x extent)
+        int kk[J];    // k (within the strip) of the data each copy lane moves
+        u32 rd[KMAJ ? 2 : FX];  // fragment read offsets (stage 0)
+    };
+    struct Frag {
+        u32x4 v[KMAJ ? FX : 1];
+        s16x4 t[KMAJ ? 1 : FX][2];
+    };
+
+    // x0: first row/column of the tile; xtot: the operand's full extent;
+    // ld: leading dimension in elements; wx0: first row/column of this wave.
+    static __device__ __forceinline__ void setup(Lane& L, int x0, int xtot, int ld, int w,
+                                                 int lane, int wx0, u32 region)
+    {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int blk = w * J + j;
+            const int row = blk * RPB + lane / LPR;
+            if constexpr (KMAJ) {
+                const int c = (lane % LPR) ^ swz_a(row);
+                L.kk[j] = c * 8;
+                L.off[j] = (x0 + row < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
+            } else {
+                const int c = (lane % LPR) ^ swz_b(row);
+                L.kk[j] = row;
+                L.off[j] = (x0 + c * 8 < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
+            }
+        }
+        if constexpr (KMAJ) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int row = wx0 + (lane & 31);
+                const int c = 2 * s + (lane >> 5);
+                L.rd[s] = region + row * (BK * 2) + ((c ^ swz_a(row)) << 4);
+            }
+        } else {
+            const int g = lane >> 4, t = lane & 15;
+            const int k = 8 * (g >> 1) + (t >> 2);
+#pragma unroll
+            for (int f = 0; f < FX; ++f) {
+                const int x = wx0 + f * 32 + 16 * (g & 1) + 4 * (t & 3);
+                L.rd[f] = region + k * (X * 2) + (((x >> 3) ^ swz_b(k)) << 4) + (x & 7) * 2;
+            }
+        }
+    }
+
+    // Descriptor of one strip (k0 .. k0 + 31), rebased so offsets fit 31 bits.
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t strip_rsrc(const void* base, int x0,
+                                                                        int xtot, int ld, int K,
+                                                                        int k0)
+    {
+        if constexpr (KMAJ)
+            return make_rsrc((const char*)base + ((int64_t)x0 * ld + k0) * 2,
+                             clamp_bytes(((int64_t)(xtot - x0 - 1) * ld + (K - k0)) * 2));
+        else
+            return make_rsrc((const char*)base + ((int64_t)k0 * ld + x0) * 2,
+                             clamp_bytes(((int64_t)(K - k0 - 1) * ld + (xtot - x0)) * 2));
+    }
+
+    template <int ST>
+    static __device__ __forceinline__ void copy(const Lane& L, __amdgpu_buffer_rsrc_t rs, int krem,
+                                                int d, int w, u32 region_lds)
+    {
+        dma16(region_lds + ST * STAGE + (w * J + d) * 1024, L.kk[d] < krem ? L.off[d] : kOob, rs);
+    }
+
+    // LDS read i (0 .. NRD-1) of slab S of stage ST.
+    template <int ST, int S>
+    static __device__ __forceinline__ void read(Frag& F, const Lane& L, lds_char* sm, int i)
+    {
+        if constexpr (KMAJ) {
+            F.v[i] = *(const lds_u32x4*)(sm + L.rd[S] + ST * STAGE + i * 32 * (BK * 2));
+        } else {
+            const int f = i >> 1, h = i & 1;
+            F.t[f][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(sm + L.rd[f] + ST * STAGE + (16 * S + 4 * h) * (X * 2)));
+        }
+    }
+
+    // The MFMA operand of block f (8 k per lane, 16-bit words).
+    static __device__ __forceinline__ s16x8 frag(const Frag& F, int f)
+    {
+        if constexpr (KMAJ)
+            return __builtin_bit_cast(s16x8, F.v[f]);
+        else
+            return __builtin_shufflevector(F.t[f][0], F.t[f][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].
+template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
 struct DmaGemm {
     static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
     static constexpr int BK = 32;
@@ -86,74 +199,39 @@ struct DmaGemm {
     static constexpr int WTN = BN / WGN;
     static constexpr int FM = WTM / 32;
     static constexpr int FN = WTN / 32;
-    static constexpr int A_STAGE = BM * BK * 2;  // bytes
-    static constexpr int B_STAGE = BK * BN * 2;
+    using OA = DmaOperand<!TA, BM, WTM, FM, NW>;
+    using OB = DmaOperand<TB, BN, WTN, FN, NW>;
+    static constexpr int A_STAGE = OA::STAGE;
+    static constexpr int B_STAGE = OB::STAGE;
     static constexpr int A_REGION = NS * A_STAGE;
     static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
-    static constexpr int JA = A_STAGE / 1024 / NW;  // copies per wave per strip
-    static constexpr int JB = B_STAGE / 1024 / NW;
-    static constexpr int LPR = BN / 8;               // lanes (16-byte chunks) per B row
-    static constexpr int RPB = 64 / LPR;             // B rows per 1 KiB block
-    static constexpr int VM_AHEAD = (NS - 3) * (JA + JB);  // copies allowed in flight at the barrier
-    static constexpr int NREAD = FM + 2 * FN;        // LDS reads per slab
-    static constexpr int NCOPY = JA + JB;            // copies per wave per strip
+    static constexpr int NREAD = OA::NRD + OB::NRD;  // LDS reads per slab
+    static constexpr int NCOPY = OA::J + OB::J;      // copies per wave per strip
+    static constexpr int VM_AHEAD = (NS - 3) * NCOPY;  // copies allowed in flight at the barrier
 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole 32x32 blocks");
-    static_assert(JA >= 1 && JB >= 1 && A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0,
-                  "strips split into whole 1 KiB copies per wave");
-    static_assert(LPR >= 16 && LPR <= 64, "B rows of 256 to 1024 bytes");
     static_assert(NS >= 3, "the barrier publishes strip t + 1 while t - 1 is free");
     static_assert(NW <= 4, "the main loop is instantiated for up to four waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     struct Frag {
-        u32x4 a[FM];
-        s16x4 b[FN][2];
+        typename OA::Frag a;
+        typename OB::Frag b;
     };
 
     struct Lane {
-        // copy offsets within a strip (already out of range for rows past M / cols past N)
-        u32 a_off[JA];
-        int a_k[JA];  // first k of the chunk this lane copies
-        u32 b_off[JB];
-        int b_k[JB];  // k row this lane copies
-        // LDS read offsets from the start of the LDS buffer (stage 0)
-        u32 a_rd[2];
-        u32 b_rd[FN];
+        typename OA::Lane a;
+        typename OB::Lane b;
     };
+
+    static __device__ __forceinline__ int lda(const GemmParams& p) { return TA ? p.M : p.K; }
+    static __device__ __forceinline__ int ldb(const GemmParams& p) { return TB ? p.K : p.N; }
 
     static __device__ __forceinline__ void setup(Lane& L, const GemmParams& p, int m0, int n0,
                                                  int w, int lane, int wm, int wn)
     {
-#pragma unroll
-        for (int j = 0; j < JA; ++j) {
-            const int blk = w * JA + j;
-            const int row = blk * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ swz_a(row);
-            L.a_k[j] = c * 8;
-            L.a_off[j] = (m0 + row < p.M) ? (u32)(row * p.K + c * 8) * 2u : kOob;
-        }
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const int blk = w * JB + j;
-            const int row = blk * RPB + lane / LPR;
-            const int c = (lane % LPR) ^ swz_b(row);
-            L.b_k[j] = row;
-            L.b_off[j] = (n0 + c * 8 < p.N) ? (u32)(row * p.N + c * 8) * 2u : kOob;
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int row = wm * WTM + (lane & 31);
-            const int c = 2 * s + (lane >> 5);
-            L.a_rd[s] = row * (BK * 2) + ((c ^ swz_a(row)) << 4);
-        }
-        const int g = lane >> 4, t = lane & 15;
-        const int k = 8 * (g >> 1) + (t >> 2);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int n = wn * WTN + fn * 32 + 16 * (g & 1) + 4 * (t & 3);
-            L.b_rd[fn] = A_REGION + k * (BN * 2) + (((n >> 3) ^ swz_b(k)) << 4) + (n & 7) * 2;
-        }
+        OA::setup(L.a, m0, p.M, lda(p), w, lane, wm * WTM, 0);
+        OB::setup(L.b, n0, p.N, ldb(p), w, lane, wn * WTN, A_REGION);
     }
 
     // Buffer descriptors of one strip, rebased to the strip's first element so
@@ -167,29 +245,22 @@ struct DmaGemm {
                                                          int strip)
     {
         const int k0 = strip * BK;
-        const char* abase = (const char*)p.A + ((int64_t)m0 * p.K + k0) * 2;
-        const int64_t abytes = ((int64_t)(p.M - m0 - 1) * p.K + (p.K - k0)) * 2;
-        const char* bbase = (const char*)p.B + ((int64_t)k0 * p.N + n0) * 2;
-        const int64_t bbytes = ((int64_t)(p.K - k0 - 1) * p.N + (p.N - n0)) * 2;
         StripRes r;
-        r.a = make_rsrc(abase, clamp_bytes(abytes));
-        r.b = make_rsrc(bbase, clamp_bytes(bbytes));
+        r.a = OA::strip_rsrc(p.A, m0, p.M, lda(p), p.K, k0);
+        r.b = OB::strip_rsrc(p.B, n0, p.N, ldb(p), p.K, k0);
         r.krem = p.K - k0;
         return r;
     }
 
-    // Copy d (0 .. NCOPY-1) of a strip into LDS stage ST: the JA copies of A
-    // first, then the JB copies of B.
+    // Copy d (0 .. NCOPY-1) of a strip into LDS stage ST: A's copies first.
     template <int ST>
     static __device__ __forceinline__ void issue_copy(const Lane& L, const StripRes& r, int d,
                                                       int w, u32 smem0)
     {
-        if (d < JA)
-            dma16(smem0 + ST * A_STAGE + (w * JA + d) * 1024,
-                  L.a_k[d] < r.krem ? L.a_off[d] : kOob, r.a);
+        if (d < OA::J)
+            OA::template copy<ST>(L.a, r.a, r.krem, d, w, smem0);
         else
-            dma16(smem0 + A_REGION + ST * B_STAGE + (w * JB + d - JA) * 1024,
-                  L.b_k[d - JA] < r.krem ? L.b_off[d - JA] : kOob, r.b);
+            OB::template copy<ST>(L.b, r.b, r.krem, d - OA::J, w, smem0 + A_REGION);
     }
 
     template <int ST>
@@ -203,32 +274,29 @@ struct DmaGemm {
             issue_copy<ST>(L, r, d, w, smem0);
     }
 
-    // Fragment read i (0 .. NREAD-1) of slab s of stage ST.
+    // Fragment read i (0 .. NREAD-1) of slab S of stage ST: A's reads first.
     template <int ST, int S>
     static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i)
     {
-        if (i < FM) {
-            const u32 off = L.a_rd[S] + ST * A_STAGE + i * 32 * (BK * 2);
-            F.a[i] = *(const lds_u32x4*)(sm + off);
-        } else {
-            const int fn = (i - FM) >> 1, h = (i - FM) & 1;
-            const u32 off = L.b_rd[fn] + ST * B_STAGE + (16 * S + 4 * h) * (BN * 2);
-            F.b[fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sm + off));
-        }
+        if (i < OA::NRD)
+            OA::template read<ST, S>(F.a, L.a, sm, i);
+        else
+            OB::template read<ST, S>(F.b, L.b, sm, i - OA::NRD);
     }
 
     static __device__ __forceinline__ void mfma_one(f32x16 (&acc)[FM][FN], const Frag& F, int i)
     {
         const int fm = i / FN, fn = i % FN;
-        const s16x8 b8 = __builtin_shufflevector(F.b[fn][0], F.b[fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const s16x8 a8 = OA::frag(F.a, fm);
+        const s16x8 b8 = OB::frag(F.b, fn);
         if constexpr (DT == DT_BF16)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, b8), __builtin_bit_cast(bf16x8, F.a[fm]), acc[fm][fn], 0,
-                0, 0);
+                __builtin_bit_cast(bf16x8, b8), __builtin_bit_cast(bf16x8, a8), acc[fm][fn], 0, 0,
+                0);
         else
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, b8), __builtin_bit_cast(f16x8, F.a[fm]), acc[fm][fn], 0,
-                0, 0);
+                __builtin_bit_cast(f16x8, b8), __builtin_bit_cast(f16x8, a8), acc[fm][fn], 0, 0,
+                0);
     }
 
     // One strip: MFMAs on slab 0 (fragments F0) then slab 1 (F1), SLOTS MFMA
@@ -384,7 +452,7 @@ struct DmaGemm {
             issue_copies<3 % NS>(L, p, m0, n0, 3, w, smem0);
         static_assert(NS <= 5, "prologue written for up to 5 stages");
         // strip 0 must be complete and visible before its first fragments are read
-        wait_copies_barrier<(NS - 2) * (JA + JB)>();
+        wait_copies_barrier<(NS - 2) * NCOPY>();
         Frag F0, F1;
 #pragma unroll
         for (int i = 0; i < NREAD; ++i)
@@ -417,12 +485,12 @@ struct DmaOcc {
     static constexpr int value = BM * BN >= 256 * 128 ? 1 : 2;
 };
 
-template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
                           amdgpu_waves_per_eu(DmaOcc<BM, BN>::value, DmaOcc<BM, BN>::value))) void
 gemm_dma_kernel(GemmParams p)
 {
-    DmaGemm<DT, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    DmaGemm<DT, TA, TB, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
 }
 
 }  // namespace tg
