@@ -258,6 +258,12 @@ def main():
                                                ow.dtype)}
             if name in MEMORY_BOUND:
                 workloads[name]["cold"] = time_cold(ow, t, stream)
+            tr = load_traffic(name)
+            if tr is not None:
+                # L2 <-> fabric bytes per launch from the committed counter record
+                workloads[name]["traffic_bytes"] = int(tr["hbm_bytes_per_launch"])
+                workloads[name]["gbs_counters"] = round(
+                    tr["hbm_bytes_per_launch"] / (r["mean_ms"] * 1e-3) / 1e9, 1)
             del t
             torch.cuda.empty_cache()
 

@@ -110,7 +110,8 @@ def run(workload: str, launches: int) -> None:
 
 def _read(path: str, counter: str):
     """(calibration KiB, [kernel KiB per launch]) from a counter_collection CSV.
-    The calibration kernel is the only other kernel the profiled program runs."""
+    The calibration kernel is the elementwise multiply of run(); the runtime's
+    small host-to-device copies also appear and are ignored."""
     other, kern = [], []
     with open(path) as f:
         for r in csv.DictReader(f):
@@ -121,9 +122,10 @@ def _read(path: str, counter: str):
                 kern.append(v)
             else:
                 other.append((r["Kernel_Name"], v))
-    if len(other) != 1:
+    calib = [o for o in other if "elementwise" in o[0]]
+    if len(calib) != 1:
         raise SystemExit("expected exactly one calibration kernel, found: %s" % other)
-    return other[0][1], kern
+    return calib[0][1], kern
 
 
 def summarize(workload: str, fetch_csv: str, write_csv: str, out: str) -> dict:
