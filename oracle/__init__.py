@@ -1,4 +1,5 @@
-"""CPU oracle for the tiled GEMM and the weight-only 4-bit dequant GEMM.
+"""CPU oracle for the tiled GEMM, the weight-only 4-bit dequant GEMM and the
+MX-format GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The library under
@@ -52,6 +53,7 @@ def _bind(lib):
         "orc_decode_bf16": ([ctypes.c_uint16], d),
         "orc_decode_e2m1": ([ctypes.c_uint8], d),
         "orc_decode_e8m0": ([ctypes.c_uint8], d),
+        "orc_decode_e4m3": ([ctypes.c_uint8], d),
         "orc_encode_f32": ([d], ctypes.c_uint32),
         "orc_encode_f16": ([d], ctypes.c_uint16),
         "orc_encode_bf16": ([d], ctypes.c_uint16),
@@ -68,6 +70,11 @@ def _bind(lib):
         "orc_dequant_w4_f64": ([i64, i64, i64, p, p, p, ctypes.c_int, p], ctypes.c_int),
         "orc_dequant_w4_entries_f64": ([i64, i64, i64, p, p, p, ctypes.c_int, i64, p, p, p],
                                        None),
+        "orc_mx_decode_a": ([i64, i64, ctypes.c_int, p, p, p], None),
+        "orc_mx_gemm_f64": ([i64, i64, i64, ctypes.c_int, p, p, p, p, ctypes.c_int, p],
+                            ctypes.c_int),
+        "orc_mx_gemm_entries_f64": ([i64, i64, i64, ctypes.c_int, p, p, p, p, ctypes.c_int, i64,
+                                     p, p, p], None),
         "orc_num_threads": ([], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
@@ -124,6 +131,9 @@ class Oracle:
 
     def decode_e8m0(self, e: int) -> float:
         return float(self.lib.orc_decode_e8m0(e))
+
+    def decode_e4m3(self, code: int) -> float:
+        return float(self.lib.orc_decode_e4m3(code))
 
     # -- GEMM ---------------------------------------------------------------
     def gemm_f64(self, A, B, dtype: int, relu: bool = False) -> np.ndarray:
@@ -246,6 +256,67 @@ class Oracle:
                                             _ptr(out))
         return out
 
+    # -- MX-format GEMM ---------------------------------------------------------
+    MX_E2M1, MX_E4M3 = 0, 1
+
+    @staticmethod
+    def _mx_check(fmt, Aq, As, Wq, Ws):
+        if fmt not in (0, 1):
+            raise ValueError("activation format must be 0 (E2M1) or 1 (E4M3)")
+        aq = np.ascontiguousarray(Aq, dtype=np.uint8)
+        a_s = np.ascontiguousarray(As, dtype=np.uint8)
+        wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+        ws = np.ascontiguousarray(Ws, dtype=np.uint8)
+        M = aq.shape[0]
+        K = aq.shape[1] * (2 if fmt == 0 else 1)
+        N = wq.shape[0]
+        if K % 32 != 0:
+            raise ValueError("K must be a multiple of 32")
+        if a_s.shape != (M, K // 32):
+            raise ValueError("activation scale shape does not match [M, K/32]")
+        if wq.shape != (N, K // 2) or ws.shape != (N, K // 32):
+            raise ValueError("packed weight / scale shapes do not match [N, K/2] / [N, K/32]")
+        return aq, a_s, wq, ws, M, N, K
+
+    def mx_decode_a(self, fmt: int, Aq, As) -> np.ndarray:
+        """Activation codes ([M, K/2] E2M1 or [M, K] E4M3) and E8M0 scales [M, K/32]
+        -> a [M, K] fp64."""
+        aq = np.ascontiguousarray(Aq, dtype=np.uint8)
+        a_s = np.ascontiguousarray(As, dtype=np.uint8)
+        M = aq.shape[0]
+        K = aq.shape[1] * (2 if fmt == 0 else 1)
+        if a_s.shape != (M, K // 32):
+            raise ValueError("activation scale shape does not match [M, K/32]")
+        out = np.empty((M, K), dtype=np.float64)
+        self.lib.orc_mx_decode_a(M, K, int(fmt), _ptr(aq), _ptr(a_s), _ptr(out))
+        return out
+
+    def mx_gemm_f64(self, fmt: int, Aq, As, Wq, Ws, relu: bool = False) -> np.ndarray:
+        """Y[m, n] = epi(sum_k a(m, k) * w(n, k)) in fp64 (MX blocks on both operands)."""
+        aq, a_s, wq, ws, M, N, K = self._mx_check(fmt, Aq, As, Wq, Ws)
+        Y = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.orc_mx_gemm_f64(M, N, K, int(fmt), _ptr(aq), _ptr(a_s), _ptr(wq), _ptr(ws),
+                                      int(bool(relu)), _ptr(Y))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+        return Y
+
+    def mx_gemm_entries_f64(self, fmt: int, Aq, As, Wq, Ws, rows, cols,
+                            relu: bool = False) -> np.ndarray:
+        """Selected entries of the MX-format GEMM, each summed one by one in fp64."""
+        aq, a_s, wq, ws, M, N, K = self._mx_check(fmt, Aq, As, Wq, Ws)
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        if r.shape != c.shape:
+            raise ValueError("rows and cols differ in length")
+        if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+            raise IndexError("entry outside the output")
+        out = np.empty(r.shape, dtype=np.float64)
+        self.lib.orc_mx_gemm_entries_f64(M, N, K, int(fmt), _ptr(aq), _ptr(a_s), _ptr(wq),
+                                         _ptr(ws), int(bool(relu)), r.size, _ptr(r), _ptr(c),
+                                         _ptr(out))
+        return out
+
 
 _default = None
 
@@ -306,3 +377,19 @@ def dequant_w4_f64(A, Wq, Ws, relu=False):
 
 def dequant_w4_entries_f64(A, Wq, Ws, rows, cols, relu=False):
     return default().dequant_w4_entries_f64(A, Wq, Ws, rows, cols, relu)
+
+
+def decode_e4m3(code):
+    return default().decode_e4m3(code)
+
+
+def mx_decode_a(fmt, Aq, As):
+    return default().mx_decode_a(fmt, Aq, As)
+
+
+def mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu=False):
+    return default().mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu)
+
+
+def mx_gemm_entries_f64(fmt, Aq, As, Wq, Ws, rows, cols, relu=False):
+    return default().mx_gemm_entries_f64(fmt, Aq, As, Wq, Ws, rows, cols, relu)

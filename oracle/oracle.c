@@ -1,5 +1,6 @@
 /*
- * Oracle for the tiled dense GEMM and the weight-only 4-bit dequant GEMM.
+ * Oracle for the tiled dense GEMM, the weight-only 4-bit dequant GEMM and the
+ * MX-format GEMM.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the library calls, links or includes
  * this file; only the tests, the smoke check and the CPU-baseline leg of the
@@ -19,7 +20,8 @@
  * Number formats are decoded and encoded from their field definitions
  * (sign / biased exponent / fraction), never through a hardware cast:
  *   IEEE-754 binary32 and binary16, bfloat16 (binary32 with a 7-bit fraction),
- *   and the OCP Microscaling (MX) v1.0 element type E2M1 and scale type E8M0.
+ *   and the OCP Microscaling (MX) v1.0 element types E2M1 and E4M3 and scale
+ *   type E8M0.
  * The 4-bit weight format is not on the pages; it follows the workload text:
  * two E2M1 codes per byte (even k in bits 3:0, odd k in bits 7:4), one E8M0
  * scale per 32 consecutive k of a weight row, C = A * W^T with W stored [N][K].
@@ -72,6 +74,16 @@ double orc_decode_e2m1(uint8_t code) { return decode_bits(code & 0xFu, 2, 1, 0);
 
 /* OCP MX E8M0: 2^(E - 127); E = 255 is NaN. */
 double orc_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* OCP MX E4M3: bit 7 sign, bits 6:3 exponent (bias 7), bits 2:0 fraction.
+ * No infinities: exponent 15 is an ordinary binade, except that S.1111.111
+ * is NaN (so the largest finite magnitude is 1.75 * 2^8 = 448). */
+double orc_decode_e4m3(uint8_t code)
+{
+    if ((code & 0x7Fu) == 0x7Fu)
+        return NAN;
+    return decode_bits(code, 4, 3, 0);
+}
 
 /* ---------------------------------------------------------------------- */
 /* Field-level encoding: one round-to-nearest-even from a double.          */
@@ -373,6 +385,96 @@ void orc_dequant_w4_entries_f64(int64_t M, int64_t N, int64_t K, const uint16_t*
         double s = 0.0;
         for (int64_t k = 0; k < K; ++k)
             s += orc_decode_bf16(A[i * K + k]) * w4_value(Wq, Ws, K, j, k);
+        out[t] = relu ? relu_f64(s) : s;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* MX-format GEMM: both operands in OCP MX v1.0 blocks of 32 along k (the  */
+/* "WFP4" GEMM of the TileLang architecture page, performance section,     */
+/* with block-format activations as well).                                 */
+/*   a(m, k) = ELEM(codeA(m, k)) * E8M0(As[m][k / 32])                     */
+/*     E2M1 activations (fmt 0): codeA = nibble k % 2 of Aq[m][k / 2]      */
+/*     E4M3 activations (fmt 1): codeA = Aq[m][k]                          */
+/*   w(n, k) = E2M1(code(n, k)) * E8M0(Ws[n][k / 32])  (as the dequant)    */
+/*   Y[m][n] = epi(sum_k a(m, k) * w(n, k))                                */
+/* The plain sum in fp64: every product is exact (at most 3 + 1 significant */
+/* bits times powers of two), so Y is exact while K * 2^-52 * sum|a w| is   */
+/* below half an ulp of the output, and NaN scales / codes give NaN.        */
+/* ---------------------------------------------------------------------- */
+
+static double mx_a_value(int fmt, const uint8_t* Aq, const uint8_t* As, int64_t K, int64_t m,
+                         int64_t k)
+{
+    double e;
+    if (fmt == 0) {
+        const uint8_t byte = Aq[m * (K / 2) + k / 2];
+        e = orc_decode_e2m1((uint8_t)((byte >> (4 * (k % 2))) & 0xF));
+    } else {
+        e = orc_decode_e4m3(Aq[m * K + k]);
+    }
+    return e * orc_decode_e8m0(As[m * (K / 32) + k / 32]);
+}
+
+/* Decode the activations to fp64 [M][K]. */
+void orc_mx_decode_a(int64_t M, int64_t K, int fmt, const uint8_t* Aq, const uint8_t* As,
+                     double* A)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            A[m * K + k] = mx_a_value(fmt, Aq, As, K, m, k);
+}
+
+int orc_mx_gemm_f64(int64_t M, int64_t N, int64_t K, int fmt, const uint8_t* Aq,
+                    const uint8_t* As, const uint8_t* Wq, const uint8_t* Ws, int relu, double* Y)
+{
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -1;
+    }
+    orc_mx_decode_a(M, K, fmt, Aq, As, Ad);
+    /* B[k][n] := w(n, k) */
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Bd[k * N + n] = w4_value(Wq, Ws, K, n, k);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double* yi = Y + i * N;
+        for (int64_t j = 0; j < N; ++j)
+            yi[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = Ad[i * K + k];
+            const double* bk = Bd + k * N;
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] += a * bk[j];
+        }
+        if (relu)
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] = relu_f64(yi[j]);
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+void orc_mx_gemm_entries_f64(int64_t M, int64_t N, int64_t K, int fmt, const uint8_t* Aq,
+                             const uint8_t* As, const uint8_t* Wq, const uint8_t* Ws, int relu,
+                             int64_t count, const int64_t* rows, const int64_t* cols, double* out)
+{
+    (void)M;
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t i = rows[t], j = cols[t];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, k);
         out[t] = relu ? relu_f64(s) : s;
     }
 }

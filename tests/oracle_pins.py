@@ -15,7 +15,13 @@ What pins what:
   * ReLU: y = max(sum, 0) with +0 for non-positive sums;
   * dequant GEMM: reductions to row sums, one-hot weights (nibble order and
     the k/32 scale index), per-group scales, and a weight decode done here from
-    the golden table.
+    the golden table;
+  * E4M3: the OCP MX v1.0 landmark values under tests/golden/ and torch's
+    float8_e4m3fn decoding of all 256 codes;
+  * MX-format GEMM: row sums, one-hot activations and weights (nibble order,
+    E4M3 row stride, both k/32 scale indexes), NaN scales and codes, and exact
+    rational brute force on operands decoded here (golden E2M1 table, torch
+    E4M3, powers of two).
 """
 
 from __future__ import annotations
@@ -121,6 +127,43 @@ def load_e8m0_golden():
     return pts
 
 
+def load_e4m3_golden():
+    pts = {}
+    with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code, val = line.split()
+            pts[int(code, 16)] = float(val)  # "nan" and "-0" parse as floats
+    return pts
+
+
+def decode_e4m3_torch(codes):
+    """E4M3 codes -> float64 through torch's float8_e4m3fn (a library decoder)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def decode_mx_a_here(fmt, Aq, As):
+    """Test-side activation decode (golden E2M1 table or torch E4M3, ldexp scales)."""
+    Aq = np.asarray(Aq, dtype=np.uint8)
+    if fmt == 0:
+        tab = load_e2m1_golden()
+        lut = np.array([tab[c] for c in range(16)], dtype=np.float64)
+        M, half = Aq.shape
+        codes = np.empty((M, 2 * half), dtype=np.uint8)
+        codes[:, 0::2] = Aq & 0xF
+        codes[:, 1::2] = Aq >> 4
+        elem = lut[codes]
+    else:
+        elem = decode_e4m3_torch(Aq)
+    scale = np.ldexp(1.0, np.asarray(As, dtype=np.int64) - 127)
+    return elem * np.repeat(scale, 32, axis=1)
+
+
 def decode_w4_here(Wq, Ws):
     """Test-side weight decode from the golden tables (independent of the oracle)."""
     tab = load_e2m1_golden()
@@ -149,6 +192,14 @@ def _dq_both(orc, A, Wq, Ws, relu=False):
     M, N = Y.shape
     rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     Ye = orc.dequant_w4_entries_f64(A, Wq, Ws, rr.ravel(), cc.ravel(), relu).reshape(M, N)
+    return Y, Ye
+
+
+def _mx_both(orc, fmt, Aq, As, Wq, Ws, relu=False):
+    Y = orc.mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu)
+    M, N = Y.shape
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Ye = orc.mx_gemm_entries_f64(fmt, Aq, As, Wq, Ws, rr.ravel(), cc.ravel(), relu).reshape(M, N)
     return Y, Ye
 
 
@@ -463,6 +514,128 @@ def check_dequant_random_vs_decoded(orc):
 
 
 # ---------------------------------------------------------------------------
+# E4M3 and the MX-format GEMM.
+# ---------------------------------------------------------------------------
+
+def check_e4m3_points(orc):
+    for code, val in load_e4m3_golden().items():
+        got = orc.decode_e4m3(code)
+        if math.isnan(val):
+            assert math.isnan(got), (code, got)
+        else:
+            assert got == val and math.copysign(1.0, got) == math.copysign(1.0, val), (code, got)
+
+
+def check_e4m3_vs_torch(orc):
+    ref = decode_e4m3_torch(np.arange(256))
+    for code in range(256):
+        got = orc.decode_e4m3(code)
+        if math.isnan(ref[code]):
+            assert math.isnan(got), (code, got)
+        else:
+            assert _same(got, ref[code]), (code, got, ref[code])
+
+
+E2M1_ONE, E4M3_ONE = 0x2, 0x38  # the codes of 1.0
+
+
+def _mx_ones(fmt, M, K):
+    if fmt == 0:
+        return np.full((M, K // 2), E2M1_ONE * 0x11, dtype=np.uint8)
+    return np.full((M, K), E4M3_ONE, dtype=np.uint8)
+
+
+def check_mx_row_sums(orc):
+    # a == 1 everywhere: Y[m][n] = sum_k w(n, k), the decoded weight row sums
+    r = np.random.Generator(np.random.PCG64(41))
+    M, N, K = 3, 5, 96
+    Wq = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    Ws = r.integers(124, 131, size=(N, K // 32)).astype(np.uint8)
+    want = np.repeat(decode_w4_here(Wq, Ws).sum(axis=1)[None, :], M, axis=0)
+    As = np.full((M, K // 32), 127, dtype=np.uint8)
+    for fmt in (0, 1):
+        for Y in _mx_both(orc, fmt, _mx_ones(fmt, M, K), As, Wq, Ws):
+            assert _same(Y + 0.0, want + 0.0), fmt
+
+
+def check_mx_one_hot(orc):
+    # one nonzero activation and one nonzero weight at the same k: Y has a
+    # single nonzero entry, the product of the two decoded values
+    tab = load_e2m1_golden()
+    M, N, K = 4, 3, 128
+    cases = ((0, 0, 0, 0, 7, 0x3c, 127, 126), (1, 2, 33, 1, 3, 0x01, 125, 129),
+             (3, 1, 62, 15, 13, 0xfe, 124, 130), (2, 0, 95, 6, 5, 0x4a, 128, 120),
+             (1, 1, 127, 9, 1, 0x81, 131, 127))
+    for fmt in (0, 1):
+        for (m0, n0, k0, ca2, cw, ca8, ea, ew) in cases:
+            ca = ca2 if fmt == 0 else ca8
+            Aq = np.zeros((M, K // 2) if fmt == 0 else (M, K), dtype=np.uint8)
+            if fmt == 0:
+                Aq[m0, k0 // 2] = ca << (4 * (k0 % 2))
+                av = tab[ca]
+            else:
+                Aq[m0, k0] = ca
+                av = float(decode_e4m3_torch(np.array([ca]))[0])
+            As = np.full((M, K // 32), 127, dtype=np.uint8)
+            As[m0, k0 // 32] = ea
+            Wq = np.zeros((N, K // 2), dtype=np.uint8)
+            Wq[n0, k0 // 2] = cw << (4 * (k0 % 2))
+            Ws = np.full((N, K // 32), 127, dtype=np.uint8)
+            Ws[n0, k0 // 32] = ew
+            want = np.zeros((M, N))
+            want[m0, n0] = av * 2.0 ** (ea - 127) * tab[cw] * 2.0 ** (ew - 127)
+            for Y in _mx_both(orc, fmt, Aq, As, Wq, Ws):
+                assert _same(Y + 0.0, want + 0.0), (fmt, m0, n0, k0)
+
+
+def check_mx_nan(orc):
+    # a NaN scale (E8M0 255) or a NaN E4M3 code poisons exactly the results
+    # that take one of its products
+    M, N, K = 3, 4, 64
+    Wq = np.full((N, K // 2), 0x22, dtype=np.uint8)
+    Ws = np.full((N, K // 32), 127, dtype=np.uint8)
+    for fmt in (0, 1):
+        Aq = _mx_ones(fmt, M, K)
+        As = np.full((M, K // 32), 127, dtype=np.uint8)
+        As[1, 1] = 255
+        for Y in _mx_both(orc, fmt, Aq, As, Wq, Ws):
+            assert np.isnan(Y[1]).all() and not np.isnan(Y[[0, 2]]).any()
+        As[1, 1] = 127
+        Ws2 = Ws.copy()
+        Ws2[2, 0] = 255
+        for Y in _mx_both(orc, fmt, Aq, As, Wq, Ws2):
+            assert np.isnan(Y[:, 2]).all() and not np.isnan(Y[:, [0, 1, 3]]).any()
+    Aq = _mx_ones(1, M, K)
+    Aq[2, 40] = 0xff
+    for Y in _mx_both(orc, 1, Aq, np.full((M, K // 32), 127, dtype=np.uint8), Wq, Ws):
+        assert np.isnan(Y[2]).all() and not np.isnan(Y[:2]).any()
+
+
+def check_mx_random_vs_decoded(orc):
+    r = np.random.Generator(np.random.PCG64(42))
+    M, N, K = 5, 7, 128
+    Wq = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    Ws = r.integers(118, 137, size=(N, K // 32)).astype(np.uint8)
+    W = decode_w4_here(Wq, Ws)
+    for fmt in (0, 1):
+        if fmt == 0:
+            Aq = r.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+        else:
+            Aq = r.integers(0, 256, size=(M, K), dtype=np.uint8)
+            Aq[(Aq & 0x7F) == 0x7F] = 0x3a  # no NaN codes here
+        As = r.integers(118, 137, size=(M, K // 32)).astype(np.uint8)
+        A = decode_mx_a_here(fmt, Aq, As)
+        assert _same(orc.mx_decode_a(fmt, Aq, As) + 0.0, A + 0.0), fmt
+        ex = exact_product(A, W.T)
+        for relu in (False, True):
+            for Y in _mx_both(orc, fmt, Aq, As, Wq, Ws, relu):
+                for i in range(M):
+                    for j in range(N):
+                        want = max(ex[i][j], Fraction(0)) if relu else ex[i][j]
+                        assert Fraction(float(Y[i, j])) == want, (fmt, relu, i, j)
+
+
+# ---------------------------------------------------------------------------
 # Operands stored transposed (C = op(A) op(B)).
 # ---------------------------------------------------------------------------
 
@@ -530,5 +703,6 @@ ALL_CHECKS = [
     check_all_ones, check_rank_one, check_brute_force_dyadic, check_brute_force_general,
     check_relu, check_round_outputs, check_dequant_row_sums, check_dequant_one_hot,
     check_dequant_group_scales, check_dequant_random_vs_decoded, check_layout_textbook_2x2,
-    check_layout_brute_force, check_layout_rank_one,
+    check_layout_brute_force, check_layout_rank_one, check_e4m3_points, check_e4m3_vs_torch,
+    check_mx_row_sums, check_mx_one_hot, check_mx_nan, check_mx_random_vs_decoded,
 ]

@@ -1,7 +1,8 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
 the pins catch every one: a dropped term, a wrong sign, a transposed operand, a
 wrong index, a swapped nibble order, a wrong scale index, ties rounded away from
-even, a lost ReLU or its sign of zero, and wrong special-value handling."""
+even, a lost ReLU or its sign of zero, wrong special-value handling, and the
+same kinds of slip in the E4M3 decode and the MX-format GEMM."""
 
 import os
 import shutil
@@ -39,6 +40,20 @@ MUTANTS = [
     ("layout_entries_b", "const int64_t ib = trans_b ? j * K + k : k * N + j;",
      "const int64_t ib = trans_b ? k * N + j : k * N + j;", 0),
     ("layout_relu_lost", "Y[i * N + j] = relu ? relu_f64(s) : s;", "Y[i * N + j] = s;", 0),
+    ("e4m3_ieee_specials", "return decode_bits(code, 4, 3, 0);", "return decode_bits(code, 4, 3, 1);", 0),
+    ("e4m3_positive_nan_only", "if ((code & 0x7Fu) == 0x7Fu)", "if (code == 0x7Fu)", 0),
+    ("e4m3_bias_8", "return decode_bits(code, 4, 3, 0);", "return 0.5 * decode_bits(code, 4, 3, 0);", 0),
+    ("mx_a_nibble_order", "(4 * (k % 2))", "(4 * (1 - k % 2))", 2),
+    ("mx_a_scale_index", "As[m * (K / 32) + k / 32]", "As[m * (K / 32) + (k / 32 + 1) % (K / 32)]", 0),
+    ("mx_a_scale_per_16", "As[m * (K / 32) + k / 32]", "As[m * (K / 32) + (k / 16) % (K / 32)]", 0),
+    ("mx_e4m3_row_stride", "e = orc_decode_e4m3(Aq[m * K + k]);", "e = orc_decode_e4m3(Aq[m * (K / 2) + k]);", 0),
+    ("mx_format_swapped", "if (fmt == 0) {", "if (fmt != 0) {", 0),
+    ("mx_gemm_drops_last_k", "yi[j] += a * bk[j];", "yi[j] += a * bk[j] * (k + 1 < K);", 2),
+    ("mx_gemm_weight_transposed", "Bd[k * N + n] = w4_value(Wq, Ws, K, n, k);",
+     "Bd[k * N + n] = w4_value(Wq, Ws, K, (n + 1) % N, k);", 1),
+    ("mx_entries_reversed_k", "s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, k);",
+     "s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, K - 1 - k);", 0),
+    ("mx_relu_lost", "yi[j] = relu_f64(yi[j]);", "yi[j] = yi[j];", 2),
 ]
 
 
