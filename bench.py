@@ -11,8 +11,8 @@ Printed: ONE JSON line (rank 0) with
               stream it runs on, against the bf16 dense MFMA peak,
   cpu_baseline the C oracle timed on host cores on a bounded row sample,
   workloads   the other workload shapes (fp32 / fp16 GEMMs, the non-divisible
-              bf16 GEMM, the 4-bit dequant GEMM and its decode-like probes),
-              each timed the same way.
+              bf16 GEMM, the 4-bit dequant GEMM and its decode-like probes,
+              the MX-format GEMMs), each timed the same way.
 """
 
 from __future__ import annotations
@@ -30,11 +30,13 @@ if ROOT not in sys.path:
 METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (4096³ bf16/fp32, 1 GPU)"
 # MI355X dense matrix peaks (256 CUs at 2.4 GHz): bf16/fp16 4096 FLOP/clk/CU,
 # fp32 256 FLOP/clk/CU; HBM3E 8 TB/s.
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
+               # scaled MFMA: E2M1 x E2M1 at the fp4 rate, E4M3 x E2M1 at the fp8 rate
+               "mx_e2m1": 10066.3, "mx_e4m3": 5033.2}
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_4096_relu"
 OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x8192x8192",
-         "w4_16x8192x8192", "w4_1x8192x8192"]
+         "w4_16x8192x8192", "w4_1x8192x8192", "mx_e2m1_8192", "mx_e4m3_8192"]
 
 
 def load_traffic(workload: str):
@@ -68,6 +70,9 @@ def make_device_inputs(w, dev):
         B = torch.from_numpy(inp["B"].view(view)).view(tdt[w.dtype]).to(dev)
         C = torch.empty((w.M, w.N), dtype=tdt[w.dtype], device=dev)
         return inp, (A, B, C)
+    if w.op == "mx":
+        t = tuple(torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws"))
+        return inp, t + (torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev),)
     A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
     Wq = torch.from_numpy(inp["Wq"]).to(dev)
     Ws = torch.from_numpy(inp["Ws"]).to(dev)
@@ -82,6 +87,9 @@ def launcher(w, tensors, stream):
     if w.op == "gemm":
         A, B, C = tensors
         return lambda: binding.gemm(A, B, C=C, epilogue=epi, stream=stream)
+    if w.op == "mx":
+        Aq, As, Wq, Ws, C = tensors
+        return lambda: binding.gemm_mx(w.dtype, Aq, As, Wq, Ws, C=C, epilogue=epi, stream=stream)
     A, Wq, Ws, C = tensors
     return lambda: binding.dequant_gemm_w4(A, Wq, Ws, C=C, epilogue=epi, stream=stream)
 
@@ -145,6 +153,8 @@ def time_cold(w, tensors, stream, launches: int = 40):
 def dtype_name(w):
     from tiled_dense_gemm_07_amd import synth
 
+    if w.op == "mx":
+        return "mx_" + synth.MX_NAMES[w.dtype]
     return {synth.F32: "f32", synth.F16: "f16", synth.BF16: "bf16"}[w.dtype]
 
 
@@ -254,8 +264,8 @@ def main():
                 "frac_mfma_peak": round(tf / PEAK_TFLOPS[dn], 4),
                 "gbs_algorithmic": round(gbs, 1),
                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                "config": binding.query_config(0 if ow.op == "gemm" else 1, ow.M, ow.N, ow.K,
-                                               ow.dtype)}
+                "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2}[ow.op],
+                                               ow.M, ow.N, ow.K, ow.dtype)}
             if name in MEMORY_BOUND:
                 workloads[name]["cold"] = time_cold(ow, t, stream)
             tr = load_traffic(name)

@@ -46,8 +46,9 @@ typedef struct ihipStream_t* tg_stream_t; /* same object as hipStream_t */
 typedef enum {
     TG_OK = 0,
     TG_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
-    TG_ERR_BAD_SHAPE = 2,    /* negative / too large size, or dequant K % 32 != 0 */
-    TG_ERR_BAD_DTYPE = 3,    /* dtype not one of tg_dtype                         */
+    TG_ERR_BAD_SHAPE = 2,    /* negative / too large size, dequant K % 32 != 0,   */
+                             /* or MX K % 128 != 0                                */
+    TG_ERR_BAD_DTYPE = 3,    /* dtype not one of tg_dtype (MX: tg_mx_format)      */
     TG_ERR_BAD_EPILOGUE = 4, /* epilogue not one of tg_epilogue                   */
     TG_ERR_ALIAS = 5,        /* C overlaps an input                               */
     TG_ERR_NO_CONFIG = 6,    /* forced config index out of range / wrong op       */
@@ -59,7 +60,10 @@ typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
 
 typedef enum { TG_EPI_NONE = 0, TG_EPI_RELU = 1 } tg_epilogue;
 
-typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1 } tg_op;
+typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1, TG_OP_MX = 2 } tg_op;
+
+/* Element format of the activations of tg_gemm_mx. */
+typedef enum { TG_MX_E2M1 = 0, TG_MX_E4M3 = 1 } tg_mx_format;
 
 /*
  * C = epilogue(A x B).
@@ -118,6 +122,35 @@ tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void
 tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, const uint8_t* Wq,
                              const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream);
 
+/*
+ * MX-format GEMM: C = epilogue(A x W^T) with the activations, too, in OCP
+ * microscaling blocks (the pages' "WFP4" GEMM of "TileLang架构深度剖析", the
+ * performance section, run natively in the block formats instead of
+ * dequantised: the matrix cores of gfx950 multiply E2M1 / E4M3 elements and
+ * apply the E8M0 block scales themselves).
+ *   Aq: activation element codes, format a_fmt:
+ *       TG_MX_E2M1: uint8 [M][K/2], two E2M1 codes per byte as in Wq below;
+ *       TG_MX_E4M3: uint8 [M][K], one OCP E4M3 code per byte (sign, 4-bit
+ *                   exponent with bias 7, 3-bit mantissa; no infinities;
+ *                   S.1111.111 is NaN; largest finite value 448).
+ *   As: uint8 [M][K/32]: one E8M0 scale byte per 32 consecutive k of a row.
+ *   Wq: uint8 [N][K/2] E2M1 weight codes, Ws: uint8 [N][K/32] E8M0 scales,
+ *       laid out as for tg_dequant_gemm_w4.
+ *   a(m, k) = elem(Aq, m, k) * 2^(As[m][k/32] - 127),
+ *   w(n, k) = e2m1(Wq, n, k) * 2^(Ws[n][k/32] - 127),
+ *   C[m][n] = sum_k a(m, k) * w(n, k), accumulated in fp32 and rounded once
+ *   to bf16; C: bf16 [M][N].  Scale byte 255 is NaN: every result that takes
+ *   a product of that block is NaN (as is every one that takes an E4M3 NaN).
+ *   The pages give no format for this workload; the one above is the OCP MX
+ *   v1.0 definition.
+ * Requirements: K % 128 == 0 (else TG_ERR_BAD_SHAPE); Aq and Wq 16-byte
+ *   aligned, As and Ws 4-byte aligned (else TG_ERR_NO_CONFIG).
+ * Errors: as tg_gemm; TG_ERR_BAD_DTYPE when a_fmt is not a tg_mx_format.
+ */
+tg_status tg_gemm_mx(int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt, const uint8_t* Aq,
+                     const uint8_t* As, const uint8_t* Wq, const uint8_t* Ws, void* C,
+                     tg_epilogue epi, tg_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* tg_status_str(tg_status s);
 
@@ -125,28 +158,32 @@ const char* tg_status_str(tg_status s);
  * Which compiled kernel configuration the library would launch for this call.
  * Writes a NUL-terminated description (tile sizes, waves, stages, swizzle
  * group, launch grid) into buf[0 .. len-1], truncating if needed.
- * op: TG_OP_GEMM or TG_OP_DEQUANT_W4 (dtype is ignored for the latter).
+ * op: TG_OP_GEMM, TG_OP_DEQUANT_W4 (dtype ignored) or TG_OP_MX (dtype
+ * carries the tg_mx_format of the activations).
  * Errors: TG_ERR_NULL_POINTER (buf NULL or len 0), TG_ERR_BAD_SHAPE,
  *   TG_ERR_BAD_DTYPE, TG_ERR_NO_CONFIG (op unknown).
  */
 tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
                           size_t len);
 
-/* As tg_query_config, for the operand layouts of tg_gemm_ex (dequant: 0, 0;
- * TG_ERR_BAD_LAYOUT otherwise). */
+/* As tg_query_config, for the operand layouts of tg_gemm_ex (dequant and MX:
+ * 0, 0; TG_ERR_BAD_LAYOUT otherwise). */
 tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, int trans_a,
                              int trans_b, char* buf, size_t len);
 
 /*
  * Offline sweep support: the compiled configurations, listed per (op, dtype),
- * can be launched by index instead of by the built-in selection table.
+ * can be launched by index instead of by the built-in selection table.  The
+ * dequant list ignores dtype; the MX list holds both activation formats and
+ * ignores dtype too (a configuration runs calls of its own format only).
  *   tg_config_count: number of configurations for (op, dtype); 0 if none.
  *   tg_config_name : description of configuration `index` (as tg_query_config).
- *   tg_gemm_config / tg_gemm_ex_config / tg_dequant_gemm_w4_config: same
- *     contract as tg_gemm / tg_gemm_ex / tg_dequant_gemm_w4, launching
+ *   tg_gemm_config / tg_gemm_ex_config / tg_dequant_gemm_w4_config /
+ *     tg_gemm_mx_config: same contract as tg_gemm / tg_gemm_ex /
+ *     tg_dequant_gemm_w4 / tg_gemm_mx, launching
  *     configuration `index`; TG_ERR_NO_CONFIG if `index` is out of range or
- *     the configuration cannot run the call (operand layout, alignment, or a
- *     K multiple it needs).
+ *     the configuration cannot run the call (operand layout, alignment, a K
+ *     multiple it needs, or another activation format).
  */
 int tg_config_count(int op, tg_dtype dtype);
 tg_status tg_config_name(int op, tg_dtype dtype, int index, char* buf, size_t len);
@@ -159,6 +196,9 @@ tg_status tg_gemm_ex_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype
 tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, const void* A,
                                     const uint8_t* Wq, const uint8_t* Ws, void* C,
                                     tg_epilogue epi, tg_stream_t stream);
+tg_status tg_gemm_mx_config(int index, int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt,
+                            const uint8_t* Aq, const uint8_t* As, const uint8_t* Wq,
+                            const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream);
 
 /*
  * The block-swizzled tile order, for host-side checking.  For a grid of

@@ -133,12 +133,54 @@ def test_gemm_ex_argument_errors(lib):
     assert buf.value.decode().startswith("gemm_bf16_256x256x32_w2x2_s4_g4_dma_tt")
 
 
+def test_mx_argument_errors(lib):
+    g = lib.tg_gemm_mx
+    PQ = 0x50000000
+    # (M, N, K, fmt, Aq, As, Wq, Ws, C, epi, stream)
+    assert g(4, 4, 128, 2, PA, PS, PB, PQ, PC, 0, None) == DTYPE
+    assert g(4, 4, 128, -1, PA, PS, PB, PQ, PC, 0, None) == DTYPE
+    assert g(4, 4, 128, 0, PA, PS, PB, PQ, PC, 2, None) == EPI
+    assert g(4, 4, 96, 0, PA, PS, PB, PQ, PC, 0, None) == SHAPE  # K % 128
+    assert g(4, 4, -128, 1, PA, PS, PB, PQ, PC, 0, None) == SHAPE
+    assert g(4, 4, 1 << 23, 1, PA, PS, PB, PQ, PC, 0, None) == SHAPE  # 256 K > 2^31
+    assert g(4, 4, 128, 0, None, PS, PB, PQ, PC, 0, None) == NULLP
+    assert g(4, 4, 128, 1, PA, None, PB, PQ, PC, 0, None) == NULLP
+    assert g(4, 4, 128, 0, PA, PS, PB, None, PC, 0, None) == NULLP
+    assert g(4, 4, 128, 0, PA, PS, PB, PQ, None, 0, None) == NULLP
+    assert g(4, 4, 128, 1, PA, PS, PB, PQ, PA + 100, 0, None) == ALIAS  # inside Aq (E4M3)
+    assert g(4, 4, 128, 0, PA, PS, PB, PQ, PS + 8, 0, None) == ALIAS   # inside As
+    assert g(0, 4, 128, 0, None, None, None, None, None, 0, None) == OK
+    # unaligned codes or scale rows: no configuration
+    assert g(4, 4, 128, 0, PA + 8, PS, PB, PQ, PC, 0, None) == NOCFG
+    assert g(4, 4, 128, 0, PA, PS + 2, PB, PQ, PC, 0, None) == NOCFG
+    assert g(4, 4, 128, 1, PA, PS, PB, PQ + 1, PC, 0, None) == NOCFG
+    # forced configurations of the other activation format, or out of range
+    names = binding.list_configs(binding.TG_OP_MX)
+    c = lib.tg_gemm_mx_config
+    for idx, name in enumerate(names):
+        other = 1 if name.startswith("mx_e2m1") else 0
+        assert c(idx, 4, 4, 128, other, PA, PS, PB, PQ, PC, 0, None) == NOCFG, name
+    assert c(len(names), 4, 4, 128, 0, PA, PS, PB, PQ, PC, 0, None) == NOCFG
+    assert c(-1, 4, 4, 128, 0, PA, PS, PB, PQ, PC, 0, None) == NOCFG
+    buf = ctypes.create_string_buffer(128)
+    assert lib.tg_query_config_ex(2, 8192, 8192, 8192, 0, 0, 0, buf, 128) == OK
+    assert buf.value.decode().startswith("mx_e2m1_256x256x128_w2x2_s4_")
+    assert lib.tg_query_config_ex(2, 8192, 8192, 8192, 1, 0, 0, buf, 128) == OK
+    assert buf.value.decode().startswith("mx_e4m3_128x256x128_w2x2_s4_")
+    assert lib.tg_query_config_ex(2, 300, 200, 256, 1, 0, 0, buf, 128) == OK
+    assert buf.value.decode().startswith("mx_e4m3_128x128x128")
+    assert lib.tg_query_config_ex(2, 64, 64, 64, 0, 0, 0, buf, 128) == SHAPE
+    assert lib.tg_query_config_ex(2, 64, 64, 128, 3, 0, 0, buf, 128) == DTYPE
+    assert lib.tg_query_config_ex(2, 64, 64, 128, 0, 1, 0, buf, 128) == BADL
+
+
 def test_launch_failure_is_reported(lib, monkeypatch):
     # TG_FAULT=launch makes the launcher report a HIP failure after validation
     # and before any HIP call.
     monkeypatch.setenv("TG_FAULT", "launch")
     assert lib.tg_gemm(4, 4, 4, 2, PA, PB, PC, 0, None) == HIP
     assert lib.tg_dequant_gemm_w4(4, 4, 64, PA, PB, PS, PC, 0, None) == HIP
+    assert lib.tg_gemm_mx(4, 4, 128, 0, PA, PS, PB, PS + 64, PC, 0, None) == HIP
     with pytest.raises(binding.TileGemmError) as ei:
         binding._check(HIP)
     assert ei.value.status == HIP
@@ -165,6 +207,9 @@ def test_config_lists(lib):
         assert len(names) == len(set(names)) and names
         # each list has a narrow (element-load) configuration for unaligned operands
         assert any(n.endswith("_narrow") for n in names)
+    mx = binding.list_configs(binding.TG_OP_MX)
+    assert len(mx) == len(set(mx)) and mx == binding.list_configs(binding.TG_OP_MX, 1)
+    assert any(n.startswith("mx_e2m1_") for n in mx) and any(n.startswith("mx_e4m3_") for n in mx)
 
 
 def _raster_reference(tiles_m, tiles_n, group_m, logical):

@@ -21,12 +21,14 @@ _DEFAULT_LIB = os.path.join(HERE, "libtilegemm.so")
 
 TG_F32, TG_F16, TG_BF16 = 0, 1, 2
 TG_EPI_NONE, TG_EPI_RELU = 0, 1
-TG_OP_GEMM, TG_OP_DEQUANT_W4 = 0, 1
+TG_OP_GEMM, TG_OP_DEQUANT_W4, TG_OP_MX = 0, 1, 2
+TG_MX_E2M1, TG_MX_E4M3 = 0, 1
 
 # exported symbols, as declared in include/tilegemm.h
 EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_query_config",
            "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
-           "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map")
+           "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
+           "tg_gemm_mx_config")
 
 _lib = None
 
@@ -78,6 +80,10 @@ def load_library():
     lib.tg_dequant_gemm_w4_config.restype = c_int
     lib.tg_tile_map.argtypes = [i64, i64, c_int, p, p]
     lib.tg_tile_map.restype = c_int
+    lib.tg_gemm_mx.argtypes = [i64, i64, i64, c_int, p, p, p, p, p, c_int, p]
+    lib.tg_gemm_mx.restype = c_int
+    lib.tg_gemm_mx_config.argtypes = [c_int, i64, i64, i64, c_int, p, p, p, p, p, c_int, p]
+    lib.tg_gemm_mx_config.restype = c_int
     _lib = lib
     return lib
 
@@ -244,6 +250,45 @@ def dequant_gemm_w4_with_config(index: int, A, Wq, Ws, C=None, epilogue=None, st
                                                     Ws.data_ptr(), C.data_ptr(),
                                                     _epi_code(epilogue),
                                                     _stream_ptr(A.device, stream)))
+    return C
+
+
+def _mx_args(fmt, Aq, As, Wq, Ws, C):
+    import torch
+
+    if fmt not in (TG_MX_E2M1, TG_MX_E4M3):
+        raise ValueError("activation format must be TG_MX_E2M1 or TG_MX_E4M3")
+    for name, t in (("Aq", Aq), ("As", As), ("Wq", Wq), ("Ws", Ws)):
+        _require_gpu_tensor(name, t)
+        if t.dtype != torch.uint8:
+            raise TypeError("%s must be uint8" % name)
+    M = Aq.shape[0]
+    K = Aq.shape[1] * (2 if fmt == TG_MX_E2M1 else 1)
+    N = Wq.shape[0]
+    if (tuple(As.shape) != (M, K // 32) or tuple(Wq.shape) != (N, K // 2)
+            or tuple(Ws.shape) != (N, K // 32) or K % 32):
+        raise ValueError("expected As [M, K/32], Wq [N, K/2], Ws [N, K/32] with K % 32 == 0")
+    if C is not None:
+        _require_gpu_tensor("C", C)
+        if tuple(C.shape) != (M, N) or C.dtype != torch.bfloat16:
+            raise ValueError("C must be bfloat16 [M, N]")
+    return M, N, K
+
+
+def gemm_mx(fmt: int, Aq, As, Wq, Ws, C=None, epilogue=None, stream=None, config=None):
+    """C = epilogue(a @ w^T) with both operands in MX blocks: activation codes Aq
+    (E2M1 [M, K/2] or E4M3 [M, K]) with E8M0 scales As [M, K/32], E2M1 weights
+    Wq [N, K/2] with E8M0 scales Ws [N, K/32]; bf16 output.  `config` forces a
+    compiled configuration by index."""
+    import torch
+
+    M, N, K = _mx_args(fmt, Aq, As, Wq, Ws, C)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=Aq.device)
+    args = (M, N, K, fmt, Aq.data_ptr(), As.data_ptr(), Wq.data_ptr(), Ws.data_ptr(),
+            C.data_ptr(), _epi_code(epilogue), _stream_ptr(Aq.device, stream))
+    lib = load_library()
+    _check(lib.tg_gemm_mx(*args) if config is None else lib.tg_gemm_mx_config(config, *args))
     return C
 
 

@@ -42,6 +42,8 @@ ConfigList list_for(int op, int dtype)
             return tg::configs_gemm_bf16();
     } else if (op == TG_OP_DEQUANT_W4) {
         return tg::configs_dequant_w4();
+    } else if (op == TG_OP_MX) {
+        return tg::configs_mx();  // both activation formats
     }
     return ConfigList{nullptr, 0};
 }
@@ -49,11 +51,14 @@ ConfigList list_for(int op, int dtype)
 void config_name(const Config& c, char* buf, size_t len)
 {
     static const char* dn[] = {"f32", "f16", "bf16"};
+    static const char* mxn[] = {"e2m1", "e4m3"};
     static const char* lay[] = {"", "_nt", "_tn", "_tt"};  // A^T-stored / B^T-stored
-    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s", c.op == 0 ? "gemm" : "w4",
-             dn[c.dtype], c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
+    const bool mx = c.op == TG_OP_MX;
+    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s",
+             c.op == 0 ? "gemm" : (mx ? "mx" : "w4"), mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
+             c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
-             lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)], c.wide ? "" : "_narrow");
+             mx ? "" : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)], c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -81,6 +86,10 @@ const Pref kPrefs[] = {
             nullptr}},
     {1, 2, {"w4_bf16_64x128x128_w2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
             "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
+    {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g4_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr,
+            nullptr}},
+    {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g4_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
+            nullptr}},
 };
 
 const Config* find_by_name(int op, int dtype, const char* name);
@@ -101,7 +110,7 @@ struct Call {
     int op, dtype;
     int64_t M, N, K;
     bool wide;    // 16-byte aligned operands whose rows are whole 16-byte chunks
-    bool ws4;     // dequant scale bytes start 4-byte aligned
+    bool ws4;     // dequant / MX scale bytes start 4-byte aligned
     bool ta, tb;  // A stored [K][M], B stored [N][K]
 };
 
@@ -110,6 +119,9 @@ bool usable(const Config& c, const Call& q)
 {
     if (c.wide && !q.wide)
         return false;
+    if (c.op == TG_OP_MX)
+        // activation format compiled in; whole 128-k strips; dword scale copies
+        return c.dtype == q.dtype && q.wide && q.ws4 && q.K % c.bk == 0;
     if (c.ta != q.ta || c.tb != q.tb)
         return false;  // operand layouts are compiled in
     if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
@@ -328,6 +340,49 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     return launch(*c, p, (hipStream_t)stream);
 }
 
+tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
+                  int a_fmt, const uint8_t* Aq, const uint8_t* As, const uint8_t* Wq,
+                  const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream)
+{
+    if (a_fmt != TG_MX_E2M1 && a_fmt != TG_MX_E4M3)
+        return TG_ERR_BAD_DTYPE;
+    if (epi != TG_EPI_NONE && epi != TG_EPI_RELU)
+        return TG_ERR_BAD_EPILOGUE;
+    tg_status s = check_shape(M, N, K, 1);
+    if (s != TG_OK)
+        return s;
+    if (K % 128 != 0)
+        return TG_ERR_BAD_SHAPE;
+    if (forced_index >= 0 && !forced)
+        return TG_ERR_NO_CONFIG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (!C || (K > 0 && (!Aq || !As || !Wq || !Ws)))
+        return TG_ERR_NULL_POINTER;
+    const size_t cbytes = (size_t)(M * N * 2);
+    const size_t abytes = (size_t)(a_fmt == TG_MX_E4M3 ? M * K : M * K / 2);
+    if (overlaps(C, cbytes, Aq, abytes) || overlaps(C, cbytes, As, (size_t)(M * K / 32)) ||
+        overlaps(C, cbytes, Wq, (size_t)(N * K / 2)) || overlaps(C, cbytes, Ws, (size_t)(N * K / 32)))
+        return TG_ERR_ALIAS;
+    Call q{TG_OP_MX, a_fmt, M, N, K, aligned16(Aq) && aligned16(Wq),
+           (((uintptr_t)As | (uintptr_t)Ws) & 3u) == 0, false, false};
+    const Config* c = forced ? forced : select_config(q);
+    if (!c || !usable(*c, q))
+        return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
+    tg::GemmParams p{};
+    p.A = Aq;
+    p.As = As;
+    p.B = Wq;
+    p.Bs = Ws;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.relu = epi == TG_EPI_RELU;
+    p.c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
+    return launch(*c, p, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +405,13 @@ tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, con
     return w4_impl(nullptr, -1, M, N, K, A, Wq, Ws, C, epi, stream);
 }
 
+tg_status tg_gemm_mx(int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt, const uint8_t* Aq,
+                     const uint8_t* As, const uint8_t* Wq, const uint8_t* Ws, void* C,
+                     tg_epilogue epi, tg_stream_t stream)
+{
+    return mx_impl(nullptr, -1, M, N, K, a_fmt, Aq, As, Wq, Ws, C, epi, stream);
+}
+
 const char* tg_status_str(tg_status s)
 {
     switch (s) {
@@ -358,9 +420,11 @@ const char* tg_status_str(tg_status s)
     case TG_ERR_NULL_POINTER:
         return "TG_ERR_NULL_POINTER: a required pointer is NULL";
     case TG_ERR_BAD_SHAPE:
-        return "TG_ERR_BAD_SHAPE: negative or too large size, or dequant K not a multiple of 32";
+        return "TG_ERR_BAD_SHAPE: negative or too large size, or K not a multiple of 32 (dequant) "
+               "or 128 (MX)";
     case TG_ERR_BAD_DTYPE:
-        return "TG_ERR_BAD_DTYPE: dtype must be TG_F32, TG_F16 or TG_BF16";
+        return "TG_ERR_BAD_DTYPE: dtype must be TG_F32, TG_F16 or TG_BF16 (MX: TG_MX_E2M1 or "
+               "TG_MX_E4M3)";
     case TG_ERR_BAD_EPILOGUE:
         return "TG_ERR_BAD_EPILOGUE: epilogue must be TG_EPI_NONE or TG_EPI_RELU";
     case TG_ERR_ALIAS:
@@ -380,23 +444,25 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
 {
     if (!buf || len == 0)
         return TG_ERR_NULL_POINTER;
-    if (op != TG_OP_GEMM && op != TG_OP_DEQUANT_W4)
+    if (op != TG_OP_GEMM && op != TG_OP_DEQUANT_W4 && op != TG_OP_MX)
         return TG_ERR_NO_CONFIG;
     if (op == TG_OP_GEMM && dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
         return TG_ERR_BAD_DTYPE;
+    if (op == TG_OP_MX && (int)dtype != TG_MX_E2M1 && (int)dtype != TG_MX_E4M3)
+        return TG_ERR_BAD_DTYPE;  // the activation format
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1) ||
-        (op == TG_OP_DEQUANT_W4 && (trans_a || trans_b)))
+        (op != TG_OP_GEMM && (trans_a || trans_b)))
         return TG_ERR_BAD_LAYOUT;
     const int dt = op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype;
-    tg_status s = check_shape(M, N, K, esize_of(dt));
+    tg_status s = check_shape(M, N, K, op == TG_OP_MX ? 1 : esize_of(dt));
     if (s != TG_OK)
         return s;
-    if (op == TG_OP_DEQUANT_W4 && K % 32 != 0)
+    if ((op == TG_OP_DEQUANT_W4 && K % 32 != 0) || (op == TG_OP_MX && K % 128 != 0))
         return TG_ERR_BAD_SHAPE;
     // assume aligned operands (what torch allocations give)
     const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
     Call q{op, dt, M, N, K, false, true, trans_a != 0, trans_b != 0};
-    q.wide = op == TG_OP_DEQUANT_W4 || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0);
+    q.wide = op != TG_OP_GEMM || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0);
     const Config* c = select_config(q);
     if (!c)
         return TG_ERR_NO_CONFIG;
@@ -459,6 +525,15 @@ tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, 
     ConfigList L = list_for(TG_OP_DEQUANT_W4, TG_BF16);
     const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
     return w4_impl(c, index < 0 ? 0 : index, M, N, K, A, Wq, Ws, C, epi, stream);
+}
+
+tg_status tg_gemm_mx_config(int index, int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt,
+                            const uint8_t* Aq, const uint8_t* As, const uint8_t* Wq,
+                            const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream)
+{
+    ConfigList L = list_for(TG_OP_MX, 0);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    return mx_impl(c, index < 0 ? 0 : index, M, N, K, a_fmt, Aq, As, Wq, Ws, C, epi, stream);
 }
 
 tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,

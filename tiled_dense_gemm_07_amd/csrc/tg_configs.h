@@ -7,8 +7,8 @@
 namespace tg {
 
 struct Config {
-    int op;     // 0 = GEMM, 1 = 4-bit dequant GEMM
-    int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
+    int op;     // 0 = GEMM, 1 = 4-bit dequant GEMM, 2 = MX-format GEMM
+    int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (MX: activation format, 0 = E2M1, 1 = E4M3)
     int bm, bn, bk;
     int wgm, wgn;  // waves along M and N (64 threads each)
     int stages;    // LDS ring depth
@@ -29,6 +29,7 @@ ConfigList configs_gemm_f32();
 ConfigList configs_gemm_f16();
 ConfigList configs_gemm_bf16();
 ConfigList configs_dequant_w4();
+ConfigList configs_mx();
 
 }  // namespace tg
 

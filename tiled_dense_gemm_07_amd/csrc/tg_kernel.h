@@ -61,9 +61,10 @@ struct DtTraits<DT_BF16> {
 };
 
 struct GemmParams {
-    const void* A;   // [M][K] row-major
-    const void* B;   // B_KN: [K][N] row-major; B_W4: packed codes [N][K/2]
-    const void* Bs;  // B_W4: scale bytes [N][K/32]; unused otherwise
+    const void* A;   // [M][K] row-major (MX: element codes, [M][K] or [M][K/2] bytes)
+    const void* B;   // B_KN: [K][N] row-major; B_W4 and MX: packed codes [N][K/2]
+    const void* Bs;  // B_W4 and MX: scale bytes [N][K/32]; unused otherwise
+    const void* As;  // MX: scale bytes of A [M][K/32]; unused otherwise
     void* C;         // [M][N] row-major
     int M, N, K;
     int tiles_m, tiles_n;

@@ -1,0 +1,472 @@
+// MX-format GEMM: both operands in OCP microscaling blocks, multiplied by the
+// gfx950 scaled matrix instruction with no dequantisation step.
+//
+// The pages' weight-only low-bit GEMM ("WFP4" GEMM in "TileLang架构深度剖析",
+// the performance section; "Dequant GEMM" in "使用 Tilelang DSL 开发
+// GPU/CPU/加速器高性能内核") with the activations also in a block format:
+//   C[m][n] = sum_k a(m, k) w(n, k),
+//   a(m, k) = elemA(m, k) * 2^(SA[m][k/32] - 127)   (E2M1 or E4M3 elements),
+//   w(n, k) = e2m1(n, k)  * 2^(SW[n][k/32] - 127),
+// fp32 accumulation, one rounding to bf16.  v_mfma_scale_f32_32x32x64_f8f6f4
+// multiplies 64 k of a 32x32 block per instruction and applies both scales
+// itself.  Its lane layout (measured on the GPU with an in-bounds probe):
+//   * lane l supplies row (or column) l % 32 and the scale byte of k-block
+//     l / 32 of the instruction's 64 k (byte 0 of the scale operand, or the
+//     byte op_sel names);
+//   * E2M1: lane l's 32 codes are k = 32 (l / 32) + 0 .. 31, low nibble first;
+//   * E4M3: lane l's bytes 0..15 are k = 16 (l / 32) + 0 .. 15 and bytes
+//     16..31 are k = 32 + 16 (l / 32) + 0 .. 15.
+// MI355X mapping (as the other LDS-DMA kernels here):
+//  * BM x BN x 128 strips, four waves in a 2 x 2 grid, NS-stage LDS ring filled
+//    by LDS-DMA copies: the codes as stored (E2M1: 64 bytes per row per strip,
+//    E4M3: 128 bytes) and the four scale bytes of each row (dword copies);
+//  * per 64-k step a wave reads, per 32-row block, one ds_read_b128 of E2M1
+//    codes or two of E4M3 codes (chunk swizzles keep them conflict-free) and
+//    issues one scaled MFMA per block pair;
+//  * a row's four scale bytes are read once per strip and shifted per lane
+//    half and k-step, so byte 0 of the scale operand is always the block the
+//    lane supplies;
+//  * one barrier per strip after its first MFMA publishes strip t + 1 and frees
+//    strip t - 1; copies of strip t + NS - 1 are staggered across waves and
+//    slots.  K must be a multiple of 128 and the scale rows 4-byte aligned;
+//    rows past M or N and strips padded past K copy zeros.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tg_kernel.h"
+#include "tg_kernel_dma.h"
+#include "tg_kernel_dma_w4.h"
+
+namespace tg {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+enum MxFmt { MX_E4M3 = 0, MX_E2M1 = 4 };  // the instruction's format codes
+
+// 128-byte rows: chunk c of row r goes to position c ^ swz8(r).  Only the
+// low five bits of r enter, so rows 32 apart (the 32-row blocks of a wave
+// tile) share a swizzle and one lane offset serves every block; any 16
+// consecutive rows of a 32-row block then read 16 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
+template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+struct DmaMx {
+    static constexpr int BK = 128;
+    static constexpr int NW = WGM * WGN;
+    static constexpr int WTM = BM / WGM;
+    static constexpr int WTN = BN / WGN;
+    static constexpr int FM = WTM / 32;
+    static constexpr int FN = WTN / 32;
+    static constexpr bool A8 = AFMT == MX_E4M3;
+    static constexpr int A_ROWB = A8 ? 128 : 64;  // code bytes per row per strip
+    static constexpr int A_STAGE = BM * A_ROWB;
+    static constexpr int W_STAGE = BN * 64;
+    static constexpr int SA_STAGE = BM * 4;
+    static constexpr int SW_STAGE = BN * 4;
+    static constexpr int W_REGION = NS * A_STAGE;
+    static constexpr int SA_REGION = W_REGION + NS * W_STAGE;
+    static constexpr int SW_REGION = SA_REGION + NS * SA_STAGE;
+    static constexpr int LDS_BYTES = SW_REGION + NS * SW_STAGE;
+    static constexpr int JA = A_STAGE / 1024 / NW;
+    static constexpr int JW = W_STAGE / 1024 / NW;
+    static constexpr int NSA = SA_STAGE / 256;  // dword scale copies of A per strip
+    static constexpr int NSW = SW_STAGE / 256;
+    static constexpr int NM = FM * FN;          // MFMAs per 64-k step
+    static constexpr int SLOTS = 2 * NM;        // MFMAs per strip
+
+    static_assert(NW == 4, "four waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
+    static_assert(JA >= 1 && JW >= 1 && A_STAGE % (1024 * NW) == 0 && W_STAGE % (1024 * NW) == 0,
+                  "strips split into whole 1 KiB copies per wave");
+    static_assert(NSA >= 1 && NSA <= NW && NSW >= 1 && NSW <= NW, "scale copies: one per wave at most");
+    static_assert(NS == 4, "four stages (scale registers alternate per strip)");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+    template <int W>
+    struct Copies {
+        static constexpr int N = JA + JW + (W < NSA ? 1 : 0) + (W < NSW ? 1 : 0);
+        static constexpr int AHEAD = (NS - 3) * N;
+    };
+    static constexpr int NCMAX = JA + JW + 2;
+
+    struct Lane {
+        u32 a_off[JA];
+        u32 w_off[JW];
+        u32 sa_off, sw_off;
+        u32 a_rd[2][A8 ? 2 : 1];  // [k-step][part]: code chunks of this lane (stage 0, fm 0)
+        u32 w_rd[2];              // [k-step] (stage 0, fn 0)
+        u32 sa_rd, sw_rd;         // this lane's row of scale bytes (stage 0, block 0)
+        int h8;                   // 8 * lane half: the lane's scale bytes start at block h
+    };
+
+    struct Frag {  // one 64-k step
+        u32x4 a[FM][A8 ? 2 : 1];
+        u32x4 w[FN];
+    };
+    struct Scales {  // one strip: [k-step][block], byte 0 = this lane's block
+        u32 a[2][FM];
+        u32 w[2][FN];
+    };
+
+    static __device__ __forceinline__ void setup(Lane& L, const GemmParams& p, int m0, int n0,
+                                                 int w, int lane, int wm, int wn)
+    {
+        const int K = p.K;
+        const int arow_b = A8 ? K : K / 2;  // code bytes per stored A row
+#pragma unroll
+        for (int j = 0; j < JA; ++j) {
+            if constexpr (A8) {
+                const int row = (w * JA + j) * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ swz8(row);
+                L.a_off[j] = (m0 + row < p.M) ? (u32)(row * arow_b + c * 16) : kOob;
+            } else {
+                const int row = (w * JA + j) * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ swz_a(row);
+                L.a_off[j] = (m0 + row < p.M) ? (u32)(row * arow_b + c * 16) : kOob;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < JW; ++j) {
+            const int row = (w * JW + j) * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ swz_a(row);
+            L.w_off[j] = (n0 + row < p.N) ? (u32)(row * (K / 2) + c * 16) : kOob;
+        }
+        {
+            const int row = w * 64 + lane;
+            L.sa_off = (w < NSA && m0 + row < p.M) ? (u32)(row * (K / 32)) : kOob;
+            L.sw_off = (w < NSW && n0 + row < p.N) ? (u32)(row * (K / 32)) : kOob;
+        }
+        const int h = lane >> 5;
+        const int ar = wm * WTM + (lane & 31);
+        const int nr = wn * WTN + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if constexpr (A8) {
+                // bytes 0..15: k = 64 q + 16 h; bytes 16..31: k = 64 q + 32 + 16 h
+                L.a_rd[q][0] = ar * A_ROWB + (((4 * q + h) ^ swz8(ar)) << 4);
+                L.a_rd[q][1] = ar * A_ROWB + (((4 * q + 2 + h) ^ swz8(ar)) << 4);
+            } else {
+                // 32 codes: k = 64 q + 32 h
+                L.a_rd[q][0] = ar * A_ROWB + (((2 * q + h) ^ swz_a(ar)) << 4);
+            }
+            L.w_rd[q] = W_REGION + nr * 64 + (((2 * q + h) ^ swz_a(nr)) << 4);
+        }
+        L.sa_rd = SA_REGION + ar * 4;
+        L.sw_rd = SW_REGION + nr * 4;
+        L.h8 = 8 * h;
+    }
+
+    // One buffer resource per array for the workgroup's whole row band (all
+    // of K); a strip adds its byte offset to the lane offsets.  Offsets of
+    // rows past M or N are kOob and stay out of range after the addition; so
+    // do the offsets of strips past K.  (Per-strip resources would cost
+    // scalar registers this kernel does not have to spare.)
+    struct Res {
+        __amdgpu_buffer_rsrc_t a, w, sa, sw;
+    };
+    struct StripOff {
+        u32 a, w, s;  // byte offsets of strip t in a row of A codes, W codes, scales
+        bool valid;
+    };
+
+    // Resource of `rows` rows of `row_bytes` bytes from base + row0 * row_bytes.
+    // The copies take it as a scalar operand; the 64-bit range arithmetic may
+    // be done on the vector ALU, so its parts are read back as wave-uniform
+    // scalars explicitly.
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t band(const void* base, int row0,
+                                                                  int rows, int row_bytes)
+    {
+        const uint64_t a = (uint64_t)((const char*)base + (int64_t)row0 * row_bytes);
+        const u32 lo = __builtin_amdgcn_readfirstlane((u32)a);
+        const u32 hi = __builtin_amdgcn_readfirstlane((u32)(a >> 32));
+        const u32 n = __builtin_amdgcn_readfirstlane(clamp_bytes((int64_t)rows * row_bytes));
+        return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), n);
+    }
+
+    static __device__ __forceinline__ Res band_res(const GemmParams& p, int m0, int n0)
+    {
+        const int K = p.K;
+        Res r;
+        r.a = band(p.A, m0, p.M - m0, A8 ? K : K / 2);
+        r.w = band(p.B, n0, p.N - n0, K / 2);
+        r.sa = band(p.As, m0, p.M - m0, K / 32);
+        r.sw = band(p.Bs, n0, p.N - n0, K / 32);
+        return r;
+    }
+
+    static __device__ __forceinline__ StripOff strip_off(const GemmParams& p, int strip)
+    {
+        const int k0 = strip * BK;
+        StripOff o;
+        o.valid = k0 < p.K;
+        o.a = (u32)(A8 ? k0 : k0 / 2);
+        o.w = (u32)(k0 / 2);
+        o.s = (u32)(k0 / 32);
+        return o;
+    }
+
+    // Copy d of wave W for strip offsets o into stage ST.
+    template <int ST, int W>
+    static __device__ __forceinline__ void issue_copy(const Lane& L, const Res& r,
+                                                      const StripOff& o, int d, u32 smem0)
+    {
+        if (d < JA)
+            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, o.valid ? L.a_off[d] + o.a : kOob,
+                  r.a);
+        else if (d < JA + JW)
+            dma16(smem0 + W_REGION + ST * W_STAGE + (W * JW + d - JA) * 1024,
+                  o.valid ? L.w_off[d - JA] + o.w : kOob, r.w);
+        else if (W < NSA && d == JA + JW)
+            dma4(smem0 + SA_REGION + ST * SA_STAGE + W * 256, o.valid ? L.sa_off + o.s : kOob,
+                 r.sa);
+        else
+            dma4(smem0 + SW_REGION + ST * SW_STAGE + W * 256, o.valid ? L.sw_off + o.s : kOob,
+                 r.sw);
+    }
+
+    template <int ST, int W>
+    static __device__ __forceinline__ void issue_copies(const Lane& L, const Res& r,
+                                                        const GemmParams& p, int strip, u32 smem0)
+    {
+        const StripOff o = strip_off(p, strip);
+#pragma unroll
+        for (int d = 0; d < Copies<W>::N; ++d)
+            issue_copy<ST, W>(L, r, o, d, smem0);
+    }
+
+    // LDS reads of k-step Q of stage ST: A blocks, then W blocks.
+    static constexpr int NRD_A = FM * (A8 ? 2 : 1);
+    static constexpr int NRD = NRD_A + FN;
+
+    template <int ST, int Q>
+    static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i)
+    {
+        if (i < NRD_A) {
+            const int fm = A8 ? (i >> 1) : i, part = A8 ? (i & 1) : 0;
+            F.a[fm][part] = *(const lds_u32x4*)(sm + L.a_rd[Q][part] + ST * A_STAGE +
+                                                fm * 32 * A_ROWB);
+        } else {
+            const int fn = i - NRD_A;
+            F.w[fn] = *(const lds_u32x4*)(sm + L.w_rd[Q] + ST * W_STAGE + fn * 32 * 64);
+        }
+    }
+
+    template <int ST>
+    static __device__ __forceinline__ void read_scales(Scales& S, const Lane& L, lds_char* sm)
+    {
+        typedef __attribute__((address_space(3))) u32 lds_u32;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const u32 v = *(const lds_u32*)(sm + L.sa_rd + ST * SA_STAGE + fm * 32 * 4);
+            S.a[0][fm] = v >> L.h8;
+            S.a[1][fm] = v >> (L.h8 + 16);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const u32 v = *(const lds_u32*)(sm + L.sw_rd + ST * SW_STAGE + fn * 32 * 4);
+            S.w[0][fn] = v >> L.h8;
+            S.w[1][fn] = v >> (L.h8 + 16);
+        }
+    }
+
+    template <int Q>
+    static __device__ __forceinline__ void mfma_one(f32x16 (&acc)[FM][FN], const Frag& F,
+                                                    const Scales& S, int i)
+    {
+        const int fm = i / FN, fn = i % FN;
+        const u32x4 wv = F.w[fn];
+        const i32x8 wop = {(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3], 0, 0, 0, 0};
+        i32x8 aop;
+        if constexpr (A8) {
+            const u32x4 lo = F.a[fm][0], hi = F.a[fm][A8 ? 1 : 0];  // A8: two parts
+            aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else {
+            const u32x4 lo = F.a[fm][0];
+            aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+        }
+        // first operand: weights (rows n of the result block), second:
+        // activations (columns m); scale byte 0 of each
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            wop, aop, acc[fm][fn], MX_E2M1, AFMT, 0, (int)S.w[Q][fn], 0, (int)S.a[Q][fm]);
+    }
+
+    // One strip (stage ST) of wave W: k-step 0 with fragments F0, then k-step 1
+    // with F1.  Slot 0 waits for strip t + 1's copies and barriers; k-step 0's
+    // slots read k-step 1 into F1; k-step 1's slots read strip t + 1's scales
+    // (into SC[(ST + 1) & 1]) and k-step 0 (into F0); copies of strip
+    // t + NS - 1 are staggered over the slots.
+    template <int ST, int W>
+    static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
+                                                 Scales (&SC)[2], const Lane& L, const Res& res,
+                                                 lds_char* sm, const GemmParams& p, int t,
+                                                 u32 smem0)
+    {
+        constexpr int NXT = (ST + 1) % NS;
+        constexpr int CPY = (ST + NS - 1) % NS;
+        constexpr int CUR = ST & 1;
+        constexpr int STEPS = NM > NRD ? NM : NRD;
+        StripOff o;
+#pragma unroll
+        for (int slot = 0; slot < 2 * STEPS; ++slot) {
+            const int i = slot % STEPS;
+            if (slot < STEPS) {
+                if (i < NM) {
+                    mfma_one<0>(acc, F0, SC[CUR], i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (i < NRD) {
+                    read_one<ST, 1>(F1, L, sm, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                if (i < NM) {
+                    mfma_one<1>(acc, F1, SC[CUR], i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (i == 0) {
+                    read_scales<NXT>(SC[CUR ^ 1], L, sm);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (i < NRD) {
+                    read_one<NXT, 0>(F0, L, sm, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (slot == 0) {
+                wait_copies_barrier<Copies<W>::AHEAD>();
+                __builtin_amdgcn_sched_barrier(0);
+                o = strip_off(p, t + NS - 1);
+            }
+#pragma unroll
+            for (int d = 0; d < Copies<W>::N; ++d) {
+                if (((d * NW + W) * 2 * STEPS) / (NCMAX * NW) == slot) {
+                    issue_copy<CPY, W>(L, res, o, d, smem0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+
+    template <int W>
+    static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], const Lane& L,
+                                                     lds_char* sm, const GemmParams& p, int m0,
+                                                     int n0, int KT, u32 smem0)
+    {
+        const Res res = band_res(p, m0, n0);
+        issue_copies<0, W>(L, res, p, 0, smem0);
+        issue_copies<1, W>(L, res, p, 1, smem0);
+        issue_copies<2, W>(L, res, p, 2, smem0);
+        wait_copies_barrier<(NS - 2) * Copies<W>::N>();
+        Frag F0, F1;
+        Scales SC[2];
+        read_scales<0>(SC[0], L, sm);
+#pragma unroll
+        for (int i = 0; i < NRD; ++i)
+            read_one<0, 0>(F0, L, sm, i);
+        // The strip count is rounded up to a multiple of NS: strips at or past
+        // KT copy only zeros, which add exactly nothing.
+        for (int t = 0; t < KT; t += NS) {
+            strip<0, W>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+            strip<1, W>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+            strip<2, W>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+            strip<3, W>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    static __device__ __forceinline__ void run(const GemmParams& p)
+    {
+        __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+        lds_char* sm = (lds_char*)smem;
+        const u32 smem0 = lds_offset(smem);
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = w / WGN;
+        const int wn = w % WGN;
+        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const int m0 = tc.m * BM;
+        const int n0 = tc.n * BN;
+        const int KT = p.K / BK;
+
+        Lane L;
+        setup(L, p, m0, n0, w, lane, wm, wn);
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[fm][fn][r] = 0.0f;
+        switch (w) {
+        case 0:
+            main_loop<0>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 1:
+            main_loop<1>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 2:
+            main_loop<2>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        default:
+            main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        }
+        // epilogue: m = lane % 32, four consecutive n per accumulator quad
+        const int lr = lane & 31;
+        const int g = lane >> 5;
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + wm * WTM + fm * 32 + lr;
+            if (m >= p.M)
+                continue;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * WTN + fn * 32 + 8 * q + 4 * g;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = acc[fm][fn][4 * q + e];
+                        v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
+                    }
+                    const int64_t idx = (int64_t)m * p.N + n;
+                    if (p.c_vec && n + 3 < p.N) {
+                        *(u32x2*)(C + idx) =
+                            u32x2{pack2(v[0], v[1], DT_BF16), pack2(v[2], v[3], DT_BF16)};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N)
+                                C[idx + e] = cvt1(v[e], DT_BF16);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Waves per SIMD: two only for the small E2M1 tile (its fragments fit in 128
+// registers), else one.
+template <int AFMT, int BM, int BN>
+struct MxOcc {
+    static constexpr int value = (AFMT == MX_E2M1 && BM * BN <= 128 * 128) ? 2 : 1;
+};
+
+template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
+                          amdgpu_waves_per_eu(MxOcc<AFMT, BM, BN>::value,
+                                              MxOcc<AFMT, BM, BN>::value))) void
+gemm_mx_kernel(GemmParams p)
+{
+    DmaMx<AFMT, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+}
+
+}  // namespace tg

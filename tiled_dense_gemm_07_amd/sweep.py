@@ -57,6 +57,16 @@ def sweep_shape(op: int, dtype: int, M: int, N: int, K: int, relu: bool, done: s
         A = torch.randn((M, K), generator=g, device=dev).to(tdt[dtype])
         B = torch.randn((K, N), generator=g, device=dev).to(tdt[dtype])
         C = torch.empty((M, N), dtype=tdt[dtype], device=dev)
+    elif op == binding.TG_OP_MX:
+        # dtype carries the activation format; codes uniform, scales 2^-4 .. 2^0
+        kq = K // 2 if dtype == binding.TG_MX_E2M1 else K
+        A = torch.randint(0, 256, (M, kq), generator=g, device=dev, dtype=torch.uint8)
+        if dtype == binding.TG_MX_E4M3:
+            A[(A & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        As = torch.randint(123, 128, (M, K // 32), generator=g, device=dev, dtype=torch.uint8)
+        Wq = torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.uint8)
+        Ws = torch.randint(123, 128, (N, K // 32), generator=g, device=dev, dtype=torch.uint8)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     else:
         A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         Wq = torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.uint8)
@@ -67,8 +77,13 @@ def sweep_shape(op: int, dtype: int, M: int, N: int, K: int, relu: bool, done: s
     for idx, name in enumerate(names):
         if name.endswith("_narrow"):
             continue  # element-load variants serve unaligned operands only
+        if op == binding.TG_OP_MX and not name.startswith("mx_" + synth.MX_NAMES[dtype]):
+            continue  # the other activation format
         if op == binding.TG_OP_GEMM:
             fn = lambda: binding.gemm_with_config(idx, A, B, C=C, epilogue=epi, stream=stream)
+        elif op == binding.TG_OP_MX:
+            fn = lambda: binding.gemm_mx(dtype, A, As, Wq, Ws, C=C, epilogue=epi, stream=stream,
+                                         config=idx)
         else:
             fn = lambda: binding.dequant_gemm_w4_with_config(idx, A, Wq, Ws, C=C, epilogue=epi,
                                                              stream=stream)
@@ -78,7 +93,7 @@ def sweep_shape(op: int, dtype: int, M: int, N: int, K: int, relu: bool, done: s
         log.write(json.dumps(rec) + "\n")
         log.flush()
         print("sweep %s %dx%dx%d %-40s %8.4f ms %8.1f TFLOP/s" % (
-            "gemm" if op == 0 else "w4", M, N, K, name, ms, rec["tflops"]), flush=True)
+            ("gemm", "w4", "mx")[op], M, N, K, name, ms, rec["tflops"]), flush=True)
     del A, C
     torch.cuda.empty_cache()
 
@@ -124,7 +139,8 @@ def main(argv=None):
     shapes = []
     if args.shapes == "workloads":
         for w in synth.WORKLOADS.values():
-            shapes.append((0 if w.op == "gemm" else 1, w.dtype, w.M, w.N, w.K, w.relu))
+            shapes.append(({"gemm": 0, "dequant_w4": 1, "mx": 2}[w.op], w.dtype, w.M, w.N, w.K,
+                           w.relu))
     elif args.shapes:
         for item in args.shapes.split(","):
             parts = item.split(":")

@@ -13,9 +13,12 @@ page), so every workload here is synthetic:
   rounded to float32, then rounded (nearest-even) to the operand type;
 * integer inputs: uniform on {-4, ..., 4}, exact in every operand type;
 * 4-bit weights: uniform bytes (so both nibbles are uniform on 0..15),
-  E8M0 scale bytes 127 + uniform{-4..0}, i.e. scales 2^-4 .. 2^0.
+  E8M0 scale bytes 127 + uniform{-4..0}, i.e. scales 2^-4 .. 2^0;
+* MX-format activations: E2M1 as the weights; E4M3 codes uniform over the 254
+  non-NaN bytes; E8M0 scale bytes as for the weights.
 
-Seeds: ``20260000 + 100 * workload_index + {0: A, 1: B, 2: codes, 3: scales}``,
+Seeds: ``20260000 + 100 * workload_index + {0: A, 1: B, 2: codes, 3: scales,
+4: activation scales}``,
 plus 50 for the integer-valued run.
 """
 
@@ -70,14 +73,44 @@ def w4_scales(N: int, K: int, seed: int, emin: int = -4, emax: int = 0) -> np.nd
     return (127 + e).astype(np.uint8)
 
 
+def e4m3_codes(M: int, K: int, seed: int) -> np.ndarray:
+    """E4M3 codes [M, K], uniform over the bytes that are not NaN (0x7F, 0xFF)."""
+    v = rng(seed).integers(0, 254, size=(M, K))
+    v = v + (v >= 0x7F)  # skip 0x7F; 253 -> 254; 0xFF is never drawn
+    return v.astype(np.uint8)
+
+
+def e4m3_codes_range(M: int, K: int, seed: int, efield_lo: int, efield_hi: int) -> np.ndarray:
+    """E4M3 codes [M, K] with uniform sign, exponent field uniform in
+    [efield_lo, efield_hi] and uniform 3-bit mantissa (never NaN for
+    efield_hi <= 14)."""
+    r = rng(seed)
+    sign = r.integers(0, 2, size=(M, K))
+    ef = r.integers(efield_lo, efield_hi + 1, size=(M, K))
+    mant = r.integers(0, 8, size=(M, K))
+    return ((sign << 7) | (ef << 3) | mant).astype(np.uint8)
+
+
+MX_E2M1, MX_E4M3 = 0, 1
+MX_NAMES = {MX_E2M1: "e2m1", MX_E4M3: "e4m3"}
+
+
+def mx_inputs(fmt: int, M: int, N: int, K: int, seed_a: int, seed_as: int, seed_codes: int,
+              seed_scales: int):
+    """Activation codes (E2M1 [M, K/2] or E4M3 [M, K]), their scale bytes [M, K/32],
+    packed weight codes [N, K/2] and weight scale bytes [N, K/32]."""
+    Aq = w4_codes(M, K, seed_a) if fmt == MX_E2M1 else e4m3_codes(M, K, seed_a)
+    return Aq, w4_scales(M, K, seed_as), w4_codes(N, K, seed_codes), w4_scales(N, K, seed_scales)
+
+
 @dataclass(frozen=True)
 class Workload:
     """One of the workload shapes; `index` keys the seeds."""
 
     name: str
     index: int
-    op: str  # "gemm" or "dequant_w4"
-    dtype: int
+    op: str  # "gemm", "dequant_w4" or "mx"
+    dtype: int  # operand type; for "mx" the activation format (MX_E2M1 / MX_E4M3)
     M: int
     N: int
     K: int
@@ -92,6 +125,10 @@ class Workload:
         if self.op == "gemm":
             es = 4 if self.dtype == F32 else 2
             return es * (self.M * self.K + self.K * self.N + self.M * self.N)
+        if self.op == "mx":
+            a = self.M * self.K // 2 if self.dtype == MX_E2M1 else self.M * self.K
+            return (a + self.M * self.K // 32 + self.N * self.K // 2 + self.N * self.K // 32
+                    + 2 * self.M * self.N)
         return 2 * self.M * self.K + self.N * self.K // 2 + self.N * self.K // 32 + 2 * self.M * self.N
 
 
@@ -107,12 +144,16 @@ WORKLOADS = {
     # memory-bound probes of the same dequant entry (decode-like M)
     "w4_1x8192x8192": Workload("w4_1x8192x8192", 6, "dequant_w4", BF16, 1, 8192, 8192, False),
     "w4_16x8192x8192": Workload("w4_16x8192x8192", 7, "dequant_w4", BF16, 16, 8192, 8192, False),
+    # the same weight format with block-format activations on the scaled MFMA
+    "mx_e2m1_8192": Workload("mx_e2m1_8192", 8, "mx", MX_E2M1, 8192, 8192, 8192, False),
+    "mx_e4m3_8192": Workload("mx_e4m3_8192", 9, "mx", MX_E4M3, 8192, 8192, 8192, False),
 }
 
 
 def seeds(w: Workload, integer: bool = False) -> dict:
     base = 20260000 + 100 * w.index + (50 if integer else 0)
-    return {"A": base + 0, "B": base + 1, "codes": base + 2, "scales": base + 3}
+    return {"A": base + 0, "B": base + 1, "codes": base + 2, "scales": base + 3,
+            "a_scales": base + 4}
 
 
 def gemm_inputs(M: int, N: int, K: int, dtype: int, seed_a: int, seed_b: int,
@@ -137,5 +178,9 @@ def make_inputs(w: Workload, integer: bool = False) -> dict:
     if w.op == "gemm":
         A, B = gemm_inputs(w.M, w.N, w.K, w.dtype, s["A"], s["B"], integer)
         return {"A": A, "B": B, "seeds": s}
+    if w.op == "mx":
+        Aq, As, Wq, Ws = mx_inputs(w.dtype, w.M, w.N, w.K, s["A"], s["a_scales"], s["codes"],
+                                   s["scales"])
+        return {"Aq": Aq, "As": As, "Wq": Wq, "Ws": Ws, "seeds": s}
     A, Wq, Ws = dequant_inputs(w.M, w.N, w.K, s["A"], s["codes"], s["scales"], integer)
     return {"A": A, "Wq": Wq, "Ws": Ws, "seeds": s}

@@ -40,10 +40,13 @@ _FAMILY_SOURCES = {
     "dma_w4": ["tg_kernel_dma_w4.h", "tg_kernel_dma.h", "tg_kernel.h", "tg_sched.h"],
     "gemv": ["tg_kernel_gemv_w4.h", "tg_kernel.h"],
     "tiled": ["tg_kernel.h", "tg_sched.h"],
+    "mx": ["tg_kernel_mx.h", "tg_kernel_dma_w4.h", "tg_kernel_dma.h", "tg_kernel.h", "tg_sched.h"],
 }
 
 
 def kernel_family(config: str) -> str:
+    if config.startswith("mx_"):
+        return "mx"
     if config.startswith("w4_") and "_dma" in config:
         return "dma_w4"
     if "_dma" in config:
@@ -68,7 +71,8 @@ def workload_config(workload: str) -> str:
     from . import binding, synth
 
     w = synth.WORKLOADS[workload]
-    return binding.query_config(0 if w.op == "gemm" else 1, w.M, w.N, w.K, w.dtype).split()[0]
+    op = {"gemm": 0, "dequant_w4": 1, "mx": 2}[w.op]
+    return binding.query_config(op, w.M, w.N, w.K, w.dtype).split()[0]
 
 
 def run(workload: str, launches: int) -> None:
@@ -98,6 +102,10 @@ def run(workload: str, launches: int) -> None:
         B = torch.from_numpy(inp["B"].view(view)).view(tdt[w.dtype]).to(dev)
         for _ in range(launches):
             binding.gemm(A, B, epilogue=epi)
+    elif w.op == "mx":
+        t = [torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws")]
+        for _ in range(launches):
+            binding.gemm_mx(w.dtype, *t, epilogue=epi)
     else:
         A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
         Wq = torch.from_numpy(inp["Wq"]).to(dev)
