@@ -161,6 +161,12 @@ def test_mx_argument_errors(lib):
         other = 1 if name.startswith("mx_e2m1") else 0
         assert c(idx, 4, 4, 128, other, PA, PS, PB, PQ, PC, 0, None) == NOCFG, name
     assert c(len(names), 4, 4, 128, 0, PA, PS, PB, PQ, PC, 0, None) == NOCFG
+    # chunked scale staging needs K % 512 == 0 and 16-byte aligned scale rows
+    for idx, name in enumerate(names):
+        if name.endswith("_sc8"):
+            fmt = 0 if name.startswith("mx_e2m1") else 1
+            assert c(idx, 4, 4, 384, fmt, PA, PS, PB, PQ, PC, 0, None) == NOCFG, name
+            assert c(idx, 4, 4, 512, fmt, PA, PS + 4, PB, PQ, PC, 0, None) == NOCFG, name
     assert c(-1, 4, 4, 128, 0, PA, PS, PB, PQ, PC, 0, None) == NOCFG
     buf = ctypes.create_string_buffer(128)
     assert lib.tg_query_config_ex(2, 8192, 8192, 8192, 0, 0, 0, buf, 128) == OK

@@ -210,17 +210,21 @@ def test_mx_zero_k_and_empty():
         binding.gemm_mx(fmt, e.view(0, 0), e.view(0, 0), e.view(7, 0), e.view(7, 0), C=C0)
 
 
-def test_mx_every_config():
-    M, N, K = 300, 264, 384
+@pytest.mark.parametrize("shape", [(300, 264, 384), (300, 264, 512), (200, 136, 1536),
+                                   (64, 72, 2560)], ids=lambda s: "x".join(map(str, s)))
+def test_mx_every_config(shape):
+    """Every configuration, forced: bit-exact where it runs; the other activation
+    format, and chunked scale staging at K % 512 != 0, refuse the call."""
+    M, N, K = shape
     for fmt in FMTS:
-        Aq, As, Wq, Ws = exact_inputs(fmt, M, N, K, 1900)
+        Aq, As, Wq, Ws = exact_inputs(fmt, M, N, K, 1900 + K)
         want = oracle.encode(BF16, oracle.mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu=True))
         for idx, name in enumerate(binding.list_configs(binding.TG_OP_MX)):
-            if not name.startswith("mx_" + FNAME[fmt]):
+            if not name.startswith("mx_" + FNAME[fmt]) or (name.endswith("_sc8") and K % 512):
                 with pytest.raises(binding.TileGemmError):
                     run_mx(fmt, Aq, As, Wq, Ws, relu=True, config=idx)
                 continue
-            say("mx config %d %s" % (idx, name))
+            say("mx config %d %s %s" % (idx, name, shape))
             got = run_mx(fmt, Aq, As, Wq, Ws, relu=True, config=idx)
             assert np.array_equal(got, want), name
 

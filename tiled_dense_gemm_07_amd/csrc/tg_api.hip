@@ -58,7 +58,8 @@ void config_name(const Config& c, char* buf, size_t len)
              c.op == 0 ? "gemm" : (mx ? "mx" : "w4"), mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
              c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
-             mx ? "" : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)], c.wide ? "" : "_narrow");
+             mx ? (c.chunked_scales ? "_sc8" : "") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
+             c.wide ? "" : "_narrow");
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -86,9 +87,9 @@ const Pref kPrefs[] = {
             nullptr}},
     {1, 2, {"w4_bf16_64x128x128_w2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
             "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
-    {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g4_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr,
-            nullptr}},
-    {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g4_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
+    {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g8_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma_sc8",
+            "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr}},
+    {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g8_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
             nullptr}},
 };
 
@@ -112,6 +113,7 @@ struct Call {
     bool wide;    // 16-byte aligned operands whose rows are whole 16-byte chunks
     bool ws4;     // dequant / MX scale bytes start 4-byte aligned
     bool ta, tb;  // A stored [K][M], B stored [N][K]
+    bool ws16 = false;  // MX scale bytes start 16-byte aligned
 };
 
 // Whether configuration c can run call q.
@@ -119,9 +121,13 @@ bool usable(const Config& c, const Call& q)
 {
     if (c.wide && !q.wide)
         return false;
-    if (c.op == TG_OP_MX)
-        // activation format compiled in; whole 128-k strips; dword scale copies
+    if (c.op == TG_OP_MX) {
+        // activation format compiled in; whole 128-k strips; dword scale
+        // copies, or 16-byte chunk copies that never straddle a row end
+        if (c.chunked_scales && (q.K % 512 != 0 || !q.ws16))
+            return false;
         return c.dtype == q.dtype && q.wide && q.ws4 && q.K % c.bk == 0;
+    }
     if (c.ta != q.ta || c.tb != q.tb)
         return false;  // operand layouts are compiled in
     if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
@@ -366,6 +372,7 @@ tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
         return TG_ERR_ALIAS;
     Call q{TG_OP_MX, a_fmt, M, N, K, aligned16(Aq) && aligned16(Wq),
            (((uintptr_t)As | (uintptr_t)Ws) & 3u) == 0, false, false};
+    q.ws16 = aligned16(As) && aligned16(Ws);
     const Config* c = forced ? forced : select_config(q);
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
@@ -462,6 +469,7 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
     // assume aligned operands (what torch allocations give)
     const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
     Call q{op, dt, M, N, K, false, true, trans_a != 0, trans_b != 0};
+    q.ws16 = true;
     q.wide = op != TG_OP_GEMM || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0);
     const Config* c = select_config(q);
     if (!c)

@@ -18,6 +18,8 @@ struct Config {
     int pipe;      // 0: single staging set; 1: deep pipeline; 2: LDS-DMA pipeline;
                    // 3: weight-streaming dequant kernel for few rows (K % bk == 0)
     const void* kernel;
+    bool chunked_scales = false;  // MX: scale bytes staged 8 strips at a time
+                                  // (K % 512 == 0, 16-byte aligned scale rows)
 };
 
 struct ConfigList {
@@ -40,10 +42,13 @@ ConfigList configs_mx();
             (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE> \
     }
 
-// Configurations of the LDS-DMA kernel (16-bit operands, BK = 32, NS stages).
-#define TG_CONFIG_DMA(DT, TA, TB, BM, BN, WGM, WGN, NS, GM)                                 \
+// Configurations of the LDS-DMA kernel (16-bit operands, 32 k per strip, NS
+// stages; TG_CONFIG_DMA_BK: BK k per strip).
+#define TG_CONFIG_DMA_BK(DT, TA, TB, BM, BN, WGM, WGN, NS, GM, BK)                           \
     tg::Config                                                                             \
     {                                                                                      \
-        0, DT, BM, BN, 32, WGM, WGN, NS, GM, true, TA, TB, 2,                              \
-            (const void*)&tg::gemm_dma_kernel<DT, TA, TB, BM, BN, WGM, WGN, NS, GM>        \
+        0, DT, BM, BN, BK, WGM, WGN, NS, GM, true, TA, TB, 2,                              \
+            (const void*)&tg::gemm_dma_kernel<DT, TA, TB, BM, BN, WGM, WGN, NS, GM, BK>    \
     }
+#define TG_CONFIG_DMA(DT, TA, TB, BM, BN, WGM, WGN, NS, GM) \
+    TG_CONFIG_DMA_BK(DT, TA, TB, BM, BN, WGM, WGN, NS, GM, 32)

@@ -69,6 +69,14 @@ __device__ __forceinline__ void wait_copies_barrier()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait until every copy and every LDS read of this wave has completed, then
+// barrier: afterwards the copies of all waves are visible and no wave still
+// reads the LDS it read before.
+__device__ __forceinline__ void wait_all_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Chunk swizzles.  A rows are 64 bytes (4 chunks): rows r, r+2, r+4, r+6 and
 // rows r, r+4, r+8, r+12 each get four different chunk positions.  B rows are
 // at least 256 bytes: the four k-rows one transposing read touches get chunk
@@ -76,32 +84,45 @@ __device__ __forceinline__ void wait_copies_barrier()
 __device__ __forceinline__ int swz_a(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 1) * 6) ^ ((k & 2) * 5); }
 
+// 128-byte rows (8 chunks): chunk c of row r goes to position c ^ swz8(r).  Only
+// the low five bits of r enter, so rows 32 apart (the 32-row blocks of a wave
+// tile) share a swizzle and one lane offset serves every block; any 16
+// consecutive rows of a 32-row block then read 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
 // One operand of the 16-bit DMA kernel: X (BM or BN) output rows/columns by
-// BK = 32 k per strip.  In global memory the operand is either k-contiguous
-// (KMAJ: each of its X rows holds consecutive k; leading dimension K) or
-// x-contiguous (each k row holds consecutive x; leading dimension = the
-// operand's full extent).  The LDS stage keeps the global orientation:
-//  * KMAJ: [X][32 k], 64-byte rows, chunk swizzle swz_a; an MFMA fragment
-//    (8 consecutive k of one row per lane) is one ds_read_b128;
-//  * x-contiguous: [32 k][X], chunk swizzle swz_b; a fragment is two
+// BK (32 or 64) k per strip.  In global memory the operand is either
+// k-contiguous (KMAJ: each of its X rows holds consecutive k; leading
+// dimension K) or x-contiguous (each k row holds consecutive x; leading
+// dimension = the operand's full extent).  The LDS stage keeps the global
+// orientation:
+//  * KMAJ: [X][BK k], rows of 64 bytes (chunk swizzle swz_a) or 128 bytes
+//    (swz8); an MFMA fragment (8 consecutive k of one row per lane) is one
+//    ds_read_b128.  A copy moves whole row segments of 2 BK bytes; 128-byte
+//    segments are whole cache lines and copy about 1.4x faster than 64-byte
+//    ones;
+//  * x-contiguous: [BK k][X], chunk swizzle swz_b; a fragment is two
 //    ds_read_b64_tr_b16 (4 consecutive k of one column each).
 // Both give the MFMA the same operand layout: lane l holds 8 consecutive k of
-// index l % 32 of a 32-wide block, starting at k = 8 (l / 32).
-template <bool KMAJ, int X, int WX, int FX, int NW>
+// index l % 32 of a 32-wide block, starting at k = 16 s + 8 (l / 32) in slab s.
+template <bool KMAJ, int X, int WX, int FX, int NW, int BK>
 struct DmaOperand {
-    static constexpr int BK = 32;
-    static constexpr int STAGE = X * BK * 2;      // bytes per LDS stage
-    static constexpr int J = STAGE / 1024 / NW;   // 1 KiB copies per wave per strip
-    static constexpr int LPR = KMAJ ? 4 : X / 8;  // 16-byte chunks per LDS row
-    static constexpr int RPB = 64 / LPR;          // LDS rows per 1 KiB copy
-    static constexpr int NRD = KMAJ ? FX : 2 * FX;  // LDS reads per slab
+    static_assert(BK == 32 || BK == 64, "strips of 32 or 64 k");
+    static constexpr int SL = BK / 16;                // MFMA slabs per strip
+    static constexpr int STAGE = X * BK * 2;          // bytes per LDS stage
+    static constexpr int J = STAGE / 1024 / NW;       // 1 KiB copies per wave per strip
+    static constexpr int LPR = KMAJ ? BK / 8 : X / 8;  // 16-byte chunks per LDS row
+    static constexpr int RPB = 64 / LPR;              // LDS rows per 1 KiB copy
+    static constexpr int NRD = KMAJ ? FX : 2 * FX;    // LDS reads per slab
     static_assert(J >= 1 && STAGE % (1024 * NW) == 0, "strips split into whole 1 KiB copies per wave");
     static_assert(KMAJ || (LPR >= 16 && LPR <= 64), "x-contiguous rows of 256 to 1024 bytes");
+
+    static __device__ __forceinline__ int kswz(int row) { return BK == 32 ? swz_a(row) : swz8(row); }
 
     struct Lane {
         u32 off[J];   // copy offsets within a strip (out of range past the x extent)
         int kk[J];    // k (within the strip) of the data each copy lane moves
-        u32 rd[KMAJ ? 2 : FX];  // fragment read offsets (stage 0)
+        u32 rd[KMAJ ? SL : FX];  // fragment read offsets (stage 0)
     };
     struct Frag {
         u32x4 v[KMAJ ? FX : 1];
@@ -118,7 +139,7 @@ struct DmaOperand {
             const int blk = w * J + j;
             const int row = blk * RPB + lane / LPR;
             if constexpr (KMAJ) {
-                const int c = (lane % LPR) ^ swz_a(row);
+                const int c = (lane % LPR) ^ kswz(row);
                 L.kk[j] = c * 8;
                 L.off[j] = (x0 + row < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
             } else {
@@ -129,10 +150,10 @@ struct DmaOperand {
         }
         if constexpr (KMAJ) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < SL; ++s) {
                 const int row = wx0 + (lane & 31);
                 const int c = 2 * s + (lane >> 5);
-                L.rd[s] = region + row * (BK * 2) + ((c ^ swz_a(row)) << 4);
+                L.rd[s] = region + row * (BK * 2) + ((c ^ kswz(row)) << 4);
             }
         } else {
             const int g = lane >> 4, t = lane & 15;
@@ -145,7 +166,7 @@ struct DmaOperand {
         }
     }
 
-    // Descriptor of one strip (k0 .. k0 + 31), rebased so offsets fit 31 bits.
+    // Descriptor of one strip (k0 .. k0 + BK - 1), rebased so offsets fit 31 bits.
     static __device__ __forceinline__ __amdgpu_buffer_rsrc_t strip_rsrc(const void* base, int x0,
                                                                         int xtot, int ld, int K,
                                                                         int k0)
@@ -188,29 +209,31 @@ struct DmaOperand {
     }
 };
 
-// TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].
-template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+// TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].  BK: k per
+// strip (32 or 64); NS: LDS stages (2 .. 5).
+template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M,
+          int BK>
 struct DmaGemm {
     static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
-    static constexpr int BK = 32;
+    static constexpr int SL = BK / 16;  // MFMA slabs per strip
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = NW * 64;
     static constexpr int WTM = BM / WGM;
     static constexpr int WTN = BN / WGN;
     static constexpr int FM = WTM / 32;
     static constexpr int FN = WTN / 32;
-    using OA = DmaOperand<!TA, BM, WTM, FM, NW>;
-    using OB = DmaOperand<TB, BN, WTN, FN, NW>;
+    using OA = DmaOperand<!TA, BM, WTM, FM, NW, BK>;
+    using OB = DmaOperand<TB, BN, WTN, FN, NW, BK>;
     static constexpr int A_STAGE = OA::STAGE;
     static constexpr int B_STAGE = OB::STAGE;
     static constexpr int A_REGION = NS * A_STAGE;
     static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
     static constexpr int NREAD = OA::NRD + OB::NRD;  // LDS reads per slab
     static constexpr int NCOPY = OA::J + OB::J;      // copies per wave per strip
-    static constexpr int VM_AHEAD = (NS - 3) * NCOPY;  // copies allowed in flight at the barrier
+    static constexpr int VM_AHEAD = NS >= 3 ? (NS - 3) * NCOPY : 0;  // copies in flight at the barrier
 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole 32x32 blocks");
-    static_assert(NS >= 3, "the barrier publishes strip t + 1 while t - 1 is free");
+    static_assert(NS >= 2 && NS <= 5, "two to five stages");
     static_assert(NW <= 4, "the main loop is instantiated for up to four waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
@@ -299,83 +322,116 @@ struct DmaGemm {
                 0);
     }
 
-    // One strip: MFMAs on slab 0 (fragments F0) then slab 1 (F1), SLOTS MFMA
-    // slots in all.
-    //   slot 0, after its MFMA and read: wait for strip t + 1's copies and
-    //           barrier; strip t + 1 is then visible and the stage of strip
-    //           t - 1 is free;
-    //   the NCOPY x NW copies of strip t + NS - 1 (NCOPY per wave) are spread
-    //           evenly over the strip and staggered across the waves, so the
-    //           address unit sees a steady stream instead of bursts that back
-    //           up into the MFMA issue;
-    //   slab 0 slots: reads of slab 1 into F1; slab 1 slots: reads of strip
-    //           t + 1's slab 0 into F0.
-    template <int ST, int W>
-    static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
+    // Reads of slab S + 1 of stage ST (or, for the last slab, slab 0 of the
+    // next stage NXT) into the fragment set the next slab uses.
+    template <int ST, int NXT, int S>
+    static __device__ __forceinline__ void read_next(Frag (&F)[2], const Lane& L, lds_char* sm,
+                                                     int i)
+    {
+        if constexpr (S + 1 < SL)
+            read_one<ST, S + 1>(F[(S + 1) & 1], L, sm, i);
+        else
+            read_one<NXT, 0>(F[0], L, sm, i);
+    }
+
+    // Step i of slab S: its MFMA, then (NS == 2, last slab, first step) the
+    // barrier, then its read of the next slab's fragments.
+    template <int ST, int NXT, int S, int I>
+    static __device__ __forceinline__ void slab_step(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+                                                     const Lane& L, lds_char* sm)
+    {
+        constexpr int NM = FM * FN;
+        if constexpr (I < NM) {
+            mfma_one(acc, F[S & 1], I);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NS == 2 && S == SL - 1 && I == 0) {
+            wait_all_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (I < NREAD) {
+            read_next<ST, NXT, S>(F, L, sm, I);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    static constexpr int NM_ = FM * FN;
+    static constexpr int STEPS = NM_ > NREAD ? NM_ : NREAD;  // slots per slab
+    static constexpr int SLOTS = SL * STEPS;                 // slots per strip
+    static constexpr int CSLOTS = NS == 2 ? (SL / 2) * STEPS : SLOTS;  // slots the copies use
+
+    // Slot SLOT of a strip (stage ST) of wave W, then the following slots: the
+    // recursion unrolls the strip at compile time whatever its length.
+    template <int ST, int W, int SLOT>
+    static __device__ __forceinline__ void slots(f32x16 (&acc)[FM][FN], Frag (&F)[2],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
-                                                 int m0, int n0, int t, u32 smem0)
+                                                 int m0, int n0, int t, u32 smem0, StripRes& r)
     {
         constexpr int NXT = (ST + 1) % NS;
         constexpr int CPY = (ST + NS - 1) % NS;
-        constexpr int NM = FM * FN;
-        constexpr int STEPS = NM > NREAD ? NM : NREAD;
-        constexpr int SLOTS = 2 * STEPS;
-        StripRes r;
+        slab_step<ST, NXT, SLOT / STEPS, SLOT % STEPS>(acc, F, L, sm);
+        if constexpr (NS >= 3 && SLOT == 0) {
+            wait_copies_barrier<VM_AHEAD>();
+            __builtin_amdgcn_sched_barrier(0);
+            r = strip_res(p, m0, n0, t + NS - 1);
+        }
+        // copy d of wave W goes to slot ((d * NW + W) * CSLOTS) / (NCOPY * NW)
 #pragma unroll
-        for (int slot = 0; slot < SLOTS; ++slot) {
-            const int i = slot % STEPS;
-            if (slot < STEPS) {
-                if (i < NM) {
-                    mfma_one(acc, F0, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (i < NREAD) {
-                    read_one<ST, 1>(F1, L, sm, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            } else {
-                if (i < NM) {
-                    mfma_one(acc, F1, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (i < NREAD) {
-                    read_one<NXT, 0>(F0, L, sm, i);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            if (slot == 0) {
-                wait_copies_barrier<VM_AHEAD>();
+        for (int d = 0; d < NCOPY; ++d) {
+            if (((d * NW + W) * CSLOTS) / (NCOPY * NW) == SLOT) {
+                issue_copy<CPY>(L, r, d, W, smem0);
                 __builtin_amdgcn_sched_barrier(0);
-                r = strip_res(p, m0, n0, t + NS - 1);
-            }
-            // copy d of wave W goes to slot ((d * NW + W) * SLOTS) / (NCOPY * NW)
-#pragma unroll
-            for (int d = 0; d < NCOPY; ++d) {
-                if (((d * NW + W) * SLOTS) / (NCOPY * NW) == slot) {
-                    issue_copy<CPY>(L, r, d, W, smem0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
         }
+        if constexpr (SLOT + 1 < SLOTS)
+            slots<ST, W, SLOT + 1>(acc, F, L, sm, p, m0, n0, t, smem0, r);
+    }
+
+    // One strip: SL slabs of FM x FN MFMAs; slab s uses fragment set F[s & 1]
+    // while the reads of the next slab fill the other set (the last slab reads
+    // slab 0 of strip t + 1 into F[0]).  Copies of strip t + NS - 1 go to the
+    // stage strip t - 1 used.
+    //   NS >= 3: the barrier sits in slot 0 (after its MFMA and read): before
+    //     it, strip t + 1's copies are waited for (at most the NCOPY x (NS - 3)
+    //     younger ones stay in flight); after it, strip t + 1 is visible and the
+    //     stage of strip t - 1 is free, and the copies are spread over the
+    //     whole strip, staggered across the waves.
+    //   NS == 2: the barrier sits at the start of the last slab, before the
+    //     reads of strip t + 1: each wave first waits for all its copies (those
+    //     of strip t + 1) and LDS reads (those of strip t, whose last slab is
+    //     in registers by then), so after the barrier strip t + 1 is visible
+    //     and no wave reads strip t's stage again.  The copies of strip t + 1
+    //     are spread over the first half of strip t so they land before the
+    //     last slab.
+    template <int ST, int W>
+    static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+                                                 const Lane& L, lds_char* sm, const GemmParams& p,
+                                                 int m0, int n0, int t, u32 smem0)
+    {
+        StripRes r;
+        if constexpr (NS == 2)
+            r = strip_res(p, m0, n0, t + 1);
+        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r);
     }
 
     // The strip loop of wave W (the copy slots differ per wave).  The strip
     // count is rounded up to a multiple of NS: strips at or past KT copy only
     // out-of-range zeros, which add exactly nothing.
     template <int W>
-    static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
+    static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], Frag (&F)[2],
                                                      const Lane& L, lds_char* sm,
                                                      const GemmParams& p, int m0, int n0, int KT,
                                                      u32 smem0)
     {
         for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, F0, F1, L, sm, p, m0, n0, t, smem0);
-            strip<1, W>(acc, F0, F1, L, sm, p, m0, n0, t + 1, smem0);
-            strip<2, W>(acc, F0, F1, L, sm, p, m0, n0, t + 2, smem0);
+            strip<0, W>(acc, F, L, sm, p, m0, n0, t, smem0);
+            strip<1, W>(acc, F, L, sm, p, m0, n0, t + 1, smem0);
+            if constexpr (NS > 2)
+                strip<2 % NS, W>(acc, F, L, sm, p, m0, n0, t + 2, smem0);
             if constexpr (NS > 3)
-                strip<3 % NS, W>(acc, F0, F1, L, sm, p, m0, n0, t + 3, smem0);
+                strip<3 % NS, W>(acc, F, L, sm, p, m0, n0, t + 3, smem0);
             if constexpr (NS > 4)
-                strip<4 % NS, W>(acc, F0, F1, L, sm, p, m0, n0, t + 4, smem0);
+                strip<4 % NS, W>(acc, F, L, sm, p, m0, n0, t + 4, smem0);
         }
     }
 
@@ -445,31 +501,31 @@ struct DmaGemm {
 
         // prologue: strips 0 .. NS-2 into stages 0 .. NS-2
         issue_copies<0>(L, p, m0, n0, 0, w, smem0);
-        issue_copies<1>(L, p, m0, n0, 1, w, smem0);
+        if constexpr (NS > 2)
+            issue_copies<1>(L, p, m0, n0, 1, w, smem0);
         if constexpr (NS > 3)
             issue_copies<2 % NS>(L, p, m0, n0, 2, w, smem0);
         if constexpr (NS > 4)
             issue_copies<3 % NS>(L, p, m0, n0, 3, w, smem0);
-        static_assert(NS <= 5, "prologue written for up to 5 stages");
         // strip 0 must be complete and visible before its first fragments are read
         wait_copies_barrier<(NS - 2) * NCOPY>();
-        Frag F0, F1;
+        Frag F[2];
 #pragma unroll
         for (int i = 0; i < NREAD; ++i)
-            read_one<0, 0>(F0, L, sm, i);
+            read_one<0, 0>(F[0], L, sm, i);
 
         switch (w) {
         case 0:
-            main_loop<0>(acc, F0, F1, L, sm, p, m0, n0, KT, smem0);
+            main_loop<0>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 1:
-            main_loop<1 % NW>(acc, F0, F1, L, sm, p, m0, n0, KT, smem0);
+            main_loop<1 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 2:
-            main_loop<2 % NW>(acc, F0, F1, L, sm, p, m0, n0, KT, smem0);
+            main_loop<2 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         default:
-            main_loop<3 % NW>(acc, F0, F1, L, sm, p, m0, n0, KT, smem0);
+            main_loop<3 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         }
         // drain the copies of the strips past the end (all out of range)
@@ -485,12 +541,13 @@ struct DmaOcc {
     static constexpr int value = BM * BN >= 256 * 128 ? 1 : 2;
 };
 
-template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M,
+          int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
                           amdgpu_waves_per_eu(DmaOcc<BM, BN>::value, DmaOcc<BM, BN>::value))) void
 gemm_dma_kernel(GemmParams p)
 {
-    DmaGemm<DT, TA, TB, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    DmaGemm<DT, TA, TB, BM, BN, WGM, WGN, NS, GROUP_M, BK>::run(p);
 }
 
 }  // namespace tg

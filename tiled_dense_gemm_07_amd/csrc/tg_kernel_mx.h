@@ -26,6 +26,12 @@
 //  * a row's four scale bytes are read once per strip and shifted per lane
 //    half and k-step, so byte 0 of the scale operand is always the block the
 //    lane supplies;
+//  * scale bytes reach LDS either per strip (one dword per row: 64 rows per
+//    copy, each in its own cache line) or, when K % 512 == 0, in chunks of 8
+//    strips (32 bytes per row, 16 per lane: 32 rows per copy), double
+//    buffered; the chunks cut the cache-line accesses of the scale copies
+//    eightfold, and those accesses, not the bytes, are what the address unit
+//    spends its cycles on;
 //  * one barrier per strip after its first MFMA publishes strip t + 1 and frees
 //    strip t - 1; copies of strip t + NS - 1 are staggered across waves and
 //    slots.  K must be a multiple of 128 and the scale rows 4-byte aligned;
@@ -45,14 +51,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 enum MxFmt { MX_E4M3 = 0, MX_E2M1 = 4 };  // the instruction's format codes
 
-// 128-byte rows: chunk c of row r goes to position c ^ swz8(r).  Only the
-// low five bits of r enter, so rows 32 apart (the 32-row blocks of a wave
-// tile) share a swizzle and one lane offset serves every block; any 16
-// consecutive rows of a 32-row block then read 16 distinct 16-byte bank
-// groups.
-__device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
-
-template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS>
 struct DmaMx {
     static constexpr int BK = 128;
     static constexpr int NW = WGM * WGN;
@@ -64,16 +63,21 @@ struct DmaMx {
     static constexpr int A_ROWB = A8 ? 128 : 64;  // code bytes per row per strip
     static constexpr int A_STAGE = BM * A_ROWB;
     static constexpr int W_STAGE = BN * 64;
-    static constexpr int SA_STAGE = BM * 4;
-    static constexpr int SW_STAGE = BN * 4;
+    static constexpr int SCH = 8;                        // strips per scale chunk (CS)
+    static constexpr int SA_STAGE = CS ? BM * 32 : BM * 4;  // bytes per scale buffer
+    static constexpr int SW_STAGE = CS ? BN * 32 : BN * 4;
+    static constexpr int NSB = CS ? 2 : NS;                 // scale buffers
     static constexpr int W_REGION = NS * A_STAGE;
     static constexpr int SA_REGION = W_REGION + NS * W_STAGE;
-    static constexpr int SW_REGION = SA_REGION + NS * SA_STAGE;
-    static constexpr int LDS_BYTES = SW_REGION + NS * SW_STAGE;
+    static constexpr int SW_REGION = SA_REGION + NSB * SA_STAGE;
+    static constexpr int LDS_BYTES = SW_REGION + NSB * SW_STAGE;
     static constexpr int JA = A_STAGE / 1024 / NW;
     static constexpr int JW = W_STAGE / 1024 / NW;
-    static constexpr int NSA = SA_STAGE / 256;  // dword scale copies of A per strip
-    static constexpr int NSW = SW_STAGE / 256;
+    static constexpr int NSA = CS ? 0 : BM * 4 / 256;   // per-strip dword scale copies of A
+    static constexpr int NSW = CS ? 0 : BN * 4 / 256;
+    static constexpr int NCA = CS ? BM / 32 : 0;        // chunk copies of A scales (CS)
+    static constexpr int NCW = CS ? BN / 32 : 0;
+    static constexpr int JS = (NCA + NCW) / NW;         // chunk copies per wave
     static constexpr int NM = FM * FN;          // MFMAs per 64-k step
     static constexpr int SLOTS = 2 * NM;        // MFMAs per strip
 
@@ -81,7 +85,9 @@ struct DmaMx {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && JW >= 1 && A_STAGE % (1024 * NW) == 0 && W_STAGE % (1024 * NW) == 0,
                   "strips split into whole 1 KiB copies per wave");
-    static_assert(NSA >= 1 && NSA <= NW && NSW >= 1 && NSW <= NW, "scale copies: one per wave at most");
+    static_assert(CS || (NSA >= 1 && NSA <= NW && NSW >= 1 && NSW <= NW),
+                  "scale copies: one per wave at most");
+    static_assert(!CS || ((NCA + NCW) % NW == 0 && JS >= 1), "chunk copies split evenly");
     static_assert(NS == 4, "four stages (scale registers alternate per strip)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
@@ -90,15 +96,18 @@ struct DmaMx {
         static constexpr int N = JA + JW + (W < NSA ? 1 : 0) + (W < NSW ? 1 : 0);
         static constexpr int AHEAD = (NS - 3) * N;
     };
-    static constexpr int NCMAX = JA + JW + 2;
+    static constexpr int NCMAX = JA + JW + (CS ? 0 : 2);
 
     struct Lane {
         u32 a_off[JA];
         u32 w_off[JW];
-        u32 sa_off, sw_off;
+        u32 sa_off, sw_off;       // per-strip scale copies (!CS)
+        u32 s_off[CS ? JS : 1];   // chunk copies (CS): row offset + 16-byte half
+        u32 s_half[CS ? JS : 1];  //   and that half (0, 1)
         u32 a_rd[2][A8 ? 2 : 1];  // [k-step][part]: code chunks of this lane (stage 0, fm 0)
         u32 w_rd[2];              // [k-step] (stage 0, fn 0)
-        u32 sa_rd, sw_rd;         // this lane's row of scale bytes (stage 0, block 0)
+        u32 sa_rd[2], sw_rd[2];   // this lane's row of scale bytes (buffer 0, block 0);
+                                  // CS: [strips 0-3 / 4-7 of the chunk]
         int h8;                   // 8 * lane half: the lane's scale bytes start at block h
     };
 
@@ -139,6 +148,21 @@ struct DmaMx {
             L.sa_off = (w < NSA && m0 + row < p.M) ? (u32)(row * (K / 32)) : kOob;
             L.sw_off = (w < NSW && n0 + row < p.N) ? (u32)(row * (K / 32)) : kOob;
         }
+        if constexpr (CS) {
+            // chunk copy g: 32 rows x 32 bytes, lane l -> row g' * 32 + l / 2 at
+            // LDS 16-byte position l & 1, which holds the row's half
+            // (l & 1) ^ bit 3 of the row (two-way bank spread for the reads)
+#pragma unroll
+            for (int d = 0; d < JS; ++d) {
+                const int g = w * JS + d;
+                const bool isa = g < NCA;
+                const int row = (isa ? g : g - NCA) * 32 + (lane >> 1);
+                const int half = (lane & 1) ^ ((row >> 3) & 1);
+                const bool ok = isa ? (m0 + row < p.M) : (n0 + row < p.N);
+                L.s_off[d] = ok ? (u32)(row * (K / 32) + half * 16) : kOob;
+                L.s_half[d] = (u32)half;
+            }
+        }
         const int h = lane >> 5;
         const int ar = wm * WTM + (lane & 31);
         const int nr = wn * WTN + (lane & 31);
@@ -154,8 +178,16 @@ struct DmaMx {
             }
             L.w_rd[q] = W_REGION + nr * 64 + (((2 * q + h) ^ swz_a(nr)) << 4);
         }
-        L.sa_rd = SA_REGION + ar * 4;
-        L.sw_rd = SW_REGION + nr * 4;
+        if constexpr (CS) {
+            const int xa = (ar >> 3) & 1, xw = (nr >> 3) & 1;
+            L.sa_rd[0] = SA_REGION + ar * 32 + (xa << 4);
+            L.sa_rd[1] = SA_REGION + ar * 32 + ((1 ^ xa) << 4);
+            L.sw_rd[0] = SW_REGION + nr * 32 + (xw << 4);
+            L.sw_rd[1] = SW_REGION + nr * 32 + ((1 ^ xw) << 4);
+        } else {
+            L.sa_rd[0] = L.sa_rd[1] = SA_REGION + ar * 4;
+            L.sw_rd[0] = L.sw_rd[1] = SW_REGION + nr * 4;
+        }
         L.h8 = 8 * h;
     }
 
@@ -227,6 +259,24 @@ struct DmaMx {
                  r.sw);
     }
 
+    // Chunk copies (CS) of wave W: the scale bytes of strips 8 c .. 8 c + 7 into
+    // buffer c & 1.  A lane's 16 bytes are inside its row or past its end as a
+    // whole (K % 512 == 0); past the end they read as zeros.
+    template <int W>
+    static __device__ __forceinline__ void issue_chunk(const Lane& L, const Res& r,
+                                                       const GemmParams& p, int c, int d,
+                                                       u32 smem0)
+    {
+        const int g = W * JS + d;
+        const u32 buf = (u32)(c & 1);
+        const bool ok = (u32)(2 * c) + L.s_half[d] < (u32)(p.K / 512);
+        const u32 off = ok ? L.s_off[d] + (u32)(c * 32) : kOob;
+        if (g < NCA)
+            dma16(smem0 + SA_REGION + buf * SA_STAGE + g * 1024, off, r.sa);
+        else
+            dma16(smem0 + SW_REGION + buf * SW_STAGE + (g - NCA) * 1024, off, r.sw);
+    }
+
     template <int ST, int W>
     static __device__ __forceinline__ void issue_copies(const Lane& L, const Res& r,
                                                         const GemmParams& p, int strip, u32 smem0)
@@ -254,19 +304,32 @@ struct DmaMx {
         }
     }
 
-    template <int ST>
-    static __device__ __forceinline__ void read_scales(Scales& S, const Lane& L, lds_char* sm)
+    // Scale bytes of strip u (SL = u % 4 at compile time).
+    template <int SL>
+    static __device__ __forceinline__ void read_scales(Scales& S, const Lane& L, lds_char* sm,
+                                                       int u)
     {
         typedef __attribute__((address_space(3))) u32 lds_u32;
+        u32 ra, rw;
+        if constexpr (CS) {
+            const bool hi = (u >> 2) & 1;           // strips 4-7 of the chunk
+            const u32 buf = (u32)((u >> 3) & 1);
+            ra = (hi ? L.sa_rd[1] : L.sa_rd[0]) + buf * SA_STAGE + SL * 4;
+            rw = (hi ? L.sw_rd[1] : L.sw_rd[0]) + buf * SW_STAGE + SL * 4;
+        } else {
+            ra = L.sa_rd[0] + SL * SA_STAGE;
+            rw = L.sw_rd[0] + SL * SW_STAGE;
+        }
+        constexpr int RA = CS ? 32 : 4;  // LDS bytes per scale row
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const u32 v = *(const lds_u32*)(sm + L.sa_rd + ST * SA_STAGE + fm * 32 * 4);
+            const u32 v = *(const lds_u32*)(sm + ra + fm * 32 * RA);
             S.a[0][fm] = v >> L.h8;
             S.a[1][fm] = v >> (L.h8 + 16);
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const u32 v = *(const lds_u32*)(sm + L.sw_rd + ST * SW_STAGE + fn * 32 * 4);
+            const u32 v = *(const lds_u32*)(sm + rw + fn * 32 * RA);
             S.w[0][fn] = v >> L.h8;
             S.w[1][fn] = v >> (L.h8 + 16);
         }
@@ -298,7 +361,10 @@ struct DmaMx {
     // with F1.  Slot 0 waits for strip t + 1's copies and barriers; k-step 0's
     // slots read k-step 1 into F1; k-step 1's slots read strip t + 1's scales
     // (into SC[(ST + 1) & 1]) and k-step 0 (into F0); copies of strip
-    // t + NS - 1 are staggered over the slots.
+    // t + NS - 1 are staggered over the slots.  CS: strip 8 c + 1 also copies
+    // scale chunk c + 1 (into the buffer chunk c - 1 used, whose last reads
+    // were before strip 8 c - 1), so the wait of strip 8 c + 2 leaves those
+    // copies in flight too, and chunk c + 1 has landed by strip 8 c + 3.
     template <int ST, int W>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
                                                  Scales (&SC)[2], const Lane& L, const Res& res,
@@ -328,7 +394,7 @@ struct DmaMx {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i == 0) {
-                    read_scales<NXT>(SC[CUR ^ 1], L, sm);
+                    read_scales<(ST + 1) & 3>(SC[CUR ^ 1], L, sm, t + 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i < NRD) {
@@ -337,9 +403,22 @@ struct DmaMx {
                 }
             }
             if (slot == 0) {
-                wait_copies_barrier<Copies<W>::AHEAD>();
+                if (CS && (t & 7) == 2)
+                    wait_copies_barrier<Copies<W>::AHEAD + JS>();
+                else
+                    wait_copies_barrier<Copies<W>::AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
                 o = strip_off(p, t + NS - 1);
+            }
+            if constexpr (CS) {
+#pragma unroll
+                for (int d = 0; d < JS; ++d) {
+                    if (slot == 2 * d + 1) {
+                        if ((t & 7) == 1)
+                            issue_chunk<W>(L, res, p, (t >> 3) + 1, d, smem0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
 #pragma unroll
             for (int d = 0; d < Copies<W>::N; ++d) {
@@ -357,13 +436,18 @@ struct DmaMx {
                                                      int n0, int KT, u32 smem0)
     {
         const Res res = band_res(p, m0, n0);
+        if constexpr (CS) {
+#pragma unroll
+            for (int d = 0; d < JS; ++d)
+                issue_chunk<W>(L, res, p, 0, d, smem0);
+        }
         issue_copies<0, W>(L, res, p, 0, smem0);
         issue_copies<1, W>(L, res, p, 1, smem0);
         issue_copies<2, W>(L, res, p, 2, smem0);
         wait_copies_barrier<(NS - 2) * Copies<W>::N>();
         Frag F0, F1;
         Scales SC[2];
-        read_scales<0>(SC[0], L, sm);
+        read_scales<0>(SC[0], L, sm, 0);
 #pragma unroll
         for (int i = 0; i < NRD; ++i)
             read_one<0, 0>(F0, L, sm, i);
@@ -460,13 +544,13 @@ struct MxOcc {
     static constexpr int value = (AFMT == MX_E2M1 && BM * BN <= 128 * 128) ? 2 : 1;
 };
 
-template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
                           amdgpu_waves_per_eu(MxOcc<AFMT, BM, BN>::value,
                                               MxOcc<AFMT, BM, BN>::value))) void
 gemm_mx_kernel(GemmParams p)
 {
-    DmaMx<AFMT, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    DmaMx<AFMT, BM, BN, WGM, WGN, NS, GROUP_M, CS>::run(p);
 }
 
 }  // namespace tg
