@@ -1,5 +1,5 @@
-"""CPU oracle for the tiled GEMM, the weight-only 4-bit dequant GEMM and the
-MX-format GEMM.
+"""CPU oracle for the tiled GEMM, the weight-only 4-bit dequant GEMM, the
+MX-format GEMM and the 2:4 structured-sparse GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The library under
@@ -75,6 +75,11 @@ def _bind(lib):
                             ctypes.c_int),
         "orc_mx_gemm_entries_f64": ([i64, i64, i64, ctypes.c_int, p, p, p, p, ctypes.c_int, i64,
                                      p, p, p], None),
+        "orc_sp24_densify": ([i64, i64, ctypes.c_int, p, p, p], None),
+        "orc_gemm_sp24_f64": ([i64, i64, i64, ctypes.c_int, p, p, p, ctypes.c_int, p],
+                              ctypes.c_int),
+        "orc_gemm_sp24_entries_f64": ([i64, i64, i64, ctypes.c_int, p, p, p, ctypes.c_int, i64,
+                                       p, p, p], None),
         "orc_num_threads": ([], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
@@ -317,6 +322,60 @@ class Oracle:
                                          _ptr(out))
         return out
 
+    # -- 2:4 structured-sparse GEMM ------------------------------------------------
+    @staticmethod
+    def _sp24_check(Ac, Ai, B, dtype):
+        ac = _bits(Ac, dtype)
+        ai = np.ascontiguousarray(Ai, dtype=np.uint8)
+        b = _bits(B, dtype)
+        M, half = ac.shape
+        K = 2 * half
+        K2, N = b.shape
+        if K != K2:
+            raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+        if K % 8 != 0:
+            raise ValueError("K must be a multiple of 8")
+        if ai.shape != (M, K // 8):
+            raise ValueError("metadata shape does not match [M, K/8]")
+        return ac, ai, b, M, N, K
+
+    def sp24_densify(self, Ac, Ai, dtype: int) -> np.ndarray:
+        """Compressed values [M, K/2] and metadata [M, K/8] -> dense A [M, K] fp64."""
+        ac = _bits(Ac, dtype)
+        ai = np.ascontiguousarray(Ai, dtype=np.uint8)
+        M, half = ac.shape
+        K = 2 * half
+        if ai.shape != (M, K // 8):
+            raise ValueError("metadata shape does not match [M, K/8]")
+        out = np.empty((M, K), dtype=np.float64)
+        self.lib.orc_sp24_densify(M, K, dtype, _ptr(ac), _ptr(ai), _ptr(out))
+        return out
+
+    def gemm_sp24_f64(self, Ac, Ai, B, dtype: int, relu: bool = False) -> np.ndarray:
+        """Y = epi(A_sparse @ B) in fp64 with A given in compressed 2:4 form."""
+        ac, ai, b, M, N, K = self._sp24_check(Ac, Ai, B, dtype)
+        Y = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.orc_gemm_sp24_f64(M, N, K, dtype, _ptr(ac), _ptr(ai), _ptr(b),
+                                        int(bool(relu)), _ptr(Y))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+        return Y
+
+    def gemm_sp24_entries_f64(self, Ac, Ai, B, dtype: int, rows, cols,
+                              relu: bool = False) -> np.ndarray:
+        """Selected entries, summed one by one from the compressed form."""
+        ac, ai, b, M, N, K = self._sp24_check(Ac, Ai, B, dtype)
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        if r.shape != c.shape:
+            raise ValueError("rows and cols differ in length")
+        if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+            raise IndexError("entry outside the output")
+        out = np.empty(r.shape, dtype=np.float64)
+        self.lib.orc_gemm_sp24_entries_f64(M, N, K, dtype, _ptr(ac), _ptr(ai), _ptr(b),
+                                           int(bool(relu)), r.size, _ptr(r), _ptr(c), _ptr(out))
+        return out
+
 
 _default = None
 
@@ -393,3 +452,15 @@ def mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu=False):
 
 def mx_gemm_entries_f64(fmt, Aq, As, Wq, Ws, rows, cols, relu=False):
     return default().mx_gemm_entries_f64(fmt, Aq, As, Wq, Ws, rows, cols, relu)
+
+
+def sp24_densify(Ac, Ai, dtype):
+    return default().sp24_densify(Ac, Ai, dtype)
+
+
+def gemm_sp24_f64(Ac, Ai, B, dtype, relu=False):
+    return default().gemm_sp24_f64(Ac, Ai, B, dtype, relu)
+
+
+def gemm_sp24_entries_f64(Ac, Ai, B, dtype, rows, cols, relu=False):
+    return default().gemm_sp24_entries_f64(Ac, Ai, B, dtype, rows, cols, relu)

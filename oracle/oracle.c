@@ -1,6 +1,6 @@
 /*
- * Oracle for the tiled dense GEMM, the weight-only 4-bit dequant GEMM and the
- * MX-format GEMM.
+ * Oracle for the tiled dense GEMM, the weight-only 4-bit dequant GEMM, the
+ * MX-format GEMM and the 2:4 structured-sparse GEMM.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the library calls, links or includes
  * this file; only the tests, the smoke check and the CPU-baseline leg of the
@@ -476,6 +476,99 @@ void orc_mx_gemm_entries_f64(int64_t M, int64_t N, int64_t K, int fmt, const uin
         for (int64_t k = 0; k < K; ++k)
             s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, k);
         out[t] = relu ? relu_f64(s) : s;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* 2:4 structured-sparse GEMM (the sparse GEMM the blog.hotdry.top page    */
+/* names for 2:4 sparsity, its monitoring-and-debugging paragraph).        */
+/*   A [M][K] is given compressed: group j of a row (k = 4j .. 4j + 3)     */
+/*   keeps two values, Ac[m][2j] at position p0 and Ac[m][2j + 1] at p1,   */
+/*   nib = (Ai[m][j / 2] >> (4 * (j % 2))) & 0xF, p0 = nib & 3,            */
+/*   p1 = nib >> 2; the other positions are zero (a repeated position      */
+/*   holds the sum of both values).                                        */
+/*   Y[m][n] = epi(sum_j sum_t Ac[m][2j + t] * B[4j + p_t][n]).            */
+/* K must be a multiple of 8 (whole metadata bytes).                       */
+/* ---------------------------------------------------------------------- */
+
+static int sp24_pos(const uint8_t* Ai, int64_t K, int64_t m, int64_t j, int t)
+{
+    const int nib = (Ai[m * (K / 8) + j / 2] >> (4 * (j % 2))) & 0xF;
+    return t == 0 ? (nib & 3) : (nib >> 2);
+}
+
+static double decode_one(int dtype, const void* X, int64_t i)
+{
+    if (dtype == ORC_F32)
+        return orc_decode_f32(((const uint32_t*)X)[i]);
+    if (dtype == ORC_F16)
+        return orc_decode_f16(((const uint16_t*)X)[i]);
+    return orc_decode_bf16(((const uint16_t*)X)[i]);
+}
+
+/* The dense A [M][K] in fp64 that the compressed form stands for. */
+void orc_sp24_densify(int64_t M, int64_t K, int dtype, const void* Ac, const uint8_t* Ai,
+                      double* A)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            A[m * K + k] = 0.0;
+        for (int64_t j = 0; j < K / 4; ++j)
+            for (int t = 0; t < 2; ++t)
+                A[m * K + 4 * j + sp24_pos(Ai, K, m, j, t)] +=
+                    decode_one(dtype, Ac, m * (K / 2) + 2 * j + t);
+    }
+}
+
+int orc_gemm_sp24_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* Ac,
+                      const uint8_t* Ai, const void* B, int relu, double* Y)
+{
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) {
+        free(Ad);
+        free(Bd);
+        return -1;
+    }
+    orc_sp24_densify(M, K, dtype, Ac, Ai, Ad);
+    orc_decode_array(dtype, K * N, B, Bd);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double* yi = Y + i * N;
+        for (int64_t j = 0; j < N; ++j)
+            yi[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = Ad[i * K + k];
+            const double* bk = Bd + k * N;
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] += a * bk[j];
+        }
+        if (relu)
+            for (int64_t j = 0; j < N; ++j)
+                yi[j] = relu_f64(yi[j]);
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* Selected entries, straight from the compressed form (no densified A). */
+void orc_gemm_sp24_entries_f64(int64_t M, int64_t N, int64_t K, int dtype, const void* Ac,
+                               const uint8_t* Ai, const void* B, int relu, int64_t count,
+                               const int64_t* rows, const int64_t* cols, double* out)
+{
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t c = 0; c < count; ++c) {
+        const int64_t i = rows[c], n = cols[c];
+        double s = 0.0;
+        for (int64_t j = 0; j < K / 4; ++j)
+            for (int t = 0; t < 2; ++t) {
+                const int64_t k = 4 * j + sp24_pos(Ai, K, i, j, t);
+                s += decode_one(dtype, Ac, i * (K / 2) + 2 * j + t) * decode_one(dtype, B, k * N + n);
+            }
+        out[c] = relu ? relu_f64(s) : s;
     }
 }
 

@@ -21,7 +21,12 @@ What pins what:
   * MX-format GEMM: row sums, one-hot activations and weights (nibble order,
     E4M3 row stride, both k/32 scale indexes), NaN scales and codes, and exact
     rational brute force on operands decoded here (golden E2M1 table, torch
-    E4M3, powers of two).
+    E4M3, powers of two);
+  * 2:4 sparse GEMM: a dense 2:4 matrix compressed here (values and position
+    nibbles) must give the exact rational product of the dense matrix, in
+    both the full and the entry-by-entry oracle; one-hot kept values pin the
+    group stride, the value order and the nibble order; a repeated position
+    must add both values.
 """
 
 from __future__ import annotations
@@ -636,6 +641,104 @@ def check_mx_random_vs_decoded(orc):
 
 
 # ---------------------------------------------------------------------------
+# 2:4 structured-sparse GEMM.
+# ---------------------------------------------------------------------------
+
+def compress_sp24_here(A):
+    """Dense [M, K] with at most two nonzeros per group of 4 k -> values
+    [M, K/2] (float64) and metadata [M, K/8]: group j keeps (v0 at p0, v1 at
+    p1), p0 < p1, the nibble p0 | p1 << 2 in byte j // 2 at bit 4 (j % 2).
+    Groups with fewer nonzeros fill the remaining slots with zero values at
+    unused positions."""
+    A = np.asarray(A, dtype=np.float64)
+    M, K = A.shape
+    vals = np.zeros((M, K // 2))
+    meta = np.zeros((M, K // 8), dtype=np.uint8)
+    for m in range(M):
+        for j in range(K // 4):
+            g = A[m, 4 * j:4 * j + 4]
+            pos = [p for p in range(4) if g[p] != 0]
+            assert len(pos) <= 2, "not 2:4 sparse"
+            for p in range(4):
+                if len(pos) == 2:
+                    break
+                if p not in pos:
+                    pos.append(p)
+            p0, p1 = sorted(pos)
+            vals[m, 2 * j], vals[m, 2 * j + 1] = g[p0], g[p1]
+            meta[m, j // 2] |= (p0 | (p1 << 2)) << (4 * (j % 2))
+    return vals, meta
+
+
+def _sp24_both(orc, Ac, Ai, B, dtype, relu=False):
+    Y = orc.gemm_sp24_f64(Ac, Ai, B, dtype, relu)
+    M, N = Y.shape
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Ye = orc.gemm_sp24_entries_f64(Ac, Ai, B, dtype, rr.ravel(), cc.ravel(), relu).reshape(M, N)
+    return Y, Ye
+
+
+def _random_sp24_dense(r, M, K, lo=-4, hi=4):
+    A = np.zeros((M, K))
+    for m in range(M):
+        for j in range(K // 4):
+            for p in r.choice(4, size=2, replace=False):
+                A[m, 4 * j + p] = r.integers(lo, hi + 1) + 0.5 * r.integers(0, 2)
+    return A
+
+
+def check_sp24_brute_force(orc):
+    r = np.random.Generator(np.random.PCG64(51))
+    for dtype, (M, N, K) in ((BF16, (5, 7, 32)), (F16, (3, 9, 48)), (F32, (4, 6, 24))):
+        A = _random_sp24_dense(r, M, K)
+        B = r.integers(-4, 5, size=(K, N)).astype(np.float64) * 0.25
+        vals, meta = compress_sp24_here(A)
+        Ac, Bs = storage_of(vals, dtype), storage_of(B, dtype)
+        assert _same(orc.sp24_densify(Ac, meta, dtype) + 0.0, A + 0.0), dtype
+        ex = exact_product(A, B)
+        for relu in (False, True):
+            for Y in _sp24_both(orc, Ac, meta, Bs, dtype, relu):
+                for i in range(M):
+                    for j in range(N):
+                        want = max(ex[i][j], Fraction(0)) if relu else ex[i][j]
+                        assert Fraction(float(Y[i, j])) == want, (dtype, relu, i, j)
+
+
+def check_sp24_one_hot(orc):
+    # one kept value: Y[m0] = v * B[4 j + p], other rows zero
+    r = np.random.Generator(np.random.PCG64(52))
+    M, N, K = 3, 5, 32
+    B = r.integers(-8, 9, size=(K, N)).astype(np.float64)
+    Bs = storage_of(B, BF16)
+    for (m0, j, t, p, v) in ((0, 0, 0, 0, 1.5), (1, 1, 1, 3, -2.0), (2, 6, 0, 2, 3.0),
+                             (1, 7, 1, 1, 0.5), (0, 5, 1, 2, -1.0)):
+        vals = np.zeros((M, K // 2))
+        meta = np.zeros((M, K // 8), dtype=np.uint8)
+        vals[m0, 2 * j + t] = v
+        other = 0 if p != 0 else 1  # the other slot's position (its value is zero)
+        nib = (p | (other << 2)) if t == 0 else (other | (p << 2))
+        meta[m0, j // 2] = nib << (4 * (j % 2))
+        want = np.zeros((M, N))
+        want[m0] = v * B[4 * j + p]
+        for Y in _sp24_both(orc, storage_of(vals, BF16), meta, Bs, BF16):
+            assert _same(Y + 0.0, want + 0.0), (m0, j, t, p)
+
+
+def check_sp24_repeated_position(orc):
+    # both values of a group at one position: that element of A is their sum
+    M, N, K = 2, 3, 16
+    B = np.arange(K * N, dtype=np.float64).reshape(K, N) - 20.0
+    vals = np.zeros((M, K // 2))
+    meta = np.zeros((M, K // 8), dtype=np.uint8)
+    vals[1, 2 * 3], vals[1, 2 * 3 + 1] = 2.0, 5.0  # group 3, both at position 1
+    meta[1, 1] = (1 | (1 << 2)) << 4
+    want = np.zeros((M, N))
+    want[1] = 7.0 * B[4 * 3 + 1]
+    for Y in _sp24_both(orc, storage_of(vals, F32), meta, storage_of(B, F32), F32):
+        assert _same(Y + 0.0, want + 0.0)
+
+
+# ---------------------------------------------------------------------------
 # Operands stored transposed (C = op(A) op(B)).
 # ---------------------------------------------------------------------------
 
@@ -705,4 +808,5 @@ ALL_CHECKS = [
     check_dequant_group_scales, check_dequant_random_vs_decoded, check_layout_textbook_2x2,
     check_layout_brute_force, check_layout_rank_one, check_e4m3_points, check_e4m3_vs_torch,
     check_mx_row_sums, check_mx_one_hot, check_mx_nan, check_mx_random_vs_decoded,
+    check_sp24_brute_force, check_sp24_one_hot, check_sp24_repeated_position,
 ]

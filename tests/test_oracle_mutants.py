@@ -54,6 +54,19 @@ MUTANTS = [
     ("mx_entries_reversed_k", "s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, k);",
      "s += mx_a_value(fmt, Aq, As, K, i, k) * w4_value(Wq, Ws, K, j, K - 1 - k);", 0),
     ("mx_relu_lost", "yi[j] = relu_f64(yi[j]);", "yi[j] = yi[j];", 2),
+    ("sp24_nibble_order", "(Ai[m * (K / 8) + j / 2] >> (4 * (j % 2)))",
+     "(Ai[m * (K / 8) + j / 2] >> (4 * (1 - j % 2)))", 0),
+    ("sp24_positions_swapped", "return t == 0 ? (nib & 3) : (nib >> 2);",
+     "return t == 0 ? (nib >> 2) : (nib & 3);", 0),
+    ("sp24_group_stride", "A[m * K + 4 * j + sp24_pos(Ai, K, m, j, t)] +=",
+     "A[m * K + 2 * j + sp24_pos(Ai, K, m, j, t)] +=", 0),
+    ("sp24_repeated_overwrites", "A[m * K + 4 * j + sp24_pos(Ai, K, m, j, t)] +=",
+     "A[m * K + 4 * j + sp24_pos(Ai, K, m, j, t)] =", 0),
+    ("sp24_value_index", "decode_one(dtype, Ac, m * (K / 2) + 2 * j + t);",
+     "decode_one(dtype, Ac, m * (K / 2) + 2 * j + (1 - t));", 0),
+    ("sp24_entries_k", "const int64_t k = 4 * j + sp24_pos(Ai, K, i, j, t);",
+     "const int64_t k = 4 * j + t;", 0),
+    ("sp24_relu_lost", "yi[j] = relu_f64(yi[j]);", "yi[j] = yi[j];", 3),
 ]
 
 
