@@ -12,7 +12,8 @@ Printed: ONE JSON line (rank 0) with
   cpu_baseline the C oracle timed on host cores on a bounded row sample,
   workloads   the other workload shapes (fp32 / fp16 GEMMs, the non-divisible
               bf16 GEMM, the 4-bit dequant GEMM and its decode-like probes,
-              the MX-format GEMMs), each timed the same way.
+              the MX-format GEMMs, the 2:4 sparse GEMM), each timed the same
+              way.
 """
 
 from __future__ import annotations
@@ -32,11 +33,14 @@ METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (4096³ bf16/fp32, 1 GPU)
 # fp32 256 FLOP/clk/CU; HBM3E 8 TB/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
                # scaled MFMA: E2M1 x E2M1 at the fp4 rate, E4M3 x E2M1 at the fp8 rate
-               "mx_e2m1": 10066.3, "mx_e4m3": 5033.2}
+               "mx_e2m1": 10066.3, "mx_e4m3": 5033.2,
+               # 2:4 sparse MFMA, dense-equivalent rate (twice the dense bf16/fp16 rate)
+               "sp24_bf16": 5033.2, "sp24_f16": 5033.2}
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_4096_relu"
 OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x8192x8192",
-         "w4_16x8192x8192", "w4_1x8192x8192", "mx_e2m1_8192", "mx_e4m3_8192"]
+         "w4_16x8192x8192", "w4_1x8192x8192", "mx_e2m1_8192", "mx_e4m3_8192",
+         "sp24_bf16_4096_relu"]
 
 
 def load_traffic(workload: str):
@@ -73,6 +77,11 @@ def make_device_inputs(w, dev):
     if w.op == "mx":
         t = tuple(torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws"))
         return inp, t + (torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev),)
+    if w.op == "sp24":
+        Ac = torch.from_numpy(inp["Ac"].view(np.int16)).view(tdt[w.dtype]).to(dev)
+        B = torch.from_numpy(inp["B"].view(np.int16)).view(tdt[w.dtype]).to(dev)
+        Ai = torch.from_numpy(inp["Ai"]).to(dev)
+        return inp, (Ac, Ai, B, torch.empty((w.M, w.N), dtype=tdt[w.dtype], device=dev))
     A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
     Wq = torch.from_numpy(inp["Wq"]).to(dev)
     Ws = torch.from_numpy(inp["Ws"]).to(dev)
@@ -87,6 +96,9 @@ def launcher(w, tensors, stream):
     if w.op == "gemm":
         A, B, C = tensors
         return lambda: binding.gemm(A, B, C=C, epilogue=epi, stream=stream)
+    if w.op == "sp24":
+        Ac, Ai, B, C = tensors
+        return lambda: binding.gemm_sp24(Ac, Ai, B, C=C, epilogue=epi, stream=stream)
     if w.op == "mx":
         Aq, As, Wq, Ws, C = tensors
         return lambda: binding.gemm_mx(w.dtype, Aq, As, Wq, Ws, C=C, epilogue=epi, stream=stream)
@@ -155,6 +167,8 @@ def dtype_name(w):
 
     if w.op == "mx":
         return "mx_" + synth.MX_NAMES[w.dtype]
+    if w.op == "sp24":
+        return "sp24_" + {synth.F16: "f16", synth.BF16: "bf16"}[w.dtype]
     return {synth.F32: "f32", synth.F16: "f16", synth.BF16: "bf16"}[w.dtype]
 
 
@@ -264,7 +278,7 @@ def main():
                 "frac_mfma_peak": round(tf / PEAK_TFLOPS[dn], 4),
                 "gbs_algorithmic": round(gbs, 1),
                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2}[ow.op],
+                "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[ow.op],
                                                ow.M, ow.N, ow.K, ow.dtype)}
             if name in MEMORY_BOUND:
                 workloads[name]["cold"] = time_cold(ow, t, stream)

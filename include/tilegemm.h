@@ -1,7 +1,7 @@
 /*
- * tilegemm — tiled dense GEMM, weight-only 4-bit dequant GEMM and MX-format
- * GEMM for one AMD Instinct MI355X (gfx950), as hand-written HIP kernels
- * behind a C ABI.
+ * tilegemm — tiled dense GEMM, weight-only 4-bit dequant GEMM, MX-format GEMM
+ * and 2:4 structured-sparse GEMM for one AMD Instinct MI355X (gfx950), as
+ * hand-written HIP kernels behind a C ABI.
  *
  * The operation follows the pages' problem statement:
  *   - "TileLang ... 一个高效 GEMM 内核" (mhpq.cn), section 3.2: the caller
@@ -61,7 +61,7 @@ typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
 
 typedef enum { TG_EPI_NONE = 0, TG_EPI_RELU = 1 } tg_epilogue;
 
-typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1, TG_OP_MX = 2 } tg_op;
+typedef enum { TG_OP_GEMM = 0, TG_OP_DEQUANT_W4 = 1, TG_OP_MX = 2, TG_OP_SP24 = 3 } tg_op;
 
 /* Element format of the activations of tg_gemm_mx. */
 typedef enum { TG_MX_E2M1 = 0, TG_MX_E4M3 = 1 } tg_mx_format;
@@ -164,6 +164,30 @@ tg_status tg_gemm_mx(int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt, const 
                      const uint8_t* As, const uint8_t* Wq, const uint8_t* Ws, void* C,
                      tg_epilogue epi, tg_stream_t stream);
 
+/*
+ * 2:4 structured-sparse GEMM: C = epilogue(A x B) with A [M][K] keeping at
+ * most two values in every group of four consecutive k, given compressed
+ * (the 2:4 sparse GEMM of "使用 Tilelang DSL 开发 GPU/CPU/加速器高性能内核",
+ * its monitoring-and-debugging paragraph, which skips the dense work):
+ *   Ac: [M][K/2] of `dtype`: group j (k = 4j .. 4j + 3) of row m keeps
+ *       Ac[m][2j] and Ac[m][2j + 1];
+ *   Ai: uint8 [M][K/8]: group j's positions as the nibble
+ *       (Ai[m][j/2] >> (4 * (j % 2))) & 0xF = p0 | p1 << 2 (p0, p1 in 0..3;
+ *       a repeated position adds both values);
+ *   B : [K][N] row-major of `dtype`; C: [M][N] of `dtype`.
+ *   C[m][n] = sum_j (Ac[m][2j] * B[4j + p0][n] + Ac[m][2j + 1] * B[4j + p1][n]),
+ *   fp32 accumulation on the sparse matrix instruction, one RNE rounding;
+ *   TG_EPI_RELU as for tg_gemm.  The pages give no storage format; this one
+ *   is the library's (two values per group in k order, 4-bit position pairs).
+ * Requirements: dtype TG_F16 or TG_BF16 (else TG_ERR_BAD_DTYPE); K % 32 == 0
+ *   (else TG_ERR_BAD_SHAPE); Ac and B 16-byte aligned, N % 8 == 0, Ai 4-byte
+ *   aligned (else TG_ERR_NO_CONFIG).
+ * Errors: as tg_gemm.
+ */
+tg_status tg_gemm_sp24(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* Ac,
+                       const uint8_t* Ai, const void* B, void* C, tg_epilogue epi,
+                       tg_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* tg_status_str(tg_status s);
 
@@ -171,16 +195,16 @@ const char* tg_status_str(tg_status s);
  * Which compiled kernel configuration the library would launch for this call.
  * Writes a NUL-terminated description (tile sizes, waves, stages, swizzle
  * group, launch grid) into buf[0 .. len-1], truncating if needed.
- * op: TG_OP_GEMM, TG_OP_DEQUANT_W4 (dtype ignored) or TG_OP_MX (dtype
- * carries the tg_mx_format of the activations).
+ * op: TG_OP_GEMM, TG_OP_DEQUANT_W4 (dtype ignored), TG_OP_MX (dtype
+ * carries the tg_mx_format of the activations) or TG_OP_SP24.
  * Errors: TG_ERR_NULL_POINTER (buf NULL or len 0), TG_ERR_BAD_SHAPE,
  *   TG_ERR_BAD_DTYPE, TG_ERR_NO_CONFIG (op unknown).
  */
 tg_status tg_query_config(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, char* buf,
                           size_t len);
 
-/* As tg_query_config, for the operand layouts of tg_gemm_ex (dequant and MX:
- * 0, 0; TG_ERR_BAD_LAYOUT otherwise). */
+/* As tg_query_config, for the operand layouts of tg_gemm_ex (dequant, MX and
+ * sparse: 0, 0; TG_ERR_BAD_LAYOUT otherwise). */
 tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype dtype, int trans_a,
                              int trans_b, char* buf, size_t len);
 
@@ -192,8 +216,8 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
  *   tg_config_count: number of configurations for (op, dtype); 0 if none.
  *   tg_config_name : description of configuration `index` (as tg_query_config).
  *   tg_gemm_config / tg_gemm_ex_config / tg_dequant_gemm_w4_config /
- *     tg_gemm_mx_config: same contract as tg_gemm / tg_gemm_ex /
- *     tg_dequant_gemm_w4 / tg_gemm_mx, launching
+ *     tg_gemm_mx_config / tg_gemm_sp24_config: same contract as tg_gemm /
+ *     tg_gemm_ex / tg_dequant_gemm_w4 / tg_gemm_mx / tg_gemm_sp24, launching
  *     configuration `index`; TG_ERR_NO_CONFIG if `index` is out of range or
  *     the configuration cannot run the call (operand layout, alignment, a K
  *     multiple it needs, or another activation format).
@@ -212,6 +236,9 @@ tg_status tg_dequant_gemm_w4_config(int index, int64_t M, int64_t N, int64_t K, 
 tg_status tg_gemm_mx_config(int index, int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt,
                             const uint8_t* Aq, const uint8_t* As, const uint8_t* Wq,
                             const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream);
+tg_status tg_gemm_sp24_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                              const void* Ac, const uint8_t* Ai, const void* B, void* C,
+                              tg_epilogue epi, tg_stream_t stream);
 
 /*
  * The block-swizzled tile order, for host-side checking.  For a grid of

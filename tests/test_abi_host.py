@@ -180,6 +180,35 @@ def test_mx_argument_errors(lib):
     assert lib.tg_query_config_ex(2, 64, 64, 128, 0, 1, 0, buf, 128) == BADL
 
 
+def test_sp24_argument_errors(lib):
+    g = lib.tg_gemm_sp24
+    # (M, N, K, dtype, Ac, Ai, B, C, epi, stream)
+    assert g(4, 8, 32, 0, PA, PS, PB, PC, 0, None) == DTYPE       # fp32 has no sparse kernel
+    assert g(4, 8, 32, 5, PA, PS, PB, PC, 0, None) == DTYPE
+    assert g(4, 8, 32, 2, PA, PS, PB, PC, 3, None) == EPI
+    assert g(4, 8, 48, 2, PA, PS, PB, PC, 0, None) == SHAPE       # K % 32
+    assert g(-4, 8, 32, 1, PA, PS, PB, PC, 0, None) == SHAPE
+    assert g(4, 8, 32, 2, None, PS, PB, PC, 0, None) == NULLP
+    assert g(4, 8, 32, 2, PA, None, PB, PC, 0, None) == NULLP
+    assert g(4, 8, 32, 2, PA, PS, None, PC, 0, None) == NULLP
+    assert g(4, 8, 32, 2, PA, PS, PB, None, 0, None) == NULLP
+    assert g(4, 8, 32, 2, PA, PS, PB, PB + 64, 0, None) == ALIAS
+    assert g(0, 8, 32, 2, None, None, None, None, 0, None) == OK
+    assert g(4, 8, 32, 2, PA + 8, PS, PB, PC, 0, None) == NOCFG   # unaligned values
+    assert g(4, 12, 32, 2, PA, PS, PB, PC, 0, None) == NOCFG      # N % 8
+    assert g(4, 8, 32, 2, PA, PS + 1, PB, PC, 0, None) == NOCFG   # unaligned metadata
+    c = lib.tg_gemm_sp24_config
+    n = lib.tg_config_count(3, 2)
+    assert n >= 1 and c(n, 4, 8, 32, 2, PA, PS, PB, PC, 0, None) == NOCFG
+    assert c(0, 4, 8, 32, 0, PA, PS, PB, PC, 0, None) == DTYPE
+    buf = ctypes.create_string_buffer(128)
+    assert lib.tg_query_config_ex(3, 4096, 4096, 4096, 2, 0, 0, buf, 128) == OK
+    assert buf.value.decode().startswith("sp24_bf16_")
+    assert lib.tg_query_config_ex(3, 64, 64, 48, 2, 0, 0, buf, 128) == SHAPE
+    assert lib.tg_query_config_ex(3, 64, 64, 64, 0, 0, 0, buf, 128) == DTYPE
+    assert lib.tg_query_config_ex(3, 64, 64, 64, 2, 0, 1, buf, 128) == BADL
+
+
 def test_launch_failure_is_reported(lib, monkeypatch):
     # TG_FAULT=launch makes the launcher report a HIP failure after validation
     # and before any HIP call.
@@ -187,6 +216,7 @@ def test_launch_failure_is_reported(lib, monkeypatch):
     assert lib.tg_gemm(4, 4, 4, 2, PA, PB, PC, 0, None) == HIP
     assert lib.tg_dequant_gemm_w4(4, 4, 64, PA, PB, PS, PC, 0, None) == HIP
     assert lib.tg_gemm_mx(4, 4, 128, 0, PA, PS, PB, PS + 64, PC, 0, None) == HIP
+    assert lib.tg_gemm_sp24(4, 8, 32, 2, PA, PS, PB, PC, 0, None) == HIP
     with pytest.raises(binding.TileGemmError) as ei:
         binding._check(HIP)
     assert ei.value.status == HIP
@@ -213,6 +243,10 @@ def test_config_lists(lib):
         assert len(names) == len(set(names)) and names
         # each list has a narrow (element-load) configuration for unaligned operands
         assert any(n.endswith("_narrow") for n in names)
+    for dt in (1, 2):
+        sp = binding.list_configs(binding.TG_OP_SP24, dt)
+        assert sp and len(sp) == len(set(sp)) and all(n.startswith("sp24_") for n in sp)
+    assert binding.list_configs(binding.TG_OP_SP24, 0) == []
     mx = binding.list_configs(binding.TG_OP_MX)
     assert len(mx) == len(set(mx)) and mx == binding.list_configs(binding.TG_OP_MX, 1)
     assert any(n.startswith("mx_e2m1_") for n in mx) and any(n.startswith("mx_e4m3_") for n in mx)

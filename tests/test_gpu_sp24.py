@@ -1,0 +1,128 @@
+"""GPU parity of the 2:4 structured-sparse GEMM (tg_gemm_sp24) against the CPU
+oracle.
+
+Bars (as for the dense 16-bit GEMM): integer-valued kept values and B give
+sums that are exact in fp32, so the result must equal one round-to-nearest-even
+of the exact sum bit for bit; N(0,1) inputs must satisfy
+|C - Y| <= 1e-2 + 1e-2 |Y| against the unrounded fp64 sum Y.  Full-size shapes
+run in the benchmark's launch configuration and are checked on sampled
+entries the oracle sums one by one from the compressed form.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import BF16, F16, assert_close_16, bits_to_f64, say, sample_entries, to_device, \
+    to_host_bits
+from tiled_dense_gemm_07_amd import binding, synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = [BF16, F16]
+DNAME = {BF16: "bf16", F16: "f16"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+
+
+def run_sp24(Ac, Ai, B, dtype, relu=False, config=None):
+    t = (to_device(Ac, dtype, DEV), torch.from_numpy(np.ascontiguousarray(Ai)).to(DEV),
+         to_device(B, dtype, DEV))
+    Ct = binding.gemm_sp24(*t, epilogue="relu" if relu else None, config=config)
+    torch.cuda.synchronize()
+    return to_host_bits(Ct, dtype)
+
+
+def check(got, Y, dtype, integer):
+    if integer:
+        want = oracle.encode(dtype, Y)
+        diff = got != want
+        assert not diff.any(), "%d of %d entries differ (first at %s)" % (
+            int(diff.sum()), diff.size, np.argwhere(diff)[0].tolist())
+    else:
+        assert_close_16(bits_to_f64(got, dtype), Y)
+
+
+SHAPES = [(1, 8, 32), (5, 24, 64), (33, 104, 96), (130, 72, 160), (257, 264, 128),
+          (300, 136, 512), (64, 520, 1056)]
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+@pytest.mark.parametrize("relu", [False, True], ids=["none", "relu"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_sp24_small(dtype, shape, relu, integer):
+    M, N, K = shape
+    Ac, Ai, B = synth.sp24_inputs(M, N, K, dtype, 2100 + M, 2200 + N, 2300 + K, integer)
+    say("sp24 %s %s relu=%s int=%s" % (DNAME[dtype], shape, relu, integer))
+    got = run_sp24(Ac, Ai, B, dtype, relu)
+    check(got, oracle.gemm_sp24_f64(Ac, Ai, B, dtype, relu), dtype, integer)
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 224), (200, 136, 512), (64, 72, 96)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_sp24_every_config(dtype, shape):
+    """Every configuration, forced, on ragged shapes (K % 64 == 32 included):
+    bit-exact with integer inputs."""
+    M, N, K = shape
+    Ac, Ai, B = synth.sp24_inputs(M, N, K, dtype, 2400, 2401, 2402, integer=True)
+    want = oracle.encode(dtype, oracle.gemm_sp24_f64(Ac, Ai, B, dtype, relu=True))
+    for idx, name in enumerate(binding.list_configs(binding.TG_OP_SP24, dtype)):
+        say("sp24 config %d %s %s" % (idx, name, shape))
+        got = run_sp24(Ac, Ai, B, dtype, relu=True, config=idx)
+        assert np.array_equal(got, want), name
+
+
+def test_sp24_patterns():
+    """Groups with a single nonzero, all-zero groups and a repeated position
+    (both values added), against the oracle's definition: bit-exact."""
+    M, N, K = 96, 72, 128
+    r = np.random.Generator(np.random.PCG64(2500))
+    vals = r.integers(-3, 4, size=(M, K // 2)).astype(np.float32)
+    vals[:, 1::4] = 0.0  # group 2j' with one nonzero value
+    vals[5] = 0.0        # an all-zero row
+    nib = r.integers(0, 16, size=(M, K // 4)).astype(np.uint8)  # any pairs, repeats included
+    Ai = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    Ac = synth.to_storage(vals, BF16)
+    B = synth.to_storage(r.integers(-4, 5, size=(K, N)).astype(np.float32), BF16)
+    say("sp24 patterns")
+    got = run_sp24(Ac, Ai, B, BF16)
+    check(got, oracle.gemm_sp24_f64(Ac, Ai, B, BF16), BF16, True)
+
+
+def test_sp24_zero_k_and_empty():
+    for dt, tdt in ((BF16, torch.bfloat16), (F16, torch.float16)):
+        say("sp24 K=0 %s" % DNAME[dt])
+        e = torch.empty((0,), dtype=tdt, device=DEV)
+        i = torch.empty((0,), dtype=torch.uint8, device=DEV)
+        C = torch.full((4, 8), 3.0, dtype=tdt, device=DEV)
+        binding.gemm_sp24(e.view(4, 0), i.view(4, 0), e.view(0, 8), C=C)
+        torch.cuda.synchronize()
+        assert (C.float() == 0).all()
+        C0 = torch.empty((0, 8), dtype=tdt, device=DEV)
+        binding.gemm_sp24(e.view(0, 0), i.view(0, 0), e.view(0, 8), C=C0)
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
+def test_sp24_workload(integer):
+    """The full-size benchmark workload in its launch configuration, sampled."""
+    w = synth.WORKLOADS["sp24_bf16_4096_relu"]
+    inp = synth.make_inputs(w, integer)
+    say("sp24 workload int=%s seeds=%s" % (integer, inp["seeds"]))
+    got = run_sp24(inp["Ac"], inp["Ai"], inp["B"], w.dtype, w.relu).reshape(w.M, w.N)
+    rows, cols = sample_entries(w.M, w.N, 2000, seed=w.index * 7 + integer)
+    Y = oracle.gemm_sp24_entries_f64(inp["Ac"], inp["Ai"], inp["B"], w.dtype, rows, cols, w.relu)
+    check(got[rows, cols], Y, w.dtype, integer)
+    vals = bits_to_f64(got, w.dtype)
+    assert (vals >= 0).all() and not np.signbit(vals).any() and np.isfinite(vals).all()

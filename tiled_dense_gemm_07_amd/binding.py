@@ -21,14 +21,14 @@ _DEFAULT_LIB = os.path.join(HERE, "libtilegemm.so")
 
 TG_F32, TG_F16, TG_BF16 = 0, 1, 2
 TG_EPI_NONE, TG_EPI_RELU = 0, 1
-TG_OP_GEMM, TG_OP_DEQUANT_W4, TG_OP_MX = 0, 1, 2
+TG_OP_GEMM, TG_OP_DEQUANT_W4, TG_OP_MX, TG_OP_SP24 = 0, 1, 2, 3
 TG_MX_E2M1, TG_MX_E4M3 = 0, 1
 
 # exported symbols, as declared in include/tilegemm.h
 EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_query_config",
            "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
            "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
-           "tg_gemm_mx_config")
+           "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config")
 
 _lib = None
 
@@ -84,6 +84,10 @@ def load_library():
     lib.tg_gemm_mx.restype = c_int
     lib.tg_gemm_mx_config.argtypes = [c_int, i64, i64, i64, c_int, p, p, p, p, p, c_int, p]
     lib.tg_gemm_mx_config.restype = c_int
+    lib.tg_gemm_sp24.argtypes = [i64, i64, i64, c_int, p, p, p, p, c_int, p]
+    lib.tg_gemm_sp24.restype = c_int
+    lib.tg_gemm_sp24_config.argtypes = [c_int, i64, i64, i64, c_int, p, p, p, p, c_int, p]
+    lib.tg_gemm_sp24_config.restype = c_int
     _lib = lib
     return lib
 
@@ -289,6 +293,36 @@ def gemm_mx(fmt: int, Aq, As, Wq, Ws, C=None, epilogue=None, stream=None, config
             C.data_ptr(), _epi_code(epilogue), _stream_ptr(Aq.device, stream))
     lib = load_library()
     _check(lib.tg_gemm_mx(*args) if config is None else lib.tg_gemm_mx_config(config, *args))
+    return C
+
+
+def gemm_sp24(Ac, Ai, B, C=None, epilogue=None, stream=None, config=None):
+    """C = epilogue(A @ B) with A 2:4 sparse along K, given as kept values Ac
+    [M, K/2] (fp16 or bf16) and position nibbles Ai [M, K/8] (uint8); B [K, N]
+    of Ac's dtype.  `config` forces a compiled configuration by index."""
+    import torch
+
+    for name, t in (("Ac", Ac), ("Ai", Ai), ("B", B)):
+        _require_gpu_tensor(name, t)
+    if Ac.dtype not in (torch.float16, torch.bfloat16) or B.dtype != Ac.dtype:
+        raise TypeError("Ac and B must both be float16 or both bfloat16")
+    if Ai.dtype != torch.uint8:
+        raise TypeError("Ai must be uint8")
+    M, half = Ac.shape
+    K = 2 * half
+    K2, N = B.shape
+    if K != K2 or tuple(Ai.shape) != (M, K // 8) or K % 8:
+        raise ValueError("expected Ac [M, K/2], Ai [M, K/8], B [K, N]")
+    if C is None:
+        C = torch.empty((M, N), dtype=Ac.dtype, device=Ac.device)
+    else:
+        _require_gpu_tensor("C", C)
+        if tuple(C.shape) != (M, N) or C.dtype != Ac.dtype:
+            raise ValueError("C must be [M, N] of Ac's dtype")
+    args = (M, N, K, _dtype_code(Ac), Ac.data_ptr(), Ai.data_ptr(), B.data_ptr(),
+            C.data_ptr(), _epi_code(epilogue), _stream_ptr(Ac.device, stream))
+    lib = load_library()
+    _check(lib.tg_gemm_sp24(*args) if config is None else lib.tg_gemm_sp24_config(config, *args))
     return C
 
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilegemm.so")
 SOURCES = ["tg_api.hip", "tg_gemm_f32.hip", "tg_gemm_f16.hip", "tg_gemm_bf16.hip",
-           "tg_dequant_w4.hip", "tg_gemm_mx.hip"]
+           "tg_dequant_w4.hip", "tg_gemm_mx.hip", "tg_gemm_sp24.hip"]
 # measurement-only probe (sustained clock of the matrix cores); its own library
 PROBE_LIB = os.path.join(HERE, "libtgprobe.so")
 PROBE_SOURCES = ["tg_probe.hip"]

@@ -44,6 +44,8 @@ ConfigList list_for(int op, int dtype)
         return tg::configs_dequant_w4();
     } else if (op == TG_OP_MX) {
         return tg::configs_mx();  // both activation formats
+    } else if (op == TG_OP_SP24) {
+        return tg::configs_sp24(dtype);
     }
     return ConfigList{nullptr, 0};
 }
@@ -54,8 +56,9 @@ void config_name(const Config& c, char* buf, size_t len)
     static const char* mxn[] = {"e2m1", "e4m3"};
     static const char* lay[] = {"", "_nt", "_tn", "_tt"};  // A^T-stored / B^T-stored
     const bool mx = c.op == TG_OP_MX;
-    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s",
-             c.op == 0 ? "gemm" : (mx ? "mx" : "w4"), mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
+    static const char* opn[] = {"gemm", "w4", "mx", "sp24"};
+    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s", opn[c.op],
+             mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
              c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
              mx ? (c.chunked_scales ? "_sc8" : "") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
@@ -90,6 +93,10 @@ const Pref kPrefs[] = {
     {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g8_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma_sc8",
             "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr}},
     {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g8_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
+            nullptr}},
+    {3, 2, {"sp24_bf16_256x128x64_w2x2_s3_g4_dma", "sp24_bf16_128x128x64_w2x2_s3_g8_dma", nullptr,
+            nullptr}},
+    {3, 1, {"sp24_f16_256x128x64_w2x2_s3_g4_dma", "sp24_f16_128x128x64_w2x2_s3_g8_dma", nullptr,
             nullptr}},
 };
 
@@ -128,6 +135,9 @@ bool usable(const Config& c, const Call& q)
             return false;
         return c.dtype == q.dtype && q.wide && q.ws4 && q.K % c.bk == 0;
     }
+    if (c.op == TG_OP_SP24)
+        // whole 32-k groups of metadata dwords; 16-byte copies of values and B
+        return c.dtype == q.dtype && q.wide && q.ws4 && q.K % 32 == 0;
     if (c.ta != q.ta || c.tb != q.tb)
         return false;  // operand layouts are compiled in
     if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
@@ -390,6 +400,47 @@ tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     return launch(*c, p, (hipStream_t)stream);
 }
 
+tg_status sp24_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
+                    tg_dtype dtype, const void* Ac, const uint8_t* Ai, const void* B, void* C,
+                    tg_epilogue epi, tg_stream_t stream)
+{
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    if (epi != TG_EPI_NONE && epi != TG_EPI_RELU)
+        return TG_ERR_BAD_EPILOGUE;
+    tg_status s = check_shape(M, N, K, 2);
+    if (s != TG_OK)
+        return s;
+    if (K % 32 != 0)
+        return TG_ERR_BAD_SHAPE;
+    if (forced_index >= 0 && !forced)
+        return TG_ERR_NO_CONFIG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (!C || (K > 0 && (!Ac || !Ai || !B)))
+        return TG_ERR_NULL_POINTER;
+    const size_t cbytes = (size_t)(M * N * 2);
+    if (overlaps(C, cbytes, Ac, (size_t)(M * K)) || overlaps(C, cbytes, Ai, (size_t)(M * K / 8)) ||
+        overlaps(C, cbytes, B, (size_t)(K * N * 2)))
+        return TG_ERR_ALIAS;
+    Call q{TG_OP_SP24, dtype, M, N, K, aligned16(Ac) && aligned16(B) && N % 8 == 0,
+           ((uintptr_t)Ai & 3u) == 0, false, false};
+    const Config* c = forced ? forced : select_config(q);
+    if (!c || !usable(*c, q))
+        return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
+    tg::GemmParams p{};
+    p.A = Ac;
+    p.As = Ai;
+    p.B = B;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.relu = epi == TG_EPI_RELU;
+    p.c_vec = 0;
+    return launch(*c, p, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -417,6 +468,13 @@ tg_status tg_gemm_mx(int64_t M, int64_t N, int64_t K, tg_mx_format a_fmt, const 
                      tg_epilogue epi, tg_stream_t stream)
 {
     return mx_impl(nullptr, -1, M, N, K, a_fmt, Aq, As, Wq, Ws, C, epi, stream);
+}
+
+tg_status tg_gemm_sp24(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* Ac,
+                       const uint8_t* Ai, const void* B, void* C, tg_epilogue epi,
+                       tg_stream_t stream)
+{
+    return sp24_impl(nullptr, -1, M, N, K, dtype, Ac, Ai, B, C, epi, stream);
 }
 
 const char* tg_status_str(tg_status s)
@@ -451,8 +509,10 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
 {
     if (!buf || len == 0)
         return TG_ERR_NULL_POINTER;
-    if (op != TG_OP_GEMM && op != TG_OP_DEQUANT_W4 && op != TG_OP_MX)
+    if (op != TG_OP_GEMM && op != TG_OP_DEQUANT_W4 && op != TG_OP_MX && op != TG_OP_SP24)
         return TG_ERR_NO_CONFIG;
+    if (op == TG_OP_SP24 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
     if (op == TG_OP_GEMM && dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
         return TG_ERR_BAD_DTYPE;
     if (op == TG_OP_MX && (int)dtype != TG_MX_E2M1 && (int)dtype != TG_MX_E4M3)
@@ -464,13 +524,15 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
     tg_status s = check_shape(M, N, K, op == TG_OP_MX ? 1 : esize_of(dt));
     if (s != TG_OK)
         return s;
-    if ((op == TG_OP_DEQUANT_W4 && K % 32 != 0) || (op == TG_OP_MX && K % 128 != 0))
+    if ((op == TG_OP_DEQUANT_W4 && K % 32 != 0) || (op == TG_OP_MX && K % 128 != 0) ||
+        (op == TG_OP_SP24 && K % 32 != 0))
         return TG_ERR_BAD_SHAPE;
     // assume aligned operands (what torch allocations give)
     const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
     Call q{op, dt, M, N, K, false, true, trans_a != 0, trans_b != 0};
     q.ws16 = true;
-    q.wide = op != TG_OP_GEMM || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0);
+    q.wide = op == TG_OP_SP24 ? N % 8 == 0
+                              : (op != TG_OP_GEMM || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0));
     const Config* c = select_config(q);
     if (!c)
         return TG_ERR_NO_CONFIG;
@@ -542,6 +604,17 @@ tg_status tg_gemm_mx_config(int index, int64_t M, int64_t N, int64_t K, tg_mx_fo
     ConfigList L = list_for(TG_OP_MX, 0);
     const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
     return mx_impl(c, index < 0 ? 0 : index, M, N, K, a_fmt, Aq, As, Wq, Ws, C, epi, stream);
+}
+
+tg_status tg_gemm_sp24_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                              const void* Ac, const uint8_t* Ai, const void* B, void* C,
+                              tg_epilogue epi, tg_stream_t stream)
+{
+    if (dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    ConfigList L = list_for(TG_OP_SP24, dtype);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    return sp24_impl(c, index < 0 ? 0 : index, M, N, K, dtype, Ac, Ai, B, C, epi, stream);
 }
 
 tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,

@@ -7,7 +7,7 @@
 namespace tg {
 
 struct Config {
-    int op;     // 0 = GEMM, 1 = 4-bit dequant GEMM, 2 = MX-format GEMM
+    int op;     // 0 = GEMM, 1 = 4-bit dequant GEMM, 2 = MX-format GEMM, 3 = 2:4 sparse GEMM
     int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (MX: activation format, 0 = E2M1, 1 = E4M3)
     int bm, bn, bk;
     int wgm, wgn;  // waves along M and N (64 threads each)
@@ -32,6 +32,7 @@ ConfigList configs_gemm_f16();
 ConfigList configs_gemm_bf16();
 ConfigList configs_dequant_w4();
 ConfigList configs_mx();
+ConfigList configs_sp24(int dtype);
 
 }  // namespace tg
 

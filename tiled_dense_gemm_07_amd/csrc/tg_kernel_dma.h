@@ -121,7 +121,8 @@ struct DmaOperand {
 
     struct Lane {
         u32 off[J];   // copy offsets within a strip (out of range past the x extent)
-        int kk[J];    // k (within the strip) of the data each copy lane moves
+        int kk[KMAJ ? J : 1];  // KMAJ: k (within the strip) of the data each copy lane moves
+        int lr;       // x-contiguous: the lane's k row within a copy (k = copy row + lr)
         u32 rd[KMAJ ? SL : FX];  // fragment read offsets (stage 0)
     };
     struct Frag {
@@ -144,10 +145,10 @@ struct DmaOperand {
                 L.off[j] = (x0 + row < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
             } else {
                 const int c = (lane % LPR) ^ swz_b(row);
-                L.kk[j] = row;
                 L.off[j] = (x0 + c * 8 < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
             }
         }
+        L.lr = lane / LPR;
         if constexpr (KMAJ) {
 #pragma unroll
             for (int s = 0; s < SL; ++s) {
@@ -183,7 +184,8 @@ struct DmaOperand {
     static __device__ __forceinline__ void copy(const Lane& L, __amdgpu_buffer_rsrc_t rs, int krem,
                                                 int d, int w, u32 region_lds)
     {
-        dma16(region_lds + ST * STAGE + (w * J + d) * 1024, L.kk[d] < krem ? L.off[d] : kOob, rs);
+        const int kk = KMAJ ? L.kk[KMAJ ? d : 0] : (w * J + d) * RPB + L.lr;
+        dma16(region_lds + ST * STAGE + (w * J + d) * 1024, kk < krem ? L.off[d] : kOob, rs);
     }
 
     // LDS read i (0 .. NRD-1) of slab S of stage ST.
@@ -208,6 +210,104 @@ struct DmaOperand {
             return __builtin_shufflevector(F.t[f][0], F.t[f][1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
+
+// Coalesced store of one wave's WTM x WTN result tile (FM x FN blocks of
+// 32 x 32 fp32, the MFMA layout where lane l holds row l % 32 and, for
+// element 4 q + e, column 8 q + 4 (l / 32) + e of its block).  The tile is
+// rounded (after ReLU) into the wave's own LDS region `st` as rows of 2 WTN
+// bytes with 16-byte chunk c of row r at position c ^ (r % CH) (CH chunks per
+// row; writes then spread over the banks), and written back to C as 16-byte
+// pieces, CH lanes per row: whole 2 WTN-byte runs of a row instead of 16-byte
+// pieces of 32 rows.  Needs N % 8 == 0 and a 16-byte aligned C (else the
+// caller stores directly); the caller has synchronised so that no wave still
+// reads or copies into LDS.
+template <int DT, int WTM, int WTN, int FM, int FN>
+__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
+                                                  const GemmParams& p, int mw0, int nw0,
+                                                  int lane, lds_char* st)
+{
+    constexpr int ROWB = WTN * 2;
+    constexpr int CH = ROWB / 16;
+    static_assert(CH >= 4 && CH <= 64 && (CH & (CH - 1)) == 0, "rows of 64 to 1024 bytes");
+    const int lr = lane & 31;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int r = fm * 32 + lr;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = acc[fm][fn][4 * q + e];
+                    v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
+                }
+                const int c = 4 * fn + q;
+                typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+                *(lds_u32x2*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4) + 8 * g) =
+                    u32x2{pack2(v[0], v[1], DT), pack2(v[2], v[3], DT)};
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
+    constexpr int RPI = 64 / CH;  // rows per store instruction
+    const int c = lane % CH;
+    const int n = nw0 + 8 * c;
+    uint16_t* C = (uint16_t*)p.C;
+#pragma unroll 4
+    for (int r0 = 0; r0 < WTM; r0 += RPI) {
+        const int r = r0 + lane / CH;
+        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+        const int m = mw0 + r;
+        if (m < p.M && n < p.N)
+            *(u32x4*)(C + (int64_t)m * p.N + n) = v;
+    }
+}
+
+// As store_tile_staged, for result blocks in the other MFMA orientation: lane
+// l holds column l % 32 and, for element r, row 8 (r / 4) + 4 (l / 32) + r % 4
+// of its block (the first MFMA operand supplied the rows).
+template <int DT, int WTM, int WTN, int FM, int FN>
+__device__ __forceinline__ void store_tile_staged_t(const f32x16 (&acc)[FM][FN],
+                                                    const GemmParams& p, int mw0, int nw0,
+                                                    int lane, lds_char* st)
+{
+    constexpr int ROWB = WTN * 2;
+    constexpr int CH = ROWB / 16;
+    static_assert(CH >= 4 && CH <= 64 && (CH & (CH - 1)) == 0, "rows of 64 to 1024 bytes");
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    const int lc = lane & 31;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int col = fn * 32 + lc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = fm * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const float x = acc[fm][fn][r];
+                *(lds_u16*)(st + row * ROWB + (((col >> 3) ^ (row & (CH - 1))) << 4) +
+                            (col & 7) * 2) = cvt1((p.relu && !(x > 0.0f)) ? 0.0f : x, DT);
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
+    constexpr int RPI = 64 / CH;
+    const int c = lane % CH;
+    const int n = nw0 + 8 * c;
+    uint16_t* C = (uint16_t*)p.C;
+#pragma unroll 4
+    for (int r0 = 0; r0 < WTM; r0 += RPI) {
+        const int r = r0 + lane / CH;
+        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+        const int m = mw0 + r;
+        if (m < p.M && n < p.N)
+            *(u32x4*)(C + (int64_t)m * p.N + n) = v;
+    }
+}
 
 // TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].  BK: k per
 // strip (32 or 64); NS: LDS stages (2 .. 5).
@@ -530,7 +630,14 @@ struct DmaGemm {
         }
         // drain the copies of the strips past the end (all out of range)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        epilogue(acc, p, m0, n0, wm, wn, lane);
+        if ((p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0 &&
+            NW * WTM * WTN * 2 <= LDS_BYTES) {
+            wait_all_barrier();  // every wave's copies landed and reads done
+            store_tile_staged<DT, WTM, WTN, FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                                   sm + w * (WTM * WTN * 2));
+        } else {
+            epilogue(acc, p, m0, n0, wm, wn, lane);
+        }
     }
 };
 

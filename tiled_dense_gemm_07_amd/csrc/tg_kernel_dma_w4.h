@@ -321,6 +321,12 @@ struct DmaW4 {
             main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
         }
+        if ((p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0 && NW * WTM * WTN * 2 <= LDS_BYTES) {
+            wait_all_barrier();  // every wave's copies landed and reads done
+            store_tile_staged<DT_BF16, WTM, WTN, FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN,
+                                                        lane, sm + w * (WTM * WTN * 2));
+            return;
+        }
         // epilogue: same lane layout as the 16-bit DMA kernel (m = lane % 32,
         // four consecutive n per accumulator quad)
         const int lr = lane & 31;

@@ -501,6 +501,12 @@ struct DmaMx {
             main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
         }
+        if ((p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0 && NW * WTM * WTN * 2 <= LDS_BYTES) {
+            wait_all_barrier();  // every wave's copies landed and reads done
+            store_tile_staged<DT_BF16, WTM, WTN, FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN,
+                                                        lane, sm + w * (WTM * WTN * 2));
+            return;
+        }
         // epilogue: m = lane % 32, four consecutive n per accumulator quad
         const int lr = lane & 31;
         const int g = lane >> 5;

@@ -57,6 +57,11 @@ def sweep_shape(op: int, dtype: int, M: int, N: int, K: int, relu: bool, done: s
         A = torch.randn((M, K), generator=g, device=dev).to(tdt[dtype])
         B = torch.randn((K, N), generator=g, device=dev).to(tdt[dtype])
         C = torch.empty((M, N), dtype=tdt[dtype], device=dev)
+    elif op == binding.TG_OP_SP24:
+        A = torch.randn((M, K // 2), generator=g, device=dev).to(tdt[dtype])
+        As = torch.randint(0, 256, (M, K // 8), generator=g, device=dev, dtype=torch.uint8)
+        B = torch.randn((K, N), generator=g, device=dev).to(tdt[dtype])
+        C = torch.empty((M, N), dtype=tdt[dtype], device=dev)
     elif op == binding.TG_OP_MX:
         # dtype carries the activation format; codes uniform, scales 2^-4 .. 2^0
         kq = K // 2 if dtype == binding.TG_MX_E2M1 else K
@@ -84,16 +89,22 @@ def sweep_shape(op: int, dtype: int, M: int, N: int, K: int, relu: bool, done: s
         elif op == binding.TG_OP_MX:
             fn = lambda: binding.gemm_mx(dtype, A, As, Wq, Ws, C=C, epilogue=epi, stream=stream,
                                          config=idx)
+        elif op == binding.TG_OP_SP24:
+            fn = lambda: binding.gemm_sp24(A, As, B, C=C, epilogue=epi, stream=stream, config=idx)
         else:
             fn = lambda: binding.dequant_gemm_w4_with_config(idx, A, Wq, Ws, C=C, epilogue=epi,
                                                              stream=stream)
+        try:
+            fn()
+        except binding.TileGemmError:
+            continue  # not for this call (operand layout, alignment, K multiple)
         ms = time_config(fn, stream)
         rec = {"op": op, "dtype": dtype, "M": M, "N": N, "K": K, "config": name, "ms": ms,
                "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
         log.write(json.dumps(rec) + "\n")
         log.flush()
         print("sweep %s %dx%dx%d %-40s %8.4f ms %8.1f TFLOP/s" % (
-            ("gemm", "w4", "mx")[op], M, N, K, name, ms, rec["tflops"]), flush=True)
+            ("gemm", "w4", "mx", "sp24")[op], M, N, K, name, ms, rec["tflops"]), flush=True)
     del A, C
     torch.cuda.empty_cache()
 
@@ -139,8 +150,8 @@ def main(argv=None):
     shapes = []
     if args.shapes == "workloads":
         for w in synth.WORKLOADS.values():
-            shapes.append(({"gemm": 0, "dequant_w4": 1, "mx": 2}[w.op], w.dtype, w.M, w.N, w.K,
-                           w.relu))
+            shapes.append(({"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[w.op], w.dtype, w.M,
+                           w.N, w.K, w.relu))
     elif args.shapes:
         for item in args.shapes.split(","):
             parts = item.split(":")

@@ -15,7 +15,9 @@ page), so every workload here is synthetic:
 * 4-bit weights: uniform bytes (so both nibbles are uniform on 0..15),
   E8M0 scale bytes 127 + uniform{-4..0}, i.e. scales 2^-4 .. 2^0;
 * MX-format activations: E2M1 as the weights; E4M3 codes uniform over the 254
-  non-NaN bytes; E8M0 scale bytes as for the weights.
+  non-NaN bytes; E8M0 scale bytes as for the weights;
+* 2:4 sparse A: kept values drawn as the floating (or integer) inputs, the
+  two kept positions of every group of 4 k uniform over the 6 pairs.
 
 Seeds: ``20260000 + 100 * workload_index + {0: A, 1: B, 2: codes, 3: scales,
 4: activation scales}``,
@@ -103,13 +105,34 @@ def mx_inputs(fmt: int, M: int, N: int, K: int, seed_a: int, seed_as: int, seed_
     return Aq, w4_scales(M, K, seed_as), w4_codes(N, K, seed_codes), w4_scales(N, K, seed_scales)
 
 
+SP24_PAIRS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))
+
+
+def sp24_meta(M: int, K: int, seed: int) -> np.ndarray:
+    """Position nibbles [M, K/8]: group j's pair (p0, p1), uniform over the 6
+    pairs, stored as p0 | p1 << 2 in byte j // 2 (low nibble for even j)."""
+    pick = rng(seed).integers(0, 6, size=(M, K // 4))
+    nib = np.array([p0 | (p1 << 2) for p0, p1 in SP24_PAIRS], dtype=np.uint8)[pick]
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def sp24_inputs(M: int, N: int, K: int, dtype: int, seed_a: int, seed_meta: int, seed_b: int,
+                integer: bool = False):
+    """Kept values Ac [M, K/2] and B [K, N] as storage words, position nibbles
+    Ai [M, K/8]."""
+    draw = integers_f32 if integer else normal_f32
+    Ac = to_storage(draw((M, K // 2), seed_a), dtype)
+    B = to_storage(draw((K, N), seed_b), dtype)
+    return Ac, sp24_meta(M, K, seed_meta), B
+
+
 @dataclass(frozen=True)
 class Workload:
     """One of the workload shapes; `index` keys the seeds."""
 
     name: str
     index: int
-    op: str  # "gemm", "dequant_w4" or "mx"
+    op: str  # "gemm", "dequant_w4", "mx" or "sp24"
     dtype: int  # operand type; for "mx" the activation format (MX_E2M1 / MX_E4M3)
     M: int
     N: int
@@ -125,6 +148,8 @@ class Workload:
         if self.op == "gemm":
             es = 4 if self.dtype == F32 else 2
             return es * (self.M * self.K + self.K * self.N + self.M * self.N)
+        if self.op == "sp24":
+            return 2 * (self.M * self.K // 2 + self.K * self.N + self.M * self.N) + self.M * self.K // 8
         if self.op == "mx":
             a = self.M * self.K // 2 if self.dtype == MX_E2M1 else self.M * self.K
             return (a + self.M * self.K // 32 + self.N * self.K // 2 + self.N * self.K // 32
@@ -147,6 +172,9 @@ WORKLOADS = {
     # the same weight format with block-format activations on the scaled MFMA
     "mx_e2m1_8192": Workload("mx_e2m1_8192", 8, "mx", MX_E2M1, 8192, 8192, 8192, False),
     "mx_e4m3_8192": Workload("mx_e4m3_8192", 9, "mx", MX_E4M3, 8192, 8192, 8192, False),
+    # 2:4 structured-sparse A (the flops are the dense-equivalent 2 M N K)
+    "sp24_bf16_4096_relu": Workload("sp24_bf16_4096_relu", 10, "sp24", BF16, 4096, 4096, 4096,
+                                    True),
 }
 
 
@@ -182,5 +210,8 @@ def make_inputs(w: Workload, integer: bool = False) -> dict:
         Aq, As, Wq, Ws = mx_inputs(w.dtype, w.M, w.N, w.K, s["A"], s["a_scales"], s["codes"],
                                    s["scales"])
         return {"Aq": Aq, "As": As, "Wq": Wq, "Ws": Ws, "seeds": s}
+    if w.op == "sp24":
+        Ac, Ai, B = sp24_inputs(w.M, w.N, w.K, w.dtype, s["A"], s["codes"], s["B"], integer)
+        return {"Ac": Ac, "Ai": Ai, "B": B, "seeds": s}
     A, Wq, Ws = dequant_inputs(w.M, w.N, w.K, s["A"], s["codes"], s["scales"], integer)
     return {"A": A, "Wq": Wq, "Ws": Ws, "seeds": s}

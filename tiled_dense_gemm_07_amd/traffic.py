@@ -41,12 +41,16 @@ _FAMILY_SOURCES = {
     "gemv": ["tg_kernel_gemv_w4.h", "tg_kernel.h"],
     "tiled": ["tg_kernel.h", "tg_sched.h"],
     "mx": ["tg_kernel_mx.h", "tg_kernel_dma_w4.h", "tg_kernel_dma.h", "tg_kernel.h", "tg_sched.h"],
+    "sp24": ["tg_kernel_sp24.h", "tg_kernel_dma_w4.h", "tg_kernel_dma.h", "tg_kernel.h",
+             "tg_sched.h"],
 }
 
 
 def kernel_family(config: str) -> str:
     if config.startswith("mx_"):
         return "mx"
+    if config.startswith("sp24_"):
+        return "sp24"
     if config.startswith("w4_") and "_dma" in config:
         return "dma_w4"
     if "_dma" in config:
@@ -71,7 +75,7 @@ def workload_config(workload: str) -> str:
     from . import binding, synth
 
     w = synth.WORKLOADS[workload]
-    op = {"gemm": 0, "dequant_w4": 1, "mx": 2}[w.op]
+    op = {"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[w.op]
     return binding.query_config(op, w.M, w.N, w.K, w.dtype).split()[0]
 
 
@@ -106,6 +110,13 @@ def run(workload: str, launches: int) -> None:
         t = [torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws")]
         for _ in range(launches):
             binding.gemm_mx(w.dtype, *t, epilogue=epi)
+    elif w.op == "sp24":
+        tdt = {synth.F16: torch.float16, synth.BF16: torch.bfloat16}[w.dtype]
+        Ac = torch.from_numpy(inp["Ac"].view(np.int16)).view(tdt).to(dev)
+        B = torch.from_numpy(inp["B"].view(np.int16)).view(tdt).to(dev)
+        Ai = torch.from_numpy(inp["Ai"]).to(dev)
+        for _ in range(launches):
+            binding.gemm_sp24(Ac, Ai, B, epilogue=epi)
     else:
         A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
         Wq = torch.from_numpy(inp["Wq"]).to(dev)
