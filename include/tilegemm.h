@@ -93,13 +93,13 @@ tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A
  *                row-major, i.e. op(B) = (stored B)^T, K x N.
  *   C: [M][N] row-major.  Same arithmetic, epilogue and rounding as tg_gemm;
  *   tg_gemm_ex(..., A, 0, B, 0, ...) is tg_gemm.
- * Transposed layouts are compiled for 16-bit operands (fp16, bf16) whose
- * pointers are 16-byte aligned and whose stored rows are whole 16-byte chunks
- * (leading dimension a multiple of 8); other transposed calls return
- * TG_ERR_NO_CONFIG before any HIP call.
+ * Every layout runs every dtype and alignment: 16-byte aligned operands whose
+ * stored rows are whole 16-byte chunks take 16-byte loads (16-bit types: the
+ * LDS-DMA kernel; fp32: the register-staged kernel), any other call takes
+ * element loads.
  * Errors: as tg_gemm; TG_ERR_BAD_LAYOUT (trans_a or trans_b not 0 or 1),
- *   TG_ERR_NO_CONFIG (see above), TG_ERR_BAD_SHAPE also when trans_a and
- *   64 * M * element_size exceeds 2^31 - 1.
+ *   TG_ERR_BAD_SHAPE also when trans_a and 64 * M * element_size exceeds
+ *   2^31 - 1.
  */
 tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, int trans_a,
                      const void* B, int trans_b, void* C, tg_epilogue epi, tg_stream_t stream);

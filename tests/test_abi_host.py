@@ -123,14 +123,25 @@ def test_gemm_ex_argument_errors(lib):
     assert g(4, 4, 4, 2, None, 1, PB, 0, PC, 0, None) == NULLP
     assert g(4, 4, 4, 2, PA, 1, PB, 0, PA + 4, 0, None) == ALIAS
     assert g(0, 4, 4, 2, None, 1, None, 1, None, 0, None) == OK
-    # transposed fp32, or transposed rows that are not whole 16-byte chunks
-    assert g(64, 64, 64, 0, PA, 1, PB, 0, PC, 0, None) == NOCFG
-    assert g(36, 64, 64, 2, PA, 1, PB, 0, PC, 0, None) == NOCFG
-    assert g(64, 64, 36, 2, PA, 0, PB, 1, PC, 0, None) == NOCFG
+    # a forced configuration compiled for another operand layout
+    gc = lib.tg_gemm_ex_config
+    for dt in (0, 1, 2):
+        for idx, name in enumerate(binding.list_configs(0, dt)):
+            lay = next((c for c in ("_nt", "_tn", "_tt") if c in name), "")
+            for ta, tb, code in ((0, 0, ""), (0, 1, "_nt"), (1, 0, "_tn"), (1, 1, "_tt")):
+                if code != lay:
+                    assert gc(idx, 64, 64, 64, dt, PA, ta, PB, tb, PC, 0, None) == NOCFG, name
     buf = ctypes.create_string_buffer(128)
     assert lib.tg_query_config_ex(1, 4, 64, 64, 2, 1, 0, buf, 128) == BADL
     assert lib.tg_query_config_ex(0, 4096, 4096, 4096, 2, 1, 1, buf, 128) == OK
     assert buf.value.decode().startswith("gemm_bf16_256x256x32_w2x2_s4_g4_dma_tt")
+    # every dtype and alignment has a configuration in every layout
+    for dt in (0, 1, 2):
+        for ta, tb, code in ((0, 1, "_nt"), (1, 0, "_tn"), (1, 1, "_tt")):
+            for M, N, K in ((4096, 4096, 4096), (37, 45, 29)):
+                assert lib.tg_query_config_ex(0, M, N, K, dt, ta, tb, buf, 128) == OK
+                name = buf.value.decode()
+                assert code in name, (dt, ta, tb, M, name)
 
 
 def test_mx_argument_errors(lib):

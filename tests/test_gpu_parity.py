@@ -102,7 +102,7 @@ def test_every_gemm_config(dtype):
     A, B = synth.gemm_inputs(M, N, K, dtype, 303, 404, integer=True)
     want = oracle.encode(dtype, oracle.gemm_f64(A, B, dtype, relu=True))
     for idx, name in _configs(0, dtype):
-        if name.endswith(("_nt", "_tn", "_tt")):
+        if _layout_of(name) is not None:
             continue  # transposed layouts: test_every_transposed_config
         say("config %d %s" % (idx, name))
         got = run_gemm(A, B, dtype, True, config=idx)
@@ -332,9 +332,11 @@ def run_gemm_ex(A_st, ta, B_st, tb, dtype, relu, config=None):
 @pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("shape", [(128, 128, 32), (200, 136, 96), (296, 264, 200),
-                                   (1000, 1032, 264), (64, 8, 8)],
+                                   (1000, 1032, 264), (64, 8, 8),
+                                   # stored rows that are not whole 16-byte chunks
+                                   (37, 45, 29), (130, 66, 70), (1, 3, 5)],
                          ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("dtype", [F16, BF16], ids=lambda d: DNAME[d])
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
 def test_transposed_layouts(dtype, shape, layout, integer):
     """op(A) x op(B) with A stored [K][M] and/or B stored [N][K] against the oracle."""
     M, N, K = shape
@@ -346,7 +348,15 @@ def test_transposed_layouts(dtype, shape, layout, integer):
     check_full(got, oracle.gemm_layout_f64(A_st, ta, B_st, tb, dtype, relu=True), dtype, integer)
 
 
-@pytest.mark.parametrize("dtype", [F16, BF16], ids=lambda d: DNAME[d])
+def _layout_of(name):
+    """(ta, tb) of a configuration name, or None for the plain layout."""
+    for code, lay in zip(LAYOUT_IDS, LAYOUTS):
+        if name.endswith("_" + code) or name.endswith("_%s_narrow" % code):
+            return lay
+    return None
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
 def test_every_transposed_config(dtype):
     """Each compiled transposed-layout configuration, forced, on a ragged shape."""
     M, N, K = 296, 264, 200
@@ -354,44 +364,54 @@ def test_every_transposed_config(dtype):
     names = binding.list_configs(0, dtype)
     ran = 0
     for idx, name in enumerate(names):
-        for code, (ta, tb) in zip(LAYOUT_IDS, LAYOUTS):
-            if not name.endswith("_" + code):
-                continue
+        lay = _layout_of(name)
+        if lay is not None:
+            ta, tb = lay
             say("config %d %s" % (idx, name))
             A_st, B_st = _store(A, ta), _store(B, tb)
             got = run_gemm_ex(A_st, ta, B_st, tb, dtype, relu=False, config=idx)
             want = oracle.encode(dtype, oracle.gemm_layout_f64(A_st, ta, B_st, tb, dtype))
             assert np.array_equal(got, want), name
             ran += 1
-    assert ran >= 6
+    assert ran >= 9
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
-def test_transposed_full_size(layout):
-    """bf16 4096^3 + ReLU in each transposed layout: sampled entries vs the oracle."""
-    M = N = K = 4096
+@pytest.mark.parametrize("wname", ["bf16_4096_relu", "f32_4096"])
+def test_transposed_full_size(wname, layout):
+    """The 4096^3 workloads in each transposed layout: sampled entries vs the oracle."""
+    w = synth.WORKLOADS[wname]
+    M, N = w.M, w.N
     ta, tb = layout
-    w = synth.WORKLOADS["bf16_4096_relu"]
     inp = synth.make_inputs(w, integer=False)
     A_st, B_st = _store(inp["A"], ta), _store(inp["B"], tb)
-    say("layout %s bf16 4096^3" % LAYOUT_IDS[LAYOUTS.index(layout)])
-    got = run_gemm_ex(A_st, ta, B_st, tb, BF16, relu=True).reshape(M, N)
+    say("layout %s %s" % (LAYOUT_IDS[LAYOUTS.index(layout)], wname))
+    got = run_gemm_ex(A_st, ta, B_st, tb, w.dtype, relu=w.relu).reshape(M, N)
     rows, cols = sample_entries(M, N, 2000, seed=91 + ta + 2 * tb)
-    Y = oracle.gemm_layout_entries_f64(A_st, ta, B_st, tb, BF16, rows, cols, relu=True)
-    check_full(got[rows, cols], Y, BF16, integer=False)
+    Y = oracle.gemm_layout_entries_f64(A_st, ta, B_st, tb, w.dtype, rows, cols, relu=w.relu)
+    check_full(got[rows, cols], Y, w.dtype, integer=False)
 
 
-def test_transposed_unsupported():
-    """fp32 and non-16-byte rows have no transposed configuration: refused."""
-    A = torch.zeros((64, 64), dtype=torch.float32, device=DEV)
-    with pytest.raises(binding.TileGemmError) as ei:
-        binding.gemm_ex(A, A, trans_a=True)
-    assert ei.value.status == 6
-    A = torch.zeros((20, 36), dtype=torch.bfloat16, device=DEV)  # stored [K=20][M=36]
-    B = torch.zeros((20, 64), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(binding.TileGemmError) as ei:
-        binding.gemm_ex(A, B, trans_a=True)
-    assert ei.value.status == 6
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
+def test_transposed_misaligned_pointers(dtype):
+    """Aligned shapes whose operand pointers are not 16-byte aligned take the
+    element-load configurations in every layout."""
+    M, N, K = 136, 72, 48
+    es = 4 if dtype == F32 else 2
+    A, B = synth.gemm_inputs(M, N, K, dtype, 1505, 1606, integer=True)
+    for code, (ta, tb) in zip(LAYOUT_IDS, LAYOUTS):
+        A_st, B_st = _store(A, ta), _store(B, tb)
+        At, Bt = to_device(A_st, dtype, DEV), to_device(B_st, dtype, DEV)
+        # the same values one element into a larger buffer: the pointer is off 16 bytes
+        Ap = torch.zeros((At.numel() + 1,), dtype=At.dtype, device=DEV)
+        Ap[1:] = At.reshape(-1)
+        Ax = Ap[1:].view(At.shape)
+        assert Ax.data_ptr() % 16 == es
+        say("misaligned %s %s" % (code, DNAME[dtype]))
+        Ct = binding.gemm_ex(Ax, Bt, trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        want = oracle.encode(dtype, oracle.gemm_layout_f64(A_st, ta, B_st, tb, dtype))
+        assert np.array_equal(to_host_bits(Ct, dtype), want), code
 
 
 def test_side_stream():

@@ -43,6 +43,16 @@ ConfigList configs_sp24(int dtype);
             (const void*)&tg::gemm_kernel<DT, BMODE, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE> \
     }
 
+// The same with transposed operand layouts compiled in (TA: A stored [K][M],
+// TB: B stored [N][K]).
+#define TG_CONFIG_T(DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE, TA, TB)                      \
+    tg::Config                                                                                \
+    {                                                                                         \
+        0, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, TA, TB, PIPE,                              \
+            (const void*)&tg::gemm_kernel<DT, B_KN, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE, \
+                                          TA, TB>                                             \
+    }
+
 // Configurations of the LDS-DMA kernel (16-bit operands, 32 k per strip, NS
 // stages; TG_CONFIG_DMA_BK: BK k per strip).
 #define TG_CONFIG_DMA_BK(DT, TA, TB, BM, BN, WGM, WGN, NS, GM, BK)                           \

@@ -27,6 +27,10 @@ static const Config kCfg[] = {
     TG_CONFIG(0, DT_F16, B_KN, 128, 64, 64, 2, 2, 2, 8, true, 0),
     TG_CONFIG(0, DT_F16, B_KN, 64, 64, 64, 2, 2, 2, 8, true, 0),
     TG_CONFIG(0, DT_F16, B_KN, 64, 64, 64, 2, 2, 2, 8, false, 0),
+    // unaligned transposed layouts: element loads
+    TG_CONFIG_T(DT_F16, 64, 64, 64, 2, 2, 2, 8, false, 0, false, true),
+    TG_CONFIG_T(DT_F16, 64, 64, 64, 2, 2, 2, 8, false, 0, true, false),
+    TG_CONFIG_T(DT_F16, 64, 64, 64, 2, 2, 2, 8, false, 0, true, true),
     TG_CONFIG(0, DT_F16, B_KN, 128, 128, 64, 2, 2, 2, 8, true, 1),
     TG_CONFIG(0, DT_F16, B_KN, 64, 64, 64, 2, 2, 2, 8, true, 1),
 };

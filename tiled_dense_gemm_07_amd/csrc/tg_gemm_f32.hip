@@ -15,6 +15,16 @@ static const Config kCfg[] = {
     TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true, 1),
     TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true, 1),
     TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true, 1),
+    // transposed-operand layouts (A stored [K][M] and/or B stored [N][K])
+    TG_CONFIG_T(DT_F32, 128, 128, 32, 2, 2, 2, 8, true, 1, false, true),
+    TG_CONFIG_T(DT_F32, 128, 128, 32, 2, 2, 2, 8, true, 1, true, false),
+    TG_CONFIG_T(DT_F32, 128, 128, 32, 2, 2, 2, 8, true, 1, true, true),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, true, 1, false, true),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, true, 1, true, false),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, true, 1, true, true),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, false, 0, false, true),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, false, 0, true, false),
+    TG_CONFIG_T(DT_F32, 64, 64, 32, 2, 2, 2, 8, false, 0, true, true),
 };
 
 ConfigList configs_gemm_f32() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tg_sched.h"
 
 namespace tg {
@@ -142,7 +144,7 @@ __device__ __forceinline__ float e8m0_to_f32(u32 e)
 // The kernel.
 // --------------------------------------------------------------------------
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE, int PIPE>
+          bool WIDE, int PIPE, bool TA = false, bool TB = false>
 struct GemmKernel {
     using TR = DtTraits<DT>;
     static constexpr int ES = TR::ES;
@@ -159,99 +161,101 @@ struct GemmKernel {
     static constexpr int B_STAGE = BN * ROWB;
     static constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    // A: 16-byte chunks per thread
-    static constexpr int ACH = BM * CPR / NT;
-    // B (row-major KN): units of VEC k-rows by UW n-columns (UW <= VEC), so
-    // that every thread owns a whole number of units; a unit is UW*ES-byte
-    // loads of VEC rows, transposed into UW LDS rows of one 16-byte chunk.
-    static constexpr int UW_RAW = (BK / VEC) * BN / NT;
-    static constexpr int UW = UW_RAW >= VEC ? VEC : UW_RAW;
-    static constexpr int BU_KN = (BK / VEC) * (BN / (UW > 0 ? UW : 1)) / NT;
-    // B (4-bit weights): units of CU codes (CU/2 bytes) of one weight row,
-    // CU in {8, 16, 32}, all under one scale byte
-    static constexpr int CU_RAW = BN * BK / NT;
-    static constexpr int CU = CU_RAW >= 32 ? 32 : CU_RAW;
-    static constexpr int BU_W4 = BN * BK / (CU > 0 ? CU : 1) / NT;
 
-    static_assert(DT != DT_F32 || BMODE == B_KN, "4-bit weights feed the bf16 path only");
-    static_assert(BMODE == B_KN || DT == DT_BF16, "4-bit weights feed the bf16 path only");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
-    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "LDS rows must be >= 128 B, power of 2");
-    static_assert(BK % (2 * VEC) == 0, "BK must hold whole MFMA k-slabs");
-    static_assert(BM * CPR % NT == 0, "A strip must split evenly over threads");
-    static_assert(BMODE != B_KN || (UW >= 1 && (UW & (UW - 1)) == 0 &&
-                                    ((BK / VEC) * (BN / UW)) % NT == 0 && BU_KN >= 1),
-                  "B units must split evenly");
-    static_assert(BMODE != B_KN || UW * ES >= 4, "B loads of at least 4 bytes");
-    static_assert(BMODE != B_W4 || (CU >= 8 && (CU & (CU - 1)) == 0 && BU_W4 >= 1 &&
-                                    (BN * BK / CU) % NT == 0),
-                  "W4 units must split evenly");
-    static_assert(BMODE != B_W4 || BK % 32 == 0, "W4 strips hold whole scale groups");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(STAGES >= 2, "at least double buffering");
+    // Both operands sit in LDS k-contiguous ([rows][BK], 16-byte chunk
+    // swizzle).  In global memory an operand is either k-contiguous (KOp: X
+    // rows of K consecutive elements: A as [M][K], B stored [N][K]) or
+    // x-contiguous (XOp: K rows of X consecutive elements: B as [K][N], A
+    // stored [K][M]), which is transposed in registers on its way to LDS.
+    template <int X>
+    struct KOp {
+        static constexpr int NCH = X * CPR / NT;  // 16-byte chunks per thread
+        static_assert(X * CPR % NT == 0 && NCH >= 1, "strip must split evenly over threads");
+        static constexpr int NREG = NCH;
 
-    struct Regs {
-        u32x4 a[ACH];
-        u32x4 b[BMODE == B_KN ? BU_KN * VEC : BU_W4];
-        u32 s[BMODE == B_W4 ? BU_W4 : 1];
-    };
-
-    // ---- global -> registers --------------------------------------------
-    static __device__ __forceinline__ void load_a(Regs& R, const GemmParams& p, int m0, int k0,
-                                                  int tid)
-    {
-        const char* base = (const char*)p.A + ((int64_t)m0 * p.K + k0) * ES;
-        const int rows_valid = p.M - m0;
-        const int64_t bytes = ((int64_t)(rows_valid - 1) * p.K + (p.K - k0)) * ES;
-        const auto rs = make_rsrc(base, clamp_bytes(bytes));
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int q = tid + NT * i;
-            const int row = q / CPR;
-            const int c = q % CPR;
-            const int kk = c * VEC;  // k offset within the strip
-            const bool rv = row < rows_valid;
-            const u32 off = (u32)(row * p.K + kk) * ES;
-            if (WIDE) {
-                const bool v = rv && (k0 + kk < p.K);
-                R.a[i] = buf_load16(rs, v ? off : kOob);
-            } else {
-                u32 w[4] = {0, 0, 0, 0};
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const bool v = rv && (k0 + kk + e < p.K);
-                    const u32 o = v ? off + e * ES : kOob;
-                    if (ES == 4)
-                        w[e] = buf_load4(rs, o);
-                    else
-                        w[e / 2] |= buf_load2(rs, o) << (16 * (e & 1));
-                }
-                R.a[i] = u32x4{w[0], w[1], w[2], w[3]};
-            }
-        }
-    }
-
-    static __device__ __forceinline__ void load_b(Regs& R, const GemmParams& p, int n0, int k0,
-                                                  int tid)
-    {
-        if constexpr (BMODE == B_KN) {
-            const char* base = (const char*)p.B + ((int64_t)k0 * p.N + n0) * ES;
-            const int64_t bytes = ((int64_t)(p.K - k0 - 1) * p.N + (p.N - n0)) * ES;
+        // rows x0 .. of an operand with xtot rows of ld = K elements
+        static __device__ __forceinline__ void load(u32x4 (&dst)[NREG], const void* ptr, int x0,
+                                                    int xtot, int K, int k0, int tid)
+        {
+            const char* base = (const char*)ptr + ((int64_t)x0 * K + k0) * ES;
+            const int rows_valid = xtot - x0;
+            const int64_t bytes = ((int64_t)(rows_valid - 1) * K + (K - k0)) * ES;
             const auto rs = make_rsrc(base, clamp_bytes(bytes));
 #pragma unroll
-            for (int i = 0; i < BU_KN; ++i) {
+            for (int i = 0; i < NCH; ++i) {
+                const int q = tid + NT * i;
+                const int row = q / CPR;
+                const int c = q % CPR;
+                const int kk = c * VEC;  // k offset within the strip
+                const bool rv = row < rows_valid;
+                const u32 off = (u32)(row * K + kk) * ES;
+                if (WIDE) {
+                    const bool v = rv && (k0 + kk < K);
+                    dst[i] = buf_load16(rs, v ? off : kOob);
+                } else {
+                    u32 w[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const bool v = rv && (k0 + kk + e < K);
+                        const u32 o = v ? off + e * ES : kOob;
+                        if (ES == 4)
+                            w[e] = buf_load4(rs, o);
+                        else
+                            w[e / 2] |= buf_load2(rs, o) << (16 * (e & 1));
+                    }
+                    dst[i] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+        }
+
+        static __device__ __forceinline__ void store(const u32x4 (&src)[NREG], char* S, int tid)
+        {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int q = tid + NT * i;
+                const int row = q / CPR;
+                const int c = q % CPR;
+                *(u32x4*)(S + row * ROWB + ((c ^ swz(row)) << 4)) = src[i];
+            }
+        }
+    };
+
+    // Units of VEC k-rows by UW x-columns (UW <= VEC), so that every thread
+    // owns a whole number of units; a unit is UW*ES-byte loads of VEC rows,
+    // transposed into UW LDS rows of one 16-byte chunk.
+    template <int X>
+    struct XOp {
+        static constexpr int UW_RAW = (BK / VEC) * X / NT;
+        static constexpr int UW = UW_RAW >= VEC ? VEC : UW_RAW;
+        static constexpr int NU = (BK / VEC) * (X / (UW > 0 ? UW : 1)) / NT;
+        static_assert(UW >= 1 && (UW & (UW - 1)) == 0 && ((BK / VEC) * (X / UW)) % NT == 0 &&
+                          NU >= 1,
+                      "units must split evenly");
+        static_assert(UW * ES >= 4, "loads of at least 4 bytes");
+        static constexpr int NREG = NU * VEC;
+
+        // columns x0 .. of an operand stored as K rows of ld = xtot elements
+        static __device__ __forceinline__ void load(u32x4 (&dst)[NREG], const void* ptr, int x0,
+                                                    int xtot, int K, int k0, int tid)
+        {
+            const int ld = xtot;
+            const char* base = (const char*)ptr + ((int64_t)k0 * ld + x0) * ES;
+            const int64_t bytes = ((int64_t)(K - k0 - 1) * ld + (xtot - x0)) * ES;
+            const auto rs = make_rsrc(base, clamp_bytes(bytes));
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
                 const int u = tid + NT * i;
-                const int nc = u % (BN / UW);
-                const int kg = u / (BN / UW);
+                const int nc = u % (X / UW);
+                const int kg = u / (X / UW);
                 const int nn = nc * UW;
 #pragma unroll
                 for (int r = 0; r < VEC; ++r) {
                     const int kr = kg * VEC + r;  // k row within the strip
-                    const bool kv = k0 + kr < p.K;
-                    const u32 off = (u32)(kr * p.N + nn) * ES;
+                    const bool kv = k0 + kr < K;
+                    const u32 off = (u32)(kr * ld + nn) * ES;
                     u32x4 w = {0, 0, 0, 0};
                     if (WIDE) {
-                        const u32 o = (kv && n0 + nn < p.N) ? off : kOob;
+                        const u32 o = (kv && x0 + nn < xtot) ? off : kOob;
                         if constexpr (UW * ES == 16) {
                             w = buf_load16(rs, o);
                         } else if constexpr (UW * ES == 8) {
@@ -265,7 +269,7 @@ struct GemmKernel {
                     } else {
 #pragma unroll
                         for (int e = 0; e < UW; ++e) {
-                            const bool v = kv && (n0 + nn + e < p.N);
+                            const bool v = kv && (x0 + nn + e < xtot);
                             const u32 o = v ? off + e * ES : kOob;
                             if (ES == 4)
                                 w[e] = buf_load4(rs, o);
@@ -273,9 +277,81 @@ struct GemmKernel {
                                 w[e / 2] |= buf_load2(rs, o) << (16 * (e & 1));
                         }
                     }
-                    R.b[i * VEC + r] = w;
+                    dst[i * VEC + r] = w;
                 }
             }
+        }
+
+        static __device__ __forceinline__ void store(const u32x4 (&src)[NREG], char* S, int tid)
+        {
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
+                const int u = tid + NT * i;
+                const int nc = u % (X / UW);
+                const int kg = u / (X / UW);
+                const u32x4* L = &src[i * VEC];
+#pragma unroll
+                for (int j = 0; j < UW; ++j) {
+                    u32x4 o;
+                    if (ES == 4) {
+                        // 4 k-rows of fp32: column j
+                        o = u32x4{L[0][j], L[1][j], L[2][j], L[3][j]};
+                    } else {
+                        // 8 k-rows of 16-bit values: column j, k pairs packed low-to-high
+                        const u32 sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                        const int d = j >> 1;
+                        o = u32x4{__builtin_amdgcn_perm(L[1][d], L[0][d], sel),
+                                  __builtin_amdgcn_perm(L[3][d], L[2][d], sel),
+                                  __builtin_amdgcn_perm(L[5][d], L[4][d], sel),
+                                  __builtin_amdgcn_perm(L[7][d], L[6][d], sel)};
+                    }
+                    const int n = nc * UW + j;
+                    *(u32x4*)(S + n * ROWB + ((kg ^ swz(n)) << 4)) = o;
+                }
+            }
+        }
+    };
+
+    using OpA = typename std::conditional<TA, XOp<BM>, KOp<BM>>::type;
+    using OpB = typename std::conditional<TB, KOp<BN>, XOp<BN>>::type;
+
+    // B (4-bit weights): units of CU codes (CU/2 bytes) of one weight row,
+    // CU in {8, 16, 32}, all under one scale byte
+    static constexpr int CU_RAW = BN * BK / NT;
+    static constexpr int CU = CU_RAW >= 32 ? 32 : CU_RAW;
+    static constexpr int BU_W4 = BN * BK / (CU > 0 ? CU : 1) / NT;
+
+    static_assert(DT != DT_F32 || BMODE == B_KN, "4-bit weights feed the bf16 path only");
+    static_assert(BMODE == B_KN || DT == DT_BF16, "4-bit weights feed the bf16 path only");
+    static_assert(BMODE == B_KN || (!TA && !TB), "4-bit weights: row-major activations only");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "LDS rows must be >= 128 B, power of 2");
+    static_assert(BK % (2 * VEC) == 0, "BK must hold whole MFMA k-slabs");
+    static_assert(BMODE != B_W4 || (CU >= 8 && (CU & (CU - 1)) == 0 && BU_W4 >= 1 &&
+                                    (BN * BK / CU) % NT == 0),
+                  "W4 units must split evenly");
+    static_assert(BMODE != B_W4 || BK % 32 == 0, "W4 strips hold whole scale groups");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(STAGES >= 2, "at least double buffering");
+
+    struct Regs {
+        u32x4 a[OpA::NREG];
+        u32x4 b[BMODE == B_KN ? OpB::NREG : BU_W4];
+        u32 s[BMODE == B_W4 ? BU_W4 : 1];
+    };
+
+    // ---- global -> registers --------------------------------------------
+    static __device__ __forceinline__ void load_a(Regs& R, const GemmParams& p, int m0, int k0,
+                                                  int tid)
+    {
+        OpA::load(R.a, p.A, m0, p.M, p.K, k0, tid);
+    }
+
+    static __device__ __forceinline__ void load_b(Regs& R, const GemmParams& p, int n0, int k0,
+                                                  int tid)
+    {
+        if constexpr (BMODE == B_KN) {
+            OpB::load(R.b, p.B, n0, p.N, p.K, k0, tid);
         } else {
             // packed codes: row n has K/2 bytes; this strip covers bytes k0/2 .. (k0+BK)/2
             const int rows_valid = p.N - n0;
@@ -325,39 +401,9 @@ struct GemmKernel {
     {
         char* As = stage;
         char* Bs = stage + A_STAGE;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int q = tid + NT * i;
-            const int row = q / CPR;
-            const int c = q % CPR;
-            *(u32x4*)(As + row * ROWB + ((c ^ swz(row)) << 4)) = R.a[i];
-        }
+        OpA::store(R.a, As, tid);
         if constexpr (BMODE == B_KN) {
-#pragma unroll
-            for (int i = 0; i < BU_KN; ++i) {
-                const int u = tid + NT * i;
-                const int nc = u % (BN / UW);
-                const int kg = u / (BN / UW);
-                const u32x4* L = &R.b[i * VEC];
-#pragma unroll
-                for (int j = 0; j < UW; ++j) {
-                    u32x4 o;
-                    if (ES == 4) {
-                        // 4 k-rows of fp32: column j
-                        o = u32x4{L[0][j], L[1][j], L[2][j], L[3][j]};
-                    } else {
-                        // 8 k-rows of 16-bit values: column j, k pairs packed low-to-high
-                        const u32 sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                        const int d = j >> 1;
-                        o = u32x4{__builtin_amdgcn_perm(L[1][d], L[0][d], sel),
-                                  __builtin_amdgcn_perm(L[3][d], L[2][d], sel),
-                                  __builtin_amdgcn_perm(L[5][d], L[4][d], sel),
-                                  __builtin_amdgcn_perm(L[7][d], L[6][d], sel)};
-                    }
-                    const int n = nc * UW + j;
-                    *(u32x4*)(Bs + n * ROWB + ((kg ^ swz(n)) << 4)) = o;
-                }
-            }
+            OpB::store(R.b, Bs, tid);
         } else {
             constexpr int UPR = BK / CU;
 #pragma unroll
@@ -630,11 +676,11 @@ struct GemmKernel {
 // PIPE 0: one register staging set, STAGES-deep LDS ring.
 // PIPE 1: the deep pipeline above (two register sets, two LDS stages).
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE, int PIPE>
+          bool WIDE, int PIPE, bool TA = false, bool TB = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64))) void
 gemm_kernel(GemmParams p)
 {
-    using Kern = GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE>;
+    using Kern = GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE, TA, TB>;
     if constexpr (PIPE == 1)
         Kern::run_deep(p);
     else
