@@ -57,9 +57,14 @@ void config_name(const Config& c, char* buf, size_t len)
     static const char* lay[] = {"", "_nt", "_tn", "_tt"};  // A^T-stored / B^T-stored
     const bool mx = c.op == TG_OP_MX;
     static const char* opn[] = {"gemm", "w4", "mx", "sp24"};
-    snprintf(buf, len, "%s_%s_%dx%dx%d_w%dx%d_s%d_g%d%s%s%s", opn[c.op],
+    char wav[24];
+    if (c.ks > 1)
+        snprintf(wav, sizeof wav, "w%dx%dx%d", c.wgm, c.wgn, c.ks);  // k-slice groups last
+    else
+        snprintf(wav, sizeof wav, "w%dx%d", c.wgm, c.wgn);
+    snprintf(buf, len, "%s_%s_%dx%dx%d_%s_s%d_g%d%s%s%s", opn[c.op],
              mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
-             c.bn, c.bk, c.wgm, c.wgn, c.stages, c.group_m,
+             c.bn, c.bk, wav, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
              mx ? (c.chunked_scales ? "_sc8" : "") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
@@ -82,12 +87,14 @@ struct Pref {
     const char* names[4];
 };
 const Pref kPrefs[] = {
+    // grids below about one tile per compute unit fall through to the last
+    // entry: 32 x 32 tiles with four k-slice wave groups
     {0, 2, {"gemm_bf16_256x256x32_w2x2_s4_g4_dma", "gemm_bf16_128x128x32_w2x2_s4_g8_dma",
-            "gemm_bf16_64x64x64_w2x2_s2_g8_deep", nullptr}},
+            "gemm_bf16_64x64x128_w2x2x2_s2_g8_deep", "gemm_bf16_32x32x256_w1x1x4_s2_g8_deep"}},
     {0, 1, {"gemm_f16_256x256x32_w2x2_s4_g4_dma", "gemm_f16_128x128x32_w2x2_s4_g8_dma",
-            "gemm_f16_64x64x64_w2x2_s2_g8_deep", nullptr}},
-    {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x32_w2x2_s2_g8_deep", nullptr,
-            nullptr}},
+            "gemm_f16_64x64x128_w2x2x2_s2_g8_deep", "gemm_f16_32x32x256_w1x1x4_s2_g8_deep"}},
+    {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x64_w2x2x2_s2_g8_deep",
+            "gemm_f32_32x32x128_w1x1x4_s2_g8_deep", nullptr}},
     {1, 2, {"w4_bf16_64x128x128_w2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
             "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
     {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g8_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma_sc8",
@@ -261,7 +268,7 @@ tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream
                 (long long)grid);
     }
     void* args[] = {&p};
-    hipError_t e = hipLaunchKernel(c.kernel, dim3((unsigned)grid), dim3(c.wgm * c.wgn * 64), args,
+    hipError_t e = hipLaunchKernel(c.kernel, dim3((unsigned)grid), dim3(c.wgm * c.wgn * c.ks * 64), args,
                                    0, stream);
     if (e != hipSuccess)
         return TG_ERR_HIP;
@@ -539,7 +546,7 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
     char name[96];
     config_name(*c, name, sizeof name);
     snprintf(buf, len, "%s grid=%lld threads=%d", name,
-             (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * 64);
+             (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * c->ks * 64);
     return TG_OK;
 }
 

@@ -20,6 +20,7 @@ struct Config {
     const void* kernel;
     bool chunked_scales = false;  // MX: scale bytes staged 8 strips at a time
                                   // (K % 512 == 0, 16-byte aligned scale rows)
+    int ks = 1;                   // k-slice wave groups (WGM x WGN waves each)
 };
 
 struct ConfigList {
@@ -51,6 +52,17 @@ ConfigList configs_sp24(int dtype);
         0, DT, BM, BN, BK, WGM, WGN, ST, GM, WIDE, TA, TB, PIPE,                              \
             (const void*)&tg::gemm_kernel<DT, B_KN, BM, BN, BK, WGM, WGN, ST, GM, WIDE, PIPE, \
                                           TA, TB>                                             \
+    }
+
+// Register-staged kernel with KS k-slice wave groups (plain layouts, 16-byte
+// loads, deep pipeline): small shapes whose tile grid leaves compute units idle.
+#define TG_CONFIG_KS(DT, BM, BN, BK, WGM, WGN, GM, KS)                                         \
+    tg::Config                                                                                \
+    {                                                                                         \
+        0, DT, BM, BN, BK, WGM, WGN, 2, GM, true, false, false, 1,                            \
+            (const void*)&tg::gemm_kernel<DT, B_KN, BM, BN, BK, WGM, WGN, 2, GM, true, 1,     \
+                                          false, false, KS>,                                  \
+            false, KS                                                                         \
     }
 
 // Configurations of the LDS-DMA kernel (16-bit operands, 32 k per strip, NS

@@ -33,6 +33,11 @@ static const Config kCfg[] = {
     TG_CONFIG_T(DT_F16, 64, 64, 64, 2, 2, 2, 8, false, 0, true, true),
     TG_CONFIG(0, DT_F16, B_KN, 128, 128, 64, 2, 2, 2, 8, true, 1),
     TG_CONFIG(0, DT_F16, B_KN, 64, 64, 64, 2, 2, 2, 8, true, 1),
+    // k-slice wave groups for grids of a few hundred tiles or less
+    TG_CONFIG_KS(DT_F16, 64, 64, 128, 2, 2, 8, 2),
+    TG_CONFIG_KS(DT_F16, 64, 64, 128, 1, 1, 8, 4),
+    TG_CONFIG_KS(DT_F16, 32, 64, 128, 1, 2, 8, 2),
+    TG_CONFIG_KS(DT_F16, 32, 32, 256, 1, 1, 8, 4),
 };
 
 ConfigList configs_gemm_f16() { return {kCfg, (int)(sizeof(kCfg) / sizeof(kCfg[0]))}; }

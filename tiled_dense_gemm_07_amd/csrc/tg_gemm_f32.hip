@@ -15,6 +15,11 @@ static const Config kCfg[] = {
     TG_CONFIG(0, DT_F32, B_KN, 256, 256, 32, 2, 2, 2, 4, true, 1),
     TG_CONFIG(0, DT_F32, B_KN, 128, 128, 32, 2, 2, 2, 8, true, 1),
     TG_CONFIG(0, DT_F32, B_KN, 64, 64, 32, 2, 2, 2, 8, true, 1),
+    // k-slice wave groups for grids of a few hundred tiles or less
+    TG_CONFIG_KS(DT_F32, 32, 32, 128, 1, 1, 8, 4),
+    TG_CONFIG_KS(DT_F32, 32, 32, 64, 1, 1, 8, 2),
+    TG_CONFIG_KS(DT_F32, 32, 64, 128, 1, 2, 8, 4),
+    TG_CONFIG_KS(DT_F32, 64, 64, 64, 2, 2, 8, 2),
     // transposed-operand layouts (A stored [K][M] and/or B stored [N][K])
     TG_CONFIG_T(DT_F32, 128, 128, 32, 2, 2, 2, 8, true, 1, false, true),
     TG_CONFIG_T(DT_F32, 128, 128, 32, 2, 2, 2, 8, true, 1, true, false),

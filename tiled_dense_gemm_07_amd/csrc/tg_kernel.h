@@ -143,13 +143,18 @@ __device__ __forceinline__ float e8m0_to_f32(u32 e)
 // --------------------------------------------------------------------------
 // The kernel.
 // --------------------------------------------------------------------------
+// KS > 1 slices each strip's k range over KS groups of WGM x WGN waves: every
+// group multiplies the whole tile over its share of the strip's slabs, and the
+// groups' partial accumulators are summed through LDS before the epilogue.
+// This puts KS times more waves on a tile, for shapes whose tile grid alone
+// cannot occupy the compute units.
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE, int PIPE, bool TA = false, bool TB = false>
+          bool WIDE, int PIPE, bool TA = false, bool TB = false, int KS = 1>
 struct GemmKernel {
     using TR = DtTraits<DT>;
     static constexpr int ES = TR::ES;
     static constexpr int VEC = TR::VEC;
-    static constexpr int NT = WGM * WGN * 64;
+    static constexpr int NT = WGM * WGN * KS * 64;
     static constexpr int WTM = BM / WGM;
     static constexpr int WTN = BN / WGN;
     static constexpr int FM = WTM / 32;
@@ -160,7 +165,11 @@ struct GemmKernel {
     static constexpr int A_STAGE = BM * ROWB;
     static constexpr int B_STAGE = BN * ROWB;
     static constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int NSL = NSLAB / KS;  // slabs per wave group per strip
+    // partial accumulators of wave groups 1 .. KS-1 (fp32 tile each)
+    static constexpr int RED_BYTES = (KS - 1) * BM * BN * 4;
+    static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
 
     // Both operands sit in LDS k-contiguous ([rows][BK], 16-byte chunk
     // swizzle).  In global memory an operand is either k-contiguous (KOp: X
@@ -333,6 +342,8 @@ struct GemmKernel {
     static_assert(BMODE != B_W4 || BK % 32 == 0, "W4 strips hold whole scale groups");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(STAGES >= 2, "at least double buffering");
+    static_assert(KS >= 1 && NSLAB % KS == 0, "k slices split each strip's slabs evenly");
+    static_assert(KS == 1 || BMODE == B_KN, "k slices: plain operands only");
 
     struct Regs {
         u32x4 a[OpA::NREG];
@@ -483,13 +494,56 @@ struct GemmKernel {
     }
 
     static __device__ __forceinline__ void compute(f32x16 (&acc)[FM][FN], const char* stage,
-                                                   int wm, int wn, int lane)
+                                                   int s0, int wm, int wn, int lane)
     {
 #pragma unroll
-        for (int s = 0; s < NSLAB; ++s) {
+        for (int s = 0; s < NSL; ++s) {
             Frags F;
-            read_frags(F, stage, s, wm, wn, lane);
+            read_frags(F, stage, s0 + s, wm, wn, lane);
             mfma_slab(acc, F);
+        }
+    }
+
+    // Sum the k-slice groups' accumulators into group 0's (KS > 1).  Entered
+    // by all waves after the last use of the LDS ring; group 0 holds the
+    // tile's sums on return.
+    static __device__ __forceinline__ void reduce_slices(f32x16 (&acc)[FM][FN], char* smem,
+                                                         int ks, int w2, int lane)
+    {
+        if constexpr (KS > 1) {
+            constexpr int WB = FM * FN * 64 * 64;  // bytes of one wave's accumulators
+            __syncthreads();
+            if (ks > 0) {
+                char* dst = smem + ((ks - 1) * WGM * WGN + w2) * WB;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *(f32x4*)(dst + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16) =
+                                f32x4{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1],
+                                      acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+            }
+            __syncthreads();
+            if (ks == 0) {
+#pragma unroll
+                for (int g = 1; g < KS; ++g) {
+                    const char* src = smem + ((g - 1) * WGM * WGN + w2) * WB;
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const f32x4 v = *(const f32x4*)(
+                                    src + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    acc[fm][fn][4 * q + e] += v[e];
+                            }
+                }
+            }
         }
     }
 
@@ -549,8 +603,10 @@ struct GemmKernel {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = tid >> 6;
-        const int wm = wave / WGN;
-        const int wn = wave % WGN;
+        const int ks = wave / (WGM * WGN);  // k-slice group
+        const int w2 = wave % (WGM * WGN);
+        const int wm = w2 / WGN;
+        const int wn = w2 % WGN;
         const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
         const int m0 = t.m * BM;
         const int n0 = t.n * BN;
@@ -583,13 +639,15 @@ struct GemmKernel {
                 load_a(R, p, m0, nxt * BK, tid);
                 load_b(R, p, n0, nxt * BK, tid);
             }
-            compute(acc, smem + (it % STAGES) * STAGE_BYTES, wm, wn, lane);
+            compute(acc, smem + (it % STAGES) * STAGE_BYTES, ks * NSL, wm, wn, lane);
             if (nxt < KT)
                 store_lds(R, smem + (nxt % STAGES) * STAGE_BYTES, tid);
             __syncthreads();
         }
 
-        epilogue(acc, p, m0, n0, wm, wn, lane);
+        reduce_slices(acc, smem, ks, w2, lane);
+        if (ks == 0)
+            epilogue(acc, p, m0, n0, wm, wn, lane);
     }
 
     // Deep pipeline (two LDS stages, two register staging sets): the global
@@ -601,29 +659,29 @@ struct GemmKernel {
     static __device__ __forceinline__ void strip_deep(f32x16 (&acc)[FM][FN], Regs& R,
                                                       Frags& Fa, Frags& Fb, char* smem,
                                                       const GemmParams& p, int it, int KT,
-                                                      int m0, int n0, int wm, int wn, int tid,
-                                                      int lane)
+                                                      int m0, int n0, int s0, int wm, int wn,
+                                                      int tid, int lane)
     {
-        static_assert(NSLAB % 2 == 0 && NSLAB >= 2, "slab fragments alternate in pairs");
+        static_assert(NSL % 2 == 0 && NSL >= 2, "slab fragments alternate in pairs");
         char* cur = smem + (it & 1) * STAGE_BYTES;
         char* nxt = smem + ((it + 1) & 1) * STAGE_BYTES;
 #pragma unroll
-        for (int s = 0; s < NSLAB; ++s) {
+        for (int s = 0; s < NSL; ++s) {
             Frags& F = (s & 1) ? Fb : Fa;    // slab s
-            Frags& G = (s & 1) ? Fa : Fb;    // slab s + 1 (or slab 0 of the next strip)
-            if (s + 1 < NSLAB)
-                read_frags(G, cur, s + 1, wm, wn, lane);
+            Frags& G = (s & 1) ? Fa : Fb;    // slab s + 1 (or the first slab of the next strip)
+            if (s + 1 < NSL)
+                read_frags(G, cur, s0 + s + 1, wm, wn, lane);
             // No branches in the steady state: a strip past the end of K loads as
             // out-of-range zeros and is written to (or read from) an LDS stage
             // nothing uses, which keeps the wait counters exact.
-            if (s == NSLAB - 2) {
+            if (s == NSL - 2) {
                 store_lds(R, nxt, tid);
                 load_a(R, p, m0, (it + 3) * BK, tid);
                 load_b(R, p, n0, (it + 3) * BK, tid);
             }
-            if (s == NSLAB - 1) {
+            if (s == NSL - 1) {
                 __syncthreads();
-                read_frags(G, nxt, 0, wm, wn, lane);
+                read_frags(G, nxt, s0, wm, wn, lane);
             }
             mfma_slab(acc, F);
         }
@@ -636,8 +694,11 @@ struct GemmKernel {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = tid >> 6;
-        const int wm = wave / WGN;
-        const int wn = wave % WGN;
+        const int ks = wave / (WGM * WGN);  // k-slice group
+        const int w2 = wave % (WGM * WGN);
+        const int wm = w2 / WGN;
+        const int wn = w2 % WGN;
+        const int s0 = ks * NSL;
         const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
         const int m0 = t.m * BM;
         const int n0 = t.n * BN;
@@ -663,24 +724,28 @@ struct GemmKernel {
         load_a(Y, p, m0, 2 * BK, tid);
         load_b(Y, p, n0, 2 * BK, tid);
         __syncthreads();
-        read_frags(Fa, smem, 0, wm, wn, lane);
+        read_frags(Fa, smem, s0, wm, wn, lane);
         // an even number of strips: a trailing all-zero strip adds nothing
         for (int it = 0; it < KT; it += 2) {
-            strip_deep(acc, X, Fa, Fb, smem, p, it, KT, m0, n0, wm, wn, tid, lane);
-            strip_deep(acc, Y, Fa, Fb, smem, p, it + 1, KT, m0, n0, wm, wn, tid, lane);
+            strip_deep(acc, X, Fa, Fb, smem, p, it, KT, m0, n0, s0, wm, wn, tid, lane);
+            strip_deep(acc, Y, Fa, Fb, smem, p, it + 1, KT, m0, n0, s0, wm, wn, tid, lane);
         }
-        epilogue(acc, p, m0, n0, wm, wn, lane);
+        reduce_slices(acc, smem, ks, w2, lane);
+        if (ks == 0)
+            epilogue(acc, p, m0, n0, wm, wn, lane);
     }
 };
 
 // PIPE 0: one register staging set, STAGES-deep LDS ring.
 // PIPE 1: the deep pipeline above (two register sets, two LDS stages).
 template <int DT, int BMODE, int BM, int BN, int BK, int WGM, int WGN, int STAGES, int GROUP_M,
-          bool WIDE, int PIPE, bool TA = false, bool TB = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64))) void
+          bool WIDE, int PIPE, bool TA = false, bool TB = false, int KS = 1>
+__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * KS * 64,
+                                                       WGM * WGN * KS * 64))) void
 gemm_kernel(GemmParams p)
 {
-    using Kern = GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE, TA, TB>;
+    using Kern =
+        GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE, TA, TB, KS>;
     if constexpr (PIPE == 1)
         Kern::run_deep(p);
     else
