@@ -54,7 +54,8 @@ typedef enum {
     TG_ERR_ALIAS = 5,        /* C overlaps an input                               */
     TG_ERR_NO_CONFIG = 6,    /* forced config index out of range / wrong op       */
     TG_ERR_HIP = 7,          /* the HIP runtime reported an error at launch       */
-    TG_ERR_BAD_LAYOUT = 8    /* trans_a / trans_b not 0 or 1                      */
+    TG_ERR_BAD_LAYOUT = 8,   /* trans_a / trans_b not 0 or 1                      */
+    TG_ERR_WORKSPACE = 9     /* split-K workspace NULL, too small or misaligned    */
 } tg_status;
 
 typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
@@ -103,6 +104,51 @@ tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A
  */
 tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, int trans_a,
                      const void* B, int trans_b, void* C, tg_epilogue epi, tg_stream_t stream);
+
+/*
+ * Split-K GEMM: C = epilogue(A x B) as tg_gemm, with each output tile's K range
+ * split over several workgroups, for shapes whose tile grid alone leaves most
+ * compute units idle (few output tiles, long K).  The mhpq.cn page names the
+ * tail effect of small problems (section 4.3); split K is the standard remedy
+ * for it and, unlike tg_gemm, needs memory for partial sums: the caller brings
+ * it as `workspace`.
+ *   A, B, C, dtype, epi: as tg_gemm (row-major, fp32 / fp16 / bf16).
+ *   splits: 0 = chosen by the library (about one workgroup per compute unit,
+ *     at least two k strips per split); n >= 1 = at most n splits (fewer when
+ *     K holds fewer strips); 1 = no split, identical to tg_gemm.
+ *   workspace: device memory, 16-byte aligned, of at least the size
+ *     tg_gemm_splitk_workspace_size reports for the same M, N, K, dtype and
+ *     splits.  It holds per-tile arrival counters and fp32 partial tiles.  It
+ *     must be zero-filled before its first use; every call leaves the counters
+ *     zero again, so it is reused without clearing.  Calls that share a
+ *     workspace must not run concurrently (issue them on one stream).
+ *   Numerics: each split sums its k range in fp32 on the matrix cores; the
+ *     split sums are added in fp32 in split order 0, 1, ... by whichever
+ *     workgroup of the tile finishes last, so the result does not depend on
+ *     the order in which workgroups run; then the ReLU and the single rounding
+ *     of tg_gemm.  Integer-valued inputs give tg_gemm's result bit for bit
+ *     (every partial sum is exact in fp32).
+ *   When no split pays off (or the operands are not 16-byte aligned with rows
+ *   of whole 16-byte chunks) the call runs tg_gemm's kernel and does not touch
+ *   the workspace, which may then be NULL.
+ * Errors: as tg_gemm; TG_ERR_BAD_SHAPE also for splits < 0; TG_ERR_ALIAS also
+ *   when the workspace overlaps A, B or C; TG_ERR_WORKSPACE when a split is
+ *   launched and the workspace is NULL, smaller than needed or not 16-byte
+ *   aligned.
+ */
+tg_status tg_gemm_splitk(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A,
+                         const void* B, void* C, tg_epilogue epi, int splits, void* workspace,
+                         size_t workspace_bytes, tg_stream_t stream);
+
+/*
+ * Workspace bytes tg_gemm_splitk (and tg_gemm_splitk_config with any
+ * configuration) needs for this call: written to *bytes, 0 when no split
+ * would be launched.  Pure host function.
+ * Errors: TG_ERR_NULL_POINTER (bytes NULL), TG_ERR_BAD_DTYPE,
+ *   TG_ERR_BAD_SHAPE (as tg_gemm, or splits < 0).
+ */
+tg_status tg_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                        int splits, size_t* bytes);
 
 /*
  * Weight-only 4-bit dequant GEMM: C = epilogue(A x W^T).
@@ -216,11 +262,13 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
  *   tg_config_count: number of configurations for (op, dtype); 0 if none.
  *   tg_config_name : description of configuration `index` (as tg_query_config).
  *   tg_gemm_config / tg_gemm_ex_config / tg_dequant_gemm_w4_config /
- *     tg_gemm_mx_config / tg_gemm_sp24_config: same contract as tg_gemm /
- *     tg_gemm_ex / tg_dequant_gemm_w4 / tg_gemm_mx / tg_gemm_sp24, launching
- *     configuration `index`; TG_ERR_NO_CONFIG if `index` is out of range or
- *     the configuration cannot run the call (operand layout, alignment, a K
- *     multiple it needs, or another activation format).
+ *     tg_gemm_mx_config / tg_gemm_sp24_config / tg_gemm_splitk_config: same
+ *     contract as tg_gemm / tg_gemm_ex / tg_dequant_gemm_w4 / tg_gemm_mx /
+ *     tg_gemm_sp24 / tg_gemm_splitk, launching configuration `index`;
+ *     TG_ERR_NO_CONFIG if `index` is out of range or the configuration cannot
+ *     run the call (operand layout, alignment, a K multiple it needs, another
+ *     activation format, or, for split K, a configuration without k-slice
+ *     wave groups: names with three wave counts, "_w1x1x4_").
  */
 int tg_config_count(int op, tg_dtype dtype);
 tg_status tg_config_name(int op, tg_dtype dtype, int index, char* buf, size_t len);
@@ -239,6 +287,10 @@ tg_status tg_gemm_mx_config(int index, int64_t M, int64_t N, int64_t K, tg_mx_fo
 tg_status tg_gemm_sp24_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                               const void* Ac, const uint8_t* Ai, const void* B, void* C,
                               tg_epilogue epi, tg_stream_t stream);
+tg_status tg_gemm_splitk_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                const void* A, const void* B, void* C, tg_epilogue epi,
+                                int splits, void* workspace, size_t workspace_bytes,
+                                tg_stream_t stream);
 
 /*
  * The block-swizzled tile order, for host-side checking.  For a grid of

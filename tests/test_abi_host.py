@@ -17,7 +17,7 @@ from tiled_dense_gemm_07_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP, BADL = range(9)
+OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP, BADL, WSP = range(10)
 
 # fake, well-separated device addresses: validation never dereferences them
 PA, PB, PC, PS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -42,7 +42,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         text = binding.status_str(s)
         assert text.startswith("TG_")
     assert "unknown" in binding.status_str(99)
@@ -142,6 +142,57 @@ def test_gemm_ex_argument_errors(lib):
                 assert lib.tg_query_config_ex(0, M, N, K, dt, ta, tb, buf, 128) == OK
                 name = buf.value.decode()
                 assert code in name, (dt, ta, tb, M, name)
+
+
+def _ws_size(lib, M, N, K, dt, splits):
+    out = ctypes.c_size_t(12345)
+    st = lib.tg_gemm_splitk_workspace_size(M, N, K, dt, splits, ctypes.byref(out))
+    return st, out.value
+
+
+def test_splitk_workspace_size(lib):
+    st, n = _ws_size(lib, 256, 256, 8192, 2, 0)
+    assert st == OK and n > 0
+    # counters plus one fp32 partial tile per split, for the largest candidate plan
+    assert n >= 256 * 256 * 4 * 2
+    assert _ws_size(lib, 256, 256, 8192, 2, 1) == (OK, 0)      # no split
+    assert _ws_size(lib, 0, 256, 8192, 2, 0) == (OK, 0)        # nothing to do
+    assert _ws_size(lib, 8192, 8192, 64, 2, 0) == (OK, 0)      # one strip: no split
+    st4, n4 = _ws_size(lib, 256, 256, 8192, 2, 4)
+    st8, n8 = _ws_size(lib, 256, 256, 8192, 2, 8)
+    assert st4 == st8 == OK and 0 < n4 < n8
+    assert _ws_size(lib, 4, 4, 4, 7, 0)[0] == DTYPE
+    assert _ws_size(lib, 4, 4, -1, 2, 0)[0] == SHAPE
+    assert _ws_size(lib, 4, 4, 4, 2, -1)[0] == SHAPE
+    assert lib.tg_gemm_splitk_workspace_size(4, 4, 4, 2, 0, None) == NULLP
+
+
+def test_splitk_argument_errors(lib):
+    g = lib.tg_gemm_splitk
+    M, N, K = 256, 256, 8192
+    _, need = _ws_size(lib, M, N, K, 2, 0)
+    PW = 0x50000000
+    # (M, N, K, dtype, A, B, C, epi, splits, workspace, bytes, stream)
+    assert g(M, N, K, 2, PA, PB, PC, 0, -1, PW, need, None) == SHAPE
+    assert g(M, N, K, 3, PA, PB, PC, 0, 0, PW, need, None) == DTYPE
+    assert g(M, N, K, 2, PA, PB, PC, 5, 0, PW, need, None) == EPI
+    assert g(M, N, K, 2, None, PB, PC, 0, 0, PW, need, None) == NULLP
+    assert g(M, N, K, 2, PA, PB, PA + 64, 0, 0, PW, need, None) == ALIAS
+    assert g(M, N, K, 2, PA, PB, PC, 0, 0, PC + 64, need, None) == ALIAS  # workspace over C
+    assert g(M, N, K, 2, PA, PB, PC, 0, 0, None, 0, None) == WSP
+    assert g(M, N, K, 2, PA, PB, PC, 0, 0, PW, need - 1, None) == WSP
+    assert g(M, N, K, 2, PA, PB, PC, 0, 0, PW + 8, need, None) == WSP    # misaligned
+    assert g(0, N, K, 2, None, None, None, 0, 0, None, 0, None) == OK
+    # forced configurations: a plain one cannot split, an index out of range
+    c = lib.tg_gemm_splitk_config
+    names = binding.list_configs(0, 2)
+    plain = next(i for i, n in enumerate(names) if n.split("_")[3].count("x") == 1)
+    assert c(plain, M, N, K, 2, PA, PB, PC, 0, 2, PW, need, None) == NOCFG
+    assert c(len(names), M, N, K, 2, PA, PB, PC, 0, 2, PW, need, None) == NOCFG
+    split = [i for i, n in enumerate(names) if n.split("_")[3].count("x") == 2]
+    assert split
+    for i in split:
+        assert c(i, M, N, K, 2, PA, PB, PC, 0, 4, None, 0, None) == WSP
 
 
 def test_mx_argument_errors(lib):

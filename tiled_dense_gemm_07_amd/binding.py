@@ -28,7 +28,8 @@ TG_MX_E2M1, TG_MX_E4M3 = 0, 1
 EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_query_config",
            "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
            "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
-           "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config")
+           "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config", "tg_gemm_splitk",
+           "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config")
 
 _lib = None
 
@@ -88,6 +89,15 @@ def load_library():
     lib.tg_gemm_sp24.restype = c_int
     lib.tg_gemm_sp24_config.argtypes = [c_int, i64, i64, i64, c_int, p, p, p, p, c_int, p]
     lib.tg_gemm_sp24_config.restype = c_int
+    lib.tg_gemm_splitk.argtypes = [i64, i64, i64, c_int, p, p, p, c_int, c_int, p,
+                                   ctypes.c_size_t, p]
+    lib.tg_gemm_splitk.restype = c_int
+    lib.tg_gemm_splitk_config.argtypes = [c_int, i64, i64, i64, c_int, p, p, p, c_int, c_int, p,
+                                          ctypes.c_size_t, p]
+    lib.tg_gemm_splitk_config.restype = c_int
+    lib.tg_gemm_splitk_workspace_size.argtypes = [i64, i64, i64, c_int, c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.tg_gemm_splitk_workspace_size.restype = c_int
     _lib = lib
     return lib
 
@@ -172,6 +182,48 @@ def gemm_with_config(index: int, A, B, C=None, epilogue=None, stream=None):
     _check(load_library().tg_gemm_config(index, M, N, K, _dtype_code(A), A.data_ptr(),
                                          B.data_ptr(), C.data_ptr(), _epi_code(epilogue),
                                          _stream_ptr(A.device, stream)))
+    return C
+
+
+def splitk_workspace_size(M: int, N: int, K: int, dtype: int, splits: int = 0) -> int:
+    """Workspace bytes :func:`gemm_splitk` needs for this shape (0: no split)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().tg_gemm_splitk_workspace_size(M, N, K, dtype, splits,
+                                                        ctypes.byref(out)))
+    return out.value
+
+
+def splitk_workspace(M: int, N: int, K: int, dtype: int, splits: int = 0, device="cuda"):
+    """A zero-filled uint8 device tensor large enough for :func:`gemm_splitk`
+    (None when no split would be launched).  Reusable across calls on one stream."""
+    import torch
+
+    n = splitk_workspace_size(M, N, K, dtype, splits)
+    return torch.zeros((n,), dtype=torch.uint8, device=device) if n else None
+
+
+def gemm_splitk(A, B, C=None, epilogue=None, splits: int = 0, workspace=None, stream=None,
+                config=None):
+    """As :func:`gemm`, with each output tile's K range split over `splits`
+    workgroups (0: chosen by the library).  workspace: a zero-filled uint8
+    device tensor of at least :func:`splitk_workspace_size` bytes (allocated
+    here when None).  config: force a compiled configuration by index."""
+    import torch
+
+    M, N, K = _gemm_args(A, B, C)
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    dt = _dtype_code(A)
+    if workspace is None:
+        workspace = splitk_workspace(M, N, K, dt, splits, device=A.device)
+    if workspace is not None:
+        _require_gpu_tensor("workspace", workspace)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib = load_library()
+    args = (M, N, K, dt, A.data_ptr(), B.data_ptr(), C.data_ptr(), _epi_code(epilogue), splits,
+            wp, wn, _stream_ptr(A.device, stream))
+    _check(lib.tg_gemm_splitk(*args) if config is None else lib.tg_gemm_splitk_config(config, *args))
     return C
 
 

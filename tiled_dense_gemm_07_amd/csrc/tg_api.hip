@@ -255,7 +255,7 @@ tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream
     tg::GemmParams p = base;
     p.tiles_m = (int)tiles(p.M, c.bm);
     p.tiles_n = (int)tiles(p.N, c.bn);
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * (p.splits > 1 ? p.splits : 1);
     if (grid > kMaxDim)
         return TG_ERR_BAD_SHAPE;
     const char* fault = getenv("TG_FAULT");
@@ -277,9 +277,88 @@ tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream
     return TG_OK;
 }
 
+// Split K (tg_gemm_splitk): the caller's request and workspace.
+struct SplitArgs {
+    int splits;  // 0: chosen by the library; >= 1: requested
+    void* workspace;
+    size_t bytes;
+};
+
+// How configuration c splits a call: S workgroups per tile over kc k each
+// (whole strips), and the workspace bytes that takes (0 when S == 1).
+struct SplitPlan {
+    int S;
+    int kc;
+    size_t bytes;
+};
+
+constexpr size_t kCounterAlign = 256;
+
+// Automatic split count: about one workgroup per compute unit, each split
+// at least kMinSplitK k deep (1024 for 16-bit operands, 512 for fp32: shorter
+// splits lose more to the pipeline fill and the partial-tile hand-off than
+// the extra workgroups gain), and at most 16 partial tiles for the last
+// workgroup to sum.  Measured on 256^2 x 8192, 128^2 x 16384, 512^2 x 8192 and
+// 64 x 4096 x 4096 (bf16), 256^2 x 4096 and 512^3 (fp32).
+constexpr int kMaxAutoSplits = 16;
+
+SplitPlan split_plan(const Config& c, int64_t M, int64_t N, int64_t K, int splits)
+{
+    const int64_t t = tiles(M, c.bm) * tiles(N, c.bn);
+    const int64_t strips = tiles(K, c.bk);
+    int64_t S = splits;
+    if (S <= 0) {
+        const int64_t kmin = c.dtype == TG_F32 ? 512 : 1024;
+        S = (256 + t - 1) / t;
+        S = S < K / kmin ? S : K / kmin;
+        S = S < kMaxAutoSplits ? S : kMaxAutoSplits;
+    }
+    if (S > strips)
+        S = strips;
+    if (S < 1)
+        S = 1;
+    const int64_t kc = ((strips + S - 1) / S) * c.bk;
+    const int64_t used = K > 0 ? (K + kc - 1) / kc : 1;  // splits with work
+    SplitPlan P{(int)used, (int)kc, 0};
+    if (used > 1)
+        P.bytes = ((size_t)t * 4 + kCounterAlign - 1) / kCounterAlign * kCounterAlign +
+                  (size_t)t * (size_t)used * (size_t)c.bm * (size_t)c.bn * 4;
+    return P;
+}
+
+// Configurations that can split K: the register-staged ones with k-slice
+// wave groups (16-byte loads, plain layouts), larger tiles first.
+int split_candidates(int dtype, const Config** out, int cap)
+{
+    ConfigList L = list_for(TG_OP_GEMM, dtype);
+    int n = 0;
+    for (int i = 0; i < L.count && n < cap; ++i)
+        if (L.items[i].ks > 1 && L.items[i].wide && !L.items[i].ta && !L.items[i].tb)
+            out[n++] = &L.items[i];
+    for (int i = 1; i < n; ++i)  // insertion sort by tile area, descending
+        for (int j = i; j > 0 && out[j]->bm * out[j]->bn > out[j - 1]->bm * out[j - 1]->bn; --j) {
+            const Config* x = out[j];
+            out[j] = out[j - 1];
+            out[j - 1] = x;
+        }
+    return n;
+}
+
+// The split configuration: 64 x 64 tiles with two k-slice groups of 2 x 2
+// waves for 16-bit operands, 32 x 32 tiles with four single-wave groups for
+// fp32 (the fastest split configurations on the shapes above).
+const Config* split_config(const Call& q)
+{
+    static const char* names[3] = {"gemm_f32_32x32x128_w1x1x4_s2_g8_deep",
+                                   "gemm_f16_64x64x128_w2x2x2_s2_g8_deep",
+                                   "gemm_bf16_64x64x128_w2x2x2_s2_g8_deep"};
+    const Config* c = find_by_name(TG_OP_GEMM, q.dtype, names[q.dtype]);
+    return c && usable(*c, q) ? c : nullptr;
+}
+
 tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
                     tg_dtype dtype, const void* A, int trans_a, const void* B, int trans_b,
-                    void* C, tg_epilogue epi, tg_stream_t stream)
+                    void* C, tg_epilogue epi, tg_stream_t stream, const SplitArgs* sk = nullptr)
 {
     if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
         return TG_ERR_BAD_DTYPE;
@@ -293,8 +372,12 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         return s;
     if (trans_a && 64 * M * es > kMaxDim)
         return TG_ERR_BAD_SHAPE;  // per-strip offsets of a [K][M] operand
+    if (sk && sk->splits < 0)
+        return TG_ERR_BAD_SHAPE;
     if (forced_index >= 0 && !forced)
         return TG_ERR_NO_CONFIG;
+    if (sk && forced && forced->ks < 2)
+        return TG_ERR_NO_CONFIG;  // only k-slice configurations split K
     if (M == 0 || N == 0)
         return TG_OK;
     // with K == 0 the operands hold no elements and are never read
@@ -303,15 +386,41 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     const size_t cbytes = (size_t)(M * N * es);
     if (overlaps(C, cbytes, A, (size_t)(M * K * es)) || overlaps(C, cbytes, B, (size_t)(K * N * es)))
         return TG_ERR_ALIAS;
+    if (sk && sk->workspace &&
+        (overlaps(sk->workspace, sk->bytes, C, cbytes) ||
+         overlaps(sk->workspace, sk->bytes, A, (size_t)(M * K * es)) ||
+         overlaps(sk->workspace, sk->bytes, B, (size_t)(K * N * es))))
+        return TG_ERR_ALIAS;
     const int v = vec_of(dtype);
     const int64_t lda = trans_a ? M : K, ldb = trans_b ? K : N;
     Call q{TG_OP_GEMM, dtype, M, N, K, false, false, trans_a != 0, trans_b != 0};
     // NULL is aligned
     q.wide = aligned16(A) && aligned16(B) && (lda % v == 0) && (ldb % v == 0);
-    const Config* c = forced ? forced : select_config(q);
+    const Config* c = forced;
+    SplitPlan plan{1, (int)K, 0};
+    if (sk && (forced || q.wide)) {
+        if (!c)
+            c = split_config(q);
+        if (c && usable(*c, q))
+            plan = split_plan(*c, M, N, K, sk->splits);
+        if (plan.S == 1 && !forced)
+            c = nullptr;  // nothing to split: the plain selection below
+    }
+    if (!c)
+        c = select_config(q);
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
+    if (plan.S > 1 && (!sk->workspace || sk->bytes < plan.bytes || !aligned16(sk->workspace)))
+        return TG_ERR_WORKSPACE;
     tg::GemmParams p{};
+    if (plan.S > 1) {
+        const size_t cnt = ((size_t)tiles(M, c->bm) * tiles(N, c->bn) * 4 + kCounterAlign - 1) /
+                           kCounterAlign * kCounterAlign;
+        p.splits = plan.S;
+        p.kc = plan.kc;
+        p.counters = (int*)sk->workspace;
+        p.ws = (float*)((char*)sk->workspace + cnt);
+    }
     p.A = A;
     p.B = B;
     p.Bs = nullptr;
@@ -464,6 +573,53 @@ tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void
     return gemm_impl(nullptr, -1, M, N, K, dtype, A, trans_a, B, trans_b, C, epi, stream);
 }
 
+tg_status tg_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                        int splits, size_t* bytes)
+{
+    if (!bytes)
+        return TG_ERR_NULL_POINTER;
+    *bytes = 0;
+    if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    tg_status s = check_shape(M, N, K, esize_of(dtype));
+    if (s != TG_OK)
+        return s;
+    if (splits < 0)
+        return TG_ERR_BAD_SHAPE;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    // enough for every split configuration, so forced configurations fit too
+    const Config* cand[16];
+    const int n = split_candidates(dtype, cand, 16);
+    for (int i = 0; i < n; ++i) {
+        const SplitPlan P = split_plan(*cand[i], M, N, K, splits);
+        if (P.bytes > *bytes)
+            *bytes = P.bytes;
+    }
+    return TG_OK;
+}
+
+tg_status tg_gemm_splitk(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A,
+                         const void* B, void* C, tg_epilogue epi, int splits, void* workspace,
+                         size_t workspace_bytes, tg_stream_t stream)
+{
+    const SplitArgs sk{splits, workspace, workspace_bytes};
+    return gemm_impl(nullptr, -1, M, N, K, dtype, A, 0, B, 0, C, epi, stream, &sk);
+}
+
+tg_status tg_gemm_splitk_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                const void* A, const void* B, void* C, tg_epilogue epi,
+                                int splits, void* workspace, size_t workspace_bytes,
+                                tg_stream_t stream)
+{
+    if (dtype != TG_F32 && dtype != TG_F16 && dtype != TG_BF16)
+        return TG_ERR_BAD_DTYPE;
+    ConfigList L = list_for(TG_OP_GEMM, dtype);
+    const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
+    const SplitArgs sk{splits, workspace, workspace_bytes};
+    return gemm_impl(c, index < 0 ? 0 : index, M, N, K, dtype, A, 0, B, 0, C, epi, stream, &sk);
+}
+
 tg_status tg_dequant_gemm_w4(int64_t M, int64_t N, int64_t K, const void* A, const uint8_t* Wq,
                              const uint8_t* Ws, void* C, tg_epilogue epi, tg_stream_t stream)
 {
@@ -507,6 +663,9 @@ const char* tg_status_str(tg_status s)
         return "TG_ERR_HIP: the HIP runtime reported an error at launch";
     case TG_ERR_BAD_LAYOUT:
         return "TG_ERR_BAD_LAYOUT: trans_a and trans_b must be 0 or 1";
+    case TG_ERR_WORKSPACE:
+        return "TG_ERR_WORKSPACE: split-K workspace NULL, smaller than "
+               "tg_gemm_splitk_workspace_size, or not 16-byte aligned";
     }
     return "unknown tg_status";
 }

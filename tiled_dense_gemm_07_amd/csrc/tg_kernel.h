@@ -72,6 +72,15 @@ struct GemmParams {
     int tiles_m, tiles_n;
     int relu;
     int c_vec;  // 1 if C rows allow 4-element vector stores
+    // split K (register-staged kernel with k-slice groups only): splits > 1
+    // workgroups per output tile, each over kc consecutive k (a multiple of
+    // the strip depth); each writes its fp32 partial tile to ws, and the last
+    // to arrive at the tile's counter sums the partials in split order and
+    // runs the epilogue.  splits <= 1: no split, ws and counters unused.
+    int splits;
+    int kc;
+    float* ws;      // [tiles][splits][BM * BN] fp32 partial tiles
+    int* counters;  // [tiles] arrival counts, zero before and after each call
 };
 
 // --------------------------------------------------------------------------
@@ -182,9 +191,10 @@ struct GemmKernel {
         static_assert(X * CPR % NT == 0 && NCH >= 1, "strip must split evenly over threads");
         static constexpr int NREG = NCH;
 
-        // rows x0 .. of an operand with xtot rows of ld = K elements
+        // rows x0 .. of an operand with xtot rows of ld = K elements; k at or
+        // past kend reads as zero
         static __device__ __forceinline__ void load(u32x4 (&dst)[NREG], const void* ptr, int x0,
-                                                    int xtot, int K, int k0, int tid)
+                                                    int xtot, int K, int k0, int kend, int tid)
         {
             const char* base = (const char*)ptr + ((int64_t)x0 * K + k0) * ES;
             const int rows_valid = xtot - x0;
@@ -199,13 +209,13 @@ struct GemmKernel {
                 const bool rv = row < rows_valid;
                 const u32 off = (u32)(row * K + kk) * ES;
                 if (WIDE) {
-                    const bool v = rv && (k0 + kk < K);
+                    const bool v = rv && (k0 + kk < kend);
                     dst[i] = buf_load16(rs, v ? off : kOob);
                 } else {
                     u32 w[4] = {0, 0, 0, 0};
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const bool v = rv && (k0 + kk + e < K);
+                        const bool v = rv && (k0 + kk + e < kend);
                         const u32 o = v ? off + e * ES : kOob;
                         if (ES == 4)
                             w[e] = buf_load4(rs, o);
@@ -243,9 +253,10 @@ struct GemmKernel {
         static_assert(UW * ES >= 4, "loads of at least 4 bytes");
         static constexpr int NREG = NU * VEC;
 
-        // columns x0 .. of an operand stored as K rows of ld = xtot elements
+        // columns x0 .. of an operand stored as K rows of ld = xtot elements;
+        // rows at or past kend read as zero
         static __device__ __forceinline__ void load(u32x4 (&dst)[NREG], const void* ptr, int x0,
-                                                    int xtot, int K, int k0, int tid)
+                                                    int xtot, int K, int k0, int kend, int tid)
         {
             const int ld = xtot;
             const char* base = (const char*)ptr + ((int64_t)k0 * ld + x0) * ES;
@@ -260,7 +271,7 @@ struct GemmKernel {
 #pragma unroll
                 for (int r = 0; r < VEC; ++r) {
                     const int kr = kg * VEC + r;  // k row within the strip
-                    const bool kv = k0 + kr < K;
+                    const bool kv = k0 + kr < kend;
                     const u32 off = (u32)(kr * ld + nn) * ES;
                     u32x4 w = {0, 0, 0, 0};
                     if (WIDE) {
@@ -352,17 +363,18 @@ struct GemmKernel {
     };
 
     // ---- global -> registers --------------------------------------------
+    // strip k0 .. k0 + BK; k at or past kend reads as zero
     static __device__ __forceinline__ void load_a(Regs& R, const GemmParams& p, int m0, int k0,
-                                                  int tid)
+                                                  int kend, int tid)
     {
-        OpA::load(R.a, p.A, m0, p.M, p.K, k0, tid);
+        OpA::load(R.a, p.A, m0, p.M, p.K, k0, kend, tid);
     }
 
     static __device__ __forceinline__ void load_b(Regs& R, const GemmParams& p, int n0, int k0,
-                                                  int tid)
+                                                  int kend, int tid)
     {
         if constexpr (BMODE == B_KN) {
-            OpB::load(R.b, p.B, n0, p.N, p.K, k0, tid);
+            OpB::load(R.b, p.B, n0, p.N, p.K, k0, kend, tid);
         } else {
             // packed codes: row n has K/2 bytes; this strip covers bytes k0/2 .. (k0+BK)/2
             const int rows_valid = p.N - n0;
@@ -626,8 +638,8 @@ struct GemmKernel {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s) {
             if (s < KT) {
-                load_a(R, p, m0, s * BK, tid);
-                load_b(R, p, n0, s * BK, tid);
+                load_a(R, p, m0, s * BK, p.K, tid);
+                load_b(R, p, n0, s * BK, p.K, tid);
                 store_lds(R, smem + s * STAGE_BYTES, tid);
             }
         }
@@ -636,8 +648,8 @@ struct GemmKernel {
         for (int it = 0; it < KT; ++it) {
             const int nxt = it + STAGES - 1;
             if (nxt < KT) {
-                load_a(R, p, m0, nxt * BK, tid);
-                load_b(R, p, n0, nxt * BK, tid);
+                load_a(R, p, m0, nxt * BK, p.K, tid);
+                load_b(R, p, n0, nxt * BK, p.K, tid);
             }
             compute(acc, smem + (it % STAGES) * STAGE_BYTES, ks * NSL, wm, wn, lane);
             if (nxt < KT)
@@ -658,9 +670,9 @@ struct GemmKernel {
     // first slab of the next strip right after the one barrier per strip.
     static __device__ __forceinline__ void strip_deep(f32x16 (&acc)[FM][FN], Regs& R,
                                                       Frags& Fa, Frags& Fb, char* smem,
-                                                      const GemmParams& p, int it, int KT,
-                                                      int m0, int n0, int s0, int wm, int wn,
-                                                      int tid, int lane)
+                                                      const GemmParams& p, int it, int kbeg,
+                                                      int kend, int m0, int n0, int s0, int wm,
+                                                      int wn, int tid, int lane)
     {
         static_assert(NSL % 2 == 0 && NSL >= 2, "slab fragments alternate in pairs");
         char* cur = smem + (it & 1) * STAGE_BYTES;
@@ -676,8 +688,8 @@ struct GemmKernel {
             // nothing uses, which keeps the wait counters exact.
             if (s == NSL - 2) {
                 store_lds(R, nxt, tid);
-                load_a(R, p, m0, (it + 3) * BK, tid);
-                load_b(R, p, n0, (it + 3) * BK, tid);
+                load_a(R, p, m0, kbeg + (it + 3) * BK, kend, tid);
+                load_b(R, p, n0, kbeg + (it + 3) * BK, kend, tid);
             }
             if (s == NSL - 1) {
                 __syncthreads();
@@ -699,10 +711,16 @@ struct GemmKernel {
         const int wm = w2 / WGN;
         const int wn = w2 % WGN;
         const int s0 = ks * NSL;
-        const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        // split K: the workgroups of one tile are consecutive ids
+        const int S = (KS > 1 && p.splits > 1) ? p.splits : 1;
+        const int tile = S > 1 ? (int)blockIdx.x / S : (int)blockIdx.x;
+        const int sp = (int)blockIdx.x - tile * S;
+        const int kbeg = S > 1 ? sp * p.kc : 0;
+        const int kend = S > 1 ? min(p.K, kbeg + p.kc) : p.K;
+        const TileCoord t = tile_of(tile, p.tiles_m, p.tiles_n, GROUP_M);
         const int m0 = t.m * BM;
         const int n0 = t.n * BN;
-        const int KT = (p.K + BK - 1) / BK;
+        const int KT = (kend - kbeg + BK - 1) / BK;
 
         f32x16 acc[FM][FN];
 #pragma unroll
@@ -715,24 +733,115 @@ struct GemmKernel {
 
         Regs X, Y;
         Frags Fa, Fb;
-        // strips at or past KT load as zeros (all offsets out of range)
-        load_a(X, p, m0, 0, tid);
-        load_b(X, p, n0, 0, tid);
+        // strips at or past kend load as zeros (all offsets out of range)
+        load_a(X, p, m0, kbeg, kend, tid);
+        load_b(X, p, n0, kbeg, kend, tid);
         store_lds(X, smem, tid);
-        load_a(X, p, m0, BK, tid);
-        load_b(X, p, n0, BK, tid);
-        load_a(Y, p, m0, 2 * BK, tid);
-        load_b(Y, p, n0, 2 * BK, tid);
+        load_a(X, p, m0, kbeg + BK, kend, tid);
+        load_b(X, p, n0, kbeg + BK, kend, tid);
+        load_a(Y, p, m0, kbeg + 2 * BK, kend, tid);
+        load_b(Y, p, n0, kbeg + 2 * BK, kend, tid);
         __syncthreads();
         read_frags(Fa, smem, s0, wm, wn, lane);
         // an even number of strips: a trailing all-zero strip adds nothing
         for (int it = 0; it < KT; it += 2) {
-            strip_deep(acc, X, Fa, Fb, smem, p, it, KT, m0, n0, s0, wm, wn, tid, lane);
-            strip_deep(acc, Y, Fa, Fb, smem, p, it + 1, KT, m0, n0, s0, wm, wn, tid, lane);
+            strip_deep(acc, X, Fa, Fb, smem, p, it, kbeg, kend, m0, n0, s0, wm, wn, tid, lane);
+            strip_deep(acc, Y, Fa, Fb, smem, p, it + 1, kbeg, kend, m0, n0, s0, wm, wn, tid,
+                       lane);
         }
         reduce_slices(acc, smem, ks, w2, lane);
+        if constexpr (KS > 1) {
+            if (S > 1) {
+                split_fixup(acc, smem, p, tile, sp, S, m0, n0, ks, w2, wm, wn, tid, lane);
+                return;
+            }
+        }
         if (ks == 0)
             epilogue(acc, p, m0, n0, wm, wn, lane);
+    }
+
+    // Split K: every workgroup of the tile stores its partial tile (k-slice
+    // group 0's sums) and counts itself in at the tile's counter; the last to
+    // arrive resets the counter, sums all partials in split order 0 .. S-1
+    // (its own from registers), so the result does not depend on arrival
+    // order, and runs the epilogue.  No workgroup waits for another.
+    //
+    // The partial tiles are written and read with device-scope cache policy
+    // (the write goes through this XCD's L2 to memory, the read does not take
+    // a stale line from another XCD's L2), so the hand-off needs no L2
+    // write-back or invalidate: the stores are complete (vmcnt drained at the
+    // barrier) before thread 0's device-scope atomic counts the workgroup in.
+    static constexpr int kDeviceScope = 16;  // SC1: coherent across the device's L2s
+
+    static __device__ __forceinline__ void split_fixup(const f32x16 (&acc)[FM][FN], char* smem,
+                                                       const GemmParams& p, int tile, int sp,
+                                                       int S, int m0, int n0, int ks, int w2,
+                                                       int wm, int wn, int tid, int lane)
+    {
+        constexpr int WB = FM * FN * 64 * 64;  // bytes of one wave's accumulators
+        const auto rs = make_rsrc(p.ws + (int64_t)tile * S * (BM * BN), (u32)(S * BM * BN * 4));
+        if (ks == 0) {
+            const u32 dst = (u32)(sp * (BM * BN * 4) + w2 * WB);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        // whole-vector cast: clang reads element 0 when
+                        // __builtin_bit_cast is applied to a vector element
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, f32x4{acc[fm][fn][4 * q],
+                                                            acc[fm][fn][4 * q + 1],
+                                                            acc[fm][fn][4 * q + 2],
+                                                            acc[fm][fn][4 * q + 3]}),
+                            rs, (int)(dst + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16), 0,
+                            kDeviceScope);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+        __syncthreads();
+        int* flag = (int*)smem;
+        if (tid == 0) {
+            const int old = atomicAdd(p.counters + tile, 1);
+            const int last = old == S - 1;
+            if (last)
+                atomicExch(p.counters + tile, 0);
+            *flag = last;
+        }
+        __syncthreads();
+        if (!*flag || ks != 0)
+            return;
+        f32x16 sum[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sum[fm][fn][r] = 0.0f;
+        for (int g = 0; g < S; ++g) {
+            const u32 src = (u32)(g * (BM * BN * 4) + w2 * WB);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v;
+                        if (g == sp)
+                            v = f32x4{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1],
+                                      acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]};
+                        else
+                            v = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, (int)(src + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16),
+                                           0, kDeviceScope));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sum[fm][fn][4 * q + e] += v[e];
+                    }
+        }
+        epilogue(sum, p, m0, n0, wm, wn, lane);
     }
 };
 
