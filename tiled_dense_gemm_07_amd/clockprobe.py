@@ -38,6 +38,8 @@ def load():
     lib.tgp_mfma_ceiling.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int,
                                                              ctypes.c_void_p]
     lib.tgp_mfma_ceiling.restype = ctypes.c_int
+    lib.tgp_mfma16_ceiling.argtypes = lib.tgp_mfma_ceiling.argtypes
+    lib.tgp_mfma16_ceiling.restype = ctypes.c_int
     lib.tgp_mx_operand_words.argtypes = [ctypes.c_int]
     lib.tgp_mx_operand_words.restype = ctypes.c_int
     lib.tgp_mx_ceiling.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 3 + [
@@ -46,10 +48,12 @@ def load():
     return lib
 
 
-def measure(data: str = "random", launches: int = 20, warmup: int = 3) -> dict:
+def measure(data: str = "random", launches: int = 20, warmup: int = 3, shape: int = 32) -> dict:
+    """shape 32: v_mfma_f32_32x32x16_bf16; 16: v_mfma_f32_16x16x32_bf16."""
     import torch
 
     lib = load()
+    entry = lib.tgp_mfma_ceiling if shape == 32 else lib.tgp_mfma16_ceiling
     dev = torch.device("cuda:0")
     words = lib.tgp_operand_words(GRID)
     g = torch.Generator(device=dev).manual_seed(20260001)
@@ -63,8 +67,8 @@ def measure(data: str = "random", launches: int = 20, warmup: int = 3) -> dict:
     s = ctypes.c_void_p(stream.cuda_stream)
 
     def launch():
-        rc = lib.tgp_mfma_ceiling(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()),
-                                  ctypes.c_void_p(clk.data_ptr()), GRID, STRIPS, s)
+        rc = entry(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                   ctypes.c_void_p(clk.data_ptr()), GRID, STRIPS, s)
         if rc != 0:
             raise RuntimeError("probe launch failed (%d)" % rc)
 
@@ -81,7 +85,8 @@ def measure(data: str = "random", launches: int = 20, warmup: int = 3) -> dict:
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     med = ts[len(ts) // 2]
     ticks, real = clk.cpu().tolist()
-    return {"data": data, "median_ms": round(med, 5), "tflops": round(FLOPS / med / 1e9, 1),
+    return {"mfma": "%dx%d" % (shape, shape), "data": data, "median_ms": round(med, 5),
+            "tflops": round(FLOPS / med / 1e9, 1),
             "clock_ghz": round(ticks / (real * 10.0), 3) if real > 0 else None}
 
 
@@ -134,8 +139,9 @@ def measure_mx(fmt: int, data: str = "random", launches: int = 10, warmup: int =
 
 
 def main():
-    for data in ("random", "zeros"):
-        print(json.dumps(measure(data)), flush=True)
+    for shape in (32, 16):
+        for data in ("random", "zeros"):
+            print(json.dumps(measure(data, shape=shape)), flush=True)
     for fmt in (0, 1):
         for data in ("random", "zeros"):
             print(json.dumps(measure_mx(fmt, data)), flush=True)

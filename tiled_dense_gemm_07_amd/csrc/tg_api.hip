@@ -89,9 +89,9 @@ struct Pref {
 const Pref kPrefs[] = {
     // grids below about one tile per compute unit fall through to the last
     // entry: 32 x 32 tiles with four k-slice wave groups
-    {0, 2, {"gemm_bf16_256x256x32_w2x2_s4_g4_dma", "gemm_bf16_128x128x32_w2x2_s4_g8_dma",
+    {0, 2, {"gemm_bf16_256x256x64_w2x4_s2_g4_dma", "gemm_bf16_128x128x32_w2x2_s4_g8_dma",
             "gemm_bf16_64x64x128_w2x2x2_s2_g8_deep", "gemm_bf16_32x32x256_w1x1x4_s2_g8_deep"}},
-    {0, 1, {"gemm_f16_256x256x32_w2x2_s4_g4_dma", "gemm_f16_128x128x32_w2x2_s4_g8_dma",
+    {0, 1, {"gemm_f16_256x256x64_w2x4_s2_g4_dma", "gemm_f16_128x128x32_w2x2_s4_g8_dma",
             "gemm_f16_64x64x128_w2x2x2_s2_g8_deep", "gemm_f16_32x32x256_w1x1x4_s2_g8_deep"}},
     {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x64_w2x2x2_s2_g8_deep",
             "gemm_f32_32x32x128_w1x1x4_s2_g8_deep", nullptr}},

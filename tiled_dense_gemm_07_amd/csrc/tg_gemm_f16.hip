@@ -9,6 +9,10 @@ static const Config kCfg[] = {
     // 64 k per strip: whole 128-byte row segments of A, two stages
     TG_CONFIG_DMA_BK(DT_F16, false, false, 256, 256, 2, 2, 2, 4, 64),
     TG_CONFIG_DMA_BK(DT_F16, false, false, 256, 256, 2, 2, 2, 8, 64),
+    // eight waves, two per SIMD (128 x 64 wave tiles)
+    TG_CONFIG_DMA_BK(DT_F16, false, false, 256, 256, 2, 4, 2, 4, 64),
+    TG_CONFIG_DMA_BK(DT_F16, false, false, 256, 256, 4, 2, 2, 4, 64),
+    TG_CONFIG_DMA(DT_F16, false, false, 256, 256, 2, 4, 3, 4),
     TG_CONFIG_DMA(DT_F16, false, false, 256, 256, 2, 2, 4, 4),
     TG_CONFIG_DMA(DT_F16, false, false, 256, 256, 2, 2, 4, 8),
     TG_CONFIG_DMA(DT_F16, false, false, 256, 256, 2, 2, 3, 4),

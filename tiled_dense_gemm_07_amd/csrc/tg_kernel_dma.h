@@ -211,6 +211,35 @@ struct DmaOperand {
     }
 };
 
+// Write-back of a staged result tile from LDS (rows of 2 CH 16-byte chunks,
+// chunk c of row r at c ^ (r % CH)) to C, RPI rows per store instruction.
+// The stores use the system-coherent write-through policy (SC0 SC1): the
+// results stream to memory as they are stored instead of sitting dirty in
+// L2 for the end-of-kernel write-back, which all tiles reach at once.
+// Measured on the 4096^3 bf16 kernel: 108.3 -> 104.2 us.  Each group of RPI
+// rows gets its own buffer base (uniform), so offsets stay below RPI rows.
+constexpr int kStoreThrough = 17;  // SC0 | SC1
+
+template <int WTM, int RPI, int CH>
+__device__ __forceinline__ void store_rows_through(const lds_char* st, const GemmParams& p,
+                                                   int mw0, int nw0, int lane)
+{
+    constexpr int ROWB = CH * 16;
+    const int c = lane % CH;
+    const int rl = lane / CH;  // row within a store instruction
+    const int n = nw0 + 8 * c;
+    const u32 off = (u32)(rl * p.N + 8 * c) * 2u;
+    uint16_t* C = (uint16_t*)p.C;
+#pragma unroll 4
+    for (int r0 = 0; r0 < WTM; r0 += RPI) {
+        const int r = r0 + rl;
+        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
+        const auto rs = make_rsrc(C + ((int64_t)(mw0 + r0) * p.N + nw0), 0x7FFFFFFFu);
+        if (mw0 + r < p.M && n < p.N)
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, kStoreThrough);
+    }
+}
+
 // Coalesced store of one wave's WTM x WTN result tile (FM x FN blocks of
 // 32 x 32 fp32, the MFMA layout where lane l holds row l % 32 and, for
 // element 4 q + e, column 8 q + 4 (l / 32) + e of its block).  The tile is
@@ -253,17 +282,7 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
     constexpr int RPI = 64 / CH;  // rows per store instruction
-    const int c = lane % CH;
-    const int n = nw0 + 8 * c;
-    uint16_t* C = (uint16_t*)p.C;
-#pragma unroll 4
-    for (int r0 = 0; r0 < WTM; r0 += RPI) {
-        const int r = r0 + lane / CH;
-        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
-        const int m = mw0 + r;
-        if (m < p.M && n < p.N)
-            *(u32x4*)(C + (int64_t)m * p.N + n) = v;
-    }
+    store_rows_through<WTM, RPI, CH>(st, p, mw0, nw0, lane);
 }
 
 // As store_tile_staged, for result blocks in the other MFMA orientation: lane
@@ -296,17 +315,7 @@ __device__ __forceinline__ void store_tile_staged_t(const f32x16 (&acc)[FM][FN],
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
     constexpr int RPI = 64 / CH;
-    const int c = lane % CH;
-    const int n = nw0 + 8 * c;
-    uint16_t* C = (uint16_t*)p.C;
-#pragma unroll 4
-    for (int r0 = 0; r0 < WTM; r0 += RPI) {
-        const int r = r0 + lane / CH;
-        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
-        const int m = mw0 + r;
-        if (m < p.M && n < p.N)
-            *(u32x4*)(C + (int64_t)m * p.N + n) = v;
-    }
+    store_rows_through<WTM, RPI, CH>(st, p, mw0, nw0, lane);
 }
 
 // TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].  BK: k per
@@ -334,7 +343,7 @@ struct DmaGemm {
 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole 32x32 blocks");
     static_assert(NS >= 2 && NS <= 5, "two to five stages");
-    static_assert(NW <= 4, "the main loop is instantiated for up to four waves");
+    static_assert(NW <= 8, "the main loop is instantiated for up to eight waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     struct Frag {
@@ -624,8 +633,20 @@ struct DmaGemm {
         case 2:
             main_loop<2 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
-        default:
+        case 3:
             main_loop<3 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 4:
+            main_loop<4 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 5:
+            main_loop<5 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 6:
+            main_loop<6 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            break;
+        default:
+            main_loop<7 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         }
         // drain the copies of the strips past the end (all out of range)
@@ -641,17 +662,19 @@ struct DmaGemm {
     }
 };
 
-// Waves per SIMD the kernel is compiled for: one for the largest tiles (all
-// 512 registers of a lane available, 256 of them accumulators), else two.
-template <int BM, int BN>
+// Waves per SIMD the kernel is compiled for: one for the largest tiles on
+// four waves (all 512 registers of a lane available, 256 of them
+// accumulators), else two.
+template <int BM, int BN, int NW>
 struct DmaOcc {
-    static constexpr int value = BM * BN >= 256 * 128 ? 1 : 2;
+    static constexpr int value = (BM * BN >= 256 * 128 && NW <= 4) ? 1 : 2;
 };
 
 template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M,
           int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
-                          amdgpu_waves_per_eu(DmaOcc<BM, BN>::value, DmaOcc<BM, BN>::value))) void
+                          amdgpu_waves_per_eu(DmaOcc<BM, BN, WGM * WGN>::value,
+                                              DmaOcc<BM, BN, WGM * WGN>::value))) void
 gemm_dma_kernel(GemmParams p)
 {
     DmaGemm<DT, TA, TB, BM, BN, WGM, WGN, NS, GROUP_M, BK>::run(p);

@@ -74,6 +74,58 @@ mfma_ceiling(const u32x4* __restrict__ src, float* __restrict__ out, uint64_t* _
     }
 }
 
+// The same MFMA work as mfma_ceiling with the 16 x 16 x 32 bf16 instruction:
+// twice the instructions of half the size (8 x 8 blocks of 16 x 16 per wave,
+// 64 v_mfma_f32_16x16x32_bf16 per strip), same accumulator registers.
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+mfma16_ceiling(const u32x4* __restrict__ src, float* __restrict__ out, uint64_t* __restrict__ clk,
+               int strips)
+{
+    const int tid = threadIdx.x;
+    uint64_t c0 = 0, r0 = 0;
+    if (blockIdx.x == 0 && tid == 0) {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    const u32x4* s = src + (size_t)(blockIdx.x * 256 + tid) * 2 * kFrag;
+    u32x4 a[kFrag], b[kFrag];
+#pragma unroll
+    for (int i = 0; i < kFrag; ++i) {
+        a[i] = s[i];
+        b[i] = s[kFrag + i];
+    }
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < strips; ++t) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, b[j]), __builtin_bit_cast(bf16x8, a[(i + t) % kFrag]),
+                    acc[i][j], 0, 0, 0);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sum += acc[i][j][r];
+    out[blockIdx.x * 256 + tid] = sum;
+    if (blockIdx.x == 0 && tid == 0) {
+        clk[0] = __builtin_amdgcn_s_memtime() - c0;
+        clk[1] = __builtin_amdgcn_s_memrealtime() - r0;
+    }
+}
+
 // The same for the MX-format GEMM at 8192^3: one workgroup of 4 waves per
 // tile of its grid, each wave issuing the scaled MFMAs of the kernel (64
 // strips x 2 k-steps x FM x FN v_mfma_scale_f32_32x32x64_f8f6f4 on register
@@ -153,6 +205,17 @@ int tgp_mfma_ceiling(const void* src, void* out, void* clk, int grid, int strips
     if (!src || !out || !clk || grid < 1 || strips < 1)
         return 1;
     hipLaunchKernelGGL(mfma_ceiling, dim3(grid), dim3(256), 0, stream, (const u32x4*)src,
+                       (float*)out, (uint64_t*)clk, strips);
+    return hipPeekAtLastError() == hipSuccess ? 0 : 2;
+}
+
+// As tgp_mfma_ceiling, with the 16 x 16 x 32 instruction (same operand buffer).
+int tgp_mfma16_ceiling(const void* src, void* out, void* clk, int grid, int strips,
+                       hipStream_t stream)
+{
+    if (!src || !out || !clk || grid < 1 || strips < 1)
+        return 1;
+    hipLaunchKernelGGL(mfma16_ceiling, dim3(grid), dim3(256), 0, stream, (const u32x4*)src,
                        (float*)out, (uint64_t*)clk, strips);
     return hipPeekAtLastError() == hipSuccess ? 0 : 2;
 }
