@@ -299,6 +299,18 @@ def test_query_config(lib):
     assert lib.tg_query_config(1, 64, 64, 40, 2, buf, 8) == SHAPE
 
 
+def test_tile_choice_fills_whole_rounds():
+    """Large 16-bit grids take the tile shape whose grid fills its last round of
+    256 workgroups best; small grids take k-slice configurations."""
+    q = lambda M, N, K, dt=binding.TG_BF16: binding.query_config(0, M, N, K, dt).split()[0]
+    assert q(3072, 3072, 3072).startswith("gemm_bf16_192x256x64")   # 192 tiles vs 144
+    assert q(6144, 4096, 4096).startswith("gemm_bf16_192x256x64")   # 2 rounds vs 1.5
+    assert q(8192, 8192, 8192).startswith("gemm_bf16_256x256x64")   # 4 whole rounds
+    assert q(2048, 2048, 8192).startswith("gemm_bf16_128x128x32")
+    assert q(1024, 1024, 1024, binding.TG_F16) == "gemm_f16_64x64x128_w2x2x2_s2_g8_deep"
+    assert q(512, 512, 8192) == "gemm_bf16_32x32x256_w1x1x4_s2_g8_deep"
+
+
 def test_config_lists(lib):
     for op, dt in ((0, 0), (0, 1), (0, 2), (1, 2)):
         names = binding.list_configs(op, dt)

@@ -154,6 +154,56 @@ bool usable(const Config& c, const Call& q)
     return true;
 }
 
+// Large 16-bit GEMMs: the LDS-DMA tile shapes, with the workgroups each
+// compute unit holds and the throughput per unit of tile area relative to
+// 256 x 256 when every compute unit is busy (measured: 4096^3, 6144 x 4096 x
+// 4096 and 8192^3 on MI355X).  The run time of a grid is about
+// ceil(tiles / slots) rounds of one tile each, so a smaller tile wins when it
+// fills the last round better: 3072^3 takes 144 tiles of 256 x 256 (one round
+// of 65536-element tiles) but 192 of 192 x 256 (one round, 25% less work per
+// tile).
+struct CostPref {
+    int dtype;
+    const char* name;
+    int per_cu;  // workgroups resident per compute unit (LDS)
+    float eff;   // throughput per tile area relative to 256 x 256
+};
+const CostPref kCostPrefs[] = {
+    {TG_BF16, "gemm_bf16_256x256x64_w2x4_s2_g4_dma", 1, 1.0f},
+    {TG_BF16, "gemm_bf16_192x256x64_w2x4_s2_g4_dma", 1, 0.94f},
+    {TG_BF16, "gemm_bf16_128x128x32_w2x2_s4_g8_dma", 2, 0.38f},
+    {TG_F16, "gemm_f16_256x256x64_w2x4_s2_g4_dma", 1, 1.0f},
+    {TG_F16, "gemm_f16_192x256x64_w2x4_s2_g4_dma", 1, 0.94f},
+    {TG_F16, "gemm_f16_128x128x32_w2x2_s4_g8_dma", 2, 0.38f},
+};
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+// The cheapest of kCostPrefs for the call, or nullptr when even that leaves
+// more than half the compute units idle (the small-grid configurations of
+// the preference lists serve those).
+const Config* cost_choice(const Call& q)
+{
+    const Config* best = nullptr;
+    double best_cost = 0.0;
+    int64_t best_tiles = 0;
+    for (const CostPref& cp : kCostPrefs) {
+        if (cp.dtype != q.dtype)
+            continue;
+        const Config* c = find_by_name(q.op, q.dtype, cp.name);
+        if (!c || !usable(*c, q))
+            continue;
+        const int64_t t = tiles(q.M, c->bm) * tiles(q.N, c->bn);
+        const int64_t slots = kComputeUnits * cp.per_cu;
+        const double cost = (double)((t + slots - 1) / slots) * c->bm * c->bn / cp.eff;
+        if (!best || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+            best_tiles = t;
+        }
+    }
+    return best && best_tiles >= kComputeUnits / 2 ? best : nullptr;
+}
+
 const Config* heuristic(const Call& q)
 {
     ConfigList L = list_for(q.op, q.dtype);
@@ -166,6 +216,10 @@ const Config* heuristic(const Call& q)
     // few activation rows: the run time is the weight stream from HBM
     if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16) {
         if (const Config* c = gemv_for(q.K))
+            return c;
+    }
+    if (q.op == TG_OP_GEMM && q.dtype != TG_F32 && !q.ta && !q.tb) {
+        if (const Config* c = cost_choice(q))
             return c;
     }
     for (const Pref& pr : kPrefs) {

@@ -13,6 +13,9 @@ static const Config kCfg[] = {
     TG_CONFIG_DMA_BK(DT_BF16, false, false, 256, 256, 2, 4, 2, 4, 64),
     TG_CONFIG_DMA_BK(DT_BF16, false, false, 256, 256, 4, 2, 2, 4, 64),
     TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 4, 3, 4),
+    // 192-row tiles: grids that divide into whole waves of 256 workgroups
+    TG_CONFIG_DMA_BK(DT_BF16, false, false, 192, 256, 2, 4, 2, 4, 64),
+    TG_CONFIG_DMA_BK(DT_BF16, false, false, 192, 256, 2, 2, 2, 4, 64),
     TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 4, 4),
     TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 4, 8),
     TG_CONFIG_DMA(DT_BF16, false, false, 256, 256, 2, 2, 3, 4),
