@@ -95,7 +95,7 @@ const Pref kPrefs[] = {
             "gemm_f16_64x64x128_w2x2x2_s2_g8_deep", "gemm_f16_32x32x256_w1x1x4_s2_g8_deep"}},
     {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x64_w2x2x2_s2_g8_deep",
             "gemm_f32_32x32x128_w1x1x4_s2_g8_deep", nullptr}},
-    {1, 2, {"w4_bf16_64x128x128_w2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
+    {1, 2, {"w4_bf16_64x128x128_w1x2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
             "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
     {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g8_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma_sc8",
             "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr}},

@@ -15,6 +15,16 @@ static const Config kCfg[] = {
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4>},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 8, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 8>},
     tg::Config{1, DT_BF16, 64, 256, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 256, 2, 2, 4, 4>},
+    // k-slice groups: every wave covers the whole tile (1 x 1 x 4) or half
+    // of it (1 x 2 x 2, 2 x 1 x 2) over its share of each strip's k
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 1, 4, 4, 4>, false, 4},
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 2>, false, 2},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 1, 4, 4, 2>, false, 2},
+    tg::Config{1, DT_BF16, 128, 64, 128, 1, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<128, 64, 1, 1, 4, 4, 4>, false, 4},
+    // six-stage rings: more copy bytes in flight per compute unit
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 6, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 6, 4, 2>, false, 2},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 6, 8, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 6, 8>},
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 1, 6, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 1, 6, 4, 4>, false, 4},
     TG_CONFIG(1, DT_BF16, B_W4, 256, 64, 128, 4, 1, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 128, 128, 128, 2, 2, 2, 4, true, 0),
     TG_CONFIG(1, DT_BF16, B_W4, 256, 128, 64, 2, 2, 2, 4, true, 0),

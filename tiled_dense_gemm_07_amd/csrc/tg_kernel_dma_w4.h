@@ -20,6 +20,13 @@
 //    (two ds_read_b128), and its A fragment of slab s is 16-byte chunk 8 h + s.
 //  * Chunk swizzles keep the fragment reads free of bank conflicts: A chunks
 //    are XORed with row & 15, code chunks with the 64-byte-row swizzle.
+//  * K-slice variant (KS = 2 or 4): the four waves form KS groups of
+//    WGM x WGN waves that all cover the whole tile; group q multiplies slabs
+//    q 8/KS .. of every strip (a lane's codes are then 16 or 8 contiguous
+//    bytes, one scale byte), so each A fragment feeds more MFMAs and every
+//    code is expanded once per tile instead of once per wave row.  The KS
+//    partial accumulators are added through LDS after the main loop in group
+//    order 0, 1, ..., KS-1, and group q stores its share of the tile.
 //  * Strips are whole (K % 128 == 0; other K use the register-staged kernel);
 //    out-of-range rows (m >= M, n >= N) and the strips padded past K copy
 //    zeros.  The barrier/copy schedule is the one of the 16-bit DMA kernel:
@@ -43,32 +50,41 @@ __device__ __forceinline__ void dma4(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t r
                  : "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1>
 struct DmaW4 {
     static constexpr int BK = 128;
-    static constexpr int NW = WGM * WGN;
+    static constexpr int NWG = WGM * WGN;   // waves of one k-slice group
+    static constexpr int NW = NWG * KS;     // waves of the workgroup
+    static constexpr int SPW = 8 / KS;      // MFMA slabs of a strip per wave
     static constexpr int WTM = BM / WGM;
     static constexpr int WTN = BN / WGN;
     static constexpr int FM = WTM / 32;
     static constexpr int FN = WTN / 32;
     static constexpr int NM = FM * FN;      // MFMAs per slab
-    static constexpr int SLOTS = 8 * NM;    // MFMAs per strip
+    static constexpr int SLOTS = SPW * NM;  // MFMAs per strip and wave
+    static constexpr int NB = FM * FN;      // 32 x 32 blocks of a wave tile
     static constexpr int A_STAGE = BM * BK * 2;
     static constexpr int W_STAGE = BN * BK / 2;
     static constexpr int S_STAGE = BN * 4;
     static constexpr int W_REGION = NS * A_STAGE;
     static constexpr int S_REGION = W_REGION + NS * W_STAGE;
-    static constexpr int LDS_BYTES = S_REGION + NS * S_STAGE;
+    static constexpr int RING_BYTES = S_REGION + NS * S_STAGE;
+    // k-slice groups add their partial tiles through LDS: one 4 KiB region
+    // per wave and block, reusing the ring after the main loop
+    static constexpr int RED_BYTES = KS > 1 ? NW * NB * 4096 : 0;
+    static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
     static constexpr int JA = A_STAGE / 1024 / NW;  // A copies per wave per strip
     static constexpr int JW = W_STAGE / 1024 / NW;  // code copies per wave per strip
     static constexpr int NSC = S_STAGE / 256;       // scale copies per strip (waves 0 .. NSC-1)
 
     static_assert(NW == 4, "four waves");
+    static_assert(KS == 1 || KS == 2 || KS == 4, "k-slice groups split the 8 slabs of a strip");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && JW >= 1 && A_STAGE % (1024 * NW) == 0 && W_STAGE % (1024 * NW) == 0,
                   "strips split into whole 1 KiB copies per wave");
     static_assert(NSC >= 1 && NSC <= NW && S_STAGE % 256 == 0, "one scale copy per wave at most");
-    static_assert(NS == 4, "four stages (code registers alternate per strip)");
+    static_assert(NS >= 4 && NS % 2 == 0, "an even ring of four or more stages (code registers "
+                                          "alternate per strip)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     template <int W>
@@ -82,22 +98,27 @@ struct DmaW4 {
         u32 a_off[JA];
         u32 w_off[JW];
         u32 s_off;
-        u32 a_rd[8];  // A fragment read offset of slab s (stage 0, fm 0)
-        u32 w_rd[2];  // code chunk 2h, 2h+1 of this lane's row (stage 0, fn 0)
-        u32 s_rd;     // scale bytes 2h, 2h+1 of this lane's row (stage 0, fn 0)
+        u32 a_rd[SPW];  // A fragment read offset of the wave's slab j (stage 0, fm 0)
+        u32 w_rd[2];    // this lane's code bytes (stage 0, fn 0): KS = 1: chunks
+                        // 2h, 2h+1; KS = 2: chunk 2h+q; KS = 4: half of chunk 2h+q/2
+        u32 s_rd;       // scale byte(s) of this lane's row (stage 0, fn 0)
+        __amdgpu_buffer_rsrc_t ra, rw, rs;  // row bands of A, codes, scales
     };
 
     struct Regs {
-        u32x4 code[FN][2];  // 32 bytes = 64 codes per n-block
-        u32 sc[FN];         // two scale bytes (k groups 2h, 2h+1)
+        u32 code[FN][SPW];  // 8 codes per slab and n-block
+        u32 sc[FN];         // scale bytes: KS = 1: k groups 2h, 2h+1; else one byte
     };
 
     static __device__ __forceinline__ int swz16(int r) { return r & 15; }
 
     static __device__ __forceinline__ void setup(Lane& L, const GemmParams& p, int m0, int n0,
-                                                 int w, int lane, int wm, int wn)
+                                                 int w, int lane, int wm, int wn, int q)
     {
         const int K = p.K;
+        L.ra = band(p.A, m0, p.M - m0, K * 2);
+        L.rw = band(p.B, n0, p.N - n0, K / 2);
+        L.rs = band(p.Bs, n0, p.N - n0, K / 32);
 #pragma unroll
         for (int j = 0; j < JA; ++j) {
             const int row = (w * JA + j) * 4 + (lane >> 4);
@@ -117,33 +138,57 @@ struct DmaW4 {
         const int h = lane >> 5;
         const int ar = wm * WTM + (lane & 31);
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            L.a_rd[s] = ar * (BK * 2) + (((8 * h + s) ^ swz16(ar)) << 4);
+        for (int j = 0; j < SPW; ++j)
+            L.a_rd[j] = ar * (BK * 2) + (((8 * h + q * SPW + j) ^ swz16(ar)) << 4);
         const int nr = wn * WTN + (lane & 31);
-        L.w_rd[0] = W_REGION + nr * 64 + (((2 * h) ^ swz_a(nr)) << 4);
-        L.w_rd[1] = W_REGION + nr * 64 + (((2 * h + 1) ^ swz_a(nr)) << 4);
-        L.s_rd = S_REGION + nr * 4 + 2 * h;
+        if (KS == 1) {
+            L.w_rd[0] = W_REGION + nr * 64 + (((2 * h) ^ swz_a(nr)) << 4);
+            L.w_rd[1] = W_REGION + nr * 64 + (((2 * h + 1) ^ swz_a(nr)) << 4);
+            L.s_rd = S_REGION + nr * 4 + 2 * h;
+        } else if (KS == 2) {
+            L.w_rd[0] = W_REGION + nr * 64 + (((2 * h + q) ^ swz_a(nr)) << 4);
+            L.w_rd[1] = L.w_rd[0];
+            L.s_rd = S_REGION + nr * 4 + 2 * h + q;
+        } else {
+            L.w_rd[0] = W_REGION + nr * 64 + (((2 * h + q / 2) ^ swz_a(nr)) << 4) + 8 * (q & 1);
+            L.w_rd[1] = L.w_rd[0];
+            L.s_rd = S_REGION + nr * 4 + 2 * h + q / 2;
+        }
     }
 
+    // Byte offsets of one strip inside a row of A, of the codes and of the
+    // scale bytes.  The buffer resources cover the tile's whole row bands
+    // (set up once, in Lane); the offsets are added to the lane offsets.
+    // Rows past M or N have kOob lane offsets, which stay out of range after
+    // the addition (offsets within a band stay below 2^31); strips past K
+    // copy kOob.
     struct StripRes {
-        __amdgpu_buffer_rsrc_t a, w, s;
+        u32 a, w, s;
         bool valid;
     };
 
-    static __device__ __forceinline__ StripRes strip_res(const GemmParams& p, int m0, int n0,
-                                                         int strip)
+    static __device__ __forceinline__ StripRes strip_res(const GemmParams& p, int, int, int strip)
     {
-        const int K = p.K;
         const int k0 = strip * BK;
         StripRes r;
-        r.valid = k0 < K;
-        r.a = make_rsrc((const char*)p.A + ((int64_t)m0 * K + k0) * 2,
-                        clamp_bytes(((int64_t)(p.M - m0 - 1) * K + (K - k0)) * 2));
-        r.w = make_rsrc((const char*)p.B + (int64_t)n0 * (K / 2) + k0 / 2,
-                        clamp_bytes((int64_t)(p.N - n0 - 1) * (K / 2) + (K - k0) / 2));
-        r.s = make_rsrc((const char*)p.Bs + (int64_t)n0 * (K / 32) + k0 / 32,
-                        clamp_bytes((int64_t)(p.N - n0 - 1) * (K / 32) + (K - k0) / 32));
+        r.valid = k0 < p.K;
+        r.a = (u32)k0 * 2u;
+        r.w = (u32)k0 / 2u;
+        r.s = (u32)k0 / 32u;
         return r;
+    }
+
+    // Resource of `rows` rows of `row_bytes` bytes from base + row0 * row_bytes,
+    // its parts read back as wave-uniform scalars (the 64-bit range arithmetic
+    // may be done on the vector ALU).
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t band(const void* base, int row0,
+                                                                  int rows, int row_bytes)
+    {
+        const uint64_t a = (uint64_t)((const char*)base + (int64_t)row0 * row_bytes);
+        const u32 lo = __builtin_amdgcn_readfirstlane((u32)a);
+        const u32 hi = __builtin_amdgcn_readfirstlane((u32)(a >> 32));
+        const u32 n = __builtin_amdgcn_readfirstlane(clamp_bytes((int64_t)rows * row_bytes));
+        return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), n);
     }
 
     template <int ST, int W>
@@ -151,12 +196,12 @@ struct DmaW4 {
                                                       u32 smem0)
     {
         if (d < JA)
-            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, r.valid ? L.a_off[d] : kOob, r.a);
+            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, r.valid ? L.a_off[d] + r.a : kOob, L.ra);
         else if (d < JA + JW)
             dma16(smem0 + W_REGION + ST * W_STAGE + (W * JW + d - JA) * 1024,
-                  r.valid ? L.w_off[d - JA] : kOob, r.w);
+                  r.valid ? L.w_off[d - JA] + r.w : kOob, L.rw);
         else
-            dma4(smem0 + S_REGION + ST * S_STAGE + W * 256, r.valid ? L.s_off : kOob, r.s);
+            dma4(smem0 + S_REGION + ST * S_STAGE + W * 256, r.valid ? L.s_off + r.s : kOob, L.rs);
     }
 
     template <int ST, int W>
@@ -172,30 +217,52 @@ struct DmaW4 {
     template <int ST>
     static __device__ __forceinline__ void read_codes(Regs& R, const Lane& L, lds_char* sm)
     {
+        typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+        typedef __attribute__((address_space(3))) uint16_t lds_u16;
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            R.code[fn][0] = *(const lds_u32x4*)(sm + L.w_rd[0] + ST * W_STAGE + fn * 32 * 64);
-            R.code[fn][1] = *(const lds_u32x4*)(sm + L.w_rd[1] + ST * W_STAGE + fn * 32 * 64);
-            R.sc[fn] = *(const __attribute__((address_space(3))) uint16_t*)(sm + L.s_rd +
-                                                                            ST * S_STAGE +
-                                                                            fn * 32 * 4);
+            const int wo = ST * W_STAGE + fn * 32 * 64;
+            const int so = ST * S_STAGE + fn * 32 * 4;
+            if constexpr (KS == 1) {
+                const u32x4 c0 = *(const lds_u32x4*)(sm + L.w_rd[0] + wo);
+                const u32x4 c1 = *(const lds_u32x4*)(sm + L.w_rd[1] + wo);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    R.code[fn][e] = c0[e];
+                    R.code[fn][4 + e] = c1[e];
+                }
+                R.sc[fn] = *(const lds_u16*)(sm + L.s_rd + so);
+            } else if constexpr (KS == 2) {
+                const u32x4 c0 = *(const lds_u32x4*)(sm + L.w_rd[0] + wo);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R.code[fn][e] = c0[e];
+                R.sc[fn] = *(const lds_u8*)(sm + L.s_rd + so);
+            } else {
+                const u32x2 c0 = *(const lds_u32x2*)(sm + L.w_rd[0] + wo);
+                R.code[fn][0] = c0[0];
+                R.code[fn][1] = c0[1];
+                R.sc[fn] = *(const lds_u8*)(sm + L.s_rd + so);
+            }
         }
     }
 
     template <int ST>
     static __device__ __forceinline__ void read_a(u32x4 (&af)[FM], const Lane& L, lds_char* sm,
-                                                  int s)
+                                                  int j)
     {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            af[fm] = *(const lds_u32x4*)(sm + L.a_rd[s] + ST * A_STAGE + fm * 32 * BK * 2);
+            af[fm] = *(const lds_u32x4*)(sm + L.a_rd[j] + ST * A_STAGE + fm * 32 * BK * 2);
     }
 
-    // B fragment of n-block fn, slab s: codes 8 s .. 8 s + 7 of the lane's 64.
-    static __device__ __forceinline__ bf16x8 dequant(const Regs& R, int fn, int s)
+    // B fragment of n-block fn, the wave's slab j: its 8 codes, scaled.
+    static __device__ __forceinline__ bf16x8 dequant(const Regs& R, int fn, int j)
     {
-        const u32 packed = R.code[fn][s >> 2][s & 3];
-        const float sc = e8m0_to_f32((R.sc[fn] >> (8 * (s >> 2))) & 0xFFu);
+        const u32 packed = R.code[fn][j];
+        const u32 sbyte = KS == 1 ? (R.sc[fn] >> (8 * (j >> 2))) & 0xFFu : R.sc[fn] & 0xFFu;
+        const float sc = e8m0_to_f32(sbyte);
         u32x4 b;
         b[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0));
         b[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1));
@@ -204,16 +271,18 @@ struct DmaW4 {
         return __builtin_bit_cast(bf16x8, b);
     }
 
-    // A fragments are read PF slabs ahead into a 4-deep ring (slab s of any
-    // strip lives in AF[s % 4]).
-    static constexpr int PF = 3;
+    // A fragments are read PF slabs ahead into a 4-deep ring: the wave's slab
+    // j of stage ST lives in AF[(ST SPW + j) % 4].  PF <= SPW, so a read never
+    // reaches past strip t + 1, which slot 0's barrier has published.
+    static constexpr int PF = SPW < 3 ? SPW : 3;
+    static_assert((NS * SPW) % 4 == 0, "the A ring wraps with the stage cycle");
 
-    // One strip (stage ST) of wave W.  Slot i = MFMA (fm, fn) of slab s with
-    // s = i / NM.  Before slot 0: codes of this strip in R[ST & 1], A slabs
-    // 0 .. PF-1 in the ring.  Slot 0 waits for strip t + 1's copies and
+    // One strip (stage ST) of wave W.  Slot i = MFMA (fm, fn) of the wave's
+    // slab j = i / NM.  Before slot 0: codes of this strip in R[ST & 1], A
+    // slabs 0 .. PF-1 in the ring.  Slot 0 waits for strip t + 1's copies and
     // barriers, then reads strip t + 1's codes into R[(ST + 1) & 1]; the last
-    // slot of slab s reads A slab s + PF (of strip t + 1 past slab 7); the
-    // copies of strip t + NS - 1 are staggered over the slots.
+    // slot of slab j reads A slab j + PF (of strip t + 1 past the wave's
+    // last slab); the copies of strip t + NS - 1 are staggered over the slots.
     template <int ST, int W>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Regs (&R)[2],
                                                  u32x4 (&AF)[4][FM], const Lane& L, lds_char* sm,
@@ -226,9 +295,10 @@ struct DmaW4 {
         StripRes r;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
-            const int s = i / NM, fm = (i % NM) / FN, fn = i % FN;
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dequant(R[CUR], fn, s),
-                                                                  __builtin_bit_cast(bf16x8, AF[s & 3][fm]),
+            const int j = i / NM, fm = (i % NM) / FN, fn = i % FN;
+            const int g = ST * SPW + j;
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dequant(R[CUR], fn, j),
+                                                                  __builtin_bit_cast(bf16x8, AF[g & 3][fm]),
                                                                   acc[fm][fn], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (i == 0) {
@@ -239,10 +309,10 @@ struct DmaW4 {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (i % NM == NM - 1) {
-                if (s + PF < 8)
-                    read_a<ST>(AF[(s + PF) & 3], L, sm, s + PF);
+                if (j + PF < SPW)
+                    read_a<ST>(AF[(g + PF) & 3], L, sm, j + PF);
                 else
-                    read_a<NXT>(AF[(s + PF) & 3], L, sm, s + PF - 8);
+                    read_a<NXT>(AF[(g + PF) & 3], L, sm, j + PF - SPW);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
@@ -255,15 +325,35 @@ struct DmaW4 {
         }
     }
 
+    // Copies of strips 0 .. NS-2 into stages 0 .. NS-2.
+    template <int S, int W>
+    static __device__ __forceinline__ void prologue_copies(const Lane& L, const GemmParams& p,
+                                                           int m0, int n0, u32 smem0)
+    {
+        if constexpr (S < NS - 1) {
+            issue_copies<S, W>(L, p, m0, n0, S, smem0);
+            prologue_copies<S + 1, W>(L, p, m0, n0, smem0);
+        }
+    }
+
+    // Strips t + ST .. t + NS - 1 of one pass around the ring.
+    template <int ST, int W>
+    static __device__ __forceinline__ void strips(f32x16 (&acc)[FM][FN], Regs (&R)[2],
+                                                  u32x4 (&AF)[4][FM], const Lane& L, lds_char* sm,
+                                                  const GemmParams& p, int m0, int n0, int t,
+                                                  u32 smem0)
+    {
+        strip<ST, W>(acc, R, AF, L, sm, p, m0, n0, t + ST, smem0);
+        if constexpr (ST + 1 < NS)
+            strips<ST + 1, W>(acc, R, AF, L, sm, p, m0, n0, t, smem0);
+    }
+
     template <int W>
     static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], const Lane& L,
                                                      lds_char* sm, const GemmParams& p, int m0,
                                                      int n0, int KT, u32 smem0)
     {
-        issue_copies<0, W>(L, p, m0, n0, 0, smem0);
-        issue_copies<1, W>(L, p, m0, n0, 1, smem0);
-        issue_copies<2 % NS, W>(L, p, m0, n0, 2, smem0);
-        static_assert(NS == 4, "prologue and loop written for four stages");
+        prologue_copies<0, W>(L, p, m0, n0, smem0);
         wait_copies_barrier<(NS - 2) * Copies<W>::N>();
         Regs R[2];
         u32x4 AF[4][FM];
@@ -274,74 +364,32 @@ struct DmaW4 {
         // The strip count is rounded up to a multiple of NS: strips at or past
         // KT copy only zeros, which add exactly nothing.
         for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, R, AF, L, sm, p, m0, n0, t, smem0);
-            strip<1, W>(acc, R, AF, L, sm, p, m0, n0, t + 1, smem0);
-            strip<2, W>(acc, R, AF, L, sm, p, m0, n0, t + 2, smem0);
-            strip<3, W>(acc, R, AF, L, sm, p, m0, n0, t + 3, smem0);
+            strips<0, W>(acc, R, AF, L, sm, p, m0, n0, t, smem0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    static __device__ __forceinline__ void run(const GemmParams& p)
+    // Direct (unstaged) store of a wave's MFMA-layout result blocks: lane l
+    // holds row l % 32 and, for element 4 q + e, column 8 q + 4 (l / 32) + e of
+    // its block.  For C rows that are not whole 16-byte chunks.
+    template <int OFM, int OFN>
+    static __device__ __forceinline__ void store_direct(const f32x16 (&acc)[OFM][OFN],
+                                                        const GemmParams& p, int mw0, int nw0,
+                                                        int lane)
     {
-        __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-        lds_char* sm = (lds_char*)smem;
-        const u32 smem0 = lds_offset(smem);
-        const int tid = threadIdx.x;
-        const int lane = tid & 63;
-        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = w / WGN;
-        const int wn = w % WGN;
-        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
-        const int m0 = tc.m * BM;
-        const int n0 = tc.n * BN;
-        const int KT = p.K / BK;
-
-        Lane L;
-        setup(L, p, m0, n0, w, lane, wm, wn);
-        f32x16 acc[FM][FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[fm][fn][r] = 0.0f;
-        switch (w) {
-        case 0:
-            main_loop<0>(acc, L, sm, p, m0, n0, KT, smem0);
-            break;
-        case 1:
-            main_loop<1>(acc, L, sm, p, m0, n0, KT, smem0);
-            break;
-        case 2:
-            main_loop<2>(acc, L, sm, p, m0, n0, KT, smem0);
-            break;
-        default:
-            main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
-            break;
-        }
-        if ((p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0 && NW * WTM * WTN * 2 <= LDS_BYTES) {
-            wait_all_barrier();  // every wave's copies landed and reads done
-            store_tile_staged<DT_BF16, WTM, WTN, FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN,
-                                                        lane, sm + w * (WTM * WTN * 2));
-            return;
-        }
-        // epilogue: same lane layout as the 16-bit DMA kernel (m = lane % 32,
-        // four consecutive n per accumulator quad)
         const int lr = lane & 31;
         const int g = lane >> 5;
         uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = m0 + wm * WTM + fm * 32 + lr;
+        for (int fm = 0; fm < OFM; ++fm) {
+            const int m = mw0 + fm * 32 + lr;
             if (m >= p.M)
                 continue;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
+            for (int fn = 0; fn < OFN; ++fn) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * WTN + fn * 32 + 8 * q + 4 * g;
+                    const int n = nw0 + fn * 32 + 8 * q + 4 * g;
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -361,13 +409,168 @@ struct DmaW4 {
             }
         }
     }
+
+    static __device__ __forceinline__ bool staged_ok(const GemmParams& p)
+    {
+        return (p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0;
+    }
+
+    // k-slice groups: how a wave tile's FM x FN blocks are shared out for the
+    // final sum and store.  Group q owns OFM x OFN blocks, block rows
+    // (q / KSN) OFM .. and block columns (q % KSN) OFN ..
+    static constexpr int KSM = FM < KS ? FM : KS;
+    static constexpr int KSN = KS / KSM;
+    static constexpr int OFM = FM / KSM;
+    static constexpr int OFN = FN / KSN;
+    static_assert(KS == 1 || (FM % KSM == 0 && FN % KSN == 0 && KSM * KSN == KS),
+                  "the wave tile's blocks divide among the k-slice groups");
+    static_assert(RED_BYTES <= 160 * 1024, "partial tiles fit in LDS");
+
+    // Partial block b of wave (group qq, position r) in LDS: four 1 KiB
+    // chunks, chunk c holding elements 4c .. 4c+3 of every lane.
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    static __device__ __forceinline__ int red_off(int r, int qq, int b, int lane)
+    {
+        return ((r * KS + qq) * NB + b) * 4096 + lane * 16;
+    }
+
+    // After the main loop of wave W (group Q): every wave writes the partial
+    // blocks the other groups own, then sums its own blocks over the groups in
+    // order 0 .. KS-1 and stores them.
+    template <int W>
+    static __device__ __forceinline__ void reduce_store(const f32x16 (&acc)[FM][FN],
+                                                        const GemmParams& p, int m0, int n0,
+                                                        int lane, lds_char* sm)
+    {
+        constexpr int Q = W / NWG;
+        constexpr int R = W % NWG;
+        constexpr int WM = R / WGN, WN = R % WGN;
+        constexpr int FM0 = (Q / KSN) * OFM, FN0 = (Q % KSN) * OFN;
+        wait_all_barrier();  // every wave's copies landed and ring reads done
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const bool own = fm >= FM0 && fm < FM0 + OFM && fn >= FN0 && fn < FN0 + OFN;
+                if (own)
+                    continue;
+                const int o = red_off(R, Q, fm * FN + fn, lane);
+                // (float vectors throughout: a bit cast of a single vector
+                // element would read element 0)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *(lds_f32x4*)(sm + o + c * 1024) =
+                        f32x4{acc[fm][fn][4 * c], acc[fm][fn][4 * c + 1], acc[fm][fn][4 * c + 2],
+                              acc[fm][fn][4 * c + 3]};
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        f32x16 sum[OFM][OFN];
+#pragma unroll
+        for (int a = 0; a < OFM; ++a)
+#pragma unroll
+            for (int b = 0; b < OFN; ++b) {
+                const int fm = FM0 + a, fn = FN0 + b;
+#pragma unroll
+                for (int qq = 0; qq < KS; ++qq) {
+                    f32x16 part;
+                    if (qq == Q) {
+                        part = acc[fm][fn];
+                    } else {
+                        const int o = red_off(R, qq, fm * FN + fn, lane);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const f32x4 v = *(const lds_f32x4*)(sm + o + c * 1024);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                part[4 * c + e] = v[e];
+                        }
+                    }
+                    if (qq == 0)
+                        sum[a][b] = part;
+                    else
+                        sum[a][b] += part;
+                }
+            }
+        const int mw0 = m0 + WM * WTM + FM0 * 32;
+        const int nw0 = n0 + WN * WTN + FN0 * 32;
+        if (staged_ok(p)) {
+            // the staging regions overlap the partials other waves still read
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            store_tile_staged<DT_BF16, OFM * 32, OFN * 32, OFM, OFN>(
+                sum, p, mw0, nw0, lane, sm + W * (OFM * 32 * OFN * 32 * 2));
+            return;
+        }
+        store_direct<OFM, OFN>(sum, p, mw0, nw0, lane);
+    }
+
+    template <int W>
+    static __device__ __forceinline__ void body(f32x16 (&acc)[FM][FN], const Lane& L,
+                                                lds_char* sm, const GemmParams& p, int m0,
+                                                int n0, int KT, u32 smem0, int lane, int wm,
+                                                int wn)
+    {
+        main_loop<W>(acc, L, sm, p, m0, n0, KT, smem0);
+        if constexpr (KS > 1) {
+            reduce_store<W>(acc, p, m0, n0, lane, sm);
+        } else {
+            if (staged_ok(p) && NW * WTM * WTN * 2 <= LDS_BYTES) {
+                wait_all_barrier();  // every wave's copies landed and reads done
+                store_tile_staged<DT_BF16, WTM, WTN, FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN,
+                                                            lane, sm + W * (WTM * WTN * 2));
+                return;
+            }
+            store_direct<FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);
+        }
+    }
+
+    static __device__ __forceinline__ void run(const GemmParams& p)
+    {
+        __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+        lds_char* sm = (lds_char*)smem;
+        const u32 smem0 = lds_offset(smem);
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int q = w / NWG;
+        const int wm = (w % NWG) / WGN;
+        const int wn = (w % NWG) % WGN;
+        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const int m0 = tc.m * BM;
+        const int n0 = tc.n * BN;
+        const int KT = p.K / BK;
+
+        Lane L;
+        setup(L, p, m0, n0, w, lane, wm, wn, q);
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[fm][fn][r] = 0.0f;
+        switch (w) {
+        case 0:
+            body<0>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+            break;
+        case 1:
+            body<1>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+            break;
+        case 2:
+            body<2>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+            break;
+        default:
+            body<3>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+            break;
+        }
+    }
 };
 
-template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
-__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64))) void
+template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1>
+__global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * KS * 64, WGM * WGN * KS * 64))) void
 dma_w4_kernel(GemmParams p)
 {
-    DmaW4<BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    DmaW4<BM, BN, WGM, WGN, NS, GROUP_M, KS>::run(p);
 }
 
 }  // namespace tg
