@@ -111,6 +111,10 @@ def test_forced_dequant_config_requirements(lib):
             assert d(idx, 64, 64, 96, PA, PB, PS, PC, 0, None) == NOCFG, name
         if name.endswith("_dma"):
             assert d(idx, 64, 64, 256, PA, PB, PS + 2, PC, 0, None) == NOCFG, name
+        if name.endswith("_sc16"):
+            # scale blocks: K % 512 == 0 and 16-byte aligned scale rows
+            assert d(idx, 64, 64, 256, PA, PB, PS, PC, 0, None) == NOCFG, name
+            assert d(idx, 64, 64, 512, PA, PB, PS + 4, PC, 0, None) == NOCFG, name
 
 
 def test_gemm_ex_argument_errors(lib):

@@ -109,11 +109,22 @@ def test_every_gemm_config(dtype):
         assert np.array_equal(got, want), name
 
 
+def _w4_config_fits(name, K):
+    """Whether a dequant configuration can run this K (whole strips or rounds
+    of its k depth; scale blocks need K % 512 == 0)."""
+    bk = int(name.split("_")[2].split("x")[2])
+    if ("_dma" in name or name.endswith("_gemv")) and K % bk:
+        return False
+    return not ("_sc16" in name and K % 512)
+
+
 def test_every_w4_config():
     M, N, K = 300, 264, 256
     A, Wq, Ws = synth.dequant_inputs(M, N, K, 505, 606, 707, integer=True)
     want = oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws))
     for idx, name in _configs(1, BF16):
+        if not _w4_config_fits(name, K):
+            continue
         say("config %d %s" % (idx, name))
         got = run_w4(A, Wq, Ws, config=idx)
         assert np.array_equal(got, want), name
@@ -136,7 +147,10 @@ def test_dequant_small(shape, integer):
 
 
 @pytest.mark.parametrize("shape", [(300, 264, 256), (70, 130, 384), (64, 128, 128),
-                                   (256, 8192, 1024), (1, 200, 640)],
+                                   (256, 8192, 1024), (1, 200, 640),
+                                   # scale blocks of 16 strips: a row's scale bytes end
+                                   # inside the first block / a second, partial block
+                                   (300, 264, 1536), (130, 200, 2560)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_every_w4_config_ragged(shape):
     """Every dequant configuration this shape allows, forced, with integer
@@ -145,10 +159,7 @@ def test_every_w4_config_ragged(shape):
     A, Wq, Ws = synth.dequant_inputs(M, N, K, 515 + M, 616 + N, 717 + K, integer=True)
     want = oracle.encode(BF16, oracle.dequant_w4_f64(A, Wq, Ws, relu=True))
     for idx, name in _configs(1, BF16):
-        if name.endswith("_narrow"):
-            continue
-        bk = int(name.split("_")[2].split("x")[2])
-        if (name.endswith("_dma") or name.endswith("_gemv")) and K % bk:
+        if name.endswith("_narrow") or not _w4_config_fits(name, K):
             continue
         say("w4 config %d %s %s" % (idx, name, shape))
         got = run_w4(A, Wq, Ws, relu=True, config=idx)

@@ -66,7 +66,7 @@ void config_name(const Config& c, char* buf, size_t len)
              mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
              c.bn, c.bk, wav, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
-             mx ? (c.chunked_scales ? "_sc8" : "") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
+             c.chunked_scales ? (mx ? "_sc8" : "_sc16") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
 }
 
@@ -151,6 +151,8 @@ bool usable(const Config& c, const Call& q)
         return false;  // whole strips / rounds of bk
     if (c.op == TG_OP_DEQUANT_W4 && c.pipe == 2 && !q.ws4)
         return false;  // scale bytes are copied as dwords
+    if (c.op == TG_OP_DEQUANT_W4 && c.chunked_scales && (q.K % 512 != 0 || !q.ws16))
+        return false;  // scale blocks: whole 16-byte pieces of 16-byte aligned rows
     return true;
 }
 
@@ -510,6 +512,7 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
         return TG_ERR_ALIAS;
     Call q{TG_OP_DEQUANT_W4, TG_BF16, M, N, K, aligned16(A) && aligned16(Wq),
            ((uintptr_t)Ws & 3u) == 0, false, false};
+    q.ws16 = aligned16(Ws);
     const Config* c = forced ? forced : select_config(q);
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call

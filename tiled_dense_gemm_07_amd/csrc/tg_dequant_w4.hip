@@ -21,6 +21,14 @@ static const Config kCfg[] = {
     tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 2>, false, 2},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 1, 4, 4, 2>, false, 2},
     tg::Config{1, DT_BF16, 128, 64, 128, 1, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<128, 64, 1, 1, 4, 4, 4>, false, 4},
+    // scale bytes staged 16 strips at a time (K % 512 == 0, 16-byte aligned scale rows)
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 2, 16>, true, 2},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4, 1, 16>, true, 1},
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 1, 4, 4, 4, 16>, true, 4},
+    // eight waves (two per SIMD): one wave's MFMAs run while the other waits
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 4, 16>, true, 4},
+    tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4, 2, 16>, true, 2},
+    tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 4>, false, 4},
     // six-stage rings: more copy bytes in flight per compute unit
     tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 6, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 6, 4, 2>, false, 2},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 6, 8, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 6, 8>},

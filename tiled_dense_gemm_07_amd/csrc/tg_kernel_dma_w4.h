@@ -27,6 +27,12 @@
 //    code is expanded once per tile instead of once per wave row.  The KS
 //    partial accumulators are added through LDS after the main loop in group
 //    order 0, 1, ..., KS-1, and group q stores its share of the tile.
+//  * Scale blocks (SB > 1): the scale bytes of SB strips (4 SB bytes per
+//    weight row) are copied together with 16-byte copies into one of two LDS
+//    buffers, in the middle of the previous block, so a strip needs no
+//    4-byte-per-lane scale copies (a third of the cache-line requests for 2%
+//    of the bytes).  Needs K % 512 == 0 and 16-byte aligned scale rows;
+//    16-byte pieces past a row's end copy zeros.
 //  * Strips are whole (K % 128 == 0; other K use the register-staged kernel);
 //    out-of-range rows (m >= M, n >= N) and the strips padded past K copy
 //    zeros.  The barrier/copy schedule is the one of the 16-bit DMA kernel:
@@ -50,7 +56,7 @@ __device__ __forceinline__ void dma4(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t r
                  : "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1>
+template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1, int SB = 1>
 struct DmaW4 {
     static constexpr int BK = 128;
     static constexpr int NWG = WGM * WGN;   // waves of one k-slice group
@@ -65,24 +71,31 @@ struct DmaW4 {
     static constexpr int NB = FM * FN;      // 32 x 32 blocks of a wave tile
     static constexpr int A_STAGE = BM * BK * 2;
     static constexpr int W_STAGE = BN * BK / 2;
-    static constexpr int S_STAGE = BN * 4;
+    static constexpr int S_STAGE = BN * 4;       // one strip's scale bytes (SB == 1)
+    static constexpr int S_BUF = BN * 4 * SB;    // one block of SB strips' scale bytes
     static constexpr int W_REGION = NS * A_STAGE;
     static constexpr int S_REGION = W_REGION + NS * W_STAGE;
-    static constexpr int RING_BYTES = S_REGION + NS * S_STAGE;
+    static constexpr int RING_BYTES = S_REGION + (SB == 1 ? NS * S_STAGE : 2 * S_BUF);
     // k-slice groups add their partial tiles through LDS: one 4 KiB region
     // per wave and block, reusing the ring after the main loop
     static constexpr int RED_BYTES = KS > 1 ? NW * NB * 4096 : 0;
     static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
     static constexpr int JA = A_STAGE / 1024 / NW;  // A copies per wave per strip
     static constexpr int JW = W_STAGE / 1024 / NW;  // code copies per wave per strip
-    static constexpr int NSC = S_STAGE / 256;       // scale copies per strip (waves 0 .. NSC-1)
+    static constexpr int NSC = SB == 1 ? S_STAGE / 256 : 0;  // scale copies per strip (waves 0 .. NSC-1)
+    static constexpr int JS = SB == 1 ? 0 : S_BUF / 1024 / NW;  // 16-byte scale-block copies per wave
+    static constexpr int SCPR = SB / 4;             // 16-byte chunks of a row's block
 
-    static_assert(NW == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
     static_assert(KS == 1 || KS == 2 || KS == 4, "k-slice groups split the 8 slabs of a strip");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && JW >= 1 && A_STAGE % (1024 * NW) == 0 && W_STAGE % (1024 * NW) == 0,
                   "strips split into whole 1 KiB copies per wave");
-    static_assert(NSC >= 1 && NSC <= NW && S_STAGE % 256 == 0, "one scale copy per wave at most");
+    static_assert(SB > 1 || (NSC >= 1 && NSC <= NW && S_STAGE % 256 == 0),
+                  "one scale copy per wave at most");
+    static_assert(SB == 1 || ((SB == 4 || SB == 8 || SB == 16) && JS >= 1 &&
+                              S_BUF % (1024 * NW) == 0),
+                  "scale blocks split into whole 1 KiB copies per wave");
     static_assert(NS >= 4 && NS % 2 == 0, "an even ring of four or more stages (code registers "
                                           "alternate per strip)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -92,12 +105,14 @@ struct DmaW4 {
         static constexpr int N = JA + JW + (W < NSC ? 1 : 0);
         static constexpr int AHEAD = (NS - 3) * N;
     };
-    static constexpr int NCMAX = JA + JW + 1;
+    static constexpr int NCMAX = JA + JW + (SB == 1 ? 1 : 0);
 
     struct Lane {
         u32 a_off[JA];
         u32 w_off[JW];
         u32 s_off;
+        u32 sb_off[JS > 0 ? JS : 1];  // SB > 1: this lane's 16 scale bytes of block 0
+        u32 sb_c[JS > 0 ? JS : 1];    // and their byte position within a row's block
         u32 a_rd[SPW];  // A fragment read offset of the wave's slab j (stage 0, fm 0)
         u32 w_rd[2];    // this lane's code bytes (stage 0, fn 0): KS = 1: chunks
                         // 2h, 2h+1; KS = 2: chunk 2h+q; KS = 4: half of chunk 2h+q/2
@@ -135,6 +150,16 @@ struct DmaW4 {
             const int row = w * 64 + lane;
             L.s_off = (w < NSC && n0 + row < p.N) ? (u32)(row * (K / 32)) : kOob;
         }
+        if constexpr (SB > 1) {
+#pragma unroll
+            for (int i = 0; i < JS; ++i) {
+                const int idx = (w * JS + i) * 64 + lane;
+                const int row = idx / SCPR;
+                const int c = idx % SCPR;
+                L.sb_c[i] = (u32)c * 16u;
+                L.sb_off[i] = n0 + row < p.N ? (u32)(row * (K / 32) + c * 16) : kOob;
+            }
+        }
         const int h = lane >> 5;
         const int ar = wm * WTM + (lane & 31);
 #pragma unroll
@@ -144,15 +169,15 @@ struct DmaW4 {
         if (KS == 1) {
             L.w_rd[0] = W_REGION + nr * 64 + (((2 * h) ^ swz_a(nr)) << 4);
             L.w_rd[1] = W_REGION + nr * 64 + (((2 * h + 1) ^ swz_a(nr)) << 4);
-            L.s_rd = S_REGION + nr * 4 + 2 * h;
+            L.s_rd = S_REGION + nr * 4 * SB + 2 * h;
         } else if (KS == 2) {
             L.w_rd[0] = W_REGION + nr * 64 + (((2 * h + q) ^ swz_a(nr)) << 4);
             L.w_rd[1] = L.w_rd[0];
-            L.s_rd = S_REGION + nr * 4 + 2 * h + q;
+            L.s_rd = S_REGION + nr * 4 * SB + 2 * h + q;
         } else {
             L.w_rd[0] = W_REGION + nr * 64 + (((2 * h + q / 2) ^ swz_a(nr)) << 4) + 8 * (q & 1);
             L.w_rd[1] = L.w_rd[0];
-            L.s_rd = S_REGION + nr * 4 + 2 * h + q / 2;
+            L.s_rd = S_REGION + nr * 4 * SB + 2 * h + q / 2;
         }
     }
 
@@ -214,8 +239,23 @@ struct DmaW4 {
             issue_copy<ST, W>(L, r, d, smem0);
     }
 
+    // SB > 1: the scale bytes of strips blk SB .. blk SB + SB - 1 into buffer
+    // blk % 2.  Pieces past a row's end (or of rows past N) copy zeros.
+    template <int W>
+    static __device__ __forceinline__ void issue_scale_block(const Lane& L, const GemmParams& p,
+                                                             int blk, u32 smem0)
+    {
+        const u32 b0 = (u32)blk * (u32)(SB * 4);
+        const u32 rowb = (u32)(p.K / 32);
+#pragma unroll
+        for (int i = 0; i < JS; ++i)
+            dma16(smem0 + S_REGION + (blk & 1) * S_BUF + (W * JS + i) * 1024,
+                  b0 + L.sb_c[i] < rowb ? L.sb_off[i] + b0 : kOob, L.rs);
+    }
+
     template <int ST>
-    static __device__ __forceinline__ void read_codes(Regs& R, const Lane& L, lds_char* sm)
+    static __device__ __forceinline__ void read_codes(Regs& R, const Lane& L, lds_char* sm,
+                                                      int strip)
     {
         typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
         typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -223,7 +263,8 @@ struct DmaW4 {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int wo = ST * W_STAGE + fn * 32 * 64;
-            const int so = ST * S_STAGE + fn * 32 * 4;
+            const int so = SB == 1 ? ST * S_STAGE + fn * 32 * 4
+                                   : ((strip / SB) & 1) * S_BUF + (strip % SB) * 4 + fn * 32 * 4 * SB;
             if constexpr (KS == 1) {
                 const u32x4 c0 = *(const lds_u32x4*)(sm + L.w_rd[0] + wo);
                 const u32x4 c1 = *(const lds_u32x4*)(sm + L.w_rd[1] + wo);
@@ -305,7 +346,11 @@ struct DmaW4 {
                 wait_copies_barrier<Copies<W>::AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
                 r = strip_res(p, m0, n0, t + NS - 1);
-                read_codes<NXT>(R[CUR ^ 1], L, sm);
+                read_codes<NXT>(R[CUR ^ 1], L, sm, t + 1);
+                if constexpr (SB > 1) {
+                    if (t % SB == SB / 2)
+                        issue_scale_block<W>(L, p, t / SB + 1, smem0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (i % NM == NM - 1) {
@@ -353,11 +398,13 @@ struct DmaW4 {
                                                      lds_char* sm, const GemmParams& p, int m0,
                                                      int n0, int KT, u32 smem0)
     {
+        if constexpr (SB > 1)
+            issue_scale_block<W>(L, p, 0, smem0);
         prologue_copies<0, W>(L, p, m0, n0, smem0);
         wait_copies_barrier<(NS - 2) * Copies<W>::N>();
         Regs R[2];
         u32x4 AF[4][FM];
-        read_codes<0>(R[0], L, sm);
+        read_codes<0>(R[0], L, sm, 0);
 #pragma unroll
         for (int s = 0; s < PF; ++s)
             read_a<0>(AF[s], L, sm, s);
@@ -523,6 +570,22 @@ struct DmaW4 {
         }
     }
 
+    // The wave index as a template argument (copy schedule, k-slice group).
+    template <int W>
+    static __device__ __forceinline__ void dispatch(int w, f32x16 (&acc)[FM][FN], const Lane& L,
+                                                    lds_char* sm, const GemmParams& p, int m0,
+                                                    int n0, int KT, u32 smem0, int lane, int wm,
+                                                    int wn)
+    {
+        if constexpr (W + 1 < NW) {
+            if (w != W) {
+                dispatch<W + 1>(w, acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+                return;
+            }
+        }
+        body<W>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
+    }
+
     static __device__ __forceinline__ void run(const GemmParams& p)
     {
         __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -549,28 +612,15 @@ struct DmaW4 {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc[fm][fn][r] = 0.0f;
-        switch (w) {
-        case 0:
-            body<0>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
-            break;
-        case 1:
-            body<1>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
-            break;
-        case 2:
-            body<2>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
-            break;
-        default:
-            body<3>(acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
-            break;
-        }
+        dispatch<0>(w, acc, L, sm, p, m0, n0, KT, smem0, lane, wm, wn);
     }
 };
 
-template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1>
+template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1, int SB = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * KS * 64, WGM * WGN * KS * 64))) void
 dma_w4_kernel(GemmParams p)
 {
-    DmaW4<BM, BN, WGM, WGN, NS, GROUP_M, KS>::run(p);
+    DmaW4<BM, BN, WGM, WGN, NS, GROUP_M, KS, SB>::run(p);
 }
 
 }  // namespace tg
