@@ -123,10 +123,18 @@ def time_kernel(fn, stream, launches: int, warmup: int):
     has left its idle clocks (the inputs are generated on the host first)."""
     import torch
 
-    t0 = time.perf_counter()
+    # one launch's duration from an event pair around a few launches (a host
+    # clock around one launch would mostly time the launch and the sync)
     fn()
     stream.synchronize()
-    once_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        fn()
+    b.record(stream)
+    stream.synchronize()
+    once_ms = max(a.elapsed_time(b) / 5, 1e-3)
     for _ in range(max(warmup, min(int(WARM_MS / once_ms) + 1, 5000))):
         fn()
     stream.synchronize()
