@@ -13,6 +13,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <string>
+#include <vector>
+
 #include "../../include/tilegemm.h"
 #include "tg_configs.h"
 #include "tg_kernel.h"
@@ -259,15 +262,38 @@ const Config* heuristic(const Call& q)
     return last;
 }
 
+// The names of every compiled configuration, per (op, dtype) list, formatted
+// once: a call's selection looks names up in the tables above, and formatting
+// every candidate's name per call took 5-20 us of host time.  (A function-local
+// static is initialised once, thread-safely.)
+const std::vector<std::string>& names_of(int op, int dtype)
+{
+    static const std::vector<std::vector<std::string>> tables = [] {
+        std::vector<std::vector<std::string>> t(4 * 3);
+        char buf[96];
+        for (int o = 0; o < 4; ++o)
+            for (int d = 0; d < 3; ++d) {
+                ConfigList L = list_for(o, d);
+                for (int i = 0; i < L.count; ++i) {
+                    config_name(L.items[i], buf, sizeof buf);
+                    t[o * 3 + d].push_back(buf);
+                }
+            }
+        return t;
+    }();
+    static const std::vector<std::string> none;
+    if (op < 0 || op >= 4 || dtype < 0 || dtype >= 3)
+        return none;
+    return tables[op * 3 + dtype];
+}
+
 const Config* find_by_name(int op, int dtype, const char* name)
 {
     ConfigList L = list_for(op, dtype);
-    char buf[96];
-    for (int i = 0; i < L.count; ++i) {
-        config_name(L.items[i], buf, sizeof buf);
-        if (strcmp(buf, name) == 0)
+    const std::vector<std::string>& names = names_of(op, dtype);
+    for (int i = 0; i < L.count && i < (int)names.size(); ++i)
+        if (strcmp(names[i].c_str(), name) == 0)
             return &L.items[i];
-    }
     return nullptr;
 }
 
