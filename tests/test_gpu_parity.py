@@ -207,6 +207,24 @@ def test_dequant_few_rows_deterministic():
         assert np.array_equal(run_w4(inp["A"], inp["Wq"], inp["Ws"]), first)
 
 
+def test_dequant_k_slices_deterministic():
+    """Every k-slice dequant configuration adds its groups' fp32 partial tiles in
+    group order: random inputs give the same bits on every launch, within
+    tolerance of the oracle."""
+    M, N, K = 130, 264, 2048
+    A, Wq, Ws = synth.dequant_inputs(M, N, K, 1201, 1202, 1203, integer=False)
+    Y = oracle.dequant_w4_f64(A, Wq, Ws)
+    names = [(i, n) for i, n in _configs(1, BF16)
+             if "_dma" in n and len(n.split("_")[3].split("x")) == 3 and _w4_config_fits(n, K)]
+    assert names, "no k-slice dequant configuration compiled"
+    for idx, name in names:
+        say("w4 k-slice determinism %s" % name)
+        first = run_w4(A, Wq, Ws, config=idx)
+        check_full(first, Y, BF16, integer=False)
+        for _ in range(2):
+            assert np.array_equal(run_w4(A, Wq, Ws, config=idx), first), name
+
+
 WORKLOADS = ["f32_512", "f16_1024", "f32_4096", "bf16_4096_relu", "bf16_4000x4032x4096_relu",
              "w4_256x8192x8192", "w4_1x8192x8192", "w4_16x8192x8192"]
 
