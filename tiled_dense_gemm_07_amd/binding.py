@@ -111,13 +111,19 @@ def _check(status: int):
         raise TileGemmError(status, status_str(status))
 
 
-def _dtype_code(t) -> int:
-    import torch
+_DTYPE_CODES = None
 
-    codes = {torch.float32: TG_F32, torch.float16: TG_F16, torch.bfloat16: TG_BF16}
-    if t.dtype not in codes:
+
+def _dtype_code(t) -> int:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+
+        _DTYPE_CODES = {torch.float32: TG_F32, torch.float16: TG_F16, torch.bfloat16: TG_BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError("unsupported dtype %s (float32, float16 or bfloat16)" % t.dtype)
-    return codes[t.dtype]
+    return code
 
 
 def _epi_code(epilogue) -> int:
@@ -129,10 +135,11 @@ def _epi_code(epilogue) -> int:
 
 
 def _stream_ptr(device, stream=None):
-    import torch
+    if stream is None:
+        import torch
 
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
 
 
 def _require_gpu_tensor(name, t):
@@ -162,10 +169,10 @@ def _gemm_args(A, B, C):
 
 def gemm(A, B, C=None, epilogue=None, stream=None):
     """C = epilogue(A @ B) on the GPU (fp32 / fp16 / bf16, row-major). Returns C."""
-    import torch
-
     M, N, K = _gemm_args(A, B, C)
     if C is None:
+        import torch
+
         C = torch.empty((M, N), dtype=A.dtype, device=A.device)
     _check(load_library().tg_gemm(M, N, K, _dtype_code(A), A.data_ptr(), B.data_ptr(),
                                   C.data_ptr(), _epi_code(epilogue), _stream_ptr(A.device, stream)))
