@@ -32,7 +32,9 @@
 //    buffers, in the middle of the previous block, so a strip needs no
 //    4-byte-per-lane scale copies (a third of the cache-line requests for 2%
 //    of the bytes).  Needs K % 512 == 0 and 16-byte aligned scale rows;
-//    16-byte pieces past a row's end copy zeros.
+//    16-byte pieces past a row's end copy zeros.  A row's 16-byte chunk c sits
+//    at position c ^ ((row >> 2) & (SB/4 - 1)), so the 32 rows one scale read
+//    touches (64 bytes apart) spread over the banks.
 //  * Strips are whole (K % 128 == 0; other K use the register-staged kernel);
 //    out-of-range rows (m >= M, n >= N) and the strips padded past K copy
 //    zeros.  The barrier/copy schedule is the one of the 16-bit DMA kernel:
@@ -113,6 +115,7 @@ struct DmaW4 {
         u32 s_off;
         u32 sb_off[JS > 0 ? JS : 1];  // SB > 1: this lane's 16 scale bytes of block 0
         u32 sb_c[JS > 0 ? JS : 1];    // and their byte position within a row's block
+        u32 s_sw;                     // SB > 1: this lane's row's chunk swizzle, in bytes
         u32 a_rd[SPW];  // A fragment read offset of the wave's slab j (stage 0, fm 0)
         u32 w_rd[2];    // this lane's code bytes (stage 0, fn 0): KS = 1: chunks
                         // 2h, 2h+1; KS = 2: chunk 2h+q; KS = 4: half of chunk 2h+q/2
@@ -155,7 +158,7 @@ struct DmaW4 {
             for (int i = 0; i < JS; ++i) {
                 const int idx = (w * JS + i) * 64 + lane;
                 const int row = idx / SCPR;
-                const int c = idx % SCPR;
+                const int c = (idx % SCPR) ^ ((row >> 2) & (SCPR - 1));  // global chunk
                 L.sb_c[i] = (u32)c * 16u;
                 L.sb_off[i] = n0 + row < p.N ? (u32)(row * (K / 32) + c * 16) : kOob;
             }
@@ -166,6 +169,7 @@ struct DmaW4 {
         for (int j = 0; j < SPW; ++j)
             L.a_rd[j] = ar * (BK * 2) + (((8 * h + q * SPW + j) ^ swz16(ar)) << 4);
         const int nr = wn * WTN + (lane & 31);
+        L.s_sw = SB > 1 ? (u32)(((nr >> 2) & (SCPR > 0 ? SCPR - 1 : 0)) << 4) : 0u;
         if (KS == 1) {
             L.w_rd[0] = W_REGION + nr * 64 + (((2 * h) ^ swz_a(nr)) << 4);
             L.w_rd[1] = W_REGION + nr * 64 + (((2 * h + 1) ^ swz_a(nr)) << 4);
@@ -263,8 +267,10 @@ struct DmaW4 {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int wo = ST * W_STAGE + fn * 32 * 64;
+            // (SB > 1: rows 32 apart share the chunk swizzle)
             const int so = SB == 1 ? ST * S_STAGE + fn * 32 * 4
-                                   : ((strip / SB) & 1) * S_BUF + (strip % SB) * 4 + fn * 32 * 4 * SB;
+                                   : ((strip / SB) & 1) * S_BUF + (int)(((u32)(strip % SB) >> 2 << 4) ^ L.s_sw) +
+                                         (strip % 4) * 4 + fn * 32 * 4 * SB;
             if constexpr (KS == 1) {
                 const u32x4 c0 = *(const lds_u32x4*)(sm + L.w_rd[0] + wo);
                 const u32x4 c1 = *(const lds_u32x4*)(sm + L.w_rd[1] + wo);
