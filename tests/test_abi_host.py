@@ -303,6 +303,26 @@ def test_query_config(lib):
     assert lib.tg_query_config(1, 64, 64, 40, 2, buf, 8) == SHAPE
 
 
+def test_tuned_table_selects_its_configurations(lib):
+    """Every shape of the generated selection table resolves to the configuration
+    it names (names are looked up in a table formatted once per process), and
+    configuration names are unique within each list."""
+    table = os.path.join(os.path.dirname(binding.__file__), "csrc", "tg_tuned.inc")
+    entries = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \"([^\"]+)\"\}", open(table).read())
+    assert entries
+    for op, dt, M, N, K, name in entries:
+        got = binding.query_config(int(op), int(M), int(N), int(K), int(dt)).split()[0]
+        assert got == name, (op, dt, M, N, K, got, name)
+    for op, dts in ((0, (0, 1, 2)), (1, (2,)), (2, (0, 1)), (3, (1, 2))):
+        for dt in dts:
+            names = binding.list_configs(op, dt)
+            assert len(names) == len(set(names)), (op, dt)
+    # repeated lookups give the same answer
+    for _ in range(3):
+        assert binding.query_config(1, 256, 8192, 8192).split()[0] == [
+            e[5] for e in entries if e[:5] == ("1", "2", "256", "8192", "8192")][0]
+
+
 def test_tile_choice_fills_whole_rounds():
     """Large 16-bit grids take the tile shape whose grid fills its last round of
     256 workgroups best; small grids take k-slice configurations."""
