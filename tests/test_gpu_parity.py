@@ -225,6 +225,30 @@ def test_dequant_k_slices_deterministic():
             assert np.array_equal(run_w4(A, Wq, Ws, config=idx), first), name
 
 
+@pytest.mark.parametrize("offset", [4, 1], ids=["ws4", "ws1"])
+def test_dequant_misaligned_scales_full_size(offset):
+    """The dequant workload shape with scale rows starting 4 bytes past a 16-byte
+    boundary (the scale-block kernel cannot take them: the per-strip LDS-DMA
+    kernel runs) or 1 byte past (the register-staged kernel runs): still
+    bit-exact on integer activations."""
+    w = synth.WORKLOADS["w4_256x8192x8192"]
+    inp = synth.make_inputs(w, integer=True)
+    A, Wq, Ws = inp["A"], inp["Wq"], inp["Ws"]
+    N, KS = Ws.shape
+    raw = torch.zeros(N * KS + 64, dtype=torch.uint8, device=DEV)
+    Wst = raw[offset:offset + N * KS].view(N, KS)
+    Wst.copy_(torch.from_numpy(Ws).to(DEV))
+    assert Wst.data_ptr() % 16 == offset % 16
+    say("w4 misaligned scales offset=%d" % offset)
+    At = to_device(A, BF16, DEV)
+    Ct = binding.dequant_gemm_w4(At, torch.from_numpy(Wq).to(DEV), Wst)
+    torch.cuda.synchronize()
+    got = to_host_bits(Ct, BF16)
+    rows, cols = sample_entries(w.M, w.N, 3000, seed=31 + offset)
+    Y = oracle.dequant_w4_entries_f64(A, Wq, Ws, rows, cols)
+    check_full(got[rows, cols], Y, BF16, integer=True)
+
+
 WORKLOADS = ["f32_512", "f16_1024", "f32_4096", "bf16_4096_relu", "bf16_4000x4032x4096_relu",
              "w4_256x8192x8192", "w4_1x8192x8192", "w4_16x8192x8192"]
 
