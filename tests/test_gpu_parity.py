@@ -150,7 +150,9 @@ def test_dequant_small(shape, integer):
                                    (256, 8192, 1024), (1, 200, 640),
                                    # scale blocks of 16 strips: a row's scale bytes end
                                    # inside the first block / a second, partial block
-                                   (300, 264, 1536), (130, 200, 2560)],
+                                   (300, 264, 1536), (130, 200, 2560),
+                                   # N % 8 != 0: results stored directly, not staged
+                                   (100, 130, 1024)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_every_w4_config_ragged(shape):
     """Every dequant configuration this shape allows, forced, with integer
