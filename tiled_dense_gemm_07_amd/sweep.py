@@ -24,10 +24,26 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "csrc", "tg_tuned.inc")
 
 
+WARM_MS = 40.0  # back-to-back work before a configuration's timed launches
+
+
 def time_config(fn, stream, launches: int = 20, warmup: int = 3) -> float:
+    """Median launch time (ms) over `launches` event-timed launches, after at
+    least `warmup` launches and WARM_MS of back-to-back work: the card leaves
+    its idle clocks only after tens of milliseconds of load."""
     import torch
 
     for _ in range(warmup):
+        fn()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        fn()
+    b.record(stream)
+    stream.synchronize()
+    once_ms = max(a.elapsed_time(b) / 5, 1e-3)
+    for _ in range(min(int(WARM_MS / once_ms) + 1, 5000)):
         fn()
     stream.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
