@@ -8,19 +8,22 @@
 // E8M0 scale per 32 k.
 //
 // MI355X mapping:
-//  * BM x BN x 128 strips, four waves in a 2 x 2 grid, NS-stage LDS ring filled
-//    by LDS-DMA copies (no VGPR staging): A as [BM][128] bf16 (256-byte rows),
-//    the packed codes as [BN][64 bytes] and the scale bytes as [BN][4].  The
+//  * BM x BN x 128 strips, WGM x WGN x KS waves (four or eight), an NS-stage
+//    LDS ring filled by LDS-DMA copies (no VGPR staging): A as [BM][128] bf16
+//    (256-byte rows), the packed codes as [BN][64 bytes] and the scale bytes
+//    as [BN][4] (or SB strips at a time, below).  The
 //    codes stay packed in LDS (a quarter of the bf16 bytes); each wave expands
 //    its own B fragments in registers (v_cvt_scalef32_pk_bf16_fp4, exact)
-//    right before the MFMA that consumes them.
+//    right before the MFMA that consumes them.  One buffer resource per operand
+//    covers the tile's row band for the whole K; a strip adds its byte offset
+//    to the lane offsets.
 //  * Inside a strip the k order is permuted the same way on both operands:
 //    MFMA slab s (0..7) takes, in lane half h, k = 64 h + 8 s .. + 7.  A lane's
 //    codes for the whole strip are then one contiguous 32-byte run of its row
 //    (two ds_read_b128), and its A fragment of slab s is 16-byte chunk 8 h + s.
 //  * Chunk swizzles keep the fragment reads free of bank conflicts: A chunks
 //    are XORed with row & 15, code chunks with the 64-byte-row swizzle.
-//  * K-slice variant (KS = 2 or 4): the four waves form KS groups of
+//  * K-slice variant (KS = 2 or 4): the waves form KS groups of
 //    WGM x WGN waves that all cover the whole tile; group q multiplies slabs
 //    q 8/KS .. of every strip (a lane's codes are then 16 or 8 contiguous
 //    bytes, one scale byte), so each A fragment feeds more MFMAs and every
