@@ -5,22 +5,25 @@ with the fused ReLU epilogue (row-major A and B, N(0,1) entries cast to bf16,
 fp32 accumulation, bf16 output), inputs already resident in HBM.  W untimed
 warm-up steps, then K timed steps between a synchronize on each side.
 
-The default warm-up is long (300 steps, about 35 ms of GEMM work): after the
-seconds of host-side input generation the card sits at idle clocks, and back-
-to-back launches of this kernel only settle at their sustained speed after
-about 30 ms (measured: 126 us for the first 50 launches, 107 us from launch
-300 on).
+Warm-up: at least W steps and at least WARM_MS of back-to-back launches.  After
+the seconds of host-side input generation the card sits at idle clocks, and
+this kernel only settles at its sustained speed after about 30 ms of launches
+(measured: 126 us for the first 50 launches, 107 us from launch 300 on).  The
+launches actually run are reported as ``warmup_launches``.
 
 Printed: ONE JSON line (rank 0) with
-  value       whole-job TFLOP/s = 2 M N K * K_steps / elapsed,
-  roofline    the kernel's average duration (HIP events recorded on the
-              stream it runs on, around the K timed launches), against the
-              bf16 dense MFMA peak,
-  cpu_baseline the C oracle timed on host cores on a bounded row sample,
-  workloads   the other workload shapes (fp32 / fp16 GEMMs, the non-divisible
-              bf16 GEMM, the 4-bit dequant GEMM and its decode-like probes,
-              the MX-format GEMMs, the 2:4 sparse GEMM), each timed the same
-              way.
+  value         whole-job TFLOP/s = 2 M N K * K_steps / elapsed (host clock),
+  roofline      the kernel's average duration (HIP events recorded on the
+                stream it runs on, around the K timed launches), against the
+                bf16 dense MFMA peak; the per-launch median / p10 / p90 of a
+                separate pass; the shader clock sampled from the SMU while the
+                kernel runs back to back, and the fraction of the peak at that
+                clock,
+  cpu_baseline  the C oracle timed on host cores on a bounded row sample,
+  workloads     the other workload shapes, each timed the same way with warm
+                caches (same buffers) and cold caches (operands rotated over
+                copies larger than the 256 MB MALL), with the oracle timed on
+                a row sample of each.
 """
 
 from __future__ import annotations
@@ -29,6 +32,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +42,7 @@ if ROOT not in sys.path:
 METRIC = "GEMM TFLOP/s and % of MI355X dense MFMA peak (4096³ bf16/fp32, 1 GPU)"
 # MI355X dense matrix peaks (256 CUs at 2.4 GHz): bf16/fp16 4096 FLOP/clk/CU,
 # fp32 256 FLOP/clk/CU; HBM3E 8 TB/s.
+PEAK_CLOCK_GHZ = 2.4
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3,
                # scaled MFMA: E2M1 x E2M1 at the fp4 rate, E4M3 x E2M1 at the fp8 rate
                "mx_e2m1": 10066.3, "mx_e4m3": 5033.2,
@@ -47,12 +52,18 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_4096_relu"
 OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x8192x8192",
          "w4_16x8192x8192", "w4_1x8192x8192", "mx_e2m1_8192", "mx_e4m3_8192",
-         "sp24_bf16_4096_relu"]
+         "sp24_bf16_4096_relu", "bf16_6144x4096x4096_relu", "bf16_3072_relu"]
+# Workloads whose run time is the operand stream from HBM: their headline
+# bandwidth is the cold-cache one.
+MEMORY_BOUND = ("w4_1x8192x8192", "w4_16x8192x8192")
+WARM_MS = 40.0      # GPU work before a workload's timed launches (clock ramp-up)
+COLD_BYTES = 1 << 30  # operand copies rotated by the cold timing (> 256 MB MALL)
+CLOCK_MS = 400.0    # back-to-back launches while the shader clock is sampled
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken with the configuration the library launches now and on that
+    """Fabric bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken with the configuration the library launches now and on that
     kernel's current sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
@@ -113,18 +124,10 @@ def launcher(w, tensors, stream):
     return lambda: binding.dequant_gemm_w4(A, Wq, Ws, C=C, epilogue=epi, stream=stream)
 
 
-WARM_MS = 40.0  # GPU work before a workload's timed launches (clock ramp-up)
-
-
-def time_kernel(fn, stream, launches: int, warmup: int):
-    """Average kernel duration (ms): one HIP event pair on the stream the
-    kernel runs on, around `launches` back-to-back launches.  The warm-up is at least
-    `warmup` launches and at least WARM_MS of back-to-back work, so the card
-    has left its idle clocks (the inputs are generated on the host first)."""
+def launch_ms(fn, stream) -> float:
+    """One launch's duration (ms) from an event pair around five launches."""
     import torch
 
-    # one launch's duration from an event pair around a few launches (a host
-    # clock around one launch would mostly time the launch and the sync)
     fn()
     stream.synchronize()
     a = torch.cuda.Event(enable_timing=True)
@@ -134,10 +137,24 @@ def time_kernel(fn, stream, launches: int, warmup: int):
         fn()
     b.record(stream)
     stream.synchronize()
-    once_ms = max(a.elapsed_time(b) / 5, 1e-3)
-    for _ in range(max(warmup, min(int(WARM_MS / once_ms) + 1, 5000))):
+    return max(a.elapsed_time(b) / 5, 1e-3)
+
+
+def warm_up(fn, stream, warmup: int) -> int:
+    """At least `warmup` launches and at least WARM_MS of back-to-back work;
+    returns the launches run."""
+    n = max(warmup, min(int(WARM_MS / launch_ms(fn, stream)) + 1, 5000))
+    for _ in range(n):
         fn()
     stream.synchronize()
+    return n + 6
+
+
+def time_mean(fn, stream, launches: int) -> float:
+    """Average kernel duration (ms): one HIP event pair on the kernel's stream
+    around `launches` back-to-back launches."""
+    import torch
+
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -145,23 +162,114 @@ def time_kernel(fn, stream, launches: int, warmup: int):
         fn()
     b.record(stream)
     stream.synchronize()
-    return {"mean_ms": a.elapsed_time(b) / launches}
+    return a.elapsed_time(b) / launches
 
 
-# Workloads whose run time is the operand stream from HBM: also timed with
-# the operands rotated over copies larger than the caches (256 MB MALL,
-# 8 x 4 MB L2), so every launch reads its bytes from HBM.
-MEMORY_BOUND = ("w4_1x8192x8192", "w4_16x8192x8192")
-COLD_BYTES = 1 << 30
-
-
-def time_cold(w, tensors, stream, launches: int = 40):
-    """Kernel duration with each launch on a different copy of the inputs
-    (together COLD_BYTES or more), so nothing is cache-resident."""
+def time_each(fns, stream, launches: int) -> dict:
+    """Per-launch durations (ms) from one event pair around each launch
+    (launch i runs fns[i % len(fns)]): median, p10, p90, mean."""
+    import numpy as np
     import torch
 
-    from tiled_dense_gemm_07_amd import binding
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fns[i % len(fns)]()
+        b.record(stream)
+    stream.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5), "mean_ms": round(float(t.mean()), 5),
+            "launches": launches}
 
+
+class ClockSampler:
+    """The GPU's shader (gfx) clock, read from the SMU metrics through amdsmi
+    every few milliseconds on a host thread while kernels run."""
+
+    def __init__(self):
+        import amdsmi
+        import torch
+
+        self.smi = amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            raise RuntimeError("amdsmi sees no GPU")
+        self.h = handles[0]
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        if bus is not None and len(handles) > 1:
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if int(bdf.split(":")[1], 16) == int(bus):
+                    self.h = h
+        self.read()  # fails here, not in the thread, if the metrics are unreadable
+        self.samples = []
+        self._stop = threading.Event()
+
+    def read(self) -> float:
+        """Current shader clock in MHz (the mean over the XCDs that report one)."""
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            if isinstance(v, (list, tuple)):
+                vals = [float(x) for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                if vals:
+                    return sum(vals) / len(vals)
+            elif isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        info = self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception:
+                pass
+            time.sleep(0.002)
+
+    def __enter__(self):
+        self.samples = []
+        self._stop.clear()
+        self.t = threading.Thread(target=self._loop, daemon=True)
+        self.t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self.t.join()
+        return False
+
+    def close(self):
+        try:
+            self.smi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def measure_clock(fn, stream, once_ms: float, sampler) -> dict:
+    """Median sampled shader clock over CLOCK_MS of back-to-back launches, and
+    the mean launch duration over the same launches."""
+    import numpy as np
+
+    n = max(20, int(CLOCK_MS / once_ms))
+    with sampler:
+        ms = time_mean(fn, stream, n)
+    s = np.array(sampler.samples[len(sampler.samples) // 10:])  # skip the first tenth
+    if s.size == 0:
+        raise RuntimeError("no clock samples")
+    return {"sustained_clock_ghz": round(float(np.median(s)) / 1000.0, 4),
+            "clock_p10_ghz": round(float(np.percentile(s, 10)) / 1000.0, 4),
+            "clock_p90_ghz": round(float(np.percentile(s, 90)) / 1000.0, 4),
+            "clock_samples": int(s.size), "clock_pass_kernel_ms": round(ms, 5),
+            "clock_pass_launches": n, "clock_source": "amdsmi gpu metrics (gfx clock)"}
+
+
+def time_cold(w, tensors, stream, launches: int = 40) -> dict:
+    """Kernel durations with each launch on a different copy of the inputs
+    (together COLD_BYTES or more), so nothing is cache-resident."""
     per = sum(x.numel() * x.element_size() for x in tensors)
     copies = max(4, -(-COLD_BYTES // per))
     sets = [tuple(x.clone() for x in tensors) for _ in range(copies)]
@@ -169,19 +277,13 @@ def time_cold(w, tensors, stream, launches: int = 40):
     for f in fns[:4]:
         f()
     stream.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fns[i % copies]()
-        b.record(stream)
-    stream.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    mean = sum(ts) / len(ts)
-    gbs = w.algorithmic_bytes() / (mean * 1e-3) / 1e9
+    r = time_each(fns, stream, max(launches, 2 * copies))
+    gbs = w.algorithmic_bytes() / (r["median_ms"] * 1e-3) / 1e9
+    tf = w.flops / (r["median_ms"] * 1e-3) / 1e12
     del sets, fns
-    return {"copies": copies, "kernel_ms": round(mean, 5), "kernel_ms_min": round(ts[0], 5),
-            "gbs_algorithmic": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    r.update({"copies": copies, "tflops": round(tf, 2), "gbs_algorithmic": round(gbs, 1),
+              "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+    return r
 
 
 def dtype_name(w):
@@ -194,29 +296,91 @@ def dtype_name(w):
     return {synth.F32: "f32", synth.F16: "f16", synth.BF16: "bf16"}[w.dtype]
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0):
-    """The oracle, as it stands, on the first R rows of C; R grows until one
-    call takes a good part of the budget."""
+def oracle_rows(w, inp, rows: int):
+    """The oracle on rows 0 .. rows-1 of C (every row is an independent sum)."""
     import numpy as np
 
     import oracle
 
-    A, B = inp["A"], inp["B"]
-    rows = 4
-    elapsed = 0.0
+    if w.op == "gemm":
+        return oracle.gemm_f64(np.ascontiguousarray(inp["A"][:rows]), inp["B"], w.dtype, w.relu)
+    if w.op == "dequant_w4":
+        return oracle.dequant_w4_f64(np.ascontiguousarray(inp["A"][:rows]), inp["Wq"], inp["Ws"],
+                                     w.relu)
+    if w.op == "mx":
+        return oracle.mx_gemm_f64(w.dtype, np.ascontiguousarray(inp["Aq"][:rows]),
+                                  np.ascontiguousarray(inp["As"][:rows]), inp["Wq"], inp["Ws"],
+                                  w.relu)
+    return oracle.gemm_sp24_f64(np.ascontiguousarray(inp["Ac"][:rows]),
+                                np.ascontiguousarray(inp["Ai"][:rows]), inp["B"], w.dtype, w.relu)
+
+
+def cpu_baseline(w, inp, budget_s: float) -> dict:
+    """The oracle, as it stands, on the first R rows of C; R grows until one
+    call takes about a quarter of the budget (or covers all of C)."""
+    import oracle
+
+    rows = 1
     while True:
         t0 = time.perf_counter()
-        oracle.gemm_f64(np.ascontiguousarray(A[:rows]), B, w.dtype, w.relu)
+        oracle_rows(w, inp, rows)
         elapsed = time.perf_counter() - t0
         if elapsed >= budget_s / 4 or rows >= w.M:
             break
         rows = min(w.M, max(rows * 2, int(rows * (budget_s / 4) / max(elapsed, 1e-3))))
     flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "rows 0..%d of C = A @ B for the %s workload (%d x %d x %d fp64 sums, "
-                      "%.1f s)" % (rows - 1, w.name, rows, w.N, w.K, elapsed),
-            "seconds": elapsed}
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "rows 0..%d of C for the %s workload (%d x %d x %d fp64 sums, %.2f s)"
+                      % (rows - 1, w.name, rows, w.N, w.K, elapsed),
+            "seconds": round(elapsed, 3)}
+
+
+def bench_workload(name, dev, stream, sampler, cpu_budget_s):
+    import torch
+
+    from tiled_dense_gemm_07_amd import binding, synth
+
+    ow = synth.WORKLOADS[name]
+    inp, t = make_device_inputs(ow, dev)
+    fn = launcher(ow, t, stream)
+    warm_up(fn, stream, 5)
+    mean_ms = time_mean(fn, stream, 30)
+    dist = time_each([fn], stream, 50)
+    tf = ow.flops / (mean_ms * 1e-3) / 1e12
+    gbs = ow.algorithmic_bytes() / (mean_ms * 1e-3) / 1e9
+    dn = dtype_name(ow)
+    rec = {
+        "kernel_ms": round(mean_ms, 5), "tflops": round(tf, 2),
+        "frac_mfma_peak": round(tf / PEAK_TFLOPS[dn], 4),
+        "gbs_algorithmic": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "per_launch": dist,
+        "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[ow.op],
+                                       ow.M, ow.N, ow.K, ow.dtype)}
+    if sampler is not None:
+        try:
+            ck = measure_clock(fn, stream, mean_ms, sampler)
+            rec["sustained_clock_ghz"] = ck["sustained_clock_ghz"]
+            rec["frac_mfma_peak_at_clock"] = round(
+                tf / (PEAK_TFLOPS[dn] * ck["sustained_clock_ghz"] / PEAK_CLOCK_GHZ), 4)
+        except Exception as e:
+            rec["sustained_clock_ghz"] = "unavailable: %s" % e
+    rec["cold"] = time_cold(ow, t, stream)
+    tr = load_traffic(name)
+    if tr is not None:
+        # L2 <-> fabric bytes per launch from the committed counter record
+        rec["fabric_bytes_per_launch"] = int(tr["fabric_bytes_per_launch"])
+        rec["fabric_over_algorithmic"] = round(tr["fabric_bytes_per_launch"] /
+                                               ow.algorithmic_bytes(), 3)
+        if tr.get("cold"):
+            # counters taken on the cold rotation: every fabric byte came from HBM
+            rec["hbm_gbs_counters_cold"] = round(
+                tr["fabric_bytes_per_launch"] / (rec["cold"]["median_ms"] * 1e-3) / 1e9, 1)
+    del t
+    torch.cuda.empty_cache()
+    if cpu_budget_s > 0:
+        rec["cpu_baseline"] = cpu_baseline(ow, inp, cpu_budget_s)
+    return rec
 
 
 def main():
@@ -226,6 +390,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--workloads", default=None,
+                    help="comma-separated subset of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -242,14 +408,17 @@ def main():
     binding.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    try:
+        sampler = ClockSampler()
+    except Exception as e:
+        sampler = None
+        sampler_err = "unavailable: %s" % e
 
     w = synth.WORKLOADS[HEADLINE]
     inp, tensors = make_device_inputs(w, dev)
     fn = launcher(w, tensors, stream)
 
-    for _ in range(args.warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm = warm_up(fn, stream, args.warmup)
     # timed region: exactly K steps; one event pair on the kernel's stream
     # around them gives the average launch duration (launches run back to
     # back, so this is the kernel's own time plus the gaps between launches)
@@ -272,53 +441,42 @@ def main():
     traffic = load_traffic(HEADLINE)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic["hbm_bytes_per_launch"] if traffic else None,
+                "traffic": traffic["fabric_bytes_per_launch"] if traffic else None,
                 "kernel_ms": round(kernel_ms, 5),
                 "algorithmic_flops_per_launch": w.flops,
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes()}
-    # the matrix cores' own ceiling on this card: the same MFMA work on
-    # register operands, no memory traffic (power-limited clock)
-    try:
-        from tiled_dense_gemm_07_amd import clockprobe
-
-        roofline["mfma_ceiling"] = [clockprobe.measure("random"), clockprobe.measure("zeros")]
-    except Exception as e:  # the probe is context only
-        roofline["mfma_ceiling"] = "unavailable: %s" % e
+    # after the timed region: per-launch distribution and the sustained clock
+    roofline["per_launch"] = time_each([fn], stream, 200)
+    if sampler is not None:
+        try:
+            ck = measure_clock(fn, stream, kernel_ms, sampler)
+            roofline.update(ck)
+            ghz = ck["sustained_clock_ghz"]
+            roofline["peak_at_clock"] = round(peak * ghz / PEAK_CLOCK_GHZ, 1)
+            roofline["frac_at_clock"] = round(achieved / roofline["peak_at_clock"], 4)
+        except Exception as e:
+            roofline["sustained_clock_ghz"] = "unavailable: %s" % e
+    else:
+        roofline["sustained_clock_ghz"] = sampler_err
+    roofline["cold"] = time_cold(w, tensors, stream)
 
     workloads = {}
     if not args.no_workloads:
-        for name in OTHER:
-            ow = synth.WORKLOADS[name]
-            _, t = make_device_inputs(ow, dev)
-            r = time_kernel(launcher(ow, t, stream), stream, launches=30, warmup=5)
-            tf = ow.flops / (r["mean_ms"] * 1e-3) / 1e12
-            gbs = ow.algorithmic_bytes() / (r["mean_ms"] * 1e-3) / 1e9
-            dn = dtype_name(ow)
-            workloads[name] = {
-                "kernel_ms": round(r["mean_ms"], 5), "tflops": round(tf, 2),
-                "frac_mfma_peak": round(tf / PEAK_TFLOPS[dn], 4),
-                "gbs_algorithmic": round(gbs, 1),
-                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[ow.op],
-                                               ow.M, ow.N, ow.K, ow.dtype)}
-            if name in MEMORY_BOUND:
-                workloads[name]["cold"] = time_cold(ow, t, stream)
-            tr = load_traffic(name)
-            if tr is not None:
-                # L2 <-> fabric bytes per launch from the committed counter record
-                workloads[name]["traffic_bytes"] = int(tr["hbm_bytes_per_launch"])
-                workloads[name]["gbs_counters"] = round(
-                    tr["hbm_bytes_per_launch"] / (r["mean_ms"] * 1e-3) / 1e9, 1)
-            del t
-            torch.cuda.empty_cache()
+        names = OTHER if not args.workloads else args.workloads.split(",")
+        for name in names:
+            workloads[name] = bench_workload(name, dev, stream, sampler,
+                                             0.0 if args.no_cpu_baseline else 1.5)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, inp, 12.0)
+    if sampler is not None:
+        sampler.close()
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "warmup_launches": warm,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": HEADLINE, "M": w.M, "N": w.N, "K": w.K, "epilogue": "relu",

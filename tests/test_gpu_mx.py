@@ -13,10 +13,18 @@ Bars:
     ranges chosen so that every product and partial sum is a multiple of a
     power of two inside the window and below 2^24 of it): bit-exact with one
     round-to-nearest-even of the exact fp64 sum;
-  * full-range random codes and scales: |C - Y| <= (1 + 2^-8) (T + A) + 2^-8 |Y|,
-    with Y the exact sum, T = sum over groups of (nonzero products) *
-    2^(e_g - 13) * scales (the truncation), A = (K / 8) 2^-24 S and
-    S = sum_k |a(m, k) w(n, k)| (the fp32 roundings), then one bf16 rounding;
+  * full-range random codes and scales, E2M1 x E2M1: the stated 4-bit
+    tolerance |C - Y| <= 1e-2 + 1e-2 |Y| on every entry, and the bound of the
+    arithmetic without truncation, |C - Y| <= (1 + 2^-8) A + 2^-8 |Y| with
+    A = (K / 8) 2^-24 S and S = sum_k |a(m, k) w(n, k)| (the fp32 roundings),
+    then one bf16 rounding.  An E2M1 x E2M1 product is a multiple of 2^-3 and
+    its group's window ends at 2^(4 - 13) or below, so it is never truncated;
+  * full-range random codes and scales, E4M3 x E2M1: products can fall below
+    the window, so the bound adds the truncation T = sum over groups of
+    (nonzero products) * 2^(e_g - 13) * scales; and at least 99% of entries
+    meet 1e-2 + 1e-2 |Y| (the truncation error is relative to each group's
+    largest product, so only entries whose sum cancels to far below its terms
+    miss it: about 0.3% in a CPU model of the arithmetic at 8192^3);
   * NaN scale bytes (E8M0 255) and NaN E4M3 codes: NaN exactly in the outputs
     whose sums take one of their products.
 Full-size shapes run in the benchmark's launch configuration and are checked
@@ -87,7 +95,10 @@ def _exponents(v, emin):
 
 
 def truncation_bound(fmt, Aq, As, Wq, Ws, rows, cols):
-    """T of the module docstring for the entries (rows[i], cols[i])."""
+    """T of the module docstring for the entries (rows[i], cols[i]); zero for
+    E2M1 activations, whose products the window always holds."""
+    if fmt == synth.MX_E2M1:
+        return np.zeros(len(rows))
     ones_a = np.full_like(As, 127)
     ones_w = np.full_like(Ws, 127)
     ea = oracle.mx_decode_a(fmt, Aq, ones_a)        # unscaled elements
@@ -115,6 +126,23 @@ def check_bound(got_bits, Y, S, T, K):
     assert not bad.any(), "%d of %d outside the bound (first at %s: got %r want %r tol %r)" % (
         int(bad.sum()), bad.size, np.argwhere(bad)[0].tolist(), got[bad][0], Y[bad][0],
         tol[bad][0])
+
+
+E4M3_MIN_FRACTION = 0.99
+
+
+def check_stated_tolerance(fmt, got_bits, Y):
+    """The 4-bit path's stated tolerance |C - Y| <= 1e-2 + 1e-2 |Y|: on every
+    entry for E2M1 activations; on at least E4M3_MIN_FRACTION of the entries
+    for E4M3 activations (checked where there are 1000 entries or more)."""
+    got = bits_to_f64(got_bits, BF16)
+    ok = np.abs(got - Y) <= 1e-2 + 1e-2 * np.abs(Y)
+    frac = float(ok.mean())
+    say("mx %s: %.5f of %d entries within 1e-2 + 1e-2 |Y|" % (FNAME[fmt], frac, ok.size))
+    if fmt == synth.MX_E2M1:
+        assert ok.all(), "%d of %d outside 1e-2 + 1e-2 |Y|" % (int((~ok).sum()), ok.size)
+    elif ok.size >= 1000:
+        assert frac >= E4M3_MIN_FRACTION, frac
 
 
 def full_bound_inputs(fmt, Aq, As, Wq, Ws, M, N):
@@ -153,6 +181,7 @@ def test_mx_random(fmt, shape):
     Y = oracle.mx_gemm_f64(fmt, Aq, As, Wq, Ws)
     S, T = full_bound_inputs(fmt, Aq, As, Wq, Ws, M, N)
     check_bound(got, Y, S, T, K)
+    check_stated_tolerance(fmt, got, Y)
 
 
 def test_mx_wide_scale_range():
@@ -246,11 +275,12 @@ def test_mx_workload(name):
     inp = synth.make_inputs(w)
     say("mx workload %s seeds=%s" % (name, inp["seeds"]))
     got = run_mx(w.dtype, inp["Aq"], inp["As"], inp["Wq"], inp["Ws"], w.relu).reshape(w.M, w.N)
-    rows, cols = sample_entries(w.M, w.N, 1500, seed=w.index * 7)
+    rows, cols = sample_entries(w.M, w.N, 4000, seed=w.index * 7)
     Y = oracle.mx_gemm_entries_f64(w.dtype, inp["Aq"], inp["As"], inp["Wq"], inp["Ws"], rows, cols,
                                    w.relu)
     a_abs, w_abs = abs_codes(w.dtype, inp["Aq"], inp["Wq"])
     S = oracle.mx_gemm_entries_f64(w.dtype, a_abs, inp["As"], w_abs, inp["Ws"], rows, cols)
     T = truncation_bound(w.dtype, inp["Aq"], inp["As"], inp["Wq"], inp["Ws"], rows, cols)
     check_bound(got[rows, cols], Y, S, T, w.K)
+    check_stated_tolerance(w.dtype, got[rows, cols], Y)
     assert np.isfinite(bits_to_f64(got, BF16)).all()

@@ -6,9 +6,9 @@ Bars (from the workload statement):
   * random inputs, fp16 / bf16 / 4-bit paths: |C - Y| <= 1e-2 + 1e-2 |Y|
     elementwise against the unrounded fp64 result Y;
   * random inputs, fp32 path: relative Frobenius error <= 1e-5.
-Small shapes are compared in full; the full-size workloads, in the launch
-configuration the benchmark uses, on sampled entries the oracle sums one by
-one, plus properties that hold everywhere (ReLU sign, guard bands).
+Every output is compared in full, the full-size workloads too (in the launch
+configuration the benchmark uses): the oracle computes all of C, once per
+input set, and the fp32 relative Frobenius error is taken over all of C.
 """
 
 from __future__ import annotations
@@ -228,12 +228,14 @@ def test_dequant_k_slices_deterministic():
 
 
 @pytest.mark.parametrize("offset", [4, 1], ids=["ws4", "ws1"])
-def test_dequant_misaligned_scales_full_size(offset):
-    """The dequant workload shape with scale rows starting 4 bytes past a 16-byte
-    boundary (the scale-block kernel cannot take them: the per-strip LDS-DMA
-    kernel runs) or 1 byte past (the register-staged kernel runs): still
-    bit-exact on integer activations."""
-    w = synth.WORKLOADS["w4_256x8192x8192"]
+@pytest.mark.parametrize("wname", ["w4_256x8192x8192", "w4_16x8192x8192", "w4_1x8192x8192"])
+def test_dequant_misaligned_scales_full_size(wname, offset):
+    """The dequant workload shapes with scale rows starting 4 bytes past a
+    16-byte boundary (M = 256: the scale-block kernel cannot take them, the
+    per-strip LDS-DMA kernel runs) or 1 byte past (M = 256: the register-staged
+    kernel runs; M <= 16: the weight-streaming kernel's byte-load variant
+    runs): every element bit-exact on integer activations."""
+    w = synth.WORKLOADS[wname]
     inp = synth.make_inputs(w, integer=True)
     A, Wq, Ws = inp["A"], inp["Wq"], inp["Ws"]
     N, KS = Ws.shape
@@ -241,24 +243,39 @@ def test_dequant_misaligned_scales_full_size(offset):
     Wst = raw[offset:offset + N * KS].view(N, KS)
     Wst.copy_(torch.from_numpy(Ws).to(DEV))
     assert Wst.data_ptr() % 16 == offset % 16
-    say("w4 misaligned scales offset=%d" % offset)
+    say("w4 misaligned scales %s offset=%d" % (wname, offset))
     At = to_device(A, BF16, DEV)
     Ct = binding.dequant_gemm_w4(At, torch.from_numpy(Wq).to(DEV), Wst)
     torch.cuda.synchronize()
-    got = to_host_bits(Ct, BF16)
-    rows, cols = sample_entries(w.M, w.N, 3000, seed=31 + offset)
-    Y = oracle.dequant_w4_entries_f64(A, Wq, Ws, rows, cols)
-    check_full(got[rows, cols], Y, BF16, integer=True)
+    got = to_host_bits(Ct, BF16).reshape(w.M, w.N)
+    check_full(got, workload_oracle(w, inp, integer=True), BF16, integer=True)
 
 
 WORKLOADS = ["f32_512", "f16_1024", "f32_4096", "bf16_4096_relu", "bf16_4000x4032x4096_relu",
-             "w4_256x8192x8192", "w4_1x8192x8192", "w4_16x8192x8192"]
+             "w4_256x8192x8192", "w4_1x8192x8192", "w4_16x8192x8192",
+             "bf16_6144x4096x4096_relu", "bf16_3072_relu"]
+
+# Full oracle results of the full-size workloads, computed once per input set
+# (the oracle takes seconds per 4096^3 product on the host's cores).
+_FULL = {}
+
+
+def workload_oracle(w, inp, integer, relu=None):
+    relu = w.relu if relu is None else relu
+    key = (w.name, integer, relu)
+    if key not in _FULL:
+        if w.op == "gemm":
+            _FULL[key] = oracle.gemm_f64(inp["A"], inp["B"], w.dtype, relu)
+        else:
+            _FULL[key] = oracle.dequant_w4_f64(inp["A"], inp["Wq"], inp["Ws"], relu)
+    return _FULL[key]
 
 
 @pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_workload(name, integer):
-    """Full-size workloads in the benchmark's launch configuration."""
+    """Full-size workloads in the benchmark's launch configuration, every
+    element of C against the oracle."""
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, integer)
     say("workload %s int=%s seeds=%s" % (name, integer, inp["seeds"]))
@@ -267,16 +284,7 @@ def test_workload(name, integer):
     else:
         got = run_w4(inp["A"], inp["Wq"], inp["Ws"], w.relu)
     got = got.reshape(w.M, w.N)
-    small = w.flops <= 2 * 1024 ** 3
-    if small and w.op == "gemm":
-        check_full(got, oracle.gemm_f64(inp["A"], inp["B"], w.dtype, w.relu), w.dtype, integer)
-    else:
-        rows, cols = sample_entries(w.M, w.N, 3000, seed=w.index * 7 + integer)
-        if w.op == "gemm":
-            Y = oracle.gemm_entries_f64(inp["A"], inp["B"], w.dtype, rows, cols, w.relu)
-        else:
-            Y = oracle.dequant_w4_entries_f64(inp["A"], inp["Wq"], inp["Ws"], rows, cols, w.relu)
-        check_full(got[rows, cols], Y, w.dtype, integer)
+    check_full(got, workload_oracle(w, inp, integer), w.dtype, integer)
     if w.relu:
         vals = bits_to_f64(got, w.dtype)
         assert (vals >= 0).all() and not np.signbit(vals).any()
@@ -434,7 +442,9 @@ def test_every_transposed_config(dtype):
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("wname", ["bf16_4096_relu", "f32_4096"])
 def test_transposed_full_size(wname, layout):
-    """The 4096^3 workloads in each transposed layout: sampled entries vs the oracle."""
+    """The 4096^3 workloads in each transposed layout: all of C against the
+    oracle's product of the logical matrices, and sampled entries against the
+    oracle indexing the stored layouts."""
     w = synth.WORKLOADS[wname]
     M, N = w.M, w.N
     ta, tb = layout
@@ -442,6 +452,7 @@ def test_transposed_full_size(wname, layout):
     A_st, B_st = _store(inp["A"], ta), _store(inp["B"], tb)
     say("layout %s %s" % (LAYOUT_IDS[LAYOUTS.index(layout)], wname))
     got = run_gemm_ex(A_st, ta, B_st, tb, w.dtype, relu=w.relu).reshape(M, N)
+    check_full(got, workload_oracle(w, inp, integer=False), w.dtype, integer=False)
     rows, cols = sample_entries(M, N, 2000, seed=91 + ta + 2 * tb)
     Y = oracle.gemm_layout_entries_f64(A_st, ta, B_st, tb, w.dtype, rows, cols, relu=w.relu)
     check_full(got[rows, cols], Y, w.dtype, integer=False)

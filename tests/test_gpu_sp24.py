@@ -116,11 +116,15 @@ def test_sp24_zero_k_and_empty():
 
 @pytest.mark.parametrize("integer", [True, False], ids=["int", "rand"])
 def test_sp24_workload(integer):
-    """The full-size benchmark workload in its launch configuration, sampled."""
+    """The full-size benchmark workload in its launch configuration: every
+    element of C against the oracle's densified product, and sampled entries
+    against the oracle's second path (sums straight from the compressed form)."""
     w = synth.WORKLOADS["sp24_bf16_4096_relu"]
     inp = synth.make_inputs(w, integer)
     say("sp24 workload int=%s seeds=%s" % (integer, inp["seeds"]))
     got = run_sp24(inp["Ac"], inp["Ai"], inp["B"], w.dtype, w.relu).reshape(w.M, w.N)
+    check(got, oracle.gemm_sp24_f64(inp["Ac"], inp["Ai"], inp["B"], w.dtype, w.relu), w.dtype,
+          integer)
     rows, cols = sample_entries(w.M, w.N, 2000, seed=w.index * 7 + integer)
     Y = oracle.gemm_sp24_entries_f64(inp["Ac"], inp["Ai"], inp["B"], w.dtype, rows, cols, w.relu)
     check(got[rows, cols], Y, w.dtype, integer)

@@ -17,9 +17,6 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilegemm.so")
 SOURCES = ["tg_api.hip", "tg_gemm_f32.hip", "tg_gemm_f16.hip", "tg_gemm_bf16.hip",
            "tg_dequant_w4.hip", "tg_gemm_mx.hip", "tg_gemm_sp24.hip"]
-# measurement-only probe (sustained clock of the matrix cores); its own library
-PROBE_LIB = os.path.join(HERE, "libtgprobe.so")
-PROBE_SOURCES = ["tg_probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -27,9 +24,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 
 def build(verbose: bool = False) -> str:
-    lib = _build_lib(SOURCES, LIB, verbose)
-    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
-    return lib
+    return _build_lib(SOURCES, LIB, verbose)
 
 
 def _build_lib(sources, lib_path: str, verbose: bool) -> str:

@@ -112,14 +112,18 @@ const Pref kPrefs[] = {
 
 const Config* find_by_name(int op, int dtype, const char* name);
 
-// The weight-streaming dequant kernel for this K (the variant with dword
-// scale loads needs K % 128 == 0), or nullptr.
-const Config* gemv_for(int64_t K)
+// The weight-streaming dequant kernel for this K and scale alignment, or
+// nullptr.  The variant with dword scale loads (bk == 128) needs K % 128 == 0
+// and scale rows that start 4-byte aligned; the byte-load variant (bk == 32)
+// takes any scale pointer.
+const Config* gemv_for(int64_t K, bool ws4)
 {
     ConfigList L = list_for(TG_OP_DEQUANT_W4, TG_BF16);
-    for (int i = 0; i < L.count; ++i)
-        if (L.items[i].pipe == 3 && K % L.items[i].bk == 0)
-            return &L.items[i];
+    for (int i = 0; i < L.count; ++i) {
+        const Config& c = L.items[i];
+        if (c.pipe == 3 && K % c.bk == 0 && (ws4 || c.bk != 128))
+            return &c;
+    }
     return nullptr;
 }
 
@@ -152,8 +156,8 @@ bool usable(const Config& c, const Call& q)
         return false;  // operand layouts are compiled in
     if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
         return false;  // whole strips / rounds of bk
-    if (c.op == TG_OP_DEQUANT_W4 && c.pipe == 2 && !q.ws4)
-        return false;  // scale bytes are copied as dwords
+    if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || (c.pipe == 3 && c.bk == 128)) && !q.ws4)
+        return false;  // scale bytes are copied / loaded as dwords
     if (c.op == TG_OP_DEQUANT_W4 && c.chunked_scales && (q.K % 512 != 0 || !q.ws16))
         return false;  // scale blocks: whole 16-byte pieces of 16-byte aligned rows
     return true;
@@ -220,7 +224,7 @@ const Config* heuristic(const Call& q)
     }
     // few activation rows: the run time is the weight stream from HBM
     if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16) {
-        if (const Config* c = gemv_for(q.K))
+        if (const Config* c = gemv_for(q.K, q.ws4))
             return c;
     }
     if (q.op == TG_OP_GEMM && q.dtype != TG_F32 && !q.ta && !q.tb) {
@@ -352,11 +356,9 @@ tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(c.kernel, dim3((unsigned)grid), dim3(c.wgm * c.wgn * c.ks * 64), args,
                                    0, stream);
-    if (e != hipSuccess)
-        return TG_ERR_HIP;
-    if (hipPeekAtLastError() != hipSuccess)
-        return TG_ERR_HIP;
-    return TG_OK;
+    // hipLaunchKernel's own status covers this launch; the thread's sticky
+    // last-error state may hold an earlier call's error and is not consulted
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 // Split K (tg_gemm_splitk): the caller's request and workspace.

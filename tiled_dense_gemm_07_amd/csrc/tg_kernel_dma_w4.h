@@ -104,6 +104,12 @@ struct DmaW4 {
     static_assert(NS >= 4 && NS % 2 == 0, "an even ring of four or more stages (code registers "
                                           "alternate per strip)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    // A scale block is issued in the middle of the block before it (strip
+    // t % SB == SB / 2) and first read SB / 2 strips later; the per-strip wait
+    // leaves (NS - 3) strips of copies in flight, so it covers the block only
+    // if at least that many strips' copies were issued after it.
+    static_assert(SB == 1 || NS <= SB / 2 + 2,
+                  "the strip wait must cover the scale block issued half a block earlier");
 
     template <int W>
     struct Copies {

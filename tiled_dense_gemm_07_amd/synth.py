@@ -175,6 +175,11 @@ WORKLOADS = {
     # 2:4 structured-sparse A (the flops are the dense-equivalent 2 M N K)
     "sp24_bf16_4096_relu": Workload("sp24_bf16_4096_relu", 10, "sp24", BF16, 4096, 4096, 4096,
                                     True),
+    # tile grids that are not whole waves of one tile per compute unit
+    # (384 and 144 tiles of 256 x 256): the tail of the last wave
+    "bf16_6144x4096x4096_relu": Workload("bf16_6144x4096x4096_relu", 11, "gemm", BF16,
+                                         6144, 4096, 4096, True),
+    "bf16_3072_relu": Workload("bf16_3072_relu", 12, "gemm", BF16, 3072, 3072, 3072, True),
 }
 
 

@@ -1,10 +1,17 @@
-"""Measured HBM traffic of one kernel launch, from rocprofv3 counters.
+"""Measured fabric traffic of one kernel launch, from rocprofv3 counters.
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) count traffic between the L2s
-and the memory fabric (MALL hits included, data still in L2 from the previous
-launch excluded).  Their scale is calibrated with one plain elementwise kernel
-that reads and writes a known number of bytes in the same process:
-factor = true bytes / counter bytes.  Two separate counter passes are needed (FETCH_SIZE, then WRITE_SIZE):
+and the memory fabric: the 256 MB MALL serves part of it, so these are
+*fabric* bytes, an upper bound on HBM bytes.  With ``--cold`` the profiled
+program rotates the operands over copies larger than the MALL, so every
+launch's first touch of each operand byte comes from HBM.  The counters' scale
+is calibrated with one plain elementwise kernel that reads and writes a known
+number of bytes (1 GiB each way, larger than the MALL) in the same process:
+factor = true bytes / counter bytes.  gfx950 issues 128-byte requests that
+FETCH_SIZE counts as 64 bytes, hence a fetch factor near 2; a cold record whose
+fabric bytes come out near the algorithmic bytes of a kernel that reads every
+byte once (the weight-streaming dequant kernel) checks that factor for its
+family.  Two separate counter passes are needed (FETCH_SIZE, then WRITE_SIZE):
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/f -o f -- \\
         python -m tiled_dense_gemm_07_amd.traffic run --workload bf16_4096_relu
@@ -13,6 +20,8 @@ factor = true bytes / counter bytes.  Two separate counter passes are needed (FE
     python -m tiled_dense_gemm_07_amd.traffic summarize --workload bf16_4096_relu \\
         --fetch OUT/f/f_counter_collection.csv --write OUT/w/w_counter_collection.csv \\
         --out profiles/traffic_bf16_4096_relu.json
+
+(add ``--cold`` to both ``run`` commands and to ``summarize`` for a cold record).
 
 The summary records which compiled configuration ran and a hash of the
 sources that kernel is built from; the benchmark reports the traffic only
@@ -79,7 +88,20 @@ def workload_config(workload: str) -> str:
     return binding.query_config(op, w.M, w.N, w.K, w.dtype).split()[0]
 
 
-def run(workload: str, launches: int) -> None:
+COLD_BYTES = 1 << 30
+
+
+def _rotated(tensors, cold: bool):
+    """The operand sets launches cycle through: the tensors themselves, or
+    (cold) enough copies that together they exceed COLD_BYTES."""
+    if not cold:
+        return [tensors]
+    per = sum(x.numel() * x.element_size() for x in tensors)
+    copies = max(4, -(-COLD_BYTES // per))
+    return [tuple(x.clone() for x in tensors) for _ in range(copies)]
+
+
+def run(workload: str, launches: int, cold: bool = False) -> None:
     """The program profiled: one calibration copy, then the workload's kernel."""
     import numpy as np
     import torch
@@ -104,27 +126,31 @@ def run(workload: str, launches: int) -> None:
         view = np.int32 if w.dtype == synth.F32 else np.int16
         A = torch.from_numpy(inp["A"].view(view)).view(tdt[w.dtype]).to(dev)
         B = torch.from_numpy(inp["B"].view(view)).view(tdt[w.dtype]).to(dev)
-        for _ in range(launches):
-            binding.gemm(A, B, epilogue=epi)
+        sets = _rotated((A, B), cold)
+        for i in range(launches):
+            binding.gemm(*sets[i % len(sets)], epilogue=epi)
     elif w.op == "mx":
-        t = [torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws")]
-        for _ in range(launches):
-            binding.gemm_mx(w.dtype, *t, epilogue=epi)
+        t = tuple(torch.from_numpy(inp[k]).to(dev) for k in ("Aq", "As", "Wq", "Ws"))
+        sets = _rotated(t, cold)
+        for i in range(launches):
+            binding.gemm_mx(w.dtype, *sets[i % len(sets)], epilogue=epi)
     elif w.op == "sp24":
         tdt = {synth.F16: torch.float16, synth.BF16: torch.bfloat16}[w.dtype]
         Ac = torch.from_numpy(inp["Ac"].view(np.int16)).view(tdt).to(dev)
         B = torch.from_numpy(inp["B"].view(np.int16)).view(tdt).to(dev)
         Ai = torch.from_numpy(inp["Ai"]).to(dev)
-        for _ in range(launches):
-            binding.gemm_sp24(Ac, Ai, B, epilogue=epi)
+        sets = _rotated((Ac, Ai, B), cold)
+        for i in range(launches):
+            binding.gemm_sp24(*sets[i % len(sets)], epilogue=epi)
     else:
         A = torch.from_numpy(inp["A"].view(np.int16)).view(torch.bfloat16).to(dev)
         Wq = torch.from_numpy(inp["Wq"]).to(dev)
         Ws = torch.from_numpy(inp["Ws"]).to(dev)
-        for _ in range(launches):
-            binding.dequant_gemm_w4(A, Wq, Ws, epilogue=epi)
+        sets = _rotated((A, Wq, Ws), cold)
+        for i in range(launches):
+            binding.dequant_gemm_w4(*sets[i % len(sets)], epilogue=epi)
     torch.cuda.synchronize()
-    print("traffic run done: %s x%d" % (workload, launches))
+    print("traffic run done: %s x%d%s" % (workload, launches, " cold" if cold else ""))
 
 
 def _read(path: str, counter: str):
@@ -147,7 +173,7 @@ def _read(path: str, counter: str):
     return calib[0][1], kern
 
 
-def summarize(workload: str, fetch_csv: str, write_csv: str, out: str) -> dict:
+def summarize(workload: str, fetch_csv: str, write_csv: str, out: str, cold: bool = False) -> dict:
     from . import synth
 
     w = synth.WORKLOADS[workload]
@@ -169,9 +195,10 @@ def summarize(workload: str, fetch_csv: str, write_csv: str, out: str) -> dict:
         "fetch_factor": f_factor, "write_factor": w_factor,
         "fetch_size_kib_per_launch": sum(f_k) / len(f_k),
         "write_size_kib_per_launch": sum(w_k) / len(w_k),
-        "hbm_fetch_bytes_per_launch": fetch,
-        "hbm_write_bytes_per_launch": write,
-        "hbm_bytes_per_launch": fetch + write,
+        "cold": cold,
+        "fabric_fetch_bytes_per_launch": fetch,
+        "fabric_write_bytes_per_launch": write,
+        "fabric_bytes_per_launch": fetch + write,
         "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
         "traffic_over_algorithmic": (fetch + write) / w.algorithmic_bytes(),
         "launches": len(f_k),
@@ -188,16 +215,19 @@ def main(argv=None):
     r = sub.add_parser("run")
     r.add_argument("--workload", required=True)
     r.add_argument("--launches", type=int, default=3)
+    r.add_argument("--cold", action="store_true")
     s = sub.add_parser("summarize")
     s.add_argument("--workload", required=True)
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--cold", action="store_true")
     args = ap.parse_args(argv)
     if args.cmd == "run":
-        run(args.workload, args.launches)
+        run(args.workload, args.launches, args.cold)
     else:
-        print(json.dumps(summarize(args.workload, args.fetch, args.write, args.out), indent=1))
+        print(json.dumps(summarize(args.workload, args.fetch, args.write, args.out, args.cold),
+                         indent=1))
     return 0
 
 
