@@ -55,7 +55,8 @@ typedef enum {
     TG_ERR_NO_CONFIG = 6,    /* forced config index out of range / wrong op       */
     TG_ERR_HIP = 7,          /* the HIP runtime reported an error at launch       */
     TG_ERR_BAD_LAYOUT = 8,   /* trans_a / trans_b not 0 or 1                      */
-    TG_ERR_WORKSPACE = 9     /* split-K workspace NULL, too small or misaligned    */
+    TG_ERR_WORKSPACE = 9,    /* split-K workspace NULL, too small or misaligned    */
+    TG_ERR_SCRATCH = 10      /* split-K partials exceed TG_SPLITK_SCRATCH_BYTES    */
 } tg_status;
 
 typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
@@ -149,6 +150,31 @@ tg_status tg_gemm_splitk(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const 
  */
 tg_status tg_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                                         int splits, size_t* bytes);
+
+/*
+ * Split-K GEMM that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, numerics and
+ * results as tg_gemm_splitk, without the workspace: the arrival counters and
+ * fp32 partial tiles live in a fixed static device array of
+ * TG_SPLITK_SCRATCH_BYTES, one per GPU, held from the library's first use on
+ * that GPU until the process ends.  The array's device address is looked up
+ * once per device (the calling thread's current device, which must be the
+ * stream's).  Each call that splits first zeroes the counters it uses with a
+ * small fill kernel on `stream` (no memset node, so it can be captured), then
+ * launches the GEMM; nothing is allocated or freed.
+ * Every call on one GPU shares the array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and give wrong results; issue them
+ * on one stream.
+ * Errors: as tg_gemm_splitk (never TG_ERR_WORKSPACE); TG_ERR_SCRATCH when the
+ *   split launched would need more than TG_SPLITK_SCRATCH_BYTES
+ *   (tg_gemm_splitk_workspace_size gives the bytes; lower `splits` or use
+ *   tg_gemm_splitk); TG_ERR_HIP also when the array's address lookup fails.
+ */
+#define TG_SPLITK_SCRATCH_BYTES (16 * 1024 * 1024)
+tg_status tg_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                 const void* A, const void* B, void* C, tg_epilogue epi,
+                                 int splits, tg_stream_t stream);
 
 /*
  * Weight-only 4-bit dequant GEMM: C = epilogue(A x W^T).

@@ -17,7 +17,7 @@ from tiled_dense_gemm_07_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP, BADL, WSP = range(10)
+OK, NULLP, SHAPE, DTYPE, EPI, ALIAS, NOCFG, HIP, BADL, WSP, SCRATCH = range(11)
 
 # fake, well-separated device addresses: validation never dereferences them
 PA, PB, PC, PS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
@@ -42,7 +42,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(10):
+    for s in range(11):
         text = binding.status_str(s)
         assert text.startswith("TG_")
     assert "unknown" in binding.status_str(99)
@@ -197,6 +197,27 @@ def test_splitk_argument_errors(lib):
     assert split
     for i in split:
         assert c(i, M, N, K, 2, PA, PB, PC, 0, 4, None, 0, None) == WSP
+
+
+def test_splitk_noalloc_argument_errors(lib):
+    """Argument errors, and a split beyond the fixed scratch array, are refused
+    before any HIP call (no device here)."""
+    g = lib.tg_gemm_splitk_noalloc
+    M, N, K = 256, 256, 8192
+    # (M, N, K, dtype, A, B, C, epi, splits, stream)
+    assert g(M, N, K, 2, PA, PB, PC, 0, -1, None) == SHAPE
+    assert g(M, N, K, 3, PA, PB, PC, 0, 0, None) == DTYPE
+    assert g(M, N, K, 2, PA, PB, PC, 5, 0, None) == EPI
+    assert g(M, N, K, 2, None, PB, PC, 0, 0, None) == NULLP
+    assert g(M, N, K, 2, PA, PB, PA + 64, 0, 0, None) == ALIAS
+    assert g(0, N, K, 2, None, None, None, 0, 0, None) == OK
+    big = (2048, 2048, 8192)
+    assert _ws_size(lib, *big, 2, 16)[1] > binding.TG_SPLITK_SCRATCH_BYTES
+    assert g(*big, 2, PA, PB, PC, 0, 16, None) == SCRATCH
+    # the automatic split of every dtype fits the array at these long-K shapes
+    for dt in (0, 1, 2):
+        for shape in ((256, 256, 8192), (64, 4096, 4096), (512, 512, 8192), (128, 128, 16384)):
+            assert 0 < _ws_size(lib, *shape, dt, 0)[1] <= binding.TG_SPLITK_SCRATCH_BYTES, shape
 
 
 def test_mx_argument_errors(lib):

@@ -29,7 +29,8 @@ EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_q
            "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
            "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
            "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config", "tg_gemm_splitk",
-           "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config")
+           "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config", "tg_gemm_splitk_noalloc")
+TG_SPLITK_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
 
@@ -98,6 +99,8 @@ def load_library():
     lib.tg_gemm_splitk_workspace_size.argtypes = [i64, i64, i64, c_int, c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]
     lib.tg_gemm_splitk_workspace_size.restype = c_int
+    lib.tg_gemm_splitk_noalloc.argtypes = [i64, i64, i64, c_int, p, p, p, c_int, c_int, p]
+    lib.tg_gemm_splitk_noalloc.restype = c_int
     _lib = lib
     return lib
 
@@ -231,6 +234,17 @@ def gemm_splitk(A, B, C=None, epilogue=None, splits: int = 0, workspace=None, st
     args = (M, N, K, dt, A.data_ptr(), B.data_ptr(), C.data_ptr(), _epi_code(epilogue), splits,
             wp, wn, _stream_ptr(A.device, stream))
     _check(lib.tg_gemm_splitk(*args) if config is None else lib.tg_gemm_splitk_config(config, *args))
+    return C
+
+
+def gemm_splitk_noalloc(A, B, C, epilogue=None, splits: int = 0, stream=None):
+    """As :func:`gemm_splitk`, with the partial tiles in the library's fixed
+    scratch array instead of a workspace (tg_gemm_splitk_noalloc): C must be
+    given, and nothing is allocated.  Calls that overlap on one GPU race."""
+    M, N, K = _gemm_args(A, B, C)
+    _check(load_library().tg_gemm_splitk_noalloc(
+        M, N, K, _dtype_code(A), A.data_ptr(), B.data_ptr(), C.data_ptr(), _epi_code(epilogue),
+        splits, _stream_ptr(A.device, stream)))
     return C
 
 

@@ -13,6 +13,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,7 +22,48 @@
 #include "tg_configs.h"
 #include "tg_kernel.h"
 
+// Scratch of tg_gemm_splitk_noalloc: the split-K arrival counters and fp32
+// partial tiles, in a fixed device array instead of caller memory.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` is only the host-side handle of the symbol: its device
+// address comes from hipGetSymbolAddress (per device, in scratch_of_device).
+static __device__ __attribute__((aligned(256))) char scratch[TG_SPLITK_SCRATCH_BYTES];
+
+// Zero n int32 counters (a fill kernel, so that a captured graph holds no
+// memset node).
+__global__ void tg_clear_counters(int* counters, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        counters[i] = 0;
+}
+
 namespace {
+
+// Device address of `scratch` on the calling thread's current device,
+// looked up once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+tg_status scratch_of_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TG_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return TG_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return TG_OK;
+}
 
 using tg::Config;
 using tg::ConfigList;
@@ -366,6 +409,7 @@ struct SplitArgs {
     int splits;  // 0: chosen by the library; >= 1: requested
     void* workspace;
     size_t bytes;
+    bool use_scratch = false;  // tg_gemm_splitk_noalloc: the static scratch array
 };
 
 // How configuration c splits a call: S workgroups per tile over kc k each
@@ -494,16 +538,33 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         c = select_config(q);
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
-    if (plan.S > 1 && (!sk->workspace || sk->bytes < plan.bytes || !aligned16(sk->workspace)))
+    void* ws = sk ? sk->workspace : nullptr;
+    if (plan.S > 1 && sk->use_scratch) {
+        if (plan.bytes > (size_t)TG_SPLITK_SCRATCH_BYTES)
+            return TG_ERR_SCRATCH;
+        if (scratch_of_device(&ws) != TG_OK)
+            return TG_ERR_HIP;
+    } else if (plan.S > 1 && (!ws || sk->bytes < plan.bytes || !aligned16(ws))) {
         return TG_ERR_WORKSPACE;
+    }
     tg::GemmParams p{};
     if (plan.S > 1) {
-        const size_t cnt = ((size_t)tiles(M, c->bm) * tiles(N, c->bn) * 4 + kCounterAlign - 1) /
-                           kCounterAlign * kCounterAlign;
+        const int64_t t = tiles(M, c->bm) * tiles(N, c->bn);
+        const size_t cnt = ((size_t)t * 4 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
         p.splits = plan.S;
         p.kc = plan.kc;
-        p.counters = (int*)sk->workspace;
-        p.ws = (float*)((char*)sk->workspace + cnt);
+        p.counters = (int*)ws;
+        p.ws = (float*)((char*)ws + cnt);
+        if (sk->use_scratch) {
+            // the array keeps the previous call's contents: its counters
+            // must start at zero
+            int* counters = p.counters;
+            int n = (int)t;
+            void* cargs[] = {&counters, &n};
+            if (hipLaunchKernel((const void*)&tg_clear_counters, dim3((unsigned)((n + 255) / 256)),
+                                dim3(256), cargs, 0, (hipStream_t)stream) != hipSuccess)
+                return TG_ERR_HIP;
+        }
     }
     p.A = A;
     p.B = B;
@@ -692,6 +753,15 @@ tg_status tg_gemm_splitk(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const 
     return gemm_impl(nullptr, -1, M, N, K, dtype, A, 0, B, 0, C, epi, stream, &sk);
 }
 
+tg_status tg_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                 const void* A, const void* B, void* C, tg_epilogue epi,
+                                 int splits, tg_stream_t stream)
+{
+    SplitArgs sk{splits, nullptr, 0};
+    sk.use_scratch = true;
+    return gemm_impl(nullptr, -1, M, N, K, dtype, A, 0, B, 0, C, epi, stream, &sk);
+}
+
 tg_status tg_gemm_splitk_config(int index, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                                 const void* A, const void* B, void* C, tg_epilogue epi,
                                 int splits, void* workspace, size_t workspace_bytes,
@@ -751,6 +821,9 @@ const char* tg_status_str(tg_status s)
     case TG_ERR_WORKSPACE:
         return "TG_ERR_WORKSPACE: split-K workspace NULL, smaller than "
                "tg_gemm_splitk_workspace_size, or not 16-byte aligned";
+    case TG_ERR_SCRATCH:
+        return "TG_ERR_SCRATCH: the split needs more than the fixed scratch array "
+               "(TG_SPLITK_SCRATCH_BYTES); use tg_gemm_splitk with a workspace, or fewer splits";
     }
     return "unknown tg_status";
 }
