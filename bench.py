@@ -16,9 +16,10 @@ Printed: ONE JSON line (rank 0) with
   roofline      the kernel's average duration (HIP events recorded on the
                 stream it runs on, around the K timed launches), against the
                 bf16 dense MFMA peak; the per-launch median / p10 / p90 of a
-                separate pass; the shader clock sampled from the SMU while the
-                kernel runs back to back, and the fraction of the peak at that
-                clock,
+                separate pass; the shader clock the kernel ran at (the
+                library's clock record: shader-clock counter against the
+                100 MHz reference counter inside the kernel, one workgroup per
+                XCD) and the fraction of the peak at that clock,
   cpu_baseline  the C oracle timed on host cores on a bounded row sample,
   workloads     the other workload shapes, each timed the same way with warm
                 caches (same buffers) and cold caches (operands rotated over
@@ -32,7 +33,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -58,7 +58,7 @@ OTHER = ["f32_4096", "bf16_4000x4032x4096_relu", "f16_1024", "f32_512", "w4_256x
 MEMORY_BOUND = ("w4_1x8192x8192", "w4_16x8192x8192")
 WARM_MS = 40.0      # GPU work before a workload's timed launches (clock ramp-up)
 COLD_BYTES = 1 << 30  # operand copies rotated by the cold timing (> 256 MB MALL)
-CLOCK_MS = 400.0    # back-to-back launches while the shader clock is sampled
+CLOCK_MS = 400.0    # back-to-back launches while the shader clock is recorded
 
 
 def load_traffic(workload: str):
@@ -184,87 +184,37 @@ def time_each(fns, stream, launches: int) -> dict:
             "launches": launches}
 
 
-class ClockSampler:
-    """The GPU's shader (gfx) clock, read from the SMU metrics through amdsmi
-    every few milliseconds on a host thread while kernels run."""
-
-    def __init__(self):
-        import amdsmi
-        import torch
-
-        self.smi = amdsmi
-        amdsmi.amdsmi_init()
-        handles = amdsmi.amdsmi_get_processor_handles()
-        if not handles:
-            raise RuntimeError("amdsmi sees no GPU")
-        self.h = handles[0]
-        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
-        if bus is not None and len(handles) > 1:
-            for h in handles:
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
-                if int(bdf.split(":")[1], 16) == int(bus):
-                    self.h = h
-        self.read()  # fails here, not in the thread, if the metrics are unreadable
-        self.samples = []
-        self._stop = threading.Event()
-
-    def read(self) -> float:
-        """Current shader clock in MHz (the mean over the XCDs that report one)."""
-        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
-        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-            v = m.get(key)
-            if isinstance(v, (list, tuple)):
-                vals = [float(x) for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-                if vals:
-                    return sum(vals) / len(vals)
-            elif isinstance(v, (int, float)) and 0 < v < 10000:
-                return float(v)
-        info = self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)
-        return float(info["clk"])
-
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self.read())
-            except Exception:
-                pass
-            time.sleep(0.002)
-
-    def __enter__(self):
-        self.samples = []
-        self._stop.clear()
-        self.t = threading.Thread(target=self._loop, daemon=True)
-        self.t.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        self.t.join()
-        return False
-
-    def close(self):
-        try:
-            self.smi.amdsmi_shut_down()
-        except Exception:
-            pass
-
-
-def measure_clock(fn, stream, once_ms: float, sampler) -> dict:
-    """Median sampled shader clock over CLOCK_MS of back-to-back launches, and
-    the mean launch duration over the same launches."""
+def measure_clock(fn, stream, once_ms: float) -> dict:
+    """The shader clock the kernel runs at, from the library's clock record:
+    CLOCK_MS of back-to-back launches in 20 batches; after each batch, the
+    record of its last launch (one workgroup per XCD: shader-clock counter
+    against the 100 MHz reference counter at its start and end)."""
     import numpy as np
+    import torch
 
-    n = max(20, int(CLOCK_MS / once_ms))
-    with sampler:
-        ms = time_mean(fn, stream, n)
-    s = np.array(sampler.samples[len(sampler.samples) // 10:])  # skip the first tenth
-    if s.size == 0:
-        raise RuntimeError("no clock samples")
-    return {"sustained_clock_ghz": round(float(np.median(s)) / 1000.0, 4),
-            "clock_p10_ghz": round(float(np.percentile(s, 10)) / 1000.0, 4),
-            "clock_p90_ghz": round(float(np.percentile(s, 90)) / 1000.0, 4),
-            "clock_samples": int(s.size), "clock_pass_kernel_ms": round(ms, 5),
-            "clock_pass_launches": n, "clock_source": "amdsmi gpu metrics (gfx clock)"}
+    from tiled_dense_gemm_07_amd import binding
+
+    stamps = torch.zeros(32, dtype=torch.int64, device=torch.device("cuda:0"))
+    per = max(5, int(CLOCK_MS / once_ms / 20))
+    clocks = []
+    binding.set_clock_stamps(stamps)
+    try:
+        for _ in range(20):
+            stamps.zero_()
+            for _ in range(per):
+                fn()
+            stream.synchronize()
+            clocks.extend(binding.stamp_clock_ghz(stamps.cpu().tolist()))
+    finally:
+        binding.set_clock_stamps(None)
+    c = np.array(clocks)
+    if c.size == 0:
+        raise RuntimeError("no clock records")
+    return {"sustained_clock_ghz": round(float(np.median(c)), 4),
+            "clock_p10_ghz": round(float(np.percentile(c, 10)), 4),
+            "clock_p90_ghz": round(float(np.percentile(c, 90)), 4),
+            "clock_records": int(c.size),
+            "clock_source": "s_memtime / s_memrealtime in workgroups 0-7 of the kernel"}
 
 
 def time_cold(w, tensors, stream, launches: int = 40) -> dict:
@@ -336,7 +286,7 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
             "seconds": round(elapsed, 3)}
 
 
-def bench_workload(name, dev, stream, sampler, cpu_budget_s):
+def bench_workload(name, dev, stream, cpu_budget_s):
     import torch
 
     from tiled_dense_gemm_07_amd import binding, synth
@@ -357,14 +307,13 @@ def bench_workload(name, dev, stream, sampler, cpu_budget_s):
         "per_launch": dist,
         "config": binding.query_config({"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[ow.op],
                                        ow.M, ow.N, ow.K, ow.dtype)}
-    if sampler is not None:
-        try:
-            ck = measure_clock(fn, stream, mean_ms, sampler)
-            rec["sustained_clock_ghz"] = ck["sustained_clock_ghz"]
-            rec["frac_mfma_peak_at_clock"] = round(
-                tf / (PEAK_TFLOPS[dn] * ck["sustained_clock_ghz"] / PEAK_CLOCK_GHZ), 4)
-        except Exception as e:
-            rec["sustained_clock_ghz"] = "unavailable: %s" % e
+    try:
+        ck = measure_clock(fn, stream, mean_ms)
+        rec["sustained_clock_ghz"] = ck["sustained_clock_ghz"]
+        rec["frac_mfma_peak_at_clock"] = round(
+            tf / (PEAK_TFLOPS[dn] * ck["sustained_clock_ghz"] / PEAK_CLOCK_GHZ), 4)
+    except Exception as e:
+        rec["sustained_clock_ghz"] = "unavailable: %s" % e
     rec["cold"] = time_cold(ow, t, stream)
     tr = load_traffic(name)
     if tr is not None:
@@ -408,11 +357,6 @@ def main():
     binding.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    try:
-        sampler = ClockSampler()
-    except Exception as e:
-        sampler = None
-        sampler_err = "unavailable: %s" % e
 
     w = synth.WORKLOADS[HEADLINE]
     inp, tensors = make_device_inputs(w, dev)
@@ -447,31 +391,26 @@ def main():
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes()}
     # after the timed region: per-launch distribution and the sustained clock
     roofline["per_launch"] = time_each([fn], stream, 200)
-    if sampler is not None:
-        try:
-            ck = measure_clock(fn, stream, kernel_ms, sampler)
-            roofline.update(ck)
-            ghz = ck["sustained_clock_ghz"]
-            roofline["peak_at_clock"] = round(peak * ghz / PEAK_CLOCK_GHZ, 1)
-            roofline["frac_at_clock"] = round(achieved / roofline["peak_at_clock"], 4)
-        except Exception as e:
-            roofline["sustained_clock_ghz"] = "unavailable: %s" % e
-    else:
-        roofline["sustained_clock_ghz"] = sampler_err
+    try:
+        ck = measure_clock(fn, stream, kernel_ms)
+        roofline.update(ck)
+        ghz = ck["sustained_clock_ghz"]
+        roofline["peak_at_clock"] = round(peak * ghz / PEAK_CLOCK_GHZ, 1)
+        roofline["frac_at_clock"] = round(achieved / roofline["peak_at_clock"], 4)
+    except Exception as e:
+        roofline["sustained_clock_ghz"] = "unavailable: %s" % e
     roofline["cold"] = time_cold(w, tensors, stream)
 
     workloads = {}
     if not args.no_workloads:
         names = OTHER if not args.workloads else args.workloads.split(",")
         for name in names:
-            workloads[name] = bench_workload(name, dev, stream, sampler,
+            workloads[name] = bench_workload(name, dev, stream,
                                              0.0 if args.no_cpu_baseline else 1.5)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, 12.0)
-    if sampler is not None:
-        sampler.close()
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

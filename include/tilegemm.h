@@ -331,6 +331,22 @@ tg_status tg_gemm_splitk_config(int index, int64_t M, int64_t N, int64_t K, tg_d
 tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,
                       int32_t* out_n);
 
+/*
+ * Clock record, a measurement aid.  The mhpq.cn page (section 4.2) reads a
+ * GEMM's speed against the theoretical ceiling first; on a power-limited card
+ * that ceiling moves with the shader clock, so a benchmark needs the clock the
+ * kernel actually ran at.  With `stamps` set (a DEVICE pointer to 32 uint64,
+ * caller-owned, NULL to switch off), every kernel launched afterwards by any
+ * entry point has wave 0 of its workgroups 0..7 (one per XCD) write
+ * stamps[4 b + 0..3] = shader-clock counter and 100 MHz reference counter at
+ * its start, then the same at its end (workgroups b < 8 only; a grid of fewer
+ * workgroups leaves the rest untouched).  Each launch overwrites the previous
+ * one's record, so read it after synchronising.  Clock of workgroup b:
+ * (t1 - t0) / ((r1 - r0) / 100 MHz).  Process-wide setting for benchmarks;
+ * calls on several threads or streams while it is set write the same buffer.
+ */
+void tg_set_clock_stamps(uint64_t* stamps);
+
 #ifdef __cplusplus
 }
 #endif

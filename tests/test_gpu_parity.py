@@ -492,3 +492,24 @@ def test_side_stream():
     s.synchronize()
     got = to_host_bits(Ct, BF16)
     assert np.array_equal(got, oracle.encode(BF16, oracle.gemm_f64(A, B, BF16)))
+
+
+def test_clock_stamps():
+    """The clock record: results unchanged with it on, and one plausible record
+    (shader clock between 0.3 and 3 GHz) per XCD for a grid of 8+ workgroups."""
+    M, N, K = 1024, 1024, 512
+    A, B = synth.gemm_inputs(M, N, K, BF16, 61, 62, integer=True)
+    want = oracle.encode(BF16, oracle.gemm_f64(A, B, BF16, relu=True))
+    stamps = torch.zeros(32, dtype=torch.int64, device=DEV)
+    say("clock stamps")
+    binding.set_clock_stamps(stamps)
+    try:
+        got = run_gemm(A, B, BF16, True)
+    finally:
+        binding.set_clock_stamps(None)
+    assert np.array_equal(got, want)
+    ghz = binding.stamp_clock_ghz(stamps.cpu().tolist())
+    assert len(ghz) == 8 and all(0.3 < g < 3.0 for g in ghz), ghz
+    stamps.zero_()
+    run_gemm(A, B, BF16, True)  # switched off: nothing written
+    assert int(stamps.abs().sum().item()) == 0

@@ -29,7 +29,8 @@ EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_q
            "tg_query_config_ex", "tg_config_count", "tg_config_name", "tg_gemm_config",
            "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
            "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config", "tg_gemm_splitk",
-           "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config", "tg_gemm_splitk_noalloc")
+           "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config", "tg_gemm_splitk_noalloc",
+           "tg_set_clock_stamps")
 TG_SPLITK_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
@@ -101,6 +102,8 @@ def load_library():
     lib.tg_gemm_splitk_workspace_size.restype = c_int
     lib.tg_gemm_splitk_noalloc.argtypes = [i64, i64, i64, c_int, p, p, p, c_int, c_int, p]
     lib.tg_gemm_splitk_noalloc.restype = c_int
+    lib.tg_set_clock_stamps.argtypes = [p]
+    lib.tg_set_clock_stamps.restype = None
     _lib = lib
     return lib
 
@@ -246,6 +249,27 @@ def gemm_splitk_noalloc(A, B, C, epilogue=None, splits: int = 0, stream=None):
         M, N, K, _dtype_code(A), A.data_ptr(), B.data_ptr(), C.data_ptr(), _epi_code(epilogue),
         splits, _stream_ptr(A.device, stream)))
     return C
+
+
+def set_clock_stamps(stamps):
+    """Record the shader clock of every following launch into `stamps`, an
+    int64 / uint64 device tensor of 32 elements (None: stop recording)."""
+    if stamps is not None:
+        _require_gpu_tensor("stamps", stamps)
+        if stamps.numel() * stamps.element_size() < 32 * 8:
+            raise ValueError("stamps must hold 32 64-bit values")
+    load_library().tg_set_clock_stamps(stamps.data_ptr() if stamps is not None else None)
+
+
+def stamp_clock_ghz(stamps) -> list:
+    """Shader clock (GHz) of each workgroup 0..7 that wrote a record into the
+    host copy of `stamps` (a sequence of 32 integers)."""
+    out = []
+    for b in range(8):
+        t0, r0, t1, r1 = (int(x) for x in stamps[4 * b:4 * b + 4])
+        if r1 > r0 and t1 > t0:
+            out.append((t1 - t0) / ((r1 - r0) / 100e6) / 1e9)
+    return out
 
 
 def _gemm_ex_args(A, B, trans_a, trans_b, C):

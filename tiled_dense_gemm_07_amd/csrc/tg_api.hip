@@ -379,9 +379,13 @@ tg_status check_shape(int64_t M, int64_t N, int64_t K, int esize)
     return TG_OK;
 }
 
+// Device buffer of the optional clock record (tg_set_clock_stamps), or NULL.
+std::atomic<unsigned long long*> g_stamps{nullptr};
+
 tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream)
 {
     tg::GemmParams p = base;
+    p.stamps = g_stamps.load(std::memory_order_relaxed);
     p.tiles_m = (int)tiles(p.M, c.bm);
     p.tiles_n = (int)tiles(p.N, c.bn);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * (p.splits > 1 ? p.splits : 1);
@@ -939,6 +943,11 @@ tg_status tg_gemm_sp24_config(int index, int64_t M, int64_t N, int64_t K, tg_dty
     ConfigList L = list_for(TG_OP_SP24, dtype);
     const Config* c = (index >= 0 && index < L.count) ? &L.items[index] : nullptr;
     return sp24_impl(c, index < 0 ? 0 : index, M, N, K, dtype, Ac, Ai, B, C, epi, stream);
+}
+
+void tg_set_clock_stamps(uint64_t* stamps)
+{
+    g_stamps.store((unsigned long long*)stamps, std::memory_order_relaxed);
 }
 
 tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,

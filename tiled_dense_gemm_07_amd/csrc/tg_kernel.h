@@ -81,7 +81,44 @@ struct GemmParams {
     int kc;
     float* ws;      // [tiles][splits][BM * BN] fp32 partial tiles
     int* counters;  // [tiles] arrival counts, zero before and after each call
+    // Optional clock record (a measurement aid, normally NULL): wave 0 of
+    // workgroups 0..7 (one per XCD under round-robin dispatch) writes the
+    // shader clock counter (s_memtime) and the 100 MHz reference counter
+    // (s_memrealtime) at its start and end: stamps[4 b + 0..3] = t0, r0, t1, r1.
+    unsigned long long* stamps;
 };
+
+struct ClockStamp {
+    unsigned long long t, r;
+    bool on;
+};
+
+__device__ __forceinline__ ClockStamp stamp_begin(const GemmParams& p)
+{
+    ClockStamp s{0, 0, false};
+    if (p.stamps != nullptr && blockIdx.x < 8 &&
+        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) {
+        s.t = __builtin_amdgcn_s_memtime();
+        s.r = __builtin_amdgcn_s_memrealtime();
+        s.on = true;
+    }
+    return s;
+}
+
+__device__ __forceinline__ void stamp_end(const GemmParams& p, const ClockStamp& s)
+{
+    if (s.on) {
+        const unsigned long long t = __builtin_amdgcn_s_memtime();
+        const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+        if (threadIdx.x == 0) {
+            unsigned long long* o = p.stamps + 4 * blockIdx.x;
+            o[0] = s.t;
+            o[1] = s.r;
+            o[2] = t;
+            o[3] = r;
+        }
+    }
+}
 
 // --------------------------------------------------------------------------
 // Buffer resources (range-checked global access).
@@ -855,10 +892,12 @@ gemm_kernel(GemmParams p)
 {
     using Kern =
         GemmKernel<DT, BMODE, BM, BN, BK, WGM, WGN, STAGES, GROUP_M, WIDE, PIPE, TA, TB, KS>;
+    const ClockStamp clk = stamp_begin(p);
     if constexpr (PIPE == 1)
         Kern::run_deep(p);
     else
         Kern::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg

@@ -677,7 +677,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN 
                                               DmaOcc<BM, BN, WGM * WGN>::value))) void
 gemm_dma_kernel(GemmParams p)
 {
+    const ClockStamp clk = stamp_begin(p);
     DmaGemm<DT, TA, TB, BM, BN, WGM, WGN, NS, GROUP_M, BK>::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg

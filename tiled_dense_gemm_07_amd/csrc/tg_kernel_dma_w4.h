@@ -635,7 +635,9 @@ template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1, int
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * KS * 64, WGM * WGN * KS * 64))) void
 dma_w4_kernel(GemmParams p)
 {
+    const ClockStamp clk = stamp_begin(p);
     DmaW4<BM, BN, WGM, WGN, NS, GROUP_M, KS, SB>::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg

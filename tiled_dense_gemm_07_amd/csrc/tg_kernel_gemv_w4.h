@@ -154,7 +154,9 @@ struct GemvW4 {
 template <bool DWORD_SCALES>
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024))) void gemv_w4_kernel(GemmParams p)
 {
+    const ClockStamp clk = stamp_begin(p);
     GemvW4<DWORD_SCALES>::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg

@@ -556,7 +556,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN 
                                               MxOcc<AFMT, BM, BN>::value))) void
 gemm_mx_kernel(GemmParams p)
 {
+    const ClockStamp clk = stamp_begin(p);
     DmaMx<AFMT, BM, BN, WGM, WGN, NS, GROUP_M, CS>::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg

@@ -393,7 +393,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN 
                           amdgpu_waves_per_eu(1, 1))) void
 gemm_sp24_kernel(GemmParams p)
 {
+    const ClockStamp clk = stamp_begin(p);
     DmaSp24<DT, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    stamp_end(p, clk);
 }
 
 }  // namespace tg
