@@ -467,33 +467,62 @@ struct DmaGemm {
     static constexpr int NM_ = FM * FN;
     static constexpr int STEPS = NM_ > NREAD ? NM_ : NREAD;  // slots per slab
     static constexpr int SLOTS = SL * STEPS;                 // slots per strip
-    static constexpr int CSLOTS = NS == 2 ? (SL / 2) * STEPS : SLOTS;  // slots the copies use
+    // NS >= 3: the copies of a strip use every slot of the strip.  NS == 2:
+    // the copies of strip t + 2 are spread over CSPREAD slabs that start
+    // with the last slab of strip t (after the barrier that frees strip t's
+    // stage) and go on into the first CSPREAD - 1 slabs of strip t + 1.
+#ifndef TG_CSPREAD
+#define TG_CSPREAD 2
+#endif
+    static constexpr int CSPREAD = TG_CSPREAD < SL ? TG_CSPREAD : SL;
+    static constexpr int CSLOTS = NS == 2 ? CSPREAD * STEPS : SLOTS;
+    // position of copy d of wave W in the copy window (slot index)
+    static constexpr int cpos(int d, int W) { return ((d * NW + W) * CSLOTS) / (NCOPY * NW); }
 
     // Slot SLOT of a strip (stage ST) of wave W, then the following slots: the
     // recursion unrolls the strip at compile time whatever its length.
     template <int ST, int W, int SLOT>
     static __device__ __forceinline__ void slots(f32x16 (&acc)[FM][FN], Frag (&F)[2],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
-                                                 int m0, int n0, int t, u32 smem0, StripRes& r)
+                                                 int m0, int n0, int t, u32 smem0, StripRes& r,
+                                                 const StripRes& r1)
     {
         constexpr int NXT = (ST + 1) % NS;
-        constexpr int CPY = (ST + NS - 1) % NS;
         slab_step<ST, NXT, SLOT / STEPS, SLOT % STEPS>(acc, F, L, sm);
-        if constexpr (NS >= 3 && SLOT == 0) {
-            wait_copies_barrier<VM_AHEAD>();
-            __builtin_amdgcn_sched_barrier(0);
-            r = strip_res(p, m0, n0, t + NS - 1);
-        }
-        // copy d of wave W goes to slot ((d * NW + W) * CSLOTS) / (NCOPY * NW)
-#pragma unroll
-        for (int d = 0; d < NCOPY; ++d) {
-            if (((d * NW + W) * CSLOTS) / (NCOPY * NW) == SLOT) {
-                issue_copy<CPY>(L, r, d, W, smem0);
+        if constexpr (NS >= 3) {
+            if constexpr (SLOT == 0) {
+                wait_copies_barrier<VM_AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
+                r = strip_res(p, m0, n0, t + NS - 1);
+            }
+            // strip t + NS - 1 into the stage strip t - 1 used: copy d of wave
+            // W at slot cpos(d, W)
+            constexpr int CPY = (ST + NS - 1) % NS;
+#pragma unroll
+            for (int d = 0; d < NCOPY; ++d) {
+                if (cpos(d, W) == SLOT) {
+                    issue_copy<CPY>(L, r, d, W, smem0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            // window positions q < STEPS: strip t + 2 into this strip's own
+            // stage, in the last slab (after the barrier); q >= STEPS: the
+            // rest of strip t + 1 into the other stage, in the first slabs
+#pragma unroll
+            for (int d = 0; d < NCOPY; ++d) {
+                constexpr int LAST = (SL - 1) * STEPS;
+                if (cpos(d, W) < STEPS && LAST + cpos(d, W) == SLOT) {
+                    issue_copy<ST>(L, r, d, W, smem0);
+                    __builtin_amdgcn_sched_barrier(0);
+                } else if (cpos(d, W) >= STEPS && cpos(d, W) - STEPS == SLOT) {
+                    issue_copy<NXT>(L, r1, d, W, smem0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         if constexpr (SLOT + 1 < SLOTS)
-            slots<ST, W, SLOT + 1>(acc, F, L, sm, p, m0, n0, t, smem0, r);
+            slots<ST, W, SLOT + 1>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
     }
 
     // One strip: SL slabs of FM x FN MFMAs; slab s uses fragment set F[s & 1]
@@ -509,18 +538,21 @@ struct DmaGemm {
     //     reads of strip t + 1: each wave first waits for all its copies (those
     //     of strip t + 1) and LDS reads (those of strip t, whose last slab is
     //     in registers by then), so after the barrier strip t + 1 is visible
-    //     and no wave reads strip t's stage again.  The copies of strip t + 1
-    //     are spread over the first half of strip t so they land before the
-    //     last slab.
+    //     and no wave reads strip t's stage again.  The copies of strip t + 2
+    //     go into that stage right away, spread over the last slab: they have
+    //     a whole strip to land before the barrier of strip t + 1 waits for
+    //     them.
     template <int ST, int W>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[2],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
                                                  int m0, int n0, int t, u32 smem0)
     {
-        StripRes r;
-        if constexpr (NS == 2)
-            r = strip_res(p, m0, n0, t + 1);
-        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r);
+        StripRes r, r1;
+        if constexpr (NS == 2) {
+            r = strip_res(p, m0, n0, t + 2);
+            r1 = strip_res(p, m0, n0, t + 1);
+        }
+        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
     }
 
     // The strip loop of wave W (the copy slots differ per wave).  The strip
@@ -608,16 +640,26 @@ struct DmaGemm {
                 for (int r = 0; r < 16; ++r)
                     acc[fm][fn][r] = 0.0f;
 
-        // prologue: strips 0 .. NS-2 into stages 0 .. NS-2
+        // prologue: strips 0 .. NS-2 into stages 0 .. NS-2 (NS == 2: strip 0
+        // and the part of strip 1 that the main loop issues in the last slab
+        // of strip -1; strip 0 issues the rest)
         issue_copies<0>(L, p, m0, n0, 0, w, smem0);
+        if constexpr (NS == 2) {
+            const StripRes r1 = strip_res(p, m0, n0, 1);
+#pragma unroll
+            for (int d = 0; d < NCOPY; ++d)
+                if (((d * NW + w) * CSLOTS) / (NCOPY * NW) < STEPS)
+                    issue_copy<1>(L, r1, d, w, smem0);
+        }
         if constexpr (NS > 2)
             issue_copies<1>(L, p, m0, n0, 1, w, smem0);
         if constexpr (NS > 3)
             issue_copies<2 % NS>(L, p, m0, n0, 2, w, smem0);
         if constexpr (NS > 4)
             issue_copies<3 % NS>(L, p, m0, n0, 3, w, smem0);
-        // strip 0 must be complete and visible before its first fragments are read
-        wait_copies_barrier<(NS - 2) * NCOPY>();
+        // strip 0 must be complete and visible before its first fragments are
+        // read (NS == 2: wait for all)
+        wait_copies_barrier<(NS == 2 ? 0 : NS - 2) * NCOPY>();
         Frag F[2];
 #pragma unroll
         for (int i = 0; i < NREAD; ++i)
