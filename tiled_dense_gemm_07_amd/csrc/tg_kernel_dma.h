@@ -211,80 +211,6 @@ struct DmaOperand {
     }
 };
 
-// Write-back of a staged result tile from LDS (rows of 2 CH 16-byte chunks,
-// chunk c of row r at c ^ (r % CH)) to C, RPI rows per store instruction.
-// The stores use the system-coherent write-through policy (SC0 SC1): the
-// results stream to memory as they are stored instead of sitting dirty in
-// L2 for the end-of-kernel write-back, which all tiles reach at once.
-// Measured on the 4096^3 bf16 kernel: 108.3 -> 104.2 us.  Each group of RPI
-// rows gets its own buffer base (uniform), so offsets stay below RPI rows.
-constexpr int kStoreThrough = 17;  // SC0 | SC1
-
-template <int WTM, int RPI, int CH>
-__device__ __forceinline__ void store_rows_through(const lds_char* st, const GemmParams& p,
-                                                   int mw0, int nw0, int lane)
-{
-    constexpr int ROWB = CH * 16;
-    const int c = lane % CH;
-    const int rl = lane / CH;  // row within a store instruction
-    const int n = nw0 + 8 * c;
-    const u32 off = (u32)(rl * p.N + 8 * c) * 2u;
-    uint16_t* C = (uint16_t*)p.C;
-#pragma unroll 4
-    for (int r0 = 0; r0 < WTM; r0 += RPI) {
-        const int r = r0 + rl;
-        const u32x4 v = *(const lds_u32x4*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4));
-        const auto rs = make_rsrc(C + ((int64_t)(mw0 + r0) * p.N + nw0), 0x7FFFFFFFu);
-        if (mw0 + r < p.M && n < p.N)
-            __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, kStoreThrough);
-    }
-}
-
-// Coalesced store of one wave's WTM x WTN result tile (FM x FN blocks of
-// 32 x 32 fp32, the MFMA layout where lane l holds row l % 32 and, for
-// element 4 q + e, column 8 q + 4 (l / 32) + e of its block).  The tile is
-// rounded (after ReLU) into the wave's own LDS region `st` as rows of 2 WTN
-// bytes with 16-byte chunk c of row r at position c ^ (r % CH) (CH chunks per
-// row; writes then spread over the banks), and written back to C as 16-byte
-// pieces, CH lanes per row: whole 2 WTN-byte runs of a row instead of 16-byte
-// pieces of 32 rows.  Needs N % 8 == 0 and a 16-byte aligned C (else the
-// caller stores directly); the caller has synchronised so that no wave still
-// reads or copies into LDS.
-template <int DT, int WTM, int WTN, int FM, int FN>
-__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
-                                                  const GemmParams& p, int mw0, int nw0,
-                                                  int lane, lds_char* st)
-{
-    constexpr int ROWB = WTN * 2;
-    constexpr int CH = ROWB / 16;
-    static_assert(CH >= 4 && CH <= 64 && (CH & (CH - 1)) == 0, "rows of 64 to 1024 bytes");
-    const int lr = lane & 31;
-    const int g = lane >> 5;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int r = fm * 32 + lr;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = acc[fm][fn][4 * q + e];
-                    v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
-                }
-                const int c = 4 * fn + q;
-                typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-                *(lds_u32x2*)(st + r * ROWB + ((c ^ (r & (CH - 1))) << 4) + 8 * g) =
-                    u32x2{pack2(v[0], v[1], DT), pack2(v[2], v[3], DT)};
-            }
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
-    constexpr int RPI = 64 / CH;  // rows per store instruction
-    store_rows_through<WTM, RPI, CH>(st, p, mw0, nw0, lane);
-}
-
 // As store_tile_staged, for result blocks in the other MFMA orientation: lane
 // l holds column l % 32 and, for element r, row 8 (r / 4) + 4 (l / 32) + r % 4
 // of its block (the first MFMA operand supplied the rows).
@@ -315,7 +241,7 @@ __device__ __forceinline__ void store_tile_staged_t(const f32x16 (&acc)[FM][FN],
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own region: no barrier needed
     constexpr int RPI = 64 / CH;
-    store_rows_through<WTM, RPI, CH>(st, p, mw0, nw0, lane);
+    store_rows_through<WTM, RPI, CH, 2>(st, p, mw0, nw0, lane);
 }
 
 // TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].  BK: k per
