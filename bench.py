@@ -167,7 +167,10 @@ def time_mean(fn, stream, launches: int) -> float:
 
 def time_each(fns, stream, launches: int) -> dict:
     """Per-launch durations (ms) from one event pair around each launch
-    (launch i runs fns[i % len(fns)]): median, p10, p90, mean."""
+    (launch i runs fns[i % len(fns)]): median, p10, p90, mean.  Each event
+    pair adds a few microseconds, so for short kernels these read high: the
+    spread, not the level, is what they show (levels come from back-to-back
+    timing and from the kernel trace)."""
     import numpy as np
     import torch
 
@@ -218,22 +221,33 @@ def measure_clock(fn, stream, once_ms: float) -> dict:
 
 
 def time_cold(w, tensors, stream, launches: int = 40) -> dict:
-    """Kernel durations with each launch on a different copy of the inputs
-    (together COLD_BYTES or more), so nothing is cache-resident."""
+    """Average kernel duration with each launch on a different copy of the
+    inputs (together COLD_BYTES or more), so nothing is cache-resident: one
+    event pair around back-to-back launches that cycle through the copies
+    (an event pair per launch adds several microseconds to each launch)."""
+    import torch
+
     per = sum(x.numel() * x.element_size() for x in tensors)
     copies = max(4, -(-COLD_BYTES // per))
     sets = [tuple(x.clone() for x in tensors) for _ in range(copies)]
     fns = [launcher(w, s_, stream) for s_ in sets]
-    for f in fns[:4]:
-        f()
+    n = max(launches, 2 * copies)
+    for i in range(n):  # warm-up pass (clocks), itself cold
+        fns[i % copies]()
     stream.synchronize()
-    r = time_each(fns, stream, max(launches, 2 * copies))
-    gbs = w.algorithmic_bytes() / (r["median_ms"] * 1e-3) / 1e9
-    tf = w.flops / (r["median_ms"] * 1e-3) / 1e12
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fns[i % copies]()
+    b.record(stream)
+    stream.synchronize()
+    ms = a.elapsed_time(b) / n
+    gbs = w.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    tf = w.flops / (ms * 1e-3) / 1e12
     del sets, fns
-    r.update({"copies": copies, "tflops": round(tf, 2), "gbs_algorithmic": round(gbs, 1),
-              "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
-    return r
+    return {"kernel_ms": round(ms, 5), "launches": n, "copies": copies, "tflops": round(tf, 2),
+            "gbs_algorithmic": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def dtype_name(w):
@@ -324,7 +338,7 @@ def bench_workload(name, dev, stream, cpu_budget_s):
         if tr.get("cold"):
             # counters taken on the cold rotation: every fabric byte came from HBM
             rec["hbm_gbs_counters_cold"] = round(
-                tr["fabric_bytes_per_launch"] / (rec["cold"]["median_ms"] * 1e-3) / 1e9, 1)
+                tr["fabric_bytes_per_launch"] / (rec["cold"]["kernel_ms"] * 1e-3) / 1e9, 1)
     del t
     torch.cuda.empty_cache()
     if cpu_budget_s > 0:

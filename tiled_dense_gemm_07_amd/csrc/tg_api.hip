@@ -147,10 +147,10 @@ const Pref kPrefs[] = {
             "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr}},
     {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g8_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
             nullptr}},
-    {3, 2, {"sp24_bf16_256x128x64_w2x2_s3_g4_dma", "sp24_bf16_128x128x64_w2x2_s3_g8_dma", nullptr,
-            nullptr}},
-    {3, 1, {"sp24_f16_256x128x64_w2x2_s3_g4_dma", "sp24_f16_128x128x64_w2x2_s3_g8_dma", nullptr,
-            nullptr}},
+    {3, 2, {"sp24_bf16_256x256x64_w2x4_s3_g4_dma", "sp24_bf16_128x256x64_w2x2_s3_g4_dma",
+            "sp24_bf16_128x128x64_w2x2_s3_g8_dma", nullptr}},
+    {3, 1, {"sp24_f16_256x256x64_w2x4_s3_g4_dma", "sp24_f16_128x256x64_w2x2_s3_g4_dma",
+            "sp24_f16_128x128x64_w2x2_s3_g8_dma", nullptr}},
 };
 
 const Config* find_by_name(int op, int dtype, const char* name);

@@ -11,14 +11,23 @@ namespace tg {
         3, DT, BM, BN, 64, 2, 2, 3, GM, true, false, false, 2,                          \
             (const void*)&tg::gemm_sp24_kernel<DT, BM, BN, 2, 2, 3, GM>                 \
     }
+// eight waves, two per SIMD (WGM x WGN = 2 x 4 or 4 x 2)
+#define TG_CONFIG_SP24_W(DT, BM, BN, WGM, WGN, GM)                                      \
+    tg::Config                                                                          \
+    {                                                                                   \
+        3, DT, BM, BN, 64, WGM, WGN, 3, GM, true, false, false, 2,                      \
+            (const void*)&tg::gemm_sp24_kernel<DT, BM, BN, WGM, WGN, 3, GM>             \
+    }
 
 static const Config kCfgBf16[] = {
+    TG_CONFIG_SP24_W(DT_BF16, 256, 256, 2, 4, 4),
     TG_CONFIG_SP24(DT_BF16, 256, 128, 4),
     TG_CONFIG_SP24(DT_BF16, 256, 128, 8),
     TG_CONFIG_SP24(DT_BF16, 128, 256, 4),
     TG_CONFIG_SP24(DT_BF16, 128, 128, 8),
 };
 static const Config kCfgF16[] = {
+    TG_CONFIG_SP24_W(DT_F16, 256, 256, 2, 4, 4),
     TG_CONFIG_SP24(DT_F16, 256, 128, 4),
     TG_CONFIG_SP24(DT_F16, 256, 128, 8),
     TG_CONFIG_SP24(DT_F16, 128, 256, 4),

@@ -19,7 +19,8 @@
 //     8..15 = k 16 + 8 (l / 32) + 0..7 - the dense kernel's fragments of two
 //     consecutive 16-k slabs.
 // MI355X mapping (the LDS-DMA GEMM's, adapted):
-//  * BM x BN x 64 strips (two 32-k steps), four waves in 2 x 2, a 3-stage
+//  * BM x BN x 64 strips (two 32-k steps), four waves in 2 x 2 or eight in
+//    2 x 4 (two per SIMD: 256 x 256 tiles, 128 x 64 wave tiles), a 3-stage
 //    LDS ring filled by LDS-DMA: Ac rows of 64 bytes (swizzle swz_a), the two
 //    metadata dwords of each row as two [BM][4] blocks (dword copies), B as
 //    [64 k][BN] (the dense kernel's x-contiguous operand, transposing reads);
@@ -67,7 +68,7 @@ struct DmaSp24 {
     static constexpr int NM = FM * FN;               // MFMAs per 32-k step
     static constexpr int NRD = 2 * FM + 4 * FN;      // LDS reads per 32-k step
 
-    static_assert(NW == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && A_STAGE % (1024 * NW) == 0, "value copies split evenly");
     static_assert(JI >= 1 && NIC % NW == 0, "metadata copies split evenly");
@@ -351,8 +352,20 @@ struct DmaSp24 {
         case 2:
             main_loop<2>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
-        default:
+        case 3:
             main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 4:
+            main_loop<4 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 5:
+            main_loop<5 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 6:
+            main_loop<6 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        default:
+            main_loop<7 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
         }
         if (((uintptr_t)p.C & 15) == 0 && NW * WTM * WTN * 2 <= LDS_BYTES) {  // N % 8 == 0 always
@@ -388,9 +401,16 @@ struct DmaSp24 {
     }
 };
 
+// Waves per SIMD: one with four waves (all registers of a lane), two with eight.
+template <int WGM, int WGN>
+struct Sp24Occ {
+    static constexpr int value = WGM * WGN > 4 ? 2 : 1;
+};
+
 template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
-                          amdgpu_waves_per_eu(1, 1))) void
+                          amdgpu_waves_per_eu(Sp24Occ<WGM, WGN>::value,
+                                              Sp24Occ<WGM, WGN>::value))) void
 gemm_sp24_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
