@@ -347,6 +347,23 @@ tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* ou
  */
 void tg_set_clock_stamps(uint64_t* stamps);
 
+/*
+ * Tuning aids for the offline sweep (tiled_dense_gemm_07_amd/sweep.py), which
+ * follows the mhpq.cn page's tuning advice (sections 4.2 and 4.3: measure
+ * candidate tilings on the target GPU, check occupancy, keep the best).
+ *   tg_set_swizzle_override: every launch afterwards, by any entry point, uses
+ *     swizzle group `group_m` (tile rows per group of the block-swizzled tile
+ *     order, a pure reordering: results are unchanged); 0 restores the
+ *     selection's own group.  Process-wide, for timing runs.
+ *   tg_config_occupancy: workgroups of compiled configuration `index` of
+ *     (op, dtype) that one compute unit holds at once (registers, LDS and
+ *     waves), from the HIP occupancy query on the current device.
+ *     Errors: TG_ERR_NULL_POINTER, TG_ERR_NO_CONFIG (index out of range),
+ *     TG_ERR_HIP (no device or the query failed).
+ */
+void tg_set_swizzle_override(int group_m);
+tg_status tg_config_occupancy(int op, tg_dtype dtype, int index, int* workgroups_per_cu);
+
 #ifdef __cplusplus
 }
 #endif

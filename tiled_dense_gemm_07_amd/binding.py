@@ -30,7 +30,7 @@ EXPORTS = ("tg_gemm", "tg_gemm_ex", "tg_dequant_gemm_w4", "tg_status_str", "tg_q
            "tg_gemm_ex_config", "tg_dequant_gemm_w4_config", "tg_tile_map", "tg_gemm_mx",
            "tg_gemm_mx_config", "tg_gemm_sp24", "tg_gemm_sp24_config", "tg_gemm_splitk",
            "tg_gemm_splitk_workspace_size", "tg_gemm_splitk_config", "tg_gemm_splitk_noalloc",
-           "tg_set_clock_stamps")
+           "tg_set_clock_stamps", "tg_set_swizzle_override", "tg_config_occupancy")
 TG_SPLITK_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _lib = None
@@ -104,6 +104,10 @@ def load_library():
     lib.tg_gemm_splitk_noalloc.restype = c_int
     lib.tg_set_clock_stamps.argtypes = [p]
     lib.tg_set_clock_stamps.restype = None
+    lib.tg_set_swizzle_override.argtypes = [c_int]
+    lib.tg_set_swizzle_override.restype = None
+    lib.tg_config_occupancy.argtypes = [c_int, c_int, c_int, ctypes.POINTER(c_int)]
+    lib.tg_config_occupancy.restype = c_int
     _lib = lib
     return lib
 
@@ -259,6 +263,18 @@ def set_clock_stamps(stamps):
         if stamps.numel() * stamps.element_size() < 32 * 8:
             raise ValueError("stamps must hold 32 64-bit values")
     load_library().tg_set_clock_stamps(stamps.data_ptr() if stamps is not None else None)
+
+
+def set_swizzle_override(group_m: int):
+    """Force swizzle group `group_m` on every following launch (0: none)."""
+    load_library().tg_set_swizzle_override(int(group_m))
+
+
+def config_occupancy(op: int, dtype: int, index: int) -> int:
+    """Workgroups of configuration `index` one compute unit holds at once."""
+    n = ctypes.c_int(0)
+    _check(load_library().tg_config_occupancy(op, dtype, index, ctypes.byref(n)))
+    return n.value
 
 
 def stamp_clock_ghz(stamps) -> list:

@@ -24,23 +24,34 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 
 def build(verbose: bool = False) -> str:
-    return _build_lib(SOURCES, LIB, verbose)
+    from . import configgen
+
+    configgen.write_all()  # generated configurations (no-op when unchanged)
+    return _build_lib(SOURCES + configgen.generated_sources(), LIB, verbose)
 
 
 def _build_lib(sources, lib_path: str, verbose: bool) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    procs = []
-    objs = []
-    for src in sources:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-c",
-                                 os.path.join(CSRC, src), "-o", obj]
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                            stderr=subprocess.STDOUT)))
-    failed = []
-    for src, p in procs:
+    jobs = max(1, min(len(sources), len(os.sched_getaffinity(0))))
+    pending = list(sources)
+    running = []
+    done = []
+    objs = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in sources]
+    # largest translation units first, at most `jobs` compiles at a time
+    pending.sort(key=lambda s: -os.path.getsize(os.path.join(CSRC, s)))
+    while pending or running:
+        while pending and len(running) < jobs:
+            src = pending.pop(0)
+            cmd = [HIPCC] + FLAGS + ["-I", os.path.join(HERE, "..", "include"), "-c",
+                                     os.path.join(CSRC, src), "-o",
+                                     os.path.join(BUILD, src.replace(".hip", ".o"))]
+            running.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                  stderr=subprocess.STDOUT)))
+        src, p = running.pop(0)
         out, _ = p.communicate()
+        done.append((src, p, out))
+    failed = []
+    for src, p, out in done:
         text = "\n".join(l for l in out.decode(errors="replace").splitlines()
                          if "not a recognized feature" not in l)
         if verbose and text.strip():

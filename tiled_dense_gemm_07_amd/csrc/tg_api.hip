@@ -9,6 +9,7 @@
 // the offline sweep (tiled_dense_gemm_07_amd/sweep.py) writes.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -68,11 +69,20 @@ tg_status scratch_of_device(void** out)
 using tg::Config;
 using tg::ConfigList;
 
+// One row of the selection table the offline sweep writes (tg_tuned.inc).
+// exact != 0: the best configuration measured for exactly this shape.
+// exact == 0: one of the best configurations measured at the representative
+// shape (M, N, K) of a shape bucket, with its measured time; a call whose
+// nearest representative this is picks among them by the cost model below.
 struct TunedEntry {
     int op;
     int dtype;
     int64_t M, N, K;
     const char* config;  // configuration name, as config_name() prints it
+    int group_m;         // swizzle group to launch with (0: the configuration's default)
+    double ms;           // measured time at (M, N, K)
+    int per_cu;          // workgroups of this configuration one compute unit holds
+    int exact;
 };
 
 #include "tg_tuned.inc"
@@ -123,35 +133,6 @@ int vec_of(int dtype) { return dtype == TG_F32 ? 4 : 8; }
 int esize_of(int dtype) { return dtype == TG_F32 ? 4 : 2; }
 
 int64_t tiles(int64_t x, int t) { return (x + t - 1) / t; }
-
-// Built-in choice when no tuned entry matches.  Each (op, dtype) has a list
-// of compiled configurations from the largest tile down; the first whose
-// grid reaches about one workgroup per compute unit (256 CUs on MI355X) wins,
-// else the last.  The lists follow the sweep's measurements on MI355X.
-struct Pref {
-    int op, dtype;
-    const char* names[4];
-};
-const Pref kPrefs[] = {
-    // grids below about one tile per compute unit fall through to the last
-    // entry: 32 x 32 tiles with four k-slice wave groups
-    {0, 2, {"gemm_bf16_256x256x64_w2x4_s2_g4_dma", "gemm_bf16_128x128x32_w2x2_s4_g8_dma",
-            "gemm_bf16_64x64x128_w2x2x2_s2_g8_deep", "gemm_bf16_32x32x256_w1x1x4_s2_g8_deep"}},
-    {0, 1, {"gemm_f16_256x256x64_w2x4_s2_g4_dma", "gemm_f16_128x128x32_w2x2_s4_g8_dma",
-            "gemm_f16_64x64x128_w2x2x2_s2_g8_deep", "gemm_f16_32x32x256_w1x1x4_s2_g8_deep"}},
-    {0, 0, {"gemm_f32_128x128x32_w2x2_s2_g8_deep", "gemm_f32_64x64x64_w2x2x2_s2_g8_deep",
-            "gemm_f32_32x32x128_w1x1x4_s2_g8_deep", nullptr}},
-    {1, 2, {"w4_bf16_64x128x128_w1x2x2_s4_g4_dma", "w4_bf16_128x64x128_w2x2_s2_g4_deep",
-            "w4_bf16_64x64x128_w2x2_s2_g8_deep", "w4_bf16_32x64x128_w1x2_s2_g8_deep"}},
-    {2, 0, {"mx_e2m1_256x256x128_w2x2_s4_g8_dma", "mx_e2m1_128x128x128_w2x2_s4_g8_dma_sc8",
-            "mx_e2m1_128x128x128_w2x2_s4_g8_dma", nullptr}},
-    {2, 1, {"mx_e4m3_128x256x128_w2x2_s4_g8_dma", "mx_e4m3_128x128x128_w2x2_s4_g8_dma", nullptr,
-            nullptr}},
-    {3, 2, {"sp24_bf16_256x256x64_w2x4_s3_g4_dma", "sp24_bf16_128x256x64_w2x2_s3_g4_dma",
-            "sp24_bf16_128x128x64_w2x2_s3_g8_dma", nullptr}},
-    {3, 1, {"sp24_f16_256x256x64_w2x4_s3_g4_dma", "sp24_f16_128x256x64_w2x2_s3_g4_dma",
-            "sp24_f16_128x128x64_w2x2_s3_g8_dma", nullptr}},
-};
 
 const Config* find_by_name(int op, int dtype, const char* name);
 
@@ -206,109 +187,6 @@ bool usable(const Config& c, const Call& q)
     return true;
 }
 
-// Large 16-bit GEMMs: the LDS-DMA tile shapes, with the workgroups each
-// compute unit holds and the throughput per unit of tile area relative to
-// 256 x 256 when every compute unit is busy (measured: 4096^3, 6144 x 4096 x
-// 4096 and 8192^3 on MI355X).  The run time of a grid is about
-// ceil(tiles / slots) rounds of one tile each, so a smaller tile wins when it
-// fills the last round better: 3072^3 takes 144 tiles of 256 x 256 (one round
-// of 65536-element tiles) but 192 of 192 x 256 (one round, 25% less work per
-// tile).
-struct CostPref {
-    int dtype;
-    const char* name;
-    int per_cu;  // workgroups resident per compute unit (LDS)
-    float eff;   // throughput per tile area relative to 256 x 256
-};
-const CostPref kCostPrefs[] = {
-    {TG_BF16, "gemm_bf16_256x256x64_w2x4_s2_g4_dma", 1, 1.0f},
-    {TG_BF16, "gemm_bf16_192x256x64_w2x4_s2_g4_dma", 1, 0.94f},
-    {TG_BF16, "gemm_bf16_128x128x32_w2x2_s4_g8_dma", 2, 0.38f},
-    {TG_F16, "gemm_f16_256x256x64_w2x4_s2_g4_dma", 1, 1.0f},
-    {TG_F16, "gemm_f16_192x256x64_w2x4_s2_g4_dma", 1, 0.94f},
-    {TG_F16, "gemm_f16_128x128x32_w2x2_s4_g8_dma", 2, 0.38f},
-};
-constexpr int64_t kComputeUnits = 256;  // MI355X
-
-// The cheapest of kCostPrefs for the call, or nullptr when even that leaves
-// more than half the compute units idle (the small-grid configurations of
-// the preference lists serve those).
-const Config* cost_choice(const Call& q)
-{
-    const Config* best = nullptr;
-    double best_cost = 0.0;
-    int64_t best_tiles = 0;
-    for (const CostPref& cp : kCostPrefs) {
-        if (cp.dtype != q.dtype)
-            continue;
-        const Config* c = find_by_name(q.op, q.dtype, cp.name);
-        if (!c || !usable(*c, q))
-            continue;
-        const int64_t t = tiles(q.M, c->bm) * tiles(q.N, c->bn);
-        const int64_t slots = kComputeUnits * cp.per_cu;
-        const double cost = (double)((t + slots - 1) / slots) * c->bm * c->bn / cp.eff;
-        if (!best || cost < best_cost) {
-            best = c;
-            best_cost = cost;
-            best_tiles = t;
-        }
-    }
-    return best && best_tiles >= kComputeUnits / 2 ? best : nullptr;
-}
-
-const Config* heuristic(const Call& q)
-{
-    ConfigList L = list_for(q.op, q.dtype);
-    if (!q.wide) {
-        for (int i = 0; i < L.count; ++i)
-            if (usable(L.items[i], q))
-                return &L.items[i];
-        return nullptr;
-    }
-    // few activation rows: the run time is the weight stream from HBM
-    if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16) {
-        if (const Config* c = gemv_for(q.K, q.ws4))
-            return c;
-    }
-    if (q.op == TG_OP_GEMM && q.dtype != TG_F32 && !q.ta && !q.tb) {
-        if (const Config* c = cost_choice(q))
-            return c;
-    }
-    for (const Pref& pr : kPrefs) {
-        if (pr.op != q.op || pr.dtype != q.dtype || q.ta || q.tb)
-            continue;
-        const Config* last = nullptr;
-        for (const char* name : pr.names) {
-            if (!name)
-                break;
-            const Config* c = find_by_name(q.op, q.dtype, name);
-            if (!c || !usable(*c, q))
-                continue;
-            last = c;
-            // small M: a tile taller than M wastes matrix-core work
-            if (q.op == 1 && q.M <= c->bm / 2)
-                continue;
-            if (tiles(q.M, c->bm) * tiles(q.N, c->bn) >= 200)
-                return c;
-        }
-        if (last)
-            return last;
-    }
-    // transposed layouts (and anything the preference lists miss): the first
-    // usable configuration, largest tile first, whose grid reaches about one
-    // workgroup per compute unit, else the last usable one
-    const Config* last = nullptr;
-    for (int i = 0; i < L.count; ++i) {
-        const Config& c = L.items[i];
-        if (!c.wide || !usable(c, q))
-            continue;
-        last = &c;
-        if (tiles(q.M, c.bm) * tiles(q.N, c.bn) >= 200)
-            return &c;
-    }
-    return last;
-}
-
 // The names of every compiled configuration, per (op, dtype) list, formatted
 // once: a call's selection looks names up in the tables above, and formatting
 // every candidate's name per call took 5-20 us of host time.  (A function-local
@@ -344,19 +222,190 @@ const Config* find_by_name(int op, int dtype, const char* name)
     return nullptr;
 }
 
-const Config* select_config(const Call& q)
+// Compute units of the calling thread's current device, queried once per
+// device (256 on MI355X; that value is also used when no device is visible,
+// as for host-side configuration queries).
+int64_t cu_count()
 {
-    for (size_t i = 0; i < sizeof(kTuned) / sizeof(kTuned[0]); ++i) {
-        const TunedEntry& e = kTuned[i];
-        if (e.config == nullptr)
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Rounds of tiles configuration c needs for an M x N output: one round is
+// every compute unit running per_cu workgroups of it at once.
+int64_t rounds(const Config& c, int64_t M, int64_t N, int per_cu)
+{
+    const int64_t slots = cu_count() * (per_cu > 0 ? per_cu : 1);
+    return (tiles(M, c.bm) * tiles(N, c.bn) + slots - 1) / slots;
+}
+
+struct Choice {
+    const Config* c;
+    int group_m;  // 0: the configuration's default
+};
+
+// Fallback when the table holds nothing usable for a call (operand layouts
+// and alignments the sweep does not time): the usable configuration whose
+// last round of tiles leaves the least work per compute unit (rounds x tile
+// area, one workgroup per unit), the larger tile on ties.
+const Config* fallback(const Call& q)
+{
+    ConfigList L = list_for(q.op, q.dtype);
+    const Config* best = nullptr;
+    int64_t best_cost = 0;
+    for (int i = 0; i < L.count; ++i) {
+        const Config& c = L.items[i];
+        if (!usable(c, q))
             continue;
-        if (e.op == q.op && e.dtype == q.dtype && e.M == q.M && e.N == q.N && e.K == q.K) {
-            const Config* c = find_by_name(q.op, q.dtype, e.config);
-            if (c && c->wide == q.wide && usable(*c, q))
-                return c;
+        const int64_t cost = rounds(c, q.M, q.N, 1) * c.bm * c.bn;
+        if (!best || cost < best_cost ||
+            (cost == best_cost && c.bm * c.bn > best->bm * best->bn)) {
+            best = &c;
+            best_cost = cost;
         }
     }
-    return heuristic(q);
+    return best;
+}
+
+double lg2(int64_t x) { return log2((double)(x > 1 ? x : 1)); }
+
+// The table, indexed once per process: exact entries and bucket
+// representatives with their configurations resolved to list entries.
+struct RepConfig {
+    const Config* c;
+    int group_m;
+    double ms;
+    int per_cu;
+};
+struct Rep {
+    int op, dtype;
+    int64_t M, N, K;
+    double lm, ln, lk;  // log2 of M, N, K
+    std::vector<RepConfig> configs;
+};
+struct ExactEntry {
+    int op, dtype;
+    int64_t M, N, K;
+    const Config* c;
+    int group_m;
+};
+struct TableIndex {
+    std::vector<ExactEntry> exact;
+    std::vector<Rep> reps;
+};
+
+const TableIndex& table_index()
+{
+    static const TableIndex idx = [] {
+        TableIndex t;
+        for (const TunedEntry& e : kTuned) {
+            if (!e.config)
+                continue;
+            const Config* c = find_by_name(e.op, e.dtype, e.config);
+            if (!c)
+                continue;  // not compiled into this build
+            if (e.exact) {
+                t.exact.push_back({e.op, e.dtype, e.M, e.N, e.K, c, e.group_m});
+                continue;
+            }
+            Rep* r = nullptr;
+            for (Rep& x : t.reps)
+                if (x.op == e.op && x.dtype == e.dtype && x.M == e.M && x.N == e.N && x.K == e.K)
+                    r = &x;
+            if (!r) {
+                t.reps.push_back({e.op, e.dtype, e.M, e.N, e.K, lg2(e.M), lg2(e.N), lg2(e.K), {}});
+                r = &t.reps.back();
+            }
+            r->configs.push_back({c, e.group_m, e.ms, e.per_cu});
+        }
+        return t;
+    }();
+    return idx;
+}
+
+// The selection: an exact table entry for the shape; else the bucket whose
+// representative shape is nearest in log2(M), log2(N), log2(K), where each of
+// its measured configurations is priced at the call's shape as
+//   measured time x rounds(call) / rounds(representative) x K / K_rep
+// (run time goes with the number of tile rounds and with K), and the cheapest
+// usable one wins; else the fallback.  Few activation rows of the dequant
+// GEMM take the weight-streaming kernel (its workgroups hold 16 rows).
+Choice select_uncached(const Call& q)
+{
+    if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16 && q.wide) {
+        if (const Config* c = gemv_for(q.K, q.ws4))
+            return {c, 0};
+    }
+    const TableIndex& t = table_index();
+    for (const ExactEntry& e : t.exact) {
+        if (e.op == q.op && e.dtype == q.dtype && e.M == q.M && e.N == q.N && e.K == q.K &&
+            e.c->wide == q.wide && usable(*e.c, q))
+            return {e.c, e.group_m};
+    }
+    const double lm = lg2(q.M), ln = lg2(q.N), lk = lg2(q.K);
+    const Rep* rep = nullptr;
+    double best_d = 0.0;
+    for (const Rep& r : t.reps) {
+        if (r.op != q.op || r.dtype != q.dtype)
+            continue;
+        const double d = fabs(lm - r.lm) + fabs(ln - r.ln) + fabs(lk - r.lk);
+        if (!rep || d < best_d) {
+            rep = &r;
+            best_d = d;
+        }
+    }
+    if (rep) {
+        const RepConfig* best = nullptr;
+        double best_est = 0.0;
+        for (const RepConfig& rc : rep->configs) {
+            if (!usable(*rc.c, q))
+                continue;
+            const double est = rc.ms * (double)rounds(*rc.c, q.M, q.N, rc.per_cu) /
+                               (double)rounds(*rc.c, rep->M, rep->N, rc.per_cu) * (double)q.K /
+                               (double)rep->K;
+            if (!best || est < best_est) {
+                best = &rc;
+                best_est = est;
+            }
+        }
+        if (best)
+            return {best->c, best->group_m};
+    }
+    return {fallback(q), 0};
+}
+
+// select_uncached with a one-entry cache per thread: a loop that repeats one
+// call pays the table search once.
+Choice select_config(const Call& q)
+{
+    thread_local Call last{-1, -1, 0, 0, 0, false, false, false, false};
+    thread_local Choice last_choice{nullptr, 0};
+    thread_local int last_device = -1;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        (void)hipGetLastError();
+    if (last.op == q.op && last.dtype == q.dtype && last.M == q.M && last.N == q.N &&
+        last.K == q.K && last.wide == q.wide && last.ws4 == q.ws4 && last.ta == q.ta &&
+        last.tb == q.tb && last.ws16 == q.ws16 && last_device == dev)
+        return last_choice;
+    last_choice = select_uncached(q);
+    last = q;
+    last_device = dev;
+    return last_choice;
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn)
@@ -381,11 +430,16 @@ tg_status check_shape(int64_t M, int64_t N, int64_t K, int esize)
 
 // Device buffer of the optional clock record (tg_set_clock_stamps), or NULL.
 std::atomic<unsigned long long*> g_stamps{nullptr};
+// Swizzle group forced on every launch by the tuning sweep (0: none).
+std::atomic<int> g_group_override{0};
 
-tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream)
+tg_status launch(const Config& c, const tg::GemmParams& base, hipStream_t stream,
+                 int group_m = 0)
 {
     tg::GemmParams p = base;
     p.stamps = g_stamps.load(std::memory_order_relaxed);
+    const int forced_group = g_group_override.load(std::memory_order_relaxed);
+    p.group_m = forced_group > 0 ? forced_group : group_m;
     p.tiles_m = (int)tiles(p.M, c.bm);
     p.tiles_n = (int)tiles(p.N, c.bn);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * (p.splits > 1 ? p.splits : 1);
@@ -529,6 +583,7 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     // NULL is aligned
     q.wide = aligned16(A) && aligned16(B) && (lda % v == 0) && (ldb % v == 0);
     const Config* c = forced;
+    int group_m = 0;
     SplitPlan plan{1, (int)K, 0};
     if (sk && (forced || q.wide)) {
         if (!c)
@@ -538,8 +593,11 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         if (plan.S == 1 && !forced)
             c = nullptr;  // nothing to split: the plain selection below
     }
-    if (!c)
-        c = select_config(q);
+    if (!c) {
+        const Choice ch = select_config(q);
+        c = ch.c;
+        group_m = ch.group_m;
+    }
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     void* ws = sk ? sk->workspace : nullptr;
@@ -579,7 +637,7 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     p.K = (int)K;
     p.relu = epi == TG_EPI_RELU;
     p.c_vec = (N % 4 == 0) && ((uintptr_t)C % (dtype == TG_F32 ? 16 : 8) == 0);
-    return launch(*c, p, (hipStream_t)stream);
+    return launch(*c, p, (hipStream_t)stream, group_m);
 }
 
 tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
@@ -606,7 +664,8 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     Call q{TG_OP_DEQUANT_W4, TG_BF16, M, N, K, aligned16(A) && aligned16(Wq),
            ((uintptr_t)Ws & 3u) == 0, false, false};
     q.ws16 = aligned16(Ws);
-    const Config* c = forced ? forced : select_config(q);
+    const Choice ch = forced ? Choice{forced, 0} : select_config(q);
+    const Config* c = ch.c;
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     tg::GemmParams p{};
@@ -619,7 +678,7 @@ tg_status w4_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     p.K = (int)K;
     p.relu = epi == TG_EPI_RELU;
     p.c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    return launch(*c, p, (hipStream_t)stream);
+    return launch(*c, p, (hipStream_t)stream, ch.group_m);
 }
 
 tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
@@ -649,7 +708,8 @@ tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     Call q{TG_OP_MX, a_fmt, M, N, K, aligned16(Aq) && aligned16(Wq),
            (((uintptr_t)As | (uintptr_t)Ws) & 3u) == 0, false, false};
     q.ws16 = aligned16(As) && aligned16(Ws);
-    const Config* c = forced ? forced : select_config(q);
+    const Choice ch = forced ? Choice{forced, 0} : select_config(q);
+    const Config* c = ch.c;
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     tg::GemmParams p{};
@@ -663,7 +723,7 @@ tg_status mx_impl(const Config* forced, int forced_index, int64_t M, int64_t N, 
     p.K = (int)K;
     p.relu = epi == TG_EPI_RELU;
     p.c_vec = (N % 4 == 0) && ((uintptr_t)C % 8 == 0);
-    return launch(*c, p, (hipStream_t)stream);
+    return launch(*c, p, (hipStream_t)stream, ch.group_m);
 }
 
 tg_status sp24_impl(const Config* forced, int forced_index, int64_t M, int64_t N, int64_t K,
@@ -691,7 +751,8 @@ tg_status sp24_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         return TG_ERR_ALIAS;
     Call q{TG_OP_SP24, dtype, M, N, K, aligned16(Ac) && aligned16(B) && N % 8 == 0,
            ((uintptr_t)Ai & 3u) == 0, false, false};
-    const Config* c = forced ? forced : select_config(q);
+    const Choice ch = forced ? Choice{forced, 0} : select_config(q);
+    const Config* c = ch.c;
     if (!c || !usable(*c, q))
         return TG_ERR_NO_CONFIG;  // no (or a forced, unusable) configuration for this call
     tg::GemmParams p{};
@@ -704,7 +765,7 @@ tg_status sp24_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     p.K = (int)K;
     p.relu = epi == TG_EPI_RELU;
     p.c_vec = 0;
-    return launch(*c, p, (hipStream_t)stream);
+    return launch(*c, p, (hipStream_t)stream, ch.group_m);
 }
 
 }  // namespace
@@ -861,13 +922,15 @@ tg_status tg_query_config_ex(int op, int64_t M, int64_t N, int64_t K, tg_dtype d
     q.ws16 = true;
     q.wide = op == TG_OP_SP24 ? N % 8 == 0
                               : (op != TG_OP_GEMM || (lda % vec_of(dt) == 0 && ldb % vec_of(dt) == 0));
-    const Config* c = select_config(q);
+    const Choice ch = select_config(q);
+    const Config* c = ch.c;
     if (!c)
         return TG_ERR_NO_CONFIG;
     char name[96];
     config_name(*c, name, sizeof name);
-    snprintf(buf, len, "%s grid=%lld threads=%d", name,
-             (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * c->ks * 64);
+    snprintf(buf, len, "%s grid=%lld threads=%d group=%d", name,
+             (long long)(tiles(M, c->bm) * tiles(N, c->bn)), c->wgm * c->wgn * c->ks * 64,
+             ch.group_m > 0 ? ch.group_m : c->group_m);
     return TG_OK;
 }
 
@@ -948,6 +1011,28 @@ tg_status tg_gemm_sp24_config(int index, int64_t M, int64_t N, int64_t K, tg_dty
 void tg_set_clock_stamps(uint64_t* stamps)
 {
     g_stamps.store((unsigned long long*)stamps, std::memory_order_relaxed);
+}
+
+void tg_set_swizzle_override(int group_m)
+{
+    g_group_override.store(group_m > 0 ? group_m : 0, std::memory_order_relaxed);
+}
+
+tg_status tg_config_occupancy(int op, tg_dtype dtype, int index, int* workgroups_per_cu)
+{
+    if (!workgroups_per_cu)
+        return TG_ERR_NULL_POINTER;
+    *workgroups_per_cu = 0;
+    ConfigList L = list_for(op, op == TG_OP_DEQUANT_W4 ? TG_BF16 : dtype);
+    if (index < 0 || index >= L.count)
+        return TG_ERR_NO_CONFIG;
+    const Config& c = L.items[index];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, c.kernel, c.wgm * c.wgn * c.ks * 64, 0) !=
+        hipSuccess)
+        return TG_ERR_HIP;
+    *workgroups_per_cu = n;
+    return TG_OK;
 }
 
 tg_status tg_tile_map(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* out_m,

@@ -86,7 +86,16 @@ struct GemmParams {
     // shader clock counter (s_memtime) and the 100 MHz reference counter
     // (s_memrealtime) at its start and end: stamps[4 b + 0..3] = t0, r0, t1, r1.
     unsigned long long* stamps;
+    // Swizzle group (tile rows per group of the block-swizzled tile order);
+    // 0: the configuration's compiled default.
+    int group_m;
 };
+
+// The swizzle group a launch uses: its override, else the compiled default.
+__device__ __forceinline__ int group_of(const GemmParams& p, int dflt)
+{
+    return p.group_m > 0 ? p.group_m : dflt;
+}
 
 struct ClockStamp {
     unsigned long long t, r;
@@ -769,7 +778,7 @@ struct GemmKernel {
         const int w2 = wave % (WGM * WGN);
         const int wm = w2 / WGN;
         const int wn = w2 % WGN;
-        const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const TileCoord t = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, group_of(p, GROUP_M));
         const int m0 = t.m * BM;
         const int n0 = t.n * BN;
         const int KT = (p.K + BK - 1) / BK;
@@ -866,7 +875,7 @@ struct GemmKernel {
         const int sp = (int)blockIdx.x - tile * S;
         const int kbeg = S > 1 ? sp * p.kc : 0;
         const int kend = S > 1 ? min(p.K, kbeg + p.kc) : p.K;
-        const TileCoord t = tile_of(tile, p.tiles_m, p.tiles_n, GROUP_M);
+        const TileCoord t = tile_of(tile, p.tiles_m, p.tiles_n, group_of(p, GROUP_M));
         const int m0 = t.m * BM;
         const int n0 = t.n * BN;
         const int KT = (kend - kbeg + BK - 1) / BK;

@@ -612,7 +612,7 @@ struct DmaW4 {
         const int q = w / NWG;
         const int wm = (w % NWG) / WGN;
         const int wn = (w % NWG) % WGN;
-        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, group_of(p, GROUP_M));
         const int m0 = tc.m * BM;
         const int n0 = tc.n * BN;
         const int KT = p.K / BK;

@@ -472,7 +472,7 @@ struct DmaMx {
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = w / WGN;
         const int wn = w % WGN;
-        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, GROUP_M);
+        const TileCoord tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, group_of(p, GROUP_M));
         const int m0 = tc.m * BM;
         const int n0 = tc.n * BN;
         const int KT = p.K / BK;
