@@ -14,7 +14,22 @@ namespace tg {
             (const void*)&tg::gemm_mx_kernel<FMT, BM, BN, 2, 2, 4, GM, CS>, CS                \
     }
 
+// WGM x WGN waves and NS stages
+#define TG_CONFIG_MX_W(FMT, BM, BN, WGM, WGN, NS, GM, CS)                                    \
+    tg::Config                                                                               \
+    {                                                                                        \
+        2, (FMT) == MX_E2M1 ? 0 : 1, BM, BN, 128, WGM, WGN, NS, GM, true, false, false, 2,    \
+            (const void*)&tg::gemm_mx_kernel<FMT, BM, BN, WGM, WGN, NS, GM, CS>, CS           \
+    }
+
 static const Config kCfg[] = {
+    // eight waves (two per SIMD) with per-strip scale copies; E4M3 on
+    // 256 x 256 tiles takes three stages (150 KiB of LDS). Eight waves with
+    // chunked scales, and E4M3 256 x 256 on four waves, compile with spills
+    // or accumulator copies in the main loop and are left out.
+    TG_CONFIG_MX_W(MX_E2M1, 256, 256, 2, 4, 4, 4, false),
+    TG_CONFIG_MX_W(MX_E4M3, 256, 256, 2, 4, 3, 4, false),
+    TG_CONFIG_MX_W(MX_E4M3, 128, 256, 2, 4, 4, 4, false),
     // scale bytes staged 8 strips at a time (K % 512 == 0)
     TG_CONFIG_MX(MX_E2M1, 256, 256, 4, true),
     TG_CONFIG_MX(MX_E2M1, 256, 256, 8, true),

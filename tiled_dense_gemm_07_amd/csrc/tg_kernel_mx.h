@@ -81,15 +81,19 @@ struct DmaMx {
     static constexpr int NM = FM * FN;          // MFMAs per 64-k step
     static constexpr int SLOTS = 2 * NM;        // MFMAs per strip
 
-    static_assert(NW == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && JW >= 1 && A_STAGE % (1024 * NW) == 0 && W_STAGE % (1024 * NW) == 0,
                   "strips split into whole 1 KiB copies per wave");
     static_assert(CS || (NSA >= 1 && NSA <= NW && NSW >= 1 && NSW <= NW),
                   "scale copies: one per wave at most");
     static_assert(!CS || ((NCA + NCW) % NW == 0 && JS >= 1), "chunk copies split evenly");
-    static_assert(NS == 4, "four stages (scale registers alternate per strip)");
+    static_assert(NS == 4 || (NS == 3 && !CS),
+                  "four stages, or three with per-strip scale copies (chunked scales track the "
+                  "strip within the chunk by stage)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SA_REGION % 32 == 0 && SW_REGION % 32 == 0 && SA_STAGE % 32 == 0,
+                  "scale regions 32-byte aligned (the chunk halves are selected by an xor)");
 
     template <int W>
     struct Copies {
@@ -106,18 +110,19 @@ struct DmaMx {
         u32 s_half[CS ? JS : 1];  //   and that half (0, 1)
         u32 a_rd[2][A8 ? 2 : 1];  // [k-step][part]: code chunks of this lane (stage 0, fm 0)
         u32 w_rd[2];              // [k-step] (stage 0, fn 0)
-        u32 sa_rd[2], sw_rd[2];   // this lane's row of scale bytes (buffer 0, block 0);
-                                  // CS: [strips 0-3 / 4-7 of the chunk]
-        int h8;                   // 8 * lane half: the lane's scale bytes start at block h
+        u32 sa_rd, sw_rd;         // this lane's row of scale bytes (buffer 0, block 0;
+                                  // CS: strips 0-3 of the chunk, strips 4-7 at ^ 16)
+        u32 sh[2];                // [k-step]: 8 * lane half + 16 * k-step, the shift that
+                                  // brings the lane's scale byte to byte 0
     };
 
     struct Frag {  // one 64-k step
         u32x4 a[FM][A8 ? 2 : 1];
         u32x4 w[FN];
     };
-    struct Scales {  // one strip: [k-step][block], byte 0 = this lane's block
-        u32 a[2][FM];
-        u32 w[2][FN];
+    struct Scales {  // one strip: a row's four scale bytes per block, as read
+        u32 a[FM];
+        u32 w[FN];
     };
 
     static __device__ __forceinline__ void setup(Lane& L, const GemmParams& p, int m0, int n0,
@@ -180,15 +185,14 @@ struct DmaMx {
         }
         if constexpr (CS) {
             const int xa = (ar >> 3) & 1, xw = (nr >> 3) & 1;
-            L.sa_rd[0] = SA_REGION + ar * 32 + (xa << 4);
-            L.sa_rd[1] = SA_REGION + ar * 32 + ((1 ^ xa) << 4);
-            L.sw_rd[0] = SW_REGION + nr * 32 + (xw << 4);
-            L.sw_rd[1] = SW_REGION + nr * 32 + ((1 ^ xw) << 4);
+            L.sa_rd = SA_REGION + ar * 32 + (xa << 4);
+            L.sw_rd = SW_REGION + nr * 32 + (xw << 4);
         } else {
-            L.sa_rd[0] = L.sa_rd[1] = SA_REGION + ar * 4;
-            L.sw_rd[0] = L.sw_rd[1] = SW_REGION + nr * 4;
+            L.sa_rd = SA_REGION + ar * 4;
+            L.sw_rd = SW_REGION + nr * 4;
         }
-        L.h8 = 8 * h;
+        L.sh[0] = 8 * h;
+        L.sh[1] = 8 * h + 16;
     }
 
     // One buffer resource per array for the workgroup's whole row band (all
@@ -312,32 +316,30 @@ struct DmaMx {
         typedef __attribute__((address_space(3))) u32 lds_u32;
         u32 ra, rw;
         if constexpr (CS) {
-            const bool hi = (u >> 2) & 1;           // strips 4-7 of the chunk
+            // strips 4-7 of the chunk: the other 16-byte half of the row (the
+            // regions and rows are 32-byte aligned, so an xor selects it)
+            const u32 hi = (u32)(u & 4) << 2;
             const u32 buf = (u32)((u >> 3) & 1);
-            ra = (hi ? L.sa_rd[1] : L.sa_rd[0]) + buf * SA_STAGE + SL * 4;
-            rw = (hi ? L.sw_rd[1] : L.sw_rd[0]) + buf * SW_STAGE + SL * 4;
+            ra = (L.sa_rd ^ hi) + buf * SA_STAGE + SL * 4;
+            rw = (L.sw_rd ^ hi) + buf * SW_STAGE + SL * 4;
         } else {
-            ra = L.sa_rd[0] + SL * SA_STAGE;
-            rw = L.sw_rd[0] + SL * SW_STAGE;
+            ra = L.sa_rd + SL * SA_STAGE;
+            rw = L.sw_rd + SL * SW_STAGE;
         }
         constexpr int RA = CS ? 32 : 4;  // LDS bytes per scale row
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const u32 v = *(const lds_u32*)(sm + ra + fm * 32 * RA);
-            S.a[0][fm] = v >> L.h8;
-            S.a[1][fm] = v >> (L.h8 + 16);
-        }
+        for (int fm = 0; fm < FM; ++fm)
+            S.a[fm] = *(const lds_u32*)(sm + ra + fm * 32 * RA);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const u32 v = *(const lds_u32*)(sm + rw + fn * 32 * RA);
-            S.w[0][fn] = v >> L.h8;
-            S.w[1][fn] = v >> (L.h8 + 16);
-        }
+        for (int fn = 0; fn < FN; ++fn)
+            S.w[fn] = *(const lds_u32*)(sm + rw + fn * 32 * RA);
     }
 
+    // MFMA i of k-step Q.  The scale words are shifted here, at their first
+    // use, so the wait for their LDS read falls a strip after it was issued.
     template <int Q>
     static __device__ __forceinline__ void mfma_one(f32x16 (&acc)[FM][FN], const Frag& F,
-                                                    const Scales& S, int i)
+                                                    const Scales& S, const Lane& L, int i)
     {
         const int fm = i / FN, fn = i % FN;
         const u32x4 wv = F.w[fn];
@@ -354,7 +356,8 @@ struct DmaMx {
         // first operand: weights (rows n of the result block), second:
         // activations (columns m); scale byte 0 of each
         acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wop, aop, acc[fm][fn], MX_E2M1, AFMT, 0, (int)S.w[Q][fn], 0, (int)S.a[Q][fm]);
+            wop, aop, acc[fm][fn], MX_E2M1, AFMT, 0, (int)(S.w[fn] >> L.sh[Q]), 0,
+            (int)(S.a[fm] >> L.sh[Q]));
     }
 
     // One strip (stage ST) of wave W: k-step 0 with fragments F0, then k-step 1
@@ -364,8 +367,12 @@ struct DmaMx {
     // t + NS - 1 are staggered over the slots.  CS: strip 8 c + 1 also copies
     // scale chunk c + 1 (into the buffer chunk c - 1 used, whose last reads
     // were before strip 8 c - 1), so the wait of strip 8 c + 2 leaves those
-    // copies in flight too, and chunk c + 1 has landed by strip 8 c + 3.
-    template <int ST, int W>
+    // copies in flight too, and chunk c + 1 has landed by strip 8 c + 3.  P is
+    // the strip's place in its chunk (CS) as a compile-time constant: a
+    // run-time test there would split the strip into branches, and the
+    // compiler then sinks the MFMAs of whole strips past them, away from the
+    // copies and reads they are meant to hide.
+    template <int ST, int CUR, int W, int P = 0>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
                                                  Scales (&SC)[2], const Lane& L, const Res& res,
                                                  lds_char* sm, const GemmParams& p, int t,
@@ -373,7 +380,9 @@ struct DmaMx {
     {
         constexpr int NXT = (ST + 1) % NS;
         constexpr int CPY = (ST + NS - 1) % NS;
-        constexpr int CUR = ST & 1;
+        // scale slot of strip t + 1: its position in the chunk (CS, NS == 4)
+        // or its stage
+        constexpr int SNX = CS ? (ST + 1) & 3 : (ST + 1) % NS;
         constexpr int STEPS = NM > NRD ? NM : NRD;
         StripOff o;
 #pragma unroll
@@ -381,7 +390,7 @@ struct DmaMx {
             const int i = slot % STEPS;
             if (slot < STEPS) {
                 if (i < NM) {
-                    mfma_one<0>(acc, F0, SC[CUR], i);
+                    mfma_one<0>(acc, F0, SC[CUR], L, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i < NRD) {
@@ -390,11 +399,11 @@ struct DmaMx {
                 }
             } else {
                 if (i < NM) {
-                    mfma_one<1>(acc, F1, SC[CUR], i);
+                    mfma_one<1>(acc, F1, SC[CUR], L, i);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i == 0) {
-                    read_scales<(ST + 1) & 3>(SC[CUR ^ 1], L, sm, t + 1);
+                    read_scales<SNX>(SC[CUR ^ 1], L, sm, t + 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i < NRD) {
@@ -403,19 +412,18 @@ struct DmaMx {
                 }
             }
             if (slot == 0) {
-                if (CS && (t & 7) == 2)
+                if constexpr (CS && P == 2)
                     wait_copies_barrier<Copies<W>::AHEAD + JS>();
                 else
                     wait_copies_barrier<Copies<W>::AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
                 o = strip_off(p, t + NS - 1);
             }
-            if constexpr (CS) {
+            if constexpr (CS && P == 1) {
 #pragma unroll
                 for (int d = 0; d < JS; ++d) {
                     if (slot == 2 * d + 1) {
-                        if ((t & 7) == 1)
-                            issue_chunk<W>(L, res, p, (t >> 3) + 1, d, smem0);
+                        issue_chunk<W>(L, res, p, (t >> 3) + 1, d, smem0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -441,9 +449,11 @@ struct DmaMx {
             for (int d = 0; d < JS; ++d)
                 issue_chunk<W>(L, res, p, 0, d, smem0);
         }
+        // strips 0 .. NS-2 into stages 0 .. NS-2
         issue_copies<0, W>(L, res, p, 0, smem0);
         issue_copies<1, W>(L, res, p, 1, smem0);
-        issue_copies<2, W>(L, res, p, 2, smem0);
+        if constexpr (NS > 3)
+            issue_copies<2, W>(L, res, p, 2, smem0);
         wait_copies_barrier<(NS - 2) * Copies<W>::N>();
         Frag F0, F1;
         Scales SC[2];
@@ -451,13 +461,44 @@ struct DmaMx {
 #pragma unroll
         for (int i = 0; i < NRD; ++i)
             read_one<0, 0>(F0, L, sm, i);
-        // The strip count is rounded up to a multiple of NS: strips at or past
-        // KT copy only zeros, which add exactly nothing.
-        for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
-            strip<1, W>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
-            strip<2, W>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
-            strip<3, W>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+        // The strip count is rounded up to a whole number of loop bodies (NS
+        // strips, 6 for NS == 3 so that the scale registers alternate per
+        // strip): strips at or past KT copy only zeros, which add nothing.
+        if constexpr (CS) {
+            // whole chunks of 8 strips, then 4 (K % 512 == 0)
+            int t = 0;
+            for (; t + 8 <= KT; t += 8) {
+                strip<0, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<3, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+                strip<0, 0, W, 4>(acc, F0, F1, SC, L, res, sm, p, t + 4, smem0);
+                strip<1, 1, W, 5>(acc, F0, F1, SC, L, res, sm, p, t + 5, smem0);
+                strip<2, 0, W, 6>(acc, F0, F1, SC, L, res, sm, p, t + 6, smem0);
+                strip<3, 1, W, 7>(acc, F0, F1, SC, L, res, sm, p, t + 7, smem0);
+            }
+            if (t < KT) {
+                strip<0, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<3, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+            }
+        } else if constexpr (NS == 4) {
+            for (int t = 0; t < KT; t += 4) {
+                strip<0, 0, W>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<3, 1, W>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+            }
+        } else {
+            for (int t = 0; t < KT; t += 6) {
+                strip<0, 0, W>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<0, 1, W>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+                strip<1, 0, W>(acc, F0, F1, SC, L, res, sm, p, t + 4, smem0);
+                strip<2, 1, W>(acc, F0, F1, SC, L, res, sm, p, t + 5, smem0);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -497,8 +538,20 @@ struct DmaMx {
         case 2:
             main_loop<2>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
-        default:
+        case 3:
             main_loop<3>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 4:
+            main_loop<4 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 5:
+            main_loop<5 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        case 6:
+            main_loop<6 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
+            break;
+        default:
+            main_loop<7 % NW>(acc, L, sm, p, m0, n0, KT, smem0);
             break;
         }
         if ((p.N & 7) == 0 && ((uintptr_t)p.C & 15) == 0 && NW * WTM * WTN * 2 <= LDS_BYTES) {
@@ -543,17 +596,17 @@ struct DmaMx {
     }
 };
 
-// Waves per SIMD: two only for the small E2M1 tile (its fragments fit in 128
-// registers), else one.
-template <int AFMT, int BM, int BN>
+// Waves per SIMD: two with eight waves or for the small E2M1 tile (its
+// fragments fit in 128 registers), else one.
+template <int AFMT, int BM, int BN, int NW>
 struct MxOcc {
-    static constexpr int value = (AFMT == MX_E2M1 && BM * BN <= 128 * 128) ? 2 : 1;
+    static constexpr int value = (NW > 4 || (AFMT == MX_E2M1 && BM * BN <= 128 * 128)) ? 2 : 1;
 };
 
 template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
-                          amdgpu_waves_per_eu(MxOcc<AFMT, BM, BN>::value,
-                                              MxOcc<AFMT, BM, BN>::value))) void
+                          amdgpu_waves_per_eu(MxOcc<AFMT, BM, BN, WGM * WGN>::value,
+                                              MxOcc<AFMT, BM, BN, WGM * WGN>::value))) void
 gemm_mx_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
