@@ -173,6 +173,19 @@ def _read(path: str, counter: str):
     return calib[0][1], kern
 
 
+def commands(workload: str, launches: int, cold: bool) -> list:
+    """The command lines that make a record (OUT: the output folder)."""
+    run = "python3 -m tiled_dense_gemm_07_amd.traffic run --workload %s --launches %d%s" % (
+        workload, launches, " --cold" if cold else "")
+    return [
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/f -o f -- " + run,
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/w -o w -- " + run,
+        "python3 -m tiled_dense_gemm_07_amd.traffic summarize --workload %s "
+        "--fetch OUT/f/f_counter_collection.csv --write OUT/w/w_counter_collection.csv "
+        "--out profiles/traffic_%s.json%s" % (workload, workload, " --cold" if cold else ""),
+    ]
+
+
 def summarize(workload: str, fetch_csv: str, write_csv: str, out: str, cold: bool = False) -> dict:
     from . import synth
 
@@ -202,6 +215,7 @@ def summarize(workload: str, fetch_csv: str, write_csv: str, out: str, cold: boo
         "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
         "traffic_over_algorithmic": (fetch + write) / w.algorithmic_bytes(),
         "launches": len(f_k),
+        "commands": commands(workload, len(f_k), cold),
     }
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
