@@ -113,7 +113,7 @@ def _w4_config_fits(name, K):
     """Whether a dequant configuration can run this K (whole strips or rounds
     of its k depth; scale blocks need K % 512 == 0)."""
     bk = int(name.split("_")[2].split("x")[2])
-    if ("_dma" in name or name.endswith("_gemv")) and K % bk:
+    if ("_dma" in name or "_gemv" in name) and K % bk:
         return False
     return not ("_sc16" in name and K % 512)
 
@@ -152,7 +152,10 @@ def test_dequant_small(shape, integer):
                                    # inside the first block / a second, partial block
                                    (300, 264, 1536), (130, 200, 2560),
                                    # N % 8 != 0: results stored directly, not staged
-                                   (100, 130, 1024)],
+                                   (100, 130, 1024),
+                                   # few rows: partial 512-wide rounds of the
+                                   # weight-streaming kernels, K % 128 != 0
+                                   (16, 100, 1056), (7, 264, 1152), (3, 40, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_every_w4_config_ragged(shape):
     """Every dequant configuration this shape allows, forced, with integer

@@ -118,10 +118,11 @@ void config_name(const Config& c, char* buf, size_t len)
         snprintf(wav, sizeof wav, "w%dx%dx%d", c.wgm, c.wgn, c.ks);  // k-slice groups last
     else
         snprintf(wav, sizeof wav, "w%dx%d", c.wgm, c.wgn);
-    snprintf(buf, len, "%s_%s_%dx%dx%d_%s_s%d_g%d%s%s%s", opn[c.op],
+    snprintf(buf, len, "%s_%s_%dx%dx%d_%s_s%d_g%d%s%s%s%s", opn[c.op],
              mx ? mxn[c.dtype] : dn[c.dtype], c.bm,
              c.bn, c.bk, wav, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
+             c.runs ? "_runs" : "",
              c.chunked_scales ? (mx ? "_sc8" : "_sc16") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
 }
@@ -140,12 +141,16 @@ const Config* find_by_name(int op, int dtype, const char* name);
 // nullptr.  The variant with dword scale loads (bk == 128) needs K % 128 == 0
 // and scale rows that start 4-byte aligned; the byte-load variant (bk == 32)
 // takes any scale pointer.
-const Config* gemv_for(int64_t K, bool ws4)
+// The row-run variant for calls of at least kGemvRunsMinM activation rows,
+// whose activation loads bound the lane-range variant.
+constexpr int64_t kGemvRunsMinM = 10;
+const Config* gemv_for(int64_t M, int64_t K, bool ws4)
 {
     ConfigList L = list_for(TG_OP_DEQUANT_W4, TG_BF16);
+    const bool runs = M >= kGemvRunsMinM;
     for (int i = 0; i < L.count; ++i) {
         const Config& c = L.items[i];
-        if (c.pipe == 3 && K % c.bk == 0 && (ws4 || c.bk != 128))
+        if (c.pipe == 3 && c.runs == runs && K % c.bk == 0 && (ws4 || c.bk != 128))
             return &c;
     }
     return nullptr;
@@ -347,7 +352,7 @@ const TableIndex& table_index()
 Choice select_uncached(const Call& q)
 {
     if (q.op == TG_OP_DEQUANT_W4 && q.M <= 16 && q.wide) {
-        if (const Config* c = gemv_for(q.K, q.ws4))
+        if (const Config* c = gemv_for(q.M, q.K, q.ws4))
             return {c, 0};
     }
     const TableIndex& t = table_index();

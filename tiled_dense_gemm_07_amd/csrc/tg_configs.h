@@ -21,6 +21,8 @@ struct Config {
     bool chunked_scales = false;  // MX: scale bytes staged 8 strips at a time
                                   // (K % 512 == 0, 16-byte aligned scale rows)
     int ks = 1;                   // k-slice wave groups (WGM x WGN waves each)
+    bool runs = false;            // weight-streaming dequant: k assigned in contiguous
+                                  // 64-byte row runs (for several activation rows)
 };
 
 struct ConfigList {

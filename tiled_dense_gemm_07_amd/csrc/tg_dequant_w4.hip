@@ -8,9 +8,16 @@
 namespace tg {
 
 static const Config kCfg[] = {
-    // few activation rows: weight-streaming kernel (bk = the K multiple it needs)
-    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, false, false, 3, (const void*)&gemv_w4_kernel<true>},
-    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, false, false, 3, (const void*)&gemv_w4_kernel<false>},
+    // few activation rows: weight-streaming kernel (bk = the K multiple it
+    // needs; lane ranges, then contiguous row runs)
+    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, false, false, 3,
+               (const void*)&gemv_w4_kernel<true, false>},
+    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, false, false, 3,
+               (const void*)&gemv_w4_kernel<false, false>},
+    tg::Config{1, DT_BF16, 16, 32, 128, 16, 1, 1, 1, true, false, false, 3,
+               (const void*)&gemv_w4_kernel<true, true>, false, 1, true},
+    tg::Config{1, DT_BF16, 16, 32, 32, 16, 1, 1, 1, true, false, false, 3,
+               (const void*)&gemv_w4_kernel<false, true>, false, 1, true},
     // many rows: LDS-DMA pipeline, codes dequantised in registers (K % 128 == 0)
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4>},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 8, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 8>},

@@ -10,18 +10,30 @@
 // tile:
 //  * a workgroup owns 32 weight rows (two groups of 16) and all of K; its 16
 //    waves split K into rounds of 512 (wave w takes rounds w, w+16, ...);
-//  * in a round, lane (n = l % 16, g = l / 16) loads 4 x 16 bytes of codes of
-//    row n covering k in [512 r + 128 g, +128) and the 4 scale bytes of those
-//    k, for each row group: every byte of a 128-byte line is used, and a wave
-//    keeps 8 KiB of weights in flight;
+//  * a round is 16 MFMA steps of 32 k.  Two assignments of k to lanes, a
+//    template parameter chosen by the activation row count:
+//    - lane ranges (RUNS = false): lane (n = l % 16, g = l / 16) takes the
+//      128 k of [512 r + 128 g, +128) (4 x 16 bytes of codes of row n and the
+//      4 scale bytes of those k); step (c, h) multiplies k = 512 r + 128 g +
+//      32 c + 8 h + 0..7 in group g.  Few VALU operations per code, and the
+//      activation loads of one row are cheap; with 16 rows each activation
+//      load touches 64 scattered 16-byte pieces, and those loads bound it;
+//    - contiguous runs (RUNS = true): step (c, h) takes k = 512 r + 128 c +
+//      32 h + 8 g + 0..7 in group g, so the four groups of one row read one
+//      contiguous 64-byte run for each activation load (16 runs per load).
+//      The codes are loaded the same way (load c: lane (n, g) takes the 16
+//      bytes of k in [512 r + 128 c + 32 g, +32)), which puts the codes of
+//      step (c, h) in dword g of group h; a 4 x 4 transpose across the lane
+//      groups (two rounds of lane-row swaps) moves them to dword h of group
+//      g.  The 16 scale bytes of a row's round are one 16-byte load;
 //  * the codes are expanded to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4
 //    applies the scale exactly) and fed straight to v_mfma_f32_16x16x32_bf16
 //    as the 16-row operand; the activation fragment of the same k (rows m of
 //    A, zero past M) is the other operand;
 //  * the 16 waves' 16 x 32 partial sums are added in LDS in a fixed order (so
 //    results do not depend on timing), then ReLU, one rounding and the store.
-// The k order inside a round is permuted the same way for A and W, which only
-// reorders the sum.
+// The k order inside an MFMA step is permuted the same way for A and W, which
+// only reorders the sum.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,7 +45,33 @@ namespace tg {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4v;
 
-template <bool DWORD_SCALES>
+// 4 x 4 transpose across the four 16-lane groups: afterwards d[h] of group g
+// is what d[g] of group h was.  A swap of lane halves (groups 2, 3 of one
+// register with groups 0, 1 of another), then a swap of odd and even groups.
+__device__ __forceinline__ void transpose4(u32 (&d)[4])
+{
+    const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    d[0] = s01[0];
+    d[1] = s01[1];
+    d[2] = s23[0];
+    d[3] = s23[1];
+}
+
+// Eight E2M1 codes (low nibble first) to eight bf16 values times scale s.
+__device__ __forceinline__ u32x4 expand8(u32 packed, float s)
+{
+    u32x4 b;
+    b[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 0));
+    b[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 1));
+    b[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 2));
+    b[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 3));
+    return b;
+}
+
+template <bool DWORD_SCALES, bool RUNS>
 struct GemvW4 {
     static constexpr int NWAVE = 16;
     static constexpr int ROWS = 32;     // weight rows per workgroup
@@ -71,59 +109,135 @@ struct GemvW4 {
         for (int q = 0; q < NG; ++q)
             acc[q] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 
-        const int rounds = (K + ROUND - 1) / ROUND;
-        for (int r = w; r < rounds; r += NWAVE) {
-            const int kq = r * ROUND + 128 * g;  // this lane's first k
-            const bool kv = kq < K;              // K is a multiple of 32; kq, +32, ... may pass it
-            // issue all weight loads of the round first (8 KiB per wave in flight)
-            u32x4 code[NG][4];
-            u32 sc[NG];
+        if constexpr (RUNS) {
+            const int rounds = (K + ROUND - 1) / ROUND;
+            for (int r = w; r < rounds; r += NWAVE) {
+                const int kr = r * ROUND;
+                // issue all loads of the round first (8 KiB of codes per wave in flight)
+                u32x4 code[NG][4];  // [group][c]: codes of k in [kr + 128 c + 32 g, +32)
+                u32x4 sc[NG];       // the row's 16 scale bytes of the round, block 4 c + h
 #pragma unroll
-            for (int q = 0; q < NG; ++q) {
-                const u32 rowoff = (u32)((16 * q + ln) * rowb);
+                for (int q = 0; q < NG; ++q) {
+                    const u32 rowoff = (u32)((16 * q + ln) * rowb);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bool v = kq + 32 * c < K;
-                    code[q][c] = buf_load16(wrs, v ? rowoff + (u32)(kq + 32 * c) / 2 : kOob);
+                    for (int c = 0; c < 4; ++c) {
+                        const int k = kr + 128 * c + 32 * g;  // K is a multiple of 32
+                        code[q][c] = buf_load16(wrs, k < K ? rowoff + (u32)k / 2 : kOob);
+                    }
+                    const u32 soff = (u32)((16 * q + ln) * srow + kr / 32);
+                    if (DWORD_SCALES && kr + ROUND <= K) {
+                        sc[q] = buf_load16(srs, soff);  // 4-byte aligned rows
+                    } else if (DWORD_SCALES) {
+                        // the last, partial round: dword i (blocks 4 i ..) only
+                        // while inside the row (K % 128 == 0 for aligned rows)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sc[q][i] = buf_load4(srs, kr + 128 * i < K ? soff + 4 * i : kOob);
+                    }
+                    // byte-aligned scale rows: their bytes are loaded per step below
                 }
-                const u32 soff = (u32)((16 * q + ln) * srow + kq / 32);
-                if (DWORD_SCALES) {
-                    sc[q] = buf_load4(srs, kv ? soff : kOob);
-                } else {
-                    u32 s4 = 0;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        s4 |= buf_load1(srs, kq + 32 * c < K ? soff + c : kOob) << (8 * c);
-                    sc[q] = s4;
-                }
-            }
-            // activation fragments: 16 bytes of row m0 + ln at the same k
-            u32x4 af[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int k = kq + 8 * j;
-                af[j] = buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
-            }
-            // every load of the round is in flight before the first is consumed
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int q = 0; q < NG; ++q) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    // a scale byte only multiplies codes of k < K (zeros past it)
-                    const u32 e = (sc[q] >> (8 * c)) & 0xFFu;
-                    const float s = e8m0_to_f32(kq + 32 * c < K ? e : 127u);
+                // activation fragments of step (c, h): 16 bytes of row m0 + ln; those
+                // of steps c and c + 1 are in flight while step c - 1 computes (all
+                // sixteen at once would not fit the 128 registers of a wave here)
+                u32x4 af[16];
+                const auto load_af = [&](int c) {
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        const u32 packed = code[q][c][h];  // 8 codes: k = kq + 32c + 8h ..
-                        u32x4 b;
-                        b[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 0));
-                        b[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 1));
-                        b[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 2));
-                        b[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 3));
-                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, af[4 * c + h]),
-                            acc[q], 0, 0, 0);
+                        const int k = kr + 128 * c + 32 * h + 8 * g;
+                        af[4 * c + h] =
+                            buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
+                    }
+                };
+                load_af(0);
+                load_af(1);
+                // every weight load of the round is in flight before the first is consumed
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (c + 2 < 4)
+                        load_af(c + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) {
+                        if (!DWORD_SCALES) {
+                            const u32 soff = (u32)((16 * q + ln) * srow + kr / 32 + 4 * c);
+                            u32 b = 0;
+#pragma unroll
+                            for (int h = 0; h < 4; ++h)
+                                b |= buf_load1(srs, kr + 32 * (4 * c + h) < K ? soff + h : kOob)
+                                     << (8 * h);
+                            sc[q][c] = b;
+                        }
+                        // group g holds dword e = codes of step (c, g), lanes 8 e ..;
+                        // step (c, h) wants, in group g, the dword g of group h
+                        u32 d[4] = {code[q][c][0], code[q][c][1], code[q][c][2], code[q][c][3]};
+                        transpose4(d);
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            const int blk = 4 * c + h;  // 32-k block of the round
+                            const u32 e = (sc[q][blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
+                            // a scale byte only multiplies codes of k < K (zeros past it)
+                            const float s = e8m0_to_f32(kr + 32 * blk < K ? e : 127u);
+                            const u32 packed = d[h];  // 8 codes: k = kr + 128 c + 32 h + 8 g ..
+                            const u32x4 b = expand8(packed, s);
+                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, af[blk]),
+                                acc[q], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        } else {
+            const int rounds = (K + ROUND - 1) / ROUND;
+            for (int r = w; r < rounds; r += NWAVE) {
+                const int kq = r * ROUND + 128 * g;  // this lane's first k
+                const bool kv = kq < K;              // K is a multiple of 32; kq, +32, ... may pass it
+                // issue all weight loads of the round first (8 KiB per wave in flight)
+                u32x4 code[NG][4];
+                u32 sc[NG];
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const u32 rowoff = (u32)((16 * q + ln) * rowb);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const bool v = kq + 32 * c < K;
+                        code[q][c] = buf_load16(wrs, v ? rowoff + (u32)(kq + 32 * c) / 2 : kOob);
+                    }
+                    const u32 soff = (u32)((16 * q + ln) * srow + kq / 32);
+                    if (DWORD_SCALES) {
+                        sc[q] = buf_load4(srs, kv ? soff : kOob);
+                    } else {
+                        u32 s4 = 0;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            s4 |= buf_load1(srs, kq + 32 * c < K ? soff + c : kOob) << (8 * c);
+                        sc[q] = s4;
+                    }
+                }
+                // activation fragments: 16 bytes of row m0 + ln at the same k
+                u32x4 af[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int k = kq + 8 * j;
+                    af[j] = buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
+                }
+                // every load of the round is in flight before the first is consumed
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        // a scale byte only multiplies codes of k < K (zeros past it)
+                        const u32 e = (sc[q] >> (8 * c)) & 0xFFu;
+                        const float s = e8m0_to_f32(kq + 32 * c < K ? e : 127u);
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            const u32 packed = code[q][c][h];  // 8 codes: k = kq + 32c + 8h ..
+                            const u32x4 b = expand8(packed, s);
+                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, af[4 * c + h]),
+                                acc[q], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -151,11 +265,11 @@ struct GemvW4 {
     }
 };
 
-template <bool DWORD_SCALES>
+template <bool DWORD_SCALES, bool RUNS>
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024))) void gemv_w4_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
-    GemvW4<DWORD_SCALES>::run(p);
+    GemvW4<DWORD_SCALES, RUNS>::run(p);
     stamp_end(p, clk);
 }
 
