@@ -69,16 +69,25 @@ def test_sp24_small(dtype, shape, relu, integer):
     check(got, oracle.gemm_sp24_f64(Ac, Ai, B, dtype, relu), dtype, integer)
 
 
-@pytest.mark.parametrize("shape", [(300, 264, 224), (200, 136, 512), (64, 72, 96)],
+@pytest.mark.parametrize("shape", [(300, 264, 224), (200, 136, 512), (64, 72, 96),
+                                   # metadata chunks of 4 strips: one chunk; 12 strips
+                                   # (one full loop); 12 + 4 and 12 + 8 strips
+                                   (130, 264, 256), (64, 72, 768), (257, 136, 1024),
+                                   (200, 136, 1280)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DNAME[d])
 def test_sp24_every_config(dtype, shape):
     """Every configuration, forced, on ragged shapes (K % 64 == 32 included):
-    bit-exact with integer inputs."""
+    bit-exact with integer inputs; the metadata-chunk configurations refuse
+    K % 256 != 0."""
     M, N, K = shape
     Ac, Ai, B = synth.sp24_inputs(M, N, K, dtype, 2400, 2401, 2402, integer=True)
     want = oracle.encode(dtype, oracle.gemm_sp24_f64(Ac, Ai, B, dtype, relu=True))
     for idx, name in enumerate(binding.list_configs(binding.TG_OP_SP24, dtype)):
+        if name.endswith("_mc4") and K % 256:
+            with pytest.raises(binding.TileGemmError):
+                run_sp24(Ac, Ai, B, dtype, relu=True, config=idx)
+            continue
         say("sp24 config %d %s %s" % (idx, name, shape))
         got = run_sp24(Ac, Ai, B, dtype, relu=True, config=idx)
         assert np.array_equal(got, want), name

@@ -123,7 +123,8 @@ void config_name(const Config& c, char* buf, size_t len)
              c.bn, c.bk, wav, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
              c.runs ? "_runs" : "",
-             c.chunked_scales ? (mx ? "_sc8" : "_sc16") : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
+             c.chunked_scales ? (mx ? "_sc8" : (c.op == TG_OP_SP24 ? "_mc4" : "_sc16"))
+                              : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
 }
 
@@ -163,7 +164,7 @@ struct Call {
     bool wide;    // 16-byte aligned operands whose rows are whole 16-byte chunks
     bool ws4;     // dequant / MX scale bytes start 4-byte aligned
     bool ta, tb;  // A stored [K][M], B stored [N][K]
-    bool ws16 = false;  // MX scale bytes start 16-byte aligned
+    bool ws16 = false;  // MX scale / sparse metadata bytes start 16-byte aligned
 };
 
 // Whether configuration c can run call q.
@@ -178,9 +179,13 @@ bool usable(const Config& c, const Call& q)
             return false;
         return c.dtype == q.dtype && q.wide && q.ws4 && q.K % c.bk == 0;
     }
-    if (c.op == TG_OP_SP24)
+    if (c.op == TG_OP_SP24) {
+        // metadata chunks of 4 strips: whole 16-byte pieces of 16-byte aligned rows
+        if (c.chunked_scales && (q.K % 256 != 0 || !q.ws16))
+            return false;
         // whole 32-k groups of metadata dwords; 16-byte copies of values and B
         return c.dtype == q.dtype && q.wide && q.ws4 && q.K % 32 == 0;
+    }
     if (c.ta != q.ta || c.tb != q.tb)
         return false;  // operand layouts are compiled in
     if (c.op == TG_OP_DEQUANT_W4 && (c.pipe == 2 || c.pipe == 3) && q.K % c.bk != 0)
@@ -756,6 +761,7 @@ tg_status sp24_impl(const Config* forced, int forced_index, int64_t M, int64_t N
         return TG_ERR_ALIAS;
     Call q{TG_OP_SP24, dtype, M, N, K, aligned16(Ac) && aligned16(B) && N % 8 == 0,
            ((uintptr_t)Ai & 3u) == 0, false, false};
+    q.ws16 = aligned16(Ai);
     const Choice ch = forced ? Choice{forced, 0} : select_config(q);
     const Config* c = ch.c;
     if (!c || !usable(*c, q))

@@ -1,5 +1,6 @@
 // 2:4 structured-sparse GEMM configurations (sparse matrix instruction,
-// 64 dense k per strip, 3 LDS stages; K % 32 == 0).
+// 64 dense k per strip, 3 LDS stages; K % 32 == 0, the metadata-chunk ones
+// K % 256 == 0).
 #include "tg_configs.h"
 #include "tg_kernel_sp24.h"
 
@@ -19,7 +20,19 @@ namespace tg {
             (const void*)&tg::gemm_sp24_kernel<DT, BM, BN, WGM, WGN, 3, GM>             \
     }
 
+// metadata copied in chunks of 4 strips (K % 256 == 0, 16-byte aligned rows)
+#define TG_CONFIG_SP24_C(DT, BM, BN, WGM, WGN, GM)                                      \
+    tg::Config                                                                          \
+    {                                                                                   \
+        3, DT, BM, BN, 64, WGM, WGN, 3, GM, true, false, false, 2,                      \
+            (const void*)&tg::gemm_sp24_kernel<DT, BM, BN, WGM, WGN, 3, GM, true>, true \
+    }
+
 static const Config kCfgBf16[] = {
+    TG_CONFIG_SP24_C(DT_BF16, 256, 256, 2, 4, 4),
+    TG_CONFIG_SP24_C(DT_BF16, 256, 128, 2, 2, 4),
+    TG_CONFIG_SP24_C(DT_BF16, 128, 256, 2, 2, 4),
+    TG_CONFIG_SP24_C(DT_BF16, 128, 128, 2, 2, 8),
     TG_CONFIG_SP24_W(DT_BF16, 256, 256, 2, 4, 4),
     TG_CONFIG_SP24(DT_BF16, 256, 128, 4),
     TG_CONFIG_SP24(DT_BF16, 256, 128, 8),
@@ -27,6 +40,10 @@ static const Config kCfgBf16[] = {
     TG_CONFIG_SP24(DT_BF16, 128, 128, 8),
 };
 static const Config kCfgF16[] = {
+    TG_CONFIG_SP24_C(DT_F16, 256, 256, 2, 4, 4),
+    TG_CONFIG_SP24_C(DT_F16, 256, 128, 2, 2, 4),
+    TG_CONFIG_SP24_C(DT_F16, 128, 256, 2, 2, 4),
+    TG_CONFIG_SP24_C(DT_F16, 128, 128, 2, 2, 8),
     TG_CONFIG_SP24_W(DT_F16, 256, 256, 2, 4, 4),
     TG_CONFIG_SP24(DT_F16, 256, 128, 4),
     TG_CONFIG_SP24(DT_F16, 256, 128, 8),

@@ -28,7 +28,18 @@
 //    and one ds_read_b32 of metadata (shifted by lane half), and per 32-column
 //    block the two slab fragments of B; one sparse MFMA per block pair;
 //  * one barrier per strip after its first MFMA; copies of strip t + 2 into
-//    the stage strip t - 1 used, spread over the strip.
+//    the stage strip t - 1 used, spread over the strip;
+//  * CS (K % 256 == 0, 16-byte aligned metadata rows): the metadata of 4
+//    strips (32 bytes per row) is copied as one chunk with 16-byte copies
+//    (32 rows per copy) into one of two LDS buffers, instead of 4 bytes per
+//    row per strip (64 rows, 64 cache lines per copy): the address path
+//    spends its cycles per line, and the per-strip copies cost a fifth of the
+//    kernel.  Chunk c + 1 is copied during strip 4 c + 1 into the buffer
+//    chunk c - 1 used; each strip's barrier waits for every copy, so it has
+//    landed by strip 4 c + 2.  The strip's place in its chunk and its stage
+//    are compile-time constants (a loop of 12 strips, then 4 or 8): a
+//    run-time test would split the strip into branches past which the
+//    compiler sinks the MFMAs.
 // K % 32 == 0: a strip past K copies zeros (values and B), so whatever
 // positions its metadata holds, its products are zero.
 #pragma once
@@ -45,7 +56,7 @@ namespace tg {
 typedef __attribute__((ext_vector_type(16))) __bf16 bf16x16;
 typedef __attribute__((ext_vector_type(16))) _Float16 f16x16;
 
-template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS>
 struct DmaSp24 {
     static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
     static constexpr int BK = 64;  // dense k per strip
@@ -57,13 +68,17 @@ struct DmaSp24 {
     using OB = DmaOperand<false, BN, WTN, FN, NW, BK>;
     static constexpr int A_STAGE = BM * 64;  // 32 kept values per row per strip
     static constexpr int I_STAGE = BM * 8;   // two metadata dwords per row per strip
+    static constexpr int CH = 4;             // strips per metadata chunk (CS)
+    static constexpr int I_CHUNK = BM * 32;  // one chunk buffer (CS)
     static constexpr int B_STAGE = OB::STAGE;
     static constexpr int I_REGION = NS * A_STAGE;
-    static constexpr int B_REGION = I_REGION + NS * I_STAGE;
+    static constexpr int B_REGION = I_REGION + (CS ? 2 * I_CHUNK : NS * I_STAGE);
     static constexpr int LDS_BYTES = B_REGION + NS * B_STAGE;
     static constexpr int JA = A_STAGE / 1024 / NW;   // value copies per wave per strip
-    static constexpr int NIC = I_STAGE / 256;        // metadata dword copies per strip
+    static constexpr int NIC = CS ? 0 : I_STAGE / 256;  // metadata dword copies per strip
     static constexpr int JI = NIC / NW;              // ... per wave
+    static constexpr int NCC = CS ? BM / 32 : 0;     // chunk copies per chunk (CS)
+    static constexpr int JC = NCC / NW;              // ... per wave
     static constexpr int NCOPY = JA + JI + OB::J;    // copies per wave per strip
     static constexpr int NM = FM * FN;               // MFMAs per 32-k step
     static constexpr int NRD = 2 * FM + 4 * FN;      // LDS reads per 32-k step
@@ -71,18 +86,22 @@ struct DmaSp24 {
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of 32x32 blocks");
     static_assert(JA >= 1 && A_STAGE % (1024 * NW) == 0, "value copies split evenly");
-    static_assert(JI >= 1 && NIC % NW == 0, "metadata copies split evenly");
+    static_assert(CS ? (JC >= 1 && NCC % NW == 0) : (JI >= 1 && NIC % NW == 0),
+                  "metadata copies split evenly");
+    static_assert(I_REGION % 1024 == 0, "chunk buffers 1 KiB aligned (the halves are selected by an xor)");
     static_assert(NS == 3, "three stages: the barrier publishes strip t + 1 while t - 1 is free");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
     struct Lane {
         u32 a_off[JA];        // value copies: row offset + chunk (kOob past M)
-        u32 i_off[JI];        // metadata copies: row offset + dword (kOob past M)
+        u32 i_off[CS ? JC : JI];  // metadata copies: row offset + dword, or (CS) row
+                                  // offset + 16-byte half of the chunk (kOob past M)
         int a_c;              // chunk this lane copies: dense k 16 a_c .. of the strip,
                               // the same for all JA copies (rows 16 apart share swz_a)
         u32 a_rd[2];          // [k-step]: this lane's 16 bytes of kept values (stage 0, fm 0)
         u32 i_rd;             // this lane's metadata dword of k-step 0 (stage 0, fm 0);
-                              // k-step 1's is BM * 4 bytes further
+                              // k-step 1's is BM * 4 bytes further.  CS: its row in
+                              // chunk buffer 0 (strips 0, 1 of the chunk; 2, 3 at ^ 16)
         int h16;              // 16 * lane half
         typename OB::Lane b;
     };
@@ -105,12 +124,23 @@ struct DmaSp24 {
             const int c = (lane & 3) ^ swz_a(row);
             L.a_off[j] = (m0 + row < p.M) ? (u32)(row * K + c * 16) : kOob;  // K/2 values x 2 B
         }
+        if constexpr (CS) {
+            // chunk copy g: rows 32 g .., lane l -> row 32 g + l / 2 at LDS 16-byte
+            // position l & 1, which holds the row's half (l & 1) ^ bit 3 of the row
 #pragma unroll
-        for (int j = 0; j < JI; ++j) {
-            const int g = w * JI + j;           // dword copy index: block (g / (BM / 64)), rows ...
-            const int blk = g / (BM / 64);      // metadata dword 0 or 1 of the strip
-            const int row = (g % (BM / 64)) * 64 + lane;
-            L.i_off[j] = (m0 + row < p.M) ? (u32)(row * (K / 8) + blk * 4) : kOob;
+            for (int j = 0; j < JC; ++j) {
+                const int row = (w * JC + j) * 32 + (lane >> 1);
+                const int half = (lane & 1) ^ ((row >> 3) & 1);
+                L.i_off[j] = (m0 + row < p.M) ? (u32)(row * (K / 8) + half * 16) : kOob;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < JI; ++j) {
+                const int g = w * JI + j;           // dword copy index: block (g / (BM / 64)), rows ...
+                const int blk = g / (BM / 64);      // metadata dword 0 or 1 of the strip
+                const int row = (g % (BM / 64)) * 64 + lane;
+                L.i_off[j] = (m0 + row < p.M) ? (u32)(row * (K / 8) + blk * 4) : kOob;
+            }
         }
         // swz_a depends on row bits 1-3 only, and rows of one lane differ by 16
         L.a_c = (lane & 3) ^ swz_a(lane >> 2);
@@ -120,7 +150,7 @@ struct DmaSp24 {
         for (int q = 0; q < 2; ++q) {
             L.a_rd[q] = ar * 64 + (((2 * q + h) ^ swz_a(ar)) << 4);
         }
-        L.i_rd = I_REGION + ar * 4;
+        L.i_rd = CS ? I_REGION + ar * 32 + (((ar >> 3) & 1) << 4) : I_REGION + ar * 4;
         L.h16 = 16 * h;
         OB::setup(L.b, n0, p.N, p.N, w, lane, wn * WTN, B_REGION);
     }
@@ -197,18 +227,39 @@ struct DmaSp24 {
             issue_copy<ST, W>(L, res, r, d, smem0);
     }
 
+    // Chunk copy j of wave W (CS): the metadata of strips 4 c .. 4 c + 3 into
+    // buffer c & 1.  Past K (K % 256 == 0) a chunk copies zeros.
+    template <int W>
+    static __device__ __forceinline__ void issue_chunk(const Lane& L, const Res& r,
+                                                       const GemmParams& p, int c, int j,
+                                                       u32 smem0)
+    {
+        const u32 off = 256 * c < p.K ? L.i_off[j] + (u32)(c * 32) : kOob;
+        dma16(smem0 + I_REGION + (u32)(c & 1) * I_CHUNK + (W * JC + j) * 1024, off, r.i);
+    }
+
     // Read i (0 .. NRD-1) of k-step Q of stage ST: values and metadata per
-    // row block, then the B fragments (two slabs) per column block.
-    template <int ST, int Q>
-    static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i)
+    // row block, then the B fragments (two slabs) per column block.  SP: the
+    // strip's place in its metadata chunk and ib the chunk buffer's offset (CS).
+    template <int ST, int Q, int SP>
+    static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i,
+                                                    u32 ib)
     {
         typedef __attribute__((address_space(3))) u32 lds_u32;
         if (i < FM) {
             F.a[i] = *(const lds_u32x4*)(sm + L.a_rd[Q] + ST * A_STAGE + i * 32 * 64);
         } else if (i < 2 * FM) {
             const int fm = i - FM;
-            F.idx[fm] = *(const lds_u32*)(sm + L.i_rd + Q * BM * 4 + ST * I_STAGE + fm * 32 * 4) >>
-                        L.h16;
+            if constexpr (CS) {
+                // row's half SP / 2, dword 2 (SP % 2) + Q of it
+                const u32 a = (L.i_rd ^ (u32)((SP >> 1) << 4)) + ib + (2 * (SP & 1) + Q) * 4 +
+                              fm * 32 * 32;
+                F.idx[fm] = *(const lds_u32*)(sm + a) >> L.h16;
+            } else {
+                F.idx[fm] = *(const lds_u32*)(sm + L.i_rd + Q * BM * 4 + ST * I_STAGE +
+                                              fm * 32 * 4) >>
+                            L.h16;
+            }
         } else {
             // B: quarter u of column block f holds 4 consecutive k of slab
             // 2 Q + u / 2 (the transposing read of the dense kernel's operand)
@@ -252,7 +303,9 @@ struct DmaSp24 {
     // (k-step 1 of this strip into F1, or k-step 0 of strip t + 1 into F0)
     // spread evenly over the NM slots; slot 0 waits for strip t + 1's copies
     // and barriers; copies of strip t + 2 are spread over the strip.
-    template <int ST, int W>
+    // CS: P is the strip's place in its metadata chunk; strip 4 c + 1 also
+    // copies chunk c + 1.
+    template <int ST, int W, int P = 0>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
                                                  const Lane& L, const Res& res, lds_char* sm,
                                                  const GemmParams& p, int n0, int t, u32 smem0)
@@ -260,6 +313,10 @@ struct DmaSp24 {
         constexpr int NXT = (ST + 1) % NS;
         constexpr int CPY = (ST + NS - 1) % NS;
         constexpr int SLOTS = 2 * NM;
+        constexpr int PN = (P + 1) % CH;  // place of strip t + 1
+        // chunk buffers of strips t and t + 1
+        const u32 ib = CS ? (u32)((t >> 2) & 1) * I_CHUNK : 0u;
+        const u32 ibn = CS ? (u32)(((t + 1) >> 2) & 1) * I_CHUNK : 0u;
         StripRes r;
 #pragma unroll
         for (int slot = 0; slot < SLOTS; ++slot) {
@@ -270,19 +327,28 @@ struct DmaSp24 {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rd = lo; rd < hi; ++rd)
-                    read_one<ST, 1>(F1, L, sm, rd);
+                    read_one<ST, 1, P>(F1, L, sm, rd, ib);
             } else {
                 mfma_one(acc, F1, i);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rd = lo; rd < hi; ++rd)
-                    read_one<NXT, 0>(F0, L, sm, rd);
+                    read_one<NXT, 0, PN>(F0, L, sm, rd, ibn);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (slot == 0) {
                 wait_copies_barrier<0>();
                 __builtin_amdgcn_sched_barrier(0);
                 r = strip_res(p, n0, t + NS - 1);
+            }
+            if constexpr (CS && P == 1) {
+#pragma unroll
+                for (int j = 0; j < JC; ++j) {
+                    if (slot == 2 * j + 1) {
+                        issue_chunk<W>(L, res, p, (t >> 2) + 1, j, smem0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
 #pragma unroll
             for (int d = 0; d < NCOPY; ++d) {
@@ -300,19 +366,56 @@ struct DmaSp24 {
                                                      int n0, int KT, u32 smem0)
     {
         const Res res = band_res(p, m0);
+        if constexpr (CS) {
+#pragma unroll
+            for (int j = 0; j < JC; ++j)
+                issue_chunk<W>(L, res, p, 0, j, smem0);
+        }
         issue_copies<0, W>(L, res, p, n0, 0, smem0);
         issue_copies<1, W>(L, res, p, n0, 1, smem0);
-        wait_copies_barrier<NCOPY>();  // strip 0 landed and visible
+        wait_copies_barrier<NCOPY>();  // chunk 0 and strip 0 landed and visible
         Frag F0, F1;
 #pragma unroll
         for (int i = 0; i < NRD; ++i)
-            read_one<0, 0>(F0, L, sm, i);
-        // The strip count is rounded up to a multiple of NS: strips at or past
-        // KT copy only zeros, which add exactly nothing.
-        for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
-            strip<1, W>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
-            strip<2, W>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
+            read_one<0, 0, 0>(F0, L, sm, i, 0u);
+        if constexpr (CS) {
+            // 12 strips (the stage and the place in the chunk both repeat),
+            // then the 4 or 8 left (K % 256 == 0)
+            int t = 0;
+            for (; t + 12 <= KT; t += 12) {
+                strip<0, W, 0>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
+                strip<1, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
+                strip<0, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 3, smem0);
+                strip<1, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 4, smem0);
+                strip<2, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 5, smem0);
+                strip<0, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 6, smem0);
+                strip<1, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 7, smem0);
+                strip<2, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 8, smem0);
+                strip<0, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 9, smem0);
+                strip<1, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 10, smem0);
+                strip<2, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 11, smem0);
+            }
+            if (t + 4 <= KT) {
+                strip<0, W, 0>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
+                strip<1, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
+                strip<0, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 3, smem0);
+                if (t + 8 <= KT) {
+                    strip<1, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 4, smem0);
+                    strip<2, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 5, smem0);
+                    strip<0, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 6, smem0);
+                    strip<1, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 7, smem0);
+                }
+            }
+        } else {
+            // The strip count is rounded up to a multiple of NS: strips at or
+            // past KT copy only zeros, which add exactly nothing.
+            for (int t = 0; t < KT; t += NS) {
+                strip<0, W>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
+                strip<1, W>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -407,14 +510,14 @@ struct Sp24Occ {
     static constexpr int value = WGM * WGN > 4 ? 2 : 1;
 };
 
-template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M>
+template <int DT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
                           amdgpu_waves_per_eu(Sp24Occ<WGM, WGN>::value,
                                               Sp24Occ<WGM, WGN>::value))) void
 gemm_sp24_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
-    DmaSp24<DT, BM, BN, WGM, WGN, NS, GROUP_M>::run(p);
+    DmaSp24<DT, BM, BN, WGM, WGN, NS, GROUP_M, CS>::run(p);
     stamp_end(p, clk);
 }
 
