@@ -25,10 +25,16 @@ namespace tg {
 static const Config kCfg[] = {
     // eight waves (two per SIMD) with per-strip scale copies; E4M3 on
     // 256 x 256 tiles takes three stages (150 KiB of LDS). Eight waves with
-    // chunked scales, and E4M3 256 x 256 on four waves, compile with spills
-    // or accumulator copies in the main loop and are left out.
+    // 8-strip scale chunks on four stages, and E4M3 256 x 256 on four waves
+    // and four stages, compile with spills or accumulator copies in the main
+    // loop and are left out.
     TG_CONFIG_MX_W(MX_E2M1, 256, 256, 2, 4, 4, 4, false),
     TG_CONFIG_MX_W(MX_E4M3, 256, 256, 2, 4, 3, 4, false),
+    // three stages with scale chunks of 4 strips (16 bytes per row; E4M3
+    // 256 x 256: 160 KiB of LDS)
+    TG_CONFIG_MX_W(MX_E4M3, 256, 256, 2, 4, 3, 4, true),
+    TG_CONFIG_MX_W(MX_E2M1, 256, 256, 2, 4, 3, 4, true),
+    TG_CONFIG_MX_W(MX_E2M1, 256, 256, 2, 2, 3, 4, true),
     TG_CONFIG_MX_W(MX_E4M3, 128, 256, 2, 4, 4, 4, false),
     // scale bytes staged 8 strips at a time (K % 512 == 0)
     TG_CONFIG_MX(MX_E2M1, 256, 256, 4, true),

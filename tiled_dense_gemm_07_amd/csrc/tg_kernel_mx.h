@@ -28,10 +28,10 @@
 //    lane supplies;
 //  * scale bytes reach LDS either per strip (one dword per row: 64 rows per
 //    copy, each in its own cache line) or, when K % 512 == 0, in chunks of 8
-//    strips (32 bytes per row, 16 per lane: 32 rows per copy), double
-//    buffered; the chunks cut the cache-line accesses of the scale copies
-//    eightfold, and those accesses, not the bytes, are what the address unit
-//    spends its cycles on;
+//    strips (32 bytes per row, 16 per lane: 32 rows per copy; 4 strips and 16
+//    bytes per row on a three-stage ring), double buffered; the chunks cut
+//    the cache-line accesses of the scale copies four- to eightfold, and those
+//    accesses, not the bytes, are what the address unit spends its cycles on;
 //  * one barrier per strip after its first MFMA publishes strip t + 1 and frees
 //    strip t - 1; copies of strip t + NS - 1 are staggered across waves and
 //    slots.  K must be a multiple of 128 and the scale rows 4-byte aligned;
@@ -63,9 +63,15 @@ struct DmaMx {
     static constexpr int A_ROWB = A8 ? 128 : 64;  // code bytes per row per strip
     static constexpr int A_STAGE = BM * A_ROWB;
     static constexpr int W_STAGE = BN * 64;
-    static constexpr int SCH = 8;                        // strips per scale chunk (CS)
-    static constexpr int SA_STAGE = CS ? BM * 32 : BM * 4;  // bytes per scale buffer
-    static constexpr int SW_STAGE = CS ? BN * 32 : BN * 4;
+    // CS: strips per scale chunk (8, or 4 on a three-stage ring, whose LDS
+    // has room for 16 bytes per row only), scale bytes per row and chunk, and
+    // the lanes and rows one 16-byte chunk copy covers
+    static constexpr int CH = CS ? (NS == 3 ? 4 : 8) : 1;
+    static constexpr int RB = 4 * CH;
+    static constexpr int LPR = CS ? RB / 16 : 1;
+    static constexpr int RPC = 64 / LPR;
+    static constexpr int SA_STAGE = CS ? BM * RB : BM * 4;  // bytes per scale buffer
+    static constexpr int SW_STAGE = CS ? BN * RB : BN * 4;
     static constexpr int NSB = CS ? 2 : NS;                 // scale buffers
     static constexpr int W_REGION = NS * A_STAGE;
     static constexpr int SA_REGION = W_REGION + NS * W_STAGE;
@@ -75,8 +81,8 @@ struct DmaMx {
     static constexpr int JW = W_STAGE / 1024 / NW;
     static constexpr int NSA = CS ? 0 : BM * 4 / 256;   // per-strip dword scale copies of A
     static constexpr int NSW = CS ? 0 : BN * 4 / 256;
-    static constexpr int NCA = CS ? BM / 32 : 0;        // chunk copies of A scales (CS)
-    static constexpr int NCW = CS ? BN / 32 : 0;
+    static constexpr int NCA = CS ? BM / RPC : 0;       // chunk copies of A scales (CS)
+    static constexpr int NCW = CS ? BN / RPC : 0;
     static constexpr int JS = (NCA + NCW) / NW;         // chunk copies per wave
     static constexpr int NM = FM * FN;          // MFMAs per 64-k step
     static constexpr int SLOTS = 2 * NM;        // MFMAs per strip
@@ -88,9 +94,7 @@ struct DmaMx {
     static_assert(CS || (NSA >= 1 && NSA <= NW && NSW >= 1 && NSW <= NW),
                   "scale copies: one per wave at most");
     static_assert(!CS || ((NCA + NCW) % NW == 0 && JS >= 1), "chunk copies split evenly");
-    static_assert(NS == 4 || (NS == 3 && !CS),
-                  "four stages, or three with per-strip scale copies (chunked scales track the "
-                  "strip within the chunk by stage)");
+    static_assert(NS == 4 || NS == 3, "three or four stages");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(SA_REGION % 32 == 0 && SW_REGION % 32 == 0 && SA_STAGE % 32 == 0,
                   "scale regions 32-byte aligned (the chunk halves are selected by an xor)");
@@ -107,11 +111,11 @@ struct DmaMx {
         u32 w_off[JW];
         u32 sa_off, sw_off;       // per-strip scale copies (!CS)
         u32 s_off[CS ? JS : 1];   // chunk copies (CS): row offset + 16-byte half
-        u32 s_half[CS ? JS : 1];  //   and that half (0, 1)
+        u32 s_half[CS ? JS : 1];  //   and that half (0, 1; always 0 for 4-strip chunks)
         u32 a_rd[2][A8 ? 2 : 1];  // [k-step][part]: code chunks of this lane (stage 0, fm 0)
         u32 w_rd[2];              // [k-step] (stage 0, fn 0)
         u32 sa_rd, sw_rd;         // this lane's row of scale bytes (buffer 0, block 0;
-                                  // CS: strips 0-3 of the chunk, strips 4-7 at ^ 16)
+                                  // 8-strip chunks: strips 0-3, strips 4-7 at ^ 16)
         u32 sh[2];                // [k-step]: 8 * lane half + 16 * k-step, the shift that
                                   // brings the lane's scale byte to byte 0
     };
@@ -154,15 +158,17 @@ struct DmaMx {
             L.sw_off = (w < NSW && n0 + row < p.N) ? (u32)(row * (K / 32)) : kOob;
         }
         if constexpr (CS) {
-            // chunk copy g: 32 rows x 32 bytes, lane l -> row g' * 32 + l / 2 at
-            // LDS 16-byte position l & 1, which holds the row's half
-            // (l & 1) ^ bit 3 of the row (two-way bank spread for the reads)
+            // chunk copy g of 8-strip chunks: 32 rows x 32 bytes, lane l -> row
+            // g' * 32 + l / 2 at LDS 16-byte position l & 1, which holds the
+            // row's half (l & 1) ^ bit 3 of the row (two-way bank spread for the
+            // reads); of 4-strip chunks: 64 rows x 16 bytes, lane l -> row
+            // g' * 64 + l
 #pragma unroll
             for (int d = 0; d < JS; ++d) {
                 const int g = w * JS + d;
                 const bool isa = g < NCA;
-                const int row = (isa ? g : g - NCA) * 32 + (lane >> 1);
-                const int half = (lane & 1) ^ ((row >> 3) & 1);
+                const int row = (isa ? g : g - NCA) * RPC + lane / LPR;
+                const int half = LPR == 2 ? (lane & 1) ^ ((row >> 3) & 1) : 0;
                 const bool ok = isa ? (m0 + row < p.M) : (n0 + row < p.N);
                 L.s_off[d] = ok ? (u32)(row * (K / 32) + half * 16) : kOob;
                 L.s_half[d] = (u32)half;
@@ -183,10 +189,13 @@ struct DmaMx {
             }
             L.w_rd[q] = W_REGION + nr * 64 + (((2 * q + h) ^ swz_a(nr)) << 4);
         }
-        if constexpr (CS) {
+        if constexpr (CS && CH == 8) {
             const int xa = (ar >> 3) & 1, xw = (nr >> 3) & 1;
             L.sa_rd = SA_REGION + ar * 32 + (xa << 4);
             L.sw_rd = SW_REGION + nr * 32 + (xw << 4);
+        } else if constexpr (CS) {
+            L.sa_rd = SA_REGION + ar * 16;
+            L.sw_rd = SW_REGION + nr * 16;
         } else {
             L.sa_rd = SA_REGION + ar * 4;
             L.sw_rd = SW_REGION + nr * 4;
@@ -263,9 +272,10 @@ struct DmaMx {
                  r.sw);
     }
 
-    // Chunk copies (CS) of wave W: the scale bytes of strips 8 c .. 8 c + 7 into
-    // buffer c & 1.  A lane's 16 bytes are inside its row or past its end as a
-    // whole (K % 512 == 0); past the end they read as zeros.
+    // Chunk copies (CS) of wave W: the scale bytes of strips CH c .. CH c +
+    // CH - 1 into buffer c & 1.  A lane's 16 bytes (four strips) are inside its
+    // row or past its end as a whole (K % 512 == 0); past the end they read as
+    // zeros.
     template <int W>
     static __device__ __forceinline__ void issue_chunk(const Lane& L, const Res& r,
                                                        const GemmParams& p, int c, int d,
@@ -273,8 +283,8 @@ struct DmaMx {
     {
         const int g = W * JS + d;
         const u32 buf = (u32)(c & 1);
-        const bool ok = (u32)(2 * c) + L.s_half[d] < (u32)(p.K / 512);
-        const u32 off = ok ? L.s_off[d] + (u32)(c * 32) : kOob;
+        const bool ok = (u32)(c * (CH / 4)) + L.s_half[d] < (u32)(p.K / 512);
+        const u32 off = ok ? L.s_off[d] + (u32)(c * RB) : kOob;
         if (g < NCA)
             dma16(smem0 + SA_REGION + buf * SA_STAGE + g * 1024, off, r.sa);
         else
@@ -315,18 +325,22 @@ struct DmaMx {
     {
         typedef __attribute__((address_space(3))) u32 lds_u32;
         u32 ra, rw;
-        if constexpr (CS) {
+        if constexpr (CS && CH == 8) {
             // strips 4-7 of the chunk: the other 16-byte half of the row (the
             // regions and rows are 32-byte aligned, so an xor selects it)
             const u32 hi = (u32)(u & 4) << 2;
             const u32 buf = (u32)((u >> 3) & 1);
             ra = (L.sa_rd ^ hi) + buf * SA_STAGE + SL * 4;
             rw = (L.sw_rd ^ hi) + buf * SW_STAGE + SL * 4;
+        } else if constexpr (CS) {
+            const u32 buf = (u32)((u >> 2) & 1);
+            ra = L.sa_rd + buf * SA_STAGE + SL * 4;
+            rw = L.sw_rd + buf * SW_STAGE + SL * 4;
         } else {
             ra = L.sa_rd + SL * SA_STAGE;
             rw = L.sw_rd + SL * SW_STAGE;
         }
-        constexpr int RA = CS ? 32 : 4;  // LDS bytes per scale row
+        constexpr int RA = CS ? RB : 4;  // LDS bytes per scale row
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             S.a[fm] = *(const lds_u32*)(sm + ra + fm * 32 * RA);
@@ -364,10 +378,12 @@ struct DmaMx {
     // with F1.  Slot 0 waits for strip t + 1's copies and barriers; k-step 0's
     // slots read k-step 1 into F1; k-step 1's slots read strip t + 1's scales
     // (into SC[(ST + 1) & 1]) and k-step 0 (into F0); copies of strip
-    // t + NS - 1 are staggered over the slots.  CS: strip 8 c + 1 also copies
+    // t + NS - 1 are staggered over the slots.  CS: strip CH c + 1 also copies
     // scale chunk c + 1 (into the buffer chunk c - 1 used, whose last reads
-    // were before strip 8 c - 1), so the wait of strip 8 c + 2 leaves those
-    // copies in flight too, and chunk c + 1 has landed by strip 8 c + 3.  P is
+    // were before strip CH c - 1).  On four stages the wait of strip CH c + 2
+    // leaves those copies in flight too, and chunk c + 1 has landed by strip
+    // CH c + 3; on three stages every strip's wait takes all copies, so it has
+    // landed by strip CH c + 2.  P is
     // the strip's place in its chunk (CS) as a compile-time constant: a
     // run-time test there would split the strip into branches, and the
     // compiler then sinks the MFMAs of whole strips past them, away from the
@@ -382,7 +398,7 @@ struct DmaMx {
         constexpr int CPY = (ST + NS - 1) % NS;
         // scale slot of strip t + 1: its position in the chunk (CS, NS == 4)
         // or its stage
-        constexpr int SNX = CS ? (ST + 1) & 3 : (ST + 1) % NS;
+        constexpr int SNX = CS ? (P + 1) & 3 : (ST + 1) % NS;
         constexpr int STEPS = NM > NRD ? NM : NRD;
         StripOff o;
 #pragma unroll
@@ -412,7 +428,7 @@ struct DmaMx {
                 }
             }
             if (slot == 0) {
-                if constexpr (CS && P == 2)
+                if constexpr (CS && NS == 4 && P == 2)
                     wait_copies_barrier<Copies<W>::AHEAD + JS>();
                 else
                     wait_copies_barrier<Copies<W>::AHEAD>();
@@ -423,7 +439,7 @@ struct DmaMx {
 #pragma unroll
                 for (int d = 0; d < JS; ++d) {
                     if (slot == 2 * d + 1) {
-                        issue_chunk<W>(L, res, p, (t >> 3) + 1, d, smem0);
+                        issue_chunk<W>(L, res, p, t / CH + 1, d, smem0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -464,7 +480,37 @@ struct DmaMx {
         // The strip count is rounded up to a whole number of loop bodies (NS
         // strips, 6 for NS == 3 so that the scale registers alternate per
         // strip): strips at or past KT copy only zeros, which add nothing.
-        if constexpr (CS) {
+        if constexpr (CS && NS == 3) {
+            // 12 strips (stage, place in the 4-strip chunk and scale register
+            // set all repeat), then the 4 or 8 left (K % 512 == 0)
+            int t = 0;
+            for (; t + 12 <= KT; t += 12) {
+                strip<0, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<0, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+                strip<1, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t + 4, smem0);
+                strip<2, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 5, smem0);
+                strip<0, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 6, smem0);
+                strip<1, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 7, smem0);
+                strip<2, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t + 8, smem0);
+                strip<0, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 9, smem0);
+                strip<1, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 10, smem0);
+                strip<2, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 11, smem0);
+            }
+            if (t + 4 <= KT) {
+                strip<0, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t, smem0);
+                strip<1, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 1, smem0);
+                strip<2, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 2, smem0);
+                strip<0, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 3, smem0);
+                if (t + 8 <= KT) {
+                    strip<1, 0, W, 0>(acc, F0, F1, SC, L, res, sm, p, t + 4, smem0);
+                    strip<2, 1, W, 1>(acc, F0, F1, SC, L, res, sm, p, t + 5, smem0);
+                    strip<0, 0, W, 2>(acc, F0, F1, SC, L, res, sm, p, t + 6, smem0);
+                    strip<1, 1, W, 3>(acc, F0, F1, SC, L, res, sm, p, t + 7, smem0);
+                }
+            }
+        } else if constexpr (CS) {
             // whole chunks of 8 strips, then 4 (K % 512 == 0)
             int t = 0;
             for (; t + 8 <= KT; t += 8) {
