@@ -63,17 +63,18 @@ CLOCK_MS = 400.0    # back-to-back launches while the shader clock is recorded
 
 def load_traffic(workload: str):
     """Fabric bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken with the configuration the library launches now and on that
-    kernel's current sources; else None."""
+    it was taken with the configuration and swizzle group the library launches
+    now and on that kernel's current sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    from tiled_dense_gemm_07_amd.traffic import source_hash, workload_config
+    from tiled_dense_gemm_07_amd.traffic import source_hash, workload_launch
 
-    config = workload_config(workload)
-    if rec.get("config") != config or rec.get("source_hash") != source_hash(config):
+    config, group = workload_launch(workload)
+    if (rec.get("config") != config or rec.get("group_m") != group or
+            rec.get("source_hash") != source_hash(config)):
         return None
     return rec
 

@@ -79,13 +79,22 @@ def source_hash(config: str) -> str:
     return h.hexdigest()[:16]
 
 
-def workload_config(workload: str) -> str:
-    """The configuration the library launches for the workload (aligned operands)."""
+def workload_launch(workload: str) -> tuple:
+    """(configuration, swizzle group) the library launches for the workload
+    (aligned operands).  The group decides which tiles share an XCD's L2, so
+    a traffic record holds for one group only."""
     from . import binding, synth
 
     w = synth.WORKLOADS[workload]
     op = {"gemm": 0, "dequant_w4": 1, "mx": 2, "sp24": 3}[w.op]
-    return binding.query_config(op, w.M, w.N, w.K, w.dtype).split()[0]
+    q = binding.query_config(op, w.M, w.N, w.K, w.dtype).split()
+    group = [int(x.split("=")[1]) for x in q if x.startswith("group=")]
+    return q[0], (group[0] if group else 0)
+
+
+def workload_config(workload: str) -> str:
+    """The configuration the library launches for the workload (aligned operands)."""
+    return workload_launch(workload)[0]
 
 
 COLD_BYTES = 1 << 30
@@ -198,10 +207,11 @@ def summarize(workload: str, fetch_csv: str, write_csv: str, out: str, cold: boo
     w_factor = COPY_BYTES / (w_copy * 1024.0)
     fetch = f_factor * 1024.0 * sum(f_k) / len(f_k)
     write = w_factor * 1024.0 * sum(w_k) / len(w_k)
-    config = workload_config(workload)
+    config, group = workload_launch(workload)
     rec = {
         "workload": workload,
         "config": config,
+        "group_m": group,
         "source_hash": source_hash(config),
         "copy_bytes": COPY_BYTES,
         "fetch_size_kib_copy": f_copy, "write_size_kib_copy": w_copy,
