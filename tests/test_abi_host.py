@@ -257,10 +257,11 @@ def test_mx_argument_errors(lib):
             assert c(idx, 4, 4, 512, fmt, PA, PS + 4, PB, PQ, PC, 0, None) == NOCFG, name
     assert c(-1, 4, 4, 128, 0, PA, PS, PB, PQ, PC, 0, None) == NOCFG
     buf = ctypes.create_string_buffer(128)
+    # (the workload shapes' exact table entries: test_tuned_table_selects_its_configurations)
     assert lib.tg_query_config_ex(2, 8192, 8192, 8192, 0, 0, 0, buf, 128) == OK
-    assert buf.value.decode().startswith("mx_e2m1_256x256x128_w2x2_s4_")
+    assert buf.value.decode().startswith("mx_e2m1_")
     assert lib.tg_query_config_ex(2, 8192, 8192, 8192, 1, 0, 0, buf, 128) == OK
-    assert buf.value.decode().startswith("mx_e4m3_128x256x128_w2x2_s4_")
+    assert buf.value.decode().startswith("mx_e4m3_")
     assert lib.tg_query_config_ex(2, 300, 200, 256, 1, 0, 0, buf, 128) == OK
     got = buf.value.decode().split()[0]
     assert got.startswith("mx_e4m3_") and not got.endswith(("_sc8", "_sc4")), got  # K % 512

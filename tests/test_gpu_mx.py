@@ -241,18 +241,22 @@ def test_mx_zero_k_and_empty():
 
 @pytest.mark.parametrize("shape", [(300, 264, 384), (300, 264, 512), (200, 136, 1536),
                                    (64, 72, 2560),
-                                   # 4-strip scale chunks on three stages: 12 + 4 strips
-                                   (130, 200, 2048)], ids=lambda s: "x".join(map(str, s)))
+                                   # 4-strip scale chunks on three stages: 12 + 4 strips;
+                                   # 256-k strips: one and two loop passes
+                                   (130, 200, 2048), (130, 264, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_mx_every_config(shape):
     """Every configuration, forced: bit-exact where it runs; the other activation
-    format, and chunked scale staging at K % 512 != 0, refuse the call."""
+    format, chunked scale staging at K % 512 != 0 and 256-k strips at K % 1024
+    != 0 refuse the call."""
     M, N, K = shape
     for fmt in FMTS:
         Aq, As, Wq, Ws = exact_inputs(fmt, M, N, K, 1900 + K)
         want = oracle.encode(BF16, oracle.mx_gemm_f64(fmt, Aq, As, Wq, Ws, relu=True))
         for idx, name in enumerate(binding.list_configs(binding.TG_OP_MX)):
-            if not name.startswith("mx_" + FNAME[fmt]) or (name.endswith(("_sc8", "_sc4")) and
-                                                            K % 512):
+            bk = int(name.split("_")[2].split("x")[2])
+            if (not name.startswith("mx_" + FNAME[fmt]) or
+                    (name.endswith(("_sc8", "_sc4")) and K % 512) or (bk == 256 and K % 1024)):
                 with pytest.raises(binding.TileGemmError):
                     run_mx(fmt, Aq, As, Wq, Ws, relu=True, config=idx)
                 continue

@@ -123,7 +123,7 @@ void config_name(const Config& c, char* buf, size_t len)
              c.bn, c.bk, wav, c.stages, c.group_m,
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
              c.runs ? "_runs" : "",
-             c.chunked_scales ? (mx ? (c.stages == 3 ? "_sc4" : "_sc8")
+             c.chunked_scales ? (mx ? (c.stages <= 3 ? "_sc4" : "_sc8")
                                     : (c.op == TG_OP_SP24 ? "_mc4" : "_sc16"))
                               : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
@@ -178,6 +178,8 @@ bool usable(const Config& c, const Call& q)
         // copies, or 16-byte chunk copies that never straddle a row end
         if (c.chunked_scales && (q.K % 512 != 0 || !q.ws16))
             return false;
+        if (c.bk == 256 && q.K % 1024 != 0)
+            return false;  // 256-k strips: whole 4-strip scale chunks
         return c.dtype == q.dtype && q.wide && q.ws4 && q.K % c.bk == 0;
     }
     if (c.op == TG_OP_SP24) {

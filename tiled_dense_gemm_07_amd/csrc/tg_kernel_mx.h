@@ -51,6 +51,48 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 enum MxFmt { MX_E4M3 = 0, MX_E2M1 = 4 };  // the instruction's format codes
 
+// Result blocks of one wave stored straight from the accumulators (C rows
+// that are not whole 16-byte runs): lane l holds row l % 32 and, for element
+// 4 q + e, column 8 q + 4 (l / 32) + e of its 32 x 32 block; ReLU, one
+// rounding to bf16.
+template <int FM, int FN>
+__device__ __forceinline__ void mx_store_direct(const f32x16 (&acc)[FM][FN], const GemmParams& p,
+                                                int mw0, int nw0, int lane)
+{
+    const int lr = lane & 31;
+    const int g = lane >> 5;
+    uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int m = mw0 + fm * 32 + lr;
+        if (m >= p.M)
+            continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = nw0 + fn * 32 + 8 * q + 4 * g;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = acc[fm][fn][4 * q + e];
+                    v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
+                }
+                const int64_t idx = (int64_t)m * p.N + n;
+                if (p.c_vec && n + 3 < p.N) {
+                    *(u32x2*)(C + idx) =
+                        u32x2{pack2(v[0], v[1], DT_BF16), pack2(v[2], v[3], DT_BF16)};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N)
+                            C[idx + e] = cvt1(v[e], DT_BF16);
+                }
+            }
+        }
+    }
+}
+
 template <int AFMT, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, bool CS>
 struct DmaMx {
     static constexpr int BK = 128;
@@ -606,39 +648,7 @@ struct DmaMx {
                                                         lane, sm + w * (WTM * WTN * 2));
             return;
         }
-        // epilogue: m = lane % 32, four consecutive n per accumulator quad
-        const int lr = lane & 31;
-        const int g = lane >> 5;
-        uint16_t* C = (uint16_t*)p.C;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = m0 + wm * WTM + fm * 32 + lr;
-            if (m >= p.M)
-                continue;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * WTN + fn * 32 + 8 * q + 4 * g;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = acc[fm][fn][4 * q + e];
-                        v[e] = (p.relu && !(x > 0.0f)) ? 0.0f : x;
-                    }
-                    const int64_t idx = (int64_t)m * p.N + n;
-                    if (p.c_vec && n + 3 < p.N) {
-                        *(u32x2*)(C + idx) =
-                            u32x2{pack2(v[0], v[1], DT_BF16), pack2(v[2], v[3], DT_BF16)};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.N)
-                                C[idx + e] = cvt1(v[e], DT_BF16);
-                    }
-                }
-            }
-        }
+        mx_store_direct<FM, FN>(acc, p, m0 + wm * WTM, n0 + wn * WTN, lane);
     }
 };
 
