@@ -23,18 +23,18 @@ namespace tg {
             (const void*)&tg::gemm_mx_kernel<FMT, BM, BN, WGM, WGN, NS, GM, CS>, CS           \
     }
 
-// E2M1 x E2M1 on 256-k strips and a two-stage ring, scales in 4-strip chunks
-// (K % 1024 == 0)
-#define TG_CONFIG_MX2(BM, BN, WGM, WGN, GM)                                                  \
+// 256-k strips on a two-stage ring, scales in 4-strip chunks (K % 1024 == 0)
+#define TG_CONFIG_MX2(FMT, BM, BN, WGM, WGN, GM)                                             \
     tg::Config                                                                               \
     {                                                                                        \
-        2, 0, BM, BN, 256, WGM, WGN, 2, GM, true, false, false, 2,                           \
-            (const void*)&tg::gemm_mx2_kernel<BM, BN, WGM, WGN, GM>, true                    \
+        2, (FMT) == MX_E2M1 ? 0 : 1, BM, BN, 256, WGM, WGN, 2, GM, true, false, false, 2,    \
+            (const void*)&tg::gemm_mx2_kernel<FMT, BM, BN, WGM, WGN, GM>, true               \
     }
 
 static const Config kCfg[] = {
-    TG_CONFIG_MX2(256, 256, 2, 2, 4),
-    TG_CONFIG_MX2(256, 256, 2, 4, 4),
+    TG_CONFIG_MX2(MX_E2M1, 256, 256, 2, 2, 4),
+    TG_CONFIG_MX2(MX_E2M1, 256, 256, 2, 4, 4),
+    TG_CONFIG_MX2(MX_E4M3, 128, 256, 2, 2, 4),
     // eight waves (two per SIMD) with per-strip scale copies; E4M3 on
     // 256 x 256 tiles takes three stages (150 KiB of LDS). Eight waves with
     // 8-strip scale chunks on four stages, and E4M3 256 x 256 on four waves

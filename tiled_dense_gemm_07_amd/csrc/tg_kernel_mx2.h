@@ -1,20 +1,24 @@
-// MX-format GEMM, E2M1 activations x E2M1 weights, on 256-k strips and a
-// two-stage LDS ring.
+// MX-format GEMM (E2M1 or E4M3 activations x E2M1 weights) on 256-k strips
+// and a two-stage LDS ring.
 //
 // The same product as tg_kernel_mx.h (the pages' "WFP4" GEMM, "TileLang架构
 // 深度剖析", the performance section, with both operands in OCP MX blocks):
 // C[m][n] = sum_k a(m, k) w(n, k), each 32 k of a row sharing one E8M0 scale,
 // fp32 accumulation, one rounding to bf16, on v_mfma_scale_f32_32x32x64_f8f6f4.
-// What differs is the strip: 256 k instead of 128, so a row's codes for a
-// strip are one whole 128-byte line.  An LDS-DMA copy then covers 8 rows x
-// 128 bytes (8 cache lines) where the 128-k kernel's covers 16 rows x 64 bytes
-// (16 half lines), and the address path, which spends its cycles per line,
-// has half the work per byte; the strip also carries twice the MFMAs per
-// barrier.  The price is the ring: a 256 x 256 tile's strip is 64 KiB, so
-// two stages fill 128 KiB of the 160 KiB LDS, and the scale chunks the rest.
-//  * four 64-k steps per strip; fragment reads of step q: lane (row r, half
-//    h) reads 16-byte chunk 2 q + h of its row, at position (2 q + h) ^
-//    swz8(r) (the copies place chunk c of row r there), conflict-free;
+// What differs is the strip: 256 k instead of 128, so a row's E2M1 codes for
+// a strip are one whole 128-byte line (E4M3: two).  An LDS-DMA copy then
+// covers whole lines (8 rows x 128 bytes, or 4 x 256) where the 128-k
+// kernel's E2M1 copies cover 16 rows x 64 bytes (16 half lines), and the
+// address path, which spends its cycles per line, has half the work per
+// byte; the strip also carries twice the MFMAs per barrier.  The price is the
+// ring: a 256 x 256 E2M1 tile's (or 128 x 256 E4M3 tile's) strip is 64 KiB,
+// so two stages fill 128 KiB of the 160 KiB LDS, and the scale chunks the
+// rest.
+//  * four 64-k steps per strip; fragment reads of step q: E2M1 lane (row r,
+//    half h) reads 16-byte chunk 2 q + h of its row (128-byte rows, chunk c
+//    at position c ^ swz8(r)); E4M3 lane (r, h) reads chunks 4 q + h and
+//    4 q + 2 + h (256-byte rows, chunk c at position c ^ (r & 15)); the
+//    copies place the chunks there, and the reads are conflict-free;
 //  * scales in chunks of 4 strips (32 bytes per row: strips 0, 1 in one
 //    16-byte half, 2, 3 in the other, the halves swapped for rows with bit 3
 //    set), copied with 16-byte copies into one of two buffers during strip
@@ -38,9 +42,10 @@
 
 namespace tg {
 
-template <int BM, int BN, int WGM, int WGN, int GROUP_M>
+template <int AFMT, int BM, int BN, int WGM, int WGN, int GROUP_M>
 struct DmaMx2 {
     static constexpr int BK = 256;
+    static constexpr bool A8 = AFMT == MX_E4M3;
     static constexpr int SL = 4;      // 64-k steps per strip
     static constexpr int CH = 4;      // strips per scale chunk
     static constexpr int NW = WGM * WGN;
@@ -48,8 +53,9 @@ struct DmaMx2 {
     static constexpr int WTN = BN / WGN;
     static constexpr int FM = WTM / 32;
     static constexpr int FN = WTN / 32;
-    static constexpr int ROWB = BK / 2;  // code bytes per row per strip
-    static constexpr int A_STAGE = BM * ROWB;
+    static constexpr int ROWB = BK / 2;  // code bytes per row per strip (E2M1)
+    static constexpr int A_ROWB = A8 ? BK : ROWB;
+    static constexpr int A_STAGE = BM * A_ROWB;
     static constexpr int W_STAGE = BN * ROWB;
     static constexpr int W_REGION = 2 * A_STAGE;
     static constexpr int SA_REGION = W_REGION + 2 * W_STAGE;
@@ -64,7 +70,8 @@ struct DmaMx2 {
     static constexpr int NCW = BN / 32;
     static constexpr int JS = (NCA + NCW) / NW;     // chunk copies per wave
     static constexpr int NM = FM * FN;              // MFMAs per step
-    static constexpr int NRD = FM + FN;             // fragment reads per step
+    static constexpr int NRD_A = FM * (A8 ? 2 : 1);
+    static constexpr int NRD = NRD_A + FN;          // fragment reads per step
     static constexpr int STEPS = NM > NRD ? NM : NRD;  // slots per step
     static constexpr int SLOTS = SL * STEPS;
     static constexpr int CSLOTS = 2 * STEPS;        // copy window: last step of t, first of t + 1
@@ -82,16 +89,20 @@ struct DmaMx2 {
         u32 a_off[JA];
         u32 w_off[JW];
         u32 s_off[JS];    // chunk copies: row offset + 16-byte half
-        u32 a_rd[SL];     // [step]: this lane's code chunk (stage 0, fm 0)
+        u32 a_rd[SL][A8 ? 2 : 1];  // [step][part]: this lane's code chunk (stage 0, fm 0)
         u32 w_rd[SL];     // [step] (stage 0, fn 0)
         u32 sa_rd, sw_rd; // this lane's row in scale buffer 0 (strips 0, 1; 2, 3 at ^ 16)
         u32 sh[2];        // 8 * lane half (+ 16 for odd steps): byte to byte 0
     };
 
     struct Frag {  // one 64-k step
-        u32x4 a[FM];
+        u32x4 a[FM][A8 ? 2 : 1];
         u32x4 w[FN];
     };
+
+    // A chunk swizzle: 128-byte rows (E2M1) as the 16-bit kernel's, 256-byte
+    // rows (E4M3) by the row's low 4 bits
+    static __device__ __forceinline__ int swz_arow(int r) { return A8 ? (r & 15) : swz8(r); }
     struct Scales {  // one strip: a row's 8 scale bytes per block, as read
         u32x2 a[FM];
         u32x2 w[FN];
@@ -102,12 +113,14 @@ struct DmaMx2 {
     {
         const int K = p.K;
         // copy j: rows 8 j' .. + 7, lane l -> row 8 j' + l / 8, LDS 16-byte
-        // position l & 7, which holds code chunk (l & 7) ^ swz8(row)
+        // position l & 7, which holds code chunk (l & 7) ^ swz8(row); E4M3 A:
+        // rows 4 j' .., lane l -> row 4 j' + l / 16, position l & 15
 #pragma unroll
         for (int j = 0; j < JA; ++j) {
-            const int row = (w * JA + j) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz8(row);
-            L.a_off[j] = (m0 + row < p.M) ? (u32)(row * (K / 2) + c * 16) : kOob;
+            constexpr int CPR = A8 ? 16 : 8;  // 16-byte chunks per row
+            const int row = (w * JA + j) * (64 / CPR) + lane / CPR;
+            const int c = (lane % CPR) ^ swz_arow(row);
+            L.a_off[j] = (m0 + row < p.M) ? (u32)(row * (A8 ? K : K / 2) + c * 16) : kOob;
         }
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
@@ -131,8 +144,14 @@ struct DmaMx2 {
         const int nr = wn * WTN + (lane & 31);
 #pragma unroll
         for (int q = 0; q < SL; ++q) {
-            // 32 codes of step q, lane half h: k = 64 q + 32 h
-            L.a_rd[q] = ar * ROWB + (((2 * q + h) ^ swz8(ar)) << 4);
+            if constexpr (A8) {
+                // bytes 0..15: k = 64 q + 16 h; bytes 16..31: k = 64 q + 32 + 16 h
+                L.a_rd[q][0] = ar * A_ROWB + (((4 * q + h) ^ swz_arow(ar)) << 4);
+                L.a_rd[q][1] = ar * A_ROWB + (((4 * q + 2 + h) ^ swz_arow(ar)) << 4);
+            } else {
+                // 32 codes of step q, lane half h: k = 64 q + 32 h
+                L.a_rd[q][0] = ar * A_ROWB + (((2 * q + h) ^ swz_arow(ar)) << 4);
+            }
             L.w_rd[q] = W_REGION + nr * ROWB + (((2 * q + h) ^ swz8(nr)) << 4);
         }
         L.sa_rd = SA_REGION + ar * 32 + (((ar >> 3) & 1) << 4);
@@ -145,7 +164,7 @@ struct DmaMx2 {
         __amdgpu_buffer_rsrc_t a, w, sa, sw;
     };
     struct StripOff {
-        u32 c;  // byte offset of the strip in a row of codes
+        u32 a, w;  // byte offsets of the strip in a row of A codes, of W codes
         bool valid;
     };
 
@@ -154,7 +173,7 @@ struct DmaMx2 {
         using Base = DmaMx<MX_E2M1, BM, BN, 2, 2, 4, GROUP_M, false>;
         const int K = p.K;
         Res r;
-        r.a = Base::band(p.A, m0, p.M - m0, K / 2);
+        r.a = Base::band(p.A, m0, p.M - m0, A8 ? K : K / 2);
         r.w = Base::band(p.B, n0, p.N - n0, K / 2);
         r.sa = Base::band(p.As, m0, p.M - m0, K / 32);
         r.sw = Base::band(p.Bs, n0, p.N - n0, K / 32);
@@ -164,7 +183,7 @@ struct DmaMx2 {
     static __device__ __forceinline__ StripOff strip_off(const GemmParams& p, int strip)
     {
         const int k0 = strip * BK;
-        return StripOff{(u32)(k0 / 2), k0 < p.K};
+        return StripOff{(u32)(A8 ? k0 : k0 / 2), (u32)(k0 / 2), k0 < p.K};
     }
 
     // Copy d of wave W for strip offset o into stage ST.
@@ -173,11 +192,11 @@ struct DmaMx2 {
                                                       const StripOff& o, int d, u32 smem0)
     {
         if (d < JA)
-            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, o.valid ? L.a_off[d] + o.c : kOob,
+            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, o.valid ? L.a_off[d] + o.a : kOob,
                   r.a);
         else
             dma16(smem0 + W_REGION + ST * W_STAGE + (W * JW + d - JA) * 1024,
-                  o.valid ? L.w_off[d - JA] + o.c : kOob, r.w);
+                  o.valid ? L.w_off[d - JA] + o.w : kOob, r.w);
     }
 
     // Chunk copy d of wave W: the scale bytes of strips 4 c .. 4 c + 3 into
@@ -200,11 +219,14 @@ struct DmaMx2 {
     template <int ST, int Q>
     static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i)
     {
-        if (i < FM)
-            F.a[i] = *(const lds_u32x4*)(sm + L.a_rd[Q] + ST * A_STAGE + i * 32 * ROWB);
-        else
-            F.w[i - FM] =
-                *(const lds_u32x4*)(sm + L.w_rd[Q] + ST * W_STAGE + (i - FM) * 32 * ROWB);
+        if (i < NRD_A) {
+            const int fm = A8 ? (i >> 1) : i, part = A8 ? (i & 1) : 0;
+            F.a[fm][part] = *(const lds_u32x4*)(sm + L.a_rd[Q][part] + ST * A_STAGE +
+                                                fm * 32 * A_ROWB);
+        } else {
+            F.w[i - NRD_A] =
+                *(const lds_u32x4*)(sm + L.w_rd[Q] + ST * W_STAGE + (i - NRD_A) * 32 * ROWB);
+        }
     }
 
     // Scale bytes of strip u, its place P in the chunk at compile time.
@@ -231,11 +253,13 @@ struct DmaMx2 {
                                                     const Scales& S, const Lane& L, int i)
     {
         const int fm = i / FN, fn = i % FN;
-        const u32x4 wv = F.w[fn], av = F.a[fm];
+        const u32x4 wv = F.w[fn], lo = F.a[fm][0], hi = F.a[fm][A8 ? 1 : 0];
         const i32x8 wop = {(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3], 0, 0, 0, 0};
-        const i32x8 aop = {(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0};
+        const i32x8 aop = A8 ? i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}
+                             : i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
         acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            wop, aop, acc[fm][fn], MX_E2M1, MX_E2M1, 0, (int)(S.w[fn][Q >> 1] >> L.sh[Q & 1]), 0,
+            wop, aop, acc[fm][fn], MX_E2M1, AFMT, 0, (int)(S.w[fn][Q >> 1] >> L.sh[Q & 1]), 0,
             (int)(S.a[fm][Q >> 1] >> L.sh[Q & 1]));
     }
 
@@ -410,14 +434,14 @@ struct DmaMx2 {
     }
 };
 
-template <int BM, int BN, int WGM, int WGN, int GROUP_M>
+template <int AFMT, int BM, int BN, int WGM, int WGN, int GROUP_M>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
                           amdgpu_waves_per_eu(WGM * WGN > 4 ? 2 : 1,
                                               WGM * WGN > 4 ? 2 : 1))) void
 gemm_mx2_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
-    DmaMx2<BM, BN, WGM, WGN, GROUP_M>::run(p);
+    DmaMx2<AFMT, BM, BN, WGM, WGN, GROUP_M>::run(p);
     stamp_end(p, clk);
 }
 
