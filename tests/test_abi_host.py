@@ -100,7 +100,7 @@ def test_forced_config_errors(lib):
 
 
 def test_forced_dequant_config_requirements(lib):
-    """The DMA dequant kernel needs whole 128-wide strips and 4-byte aligned
+    """The DMA dequant kernel needs whole 128- or 256-wide strips and 4-byte aligned
     scale bytes; the weight-streaming kernel needs K % bk == 0.  A forced
     configuration that cannot run the call is refused before any HIP call."""
     names = binding.list_configs(1, 2)
@@ -111,10 +111,13 @@ def test_forced_dequant_config_requirements(lib):
             assert d(idx, 64, 64, 96, PA, PB, PS, PC, 0, None) == NOCFG, name
         if name.endswith("_dma"):
             assert d(idx, 64, 64, 256, PA, PB, PS + 2, PC, 0, None) == NOCFG, name
-        if name.endswith("_sc16"):
+        if name.endswith("_sc16") or name.endswith("_sc8"):
             # scale blocks: K % 512 == 0 and 16-byte aligned scale rows
             assert d(idx, 64, 64, 256, PA, PB, PS, PC, 0, None) == NOCFG, name
             assert d(idx, 64, 64, 512, PA, PB, PS + 4, PC, 0, None) == NOCFG, name
+        if "x256_" in name and name.startswith("w4_bf16_64x128x256_"):
+            # 256-k strips: K % 256 == 0
+            assert d(idx, 64, 64, 640, PA, PB, PS, PC, 0, None) == NOCFG, name
 
 
 def test_gemm_ex_argument_errors(lib):

@@ -115,7 +115,7 @@ def _w4_config_fits(name, K):
     bk = int(name.split("_")[2].split("x")[2])
     if ("_dma" in name or "_gemv" in name) and K % bk:
         return False
-    return not ("_sc16" in name and K % 512)
+    return not (("_sc16" in name or "_sc8" in name) and K % 512)
 
 
 def test_every_w4_config():
@@ -151,6 +151,9 @@ def test_dequant_small(shape, integer):
                                    # scale blocks of 16 strips: a row's scale bytes end
                                    # inside the first block / a second, partial block
                                    (300, 264, 1536), (130, 200, 2560),
+                                   # 256-k strips on three stages: 8 strips (a six-strip
+                                   # loop pass and two more), 12 (two passes)
+                                   (70, 136, 2048), (64, 136, 3072),
                                    # N % 8 != 0: results stored directly, not staged
                                    (100, 130, 1024),
                                    # few rows: partial 512-wide rounds of the

@@ -124,7 +124,7 @@ void config_name(const Config& c, char* buf, size_t len)
              c.pipe == 1 ? "_deep" : (c.pipe == 2 ? "_dma" : (c.pipe == 3 ? "_gemv" : "")),
              c.runs ? "_runs" : "",
              c.chunked_scales ? (mx ? (c.stages <= 3 ? "_sc4" : "_sc8")
-                                    : (c.op == TG_OP_SP24 ? "_mc4" : "_sc16"))
+                                    : (c.op == TG_OP_SP24 ? "_mc4" : (c.bk == 256 ? "_sc8" : "_sc16")))
                               : lay[(c.ta ? 2 : 0) + (c.tb ? 1 : 0)],
              c.wide ? "" : "_narrow");
 }

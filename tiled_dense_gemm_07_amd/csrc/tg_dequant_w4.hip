@@ -32,6 +32,12 @@ static const Config kCfg[] = {
     tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 2, 16>, true, 2},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4, 1, 16>, true, 1},
     tg::Config{1, DT_BF16, 64, 128, 128, 1, 1, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 1, 4, 4, 4, 16>, true, 4},
+    // 256-k strips on a three-stage ring, scale blocks of 8 strips (K % 512 == 0,
+    // 16-byte aligned scale rows): half the barriers, whole 128-byte code rows
+    tg::Config{1, DT_BF16, 64, 128, 256, 1, 2, 3, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 3, 4, 2, 8, 256>, true, 2},
+    tg::Config{1, DT_BF16, 64, 128, 256, 2, 2, 3, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 3, 4, 2, 8, 256>, true, 2},
+    tg::Config{1, DT_BF16, 64, 128, 256, 1, 1, 3, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 1, 3, 4, 4, 8, 256>, true, 4},
+    tg::Config{1, DT_BF16, 64, 128, 256, 2, 2, 3, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 3, 4, 1, 8, 256>, true, 1},
     // eight waves (two per SIMD): one wave's MFMAs run while the other waits
     tg::Config{1, DT_BF16, 64, 128, 128, 1, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 1, 2, 4, 4, 4, 16>, true, 4},
     tg::Config{1, DT_BF16, 64, 128, 128, 2, 2, 4, 4, true, false, false, 2, (const void*)&dma_w4_kernel<64, 128, 2, 2, 4, 4, 2, 16>, true, 2},

@@ -113,32 +113,14 @@ struct GemvW4 {
             const int rounds = (K + ROUND - 1) / ROUND;
             for (int r = w; r < rounds; r += NWAVE) {
                 const int kr = r * ROUND;
-                // issue all loads of the round first (8 KiB of codes per wave in flight)
+                // every code load of the round is issued before the first is
+                // consumed (8 KiB per wave in flight), after the activation
+                // fragments of steps 0 and 1 (16 bytes of row m0 + ln per
+                // lane) and the scales: vector loads complete in order, so
+                // steps 0 and 1 wait only for their own codes, not for the
+                // whole round.
                 u32x4 code[NG][4];  // [group][c]: codes of k in [kr + 128 c + 32 g, +32)
                 u32x4 sc[NG];       // the row's 16 scale bytes of the round, block 4 c + h
-#pragma unroll
-                for (int q = 0; q < NG; ++q) {
-                    const u32 rowoff = (u32)((16 * q + ln) * rowb);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int k = kr + 128 * c + 32 * g;  // K is a multiple of 32
-                        code[q][c] = buf_load16(wrs, k < K ? rowoff + (u32)k / 2 : kOob);
-                    }
-                    const u32 soff = (u32)((16 * q + ln) * srow + kr / 32);
-                    if (DWORD_SCALES && kr + ROUND <= K) {
-                        sc[q] = buf_load16(srs, soff);  // 4-byte aligned rows
-                    } else if (DWORD_SCALES) {
-                        // the last, partial round: dword i (blocks 4 i ..) only
-                        // while inside the row (K % 128 == 0 for aligned rows)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sc[q][i] = buf_load4(srs, kr + 128 * i < K ? soff + 4 * i : kOob);
-                    }
-                    // byte-aligned scale rows: their bytes are loaded per step below
-                }
-                // activation fragments of step (c, h): 16 bytes of row m0 + ln; those
-                // of steps c and c + 1 are in flight while step c - 1 computes (all
-                // sixteen at once would not fit the 128 registers of a wave here)
                 u32x4 af[16];
                 const auto load_af = [&](int c) {
 #pragma unroll
@@ -148,12 +130,41 @@ struct GemvW4 {
                             buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
                     }
                 };
+                const auto load_codes = [&](int c) {
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) {
+                        const u32 rowoff = (u32)((16 * q + ln) * rowb);
+                        const int k = kr + 128 * c + 32 * g;  // K is a multiple of 32
+                        code[q][c] = buf_load16(wrs, k < K ? rowoff + (u32)k / 2 : kOob);
+                    }
+                };
                 load_af(0);
                 load_af(1);
-                // every weight load of the round is in flight before the first is consumed
+                if constexpr (DWORD_SCALES) {
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) {
+                        const u32 soff = (u32)((16 * q + ln) * srow + kr / 32);
+                        if (kr + ROUND <= K) {
+                            sc[q] = buf_load16(srs, soff);  // 4-byte aligned rows
+                        } else {
+                            // the last, partial round: dword i (blocks 4 i ..) only
+                            // while inside the row (K % 128 == 0 for aligned rows)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                sc[q][i] = buf_load4(srs, kr + 128 * i < K ? soff + 4 * i : kOob);
+                        }
+                    }
+                }
+                // (byte-aligned scale rows: their bytes are loaded per step below)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    load_codes(c);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
+                    // the activation fragments of step c + 2 are loaded during
+                    // step c (all sixteen at once would not fit the 128
+                    // registers of a wave)
                     if (c + 2 < 4)
                         load_af(c + 2);
                     __builtin_amdgcn_sched_barrier(0);
@@ -192,17 +203,22 @@ struct GemvW4 {
             for (int r = w; r < rounds; r += NWAVE) {
                 const int kq = r * ROUND + 128 * g;  // this lane's first k
                 const bool kv = kq < K;              // K is a multiple of 32; kq, +32, ... may pass it
-                // issue all weight loads of the round first (8 KiB per wave in flight)
-                u32x4 code[NG][4];
+                // every load of the round is issued before the first is
+                // consumed (8 KiB of codes per wave in flight), in the order
+                // the steps consume them: vector loads complete in order, so a
+                // step waits only for its own loads and those before them.
+                // The activation fragments (16 bytes of row m0 + ln at the
+                // lane's k, mostly from L2) and the scales come first, then
+                // the codes of group 0, then those of group 1.
+                u32x4 af[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int k = kq + 8 * j;
+                    af[j] = buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
+                }
                 u32 sc[NG];
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
-                    const u32 rowoff = (u32)((16 * q + ln) * rowb);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const bool v = kq + 32 * c < K;
-                        code[q][c] = buf_load16(wrs, v ? rowoff + (u32)(kq + 32 * c) / 2 : kOob);
-                    }
                     const u32 soff = (u32)((16 * q + ln) * srow + kq / 32);
                     if (DWORD_SCALES) {
                         sc[q] = buf_load4(srs, kv ? soff : kOob);
@@ -214,12 +230,15 @@ struct GemvW4 {
                         sc[q] = s4;
                     }
                 }
-                // activation fragments: 16 bytes of row m0 + ln at the same k
-                u32x4 af[16];
+                u32x4 code[NG][4];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int k = kq + 8 * j;
-                    af[j] = buf_load16(ars, (arow && k < K) ? (u32)(ln * K + k) * 2u : kOob);
+                for (int q = 0; q < NG; ++q) {
+                    const u32 rowoff = (u32)((16 * q + ln) * rowb);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const bool v = kq + 32 * c < K;
+                        code[q][c] = buf_load16(wrs, v ? rowoff + (u32)(kq + 32 * c) / 2 : kOob);
+                    }
                 }
                 // every load of the round is in flight before the first is consumed
                 __builtin_amdgcn_sched_barrier(0);
