@@ -100,8 +100,8 @@ def default_group(bm: int, bn: int) -> int:
 # (k-contiguous LDS rows), B row-major (n-contiguous LDS rows read by the
 # transposing LDS read), 32 or 64 k per strip, 2-4 stages, 4 or 8 waves.
 # ---------------------------------------------------------------------------
-DMA_BM = (128, 192, 256)
-DMA_BN = (128, 256)
+DMA_BM = (64, 128, 192, 256)
+DMA_BN = (64, 128, 256)
 DMA_BK = (32, 64)
 DMA_WAVES = ((2, 2), (2, 4), (4, 2))
 DMA_STAGES = (2, 3, 4)
@@ -140,8 +140,8 @@ def dma_candidates(dtype: int):
                         sa, sb = bm * bk * 2, bn * bk * 2
                         if sa % (1024 * nw) or sb % (1024 * nw):
                             continue  # whole 1 KiB copies per wave
-                        if not 16 <= bn // 8 <= 64:
-                            continue  # n-contiguous LDS rows of 256 to 1024 bytes
+                        if not 8 <= bn // 8 <= 64:
+                            continue  # n-contiguous LDS rows of 128 to 1024 bytes
                         lds = ns * (sa + sb)
                         if lds > LDS_BYTES:
                             continue

@@ -83,6 +83,11 @@ __device__ __forceinline__ void wait_all_barrier()
 // masks 0, 6, 10, 12, distinct in bits 1-2 and in bits 2-3.
 __device__ __forceinline__ int swz_a(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 1) * 6) ^ ((k & 2) * 5); }
+// x-contiguous rows of 128 bytes (64 columns): two rows share a 256-byte bank
+// line, so of the four k-rows one half of a transposing read touches (32
+// columns = 4 chunks each), rows k and k + 2 must take complementary chunk
+// halves: chunk mask 4 on rows with k & 2.
+__device__ __forceinline__ int swz_b8(int k) { return (k & 2) * 2; }
 
 // 128-byte rows (8 chunks): chunk c of row r goes to position c ^ swz8(r).  Only
 // the low five bits of r enter, so rows 32 apart (the 32-row blocks of a wave
@@ -115,9 +120,10 @@ struct DmaOperand {
     static constexpr int RPB = 64 / LPR;              // LDS rows per 1 KiB copy
     static constexpr int NRD = KMAJ ? FX : 2 * FX;    // LDS reads per slab
     static_assert(J >= 1 && STAGE % (1024 * NW) == 0, "strips split into whole 1 KiB copies per wave");
-    static_assert(KMAJ || (LPR >= 16 && LPR <= 64), "x-contiguous rows of 256 to 1024 bytes");
+    static_assert(KMAJ || (LPR >= 8 && LPR <= 64), "x-contiguous rows of 128 to 1024 bytes");
 
     static __device__ __forceinline__ int kswz(int row) { return BK == 32 ? swz_a(row) : swz8(row); }
+    static __device__ __forceinline__ int xswz(int k) { return LPR == 8 ? swz_b8(k) : swz_b(k); }
 
     struct Lane {
         u32 off[J];   // copy offsets within a strip (out of range past the x extent)
@@ -144,7 +150,7 @@ struct DmaOperand {
                 L.kk[j] = c * 8;
                 L.off[j] = (x0 + row < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
             } else {
-                const int c = (lane % LPR) ^ swz_b(row);
+                const int c = (lane % LPR) ^ xswz(row);
                 L.off[j] = (x0 + c * 8 < xtot) ? (u32)(row * ld + c * 8) * 2u : kOob;
             }
         }
@@ -162,7 +168,7 @@ struct DmaOperand {
 #pragma unroll
             for (int f = 0; f < FX; ++f) {
                 const int x = wx0 + f * 32 + 16 * (g & 1) + 4 * (t & 3);
-                L.rd[f] = region + k * (X * 2) + (((x >> 3) ^ swz_b(k)) << 4) + (x & 7) * 2;
+                L.rd[f] = region + k * (X * 2) + (((x >> 3) ^ xswz(k)) << 4) + (x & 7) * 2;
             }
         }
     }
