@@ -44,7 +44,7 @@ def test_candidates_fit_the_budgets(dt):
             lds = c.stages * (c.bm + c.bn) * c.bk * 2
             assert (c.bm * c.bk * 2) % (1024 * nw) == 0 and (c.bn * c.bk * 2) % (1024 * nw) == 0
             assert 128 <= c.bn * 2 <= 1024  # n-contiguous LDS rows
-            assert 2 <= c.stages <= 4 and c.bk in (32, 64)
+            assert 2 <= c.stages <= 4 and c.bk in (32, 64, 128)
         else:
             lds = max(2 * (c.bm + c.bn) * c.bk * es, (c.ks - 1) * c.bm * c.bn * 4)
             nslab = c.bk // (2 * (4 if dt == configgen.F32 else 8))

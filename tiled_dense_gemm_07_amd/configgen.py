@@ -98,11 +98,11 @@ def default_group(bm: int, bn: int) -> int:
 # ---------------------------------------------------------------------------
 # LDS-DMA GEMM (DmaGemm in tg_kernel_dma.h): 16-bit operands, A row-major
 # (k-contiguous LDS rows), B row-major (n-contiguous LDS rows read by the
-# transposing LDS read), 32 or 64 k per strip, 2-4 stages, 4 or 8 waves.
+# transposing LDS read), 32, 64 or 128 k per strip, 2-4 stages, 4 or 8 waves.
 # ---------------------------------------------------------------------------
 DMA_BM = (64, 128, 192, 256)
 DMA_BN = (64, 128, 256)
-DMA_BK = (32, 64)
+DMA_BK = (32, 64, 128)
 DMA_WAVES = ((2, 2), (2, 4), (4, 2))
 DMA_STAGES = (2, 3, 4)
 

@@ -96,13 +96,13 @@ __device__ __forceinline__ int swz_b8(int k) { return (k & 2) * 2; }
 __device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 // One operand of the 16-bit DMA kernel: X (BM or BN) output rows/columns by
-// BK (32 or 64) k per strip.  In global memory the operand is either
+// BK (32, 64 or 128) k per strip.  In global memory the operand is either
 // k-contiguous (KMAJ: each of its X rows holds consecutive k; leading
 // dimension K) or x-contiguous (each k row holds consecutive x; leading
 // dimension = the operand's full extent).  The LDS stage keeps the global
 // orientation:
-//  * KMAJ: [X][BK k], rows of 64 bytes (chunk swizzle swz_a) or 128 bytes
-//    (swz8); an MFMA fragment (8 consecutive k of one row per lane) is one
+//  * KMAJ: [X][BK k], rows of 64 bytes (chunk swizzle swz_a), 128 bytes
+//    (swz8) or 256 bytes; an MFMA fragment (8 consecutive k of one row per lane) is one
 //    ds_read_b128.  A copy moves whole row segments of 2 BK bytes; 128-byte
 //    segments are whole cache lines and copy about 1.4x faster than 64-byte
 //    ones;
@@ -112,7 +112,7 @@ __device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 // index l % 32 of a 32-wide block, starting at k = 16 s + 8 (l / 32) in slab s.
 template <bool KMAJ, int X, int WX, int FX, int NW, int BK>
 struct DmaOperand {
-    static_assert(BK == 32 || BK == 64, "strips of 32 or 64 k");
+    static_assert(BK == 32 || BK == 64 || BK == 128, "strips of 32, 64 or 128 k");
     static constexpr int SL = BK / 16;                // MFMA slabs per strip
     static constexpr int STAGE = X * BK * 2;          // bytes per LDS stage
     static constexpr int J = STAGE / 1024 / NW;       // 1 KiB copies per wave per strip
@@ -122,7 +122,13 @@ struct DmaOperand {
     static_assert(J >= 1 && STAGE % (1024 * NW) == 0, "strips split into whole 1 KiB copies per wave");
     static_assert(KMAJ || (LPR >= 8 && LPR <= 64), "x-contiguous rows of 128 to 1024 bytes");
 
-    static __device__ __forceinline__ int kswz(int row) { return BK == 32 ? swz_a(row) : swz8(row); }
+    // k-contiguous rows of 64, 128 or 256 bytes (256: chunk c of row r at
+    // position c ^ (r & 15), so any 16 consecutive rows read 16 distinct
+    // positions and rows 32 apart share the swizzle)
+    static __device__ __forceinline__ int kswz(int row)
+    {
+        return BK == 32 ? swz_a(row) : (BK == 64 ? swz8(row) : (row & 15));
+    }
     static __device__ __forceinline__ int xswz(int k) { return LPR == 8 ? swz_b8(k) : swz_b(k); }
 
     struct Lane {
@@ -251,7 +257,7 @@ __device__ __forceinline__ void store_tile_staged_t(const f32x16 (&acc)[FM][FN],
 }
 
 // TA: A stored [K][M] (C = A^T-stored x B); TB: B stored [N][K].  BK: k per
-// strip (32 or 64); NS: LDS stages (2 .. 5).
+// strip (32, 64 or 128); NS: LDS stages (2 .. 5).
 template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M,
           int BK>
 struct DmaGemm {
