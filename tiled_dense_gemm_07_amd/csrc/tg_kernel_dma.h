@@ -62,6 +62,15 @@ __device__ __forceinline__ void dma16(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t 
                  : "memory");
 }
 
+// The same with a wave-uniform byte offset added to every lane's address
+// (the strip's place in a row band that one buffer resource covers).
+__device__ __forceinline__ void dma16_so(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t rs, u32 soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds),
+                 "v"(voff), "s"(rs), "s"(soff)
+                 : "memory");
+}
+
 // Wait until at most N copies of this wave are in flight, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_copies_barrier()
@@ -136,6 +145,15 @@ struct DmaOperand {
         int kk[KMAJ ? J : 1];  // KMAJ: k (within the strip) of the data each copy lane moves
         int lr;       // x-contiguous: the lane's k row within a copy (k = copy row + lr)
         u32 rd[KMAJ ? SL : FX];  // fragment read offsets (stage 0)
+        __amdgpu_buffer_rsrc_t band;  // KMAJ: the tile's rows over the whole K
+    };
+    // Where one strip's copies read: KMAJ, the tile's row band and the
+    // strip's byte offset in it (set up once per tile, so a strip costs one
+    // scalar multiply); x-contiguous, a resource rebased to the strip's first
+    // k row, so that offsets stay within 31 bits however large the operand.
+    struct Strip {
+        __amdgpu_buffer_rsrc_t rs;
+        u32 so;
     };
     struct Frag {
         u32x4 v[KMAJ ? FX : 1];
@@ -145,8 +163,11 @@ struct DmaOperand {
     // x0: first row/column of the tile; xtot: the operand's full extent;
     // ld: leading dimension in elements; wx0: first row/column of this wave.
     static __device__ __forceinline__ void setup(Lane& L, int x0, int xtot, int ld, int w,
-                                                 int lane, int wx0, u32 region)
+                                                 int lane, int wx0, u32 region, const void* base,
+                                                 int K)
     {
+        if constexpr (KMAJ)
+            L.band = strip_rsrc(base, x0, xtot, ld, K, 0);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int blk = w * J + j;
@@ -192,12 +213,30 @@ struct DmaOperand {
                              clamp_bytes(((int64_t)(K - k0 - 1) * ld + (xtot - x0)) * 2));
     }
 
+    static __device__ __forceinline__ Strip strip(const Lane& L, const void* base, int x0,
+                                                  int xtot, int ld, int K, int k0)
+    {
+        Strip s;
+        if constexpr (KMAJ) {
+            s.rs = L.band;
+            s.so = (u32)k0 * 2u;
+        } else {
+            s.rs = strip_rsrc(base, x0, xtot, ld, K, k0);
+            s.so = 0u;
+        }
+        return s;
+    }
+
     template <int ST>
-    static __device__ __forceinline__ void copy(const Lane& L, __amdgpu_buffer_rsrc_t rs, int krem,
-                                                int d, int w, u32 region_lds)
+    static __device__ __forceinline__ void copy(const Lane& L, const Strip& sr, int krem, int d,
+                                                int w, u32 region_lds)
     {
         const int kk = KMAJ ? L.kk[KMAJ ? d : 0] : (w * J + d) * RPB + L.lr;
-        dma16(region_lds + ST * STAGE + (w * J + d) * 1024, kk < krem ? L.off[d] : kOob, rs);
+        const u32 lds = region_lds + ST * STAGE + (w * J + d) * 1024;
+        if constexpr (KMAJ)
+            dma16_so(lds, kk < krem ? L.off[d] : kOob, sr.rs, sr.so);
+        else
+            dma16(lds, kk < krem ? L.off[d] : kOob, sr.rs);
     }
 
     // LDS read i (0 .. NRD-1) of slab S of stage ST.
@@ -300,24 +339,24 @@ struct DmaGemm {
     static __device__ __forceinline__ void setup(Lane& L, const GemmParams& p, int m0, int n0,
                                                  int w, int lane, int wm, int wn)
     {
-        OA::setup(L.a, m0, p.M, lda(p), w, lane, wm * WTM, 0);
-        OB::setup(L.b, n0, p.N, ldb(p), w, lane, wn * WTN, A_REGION);
+        OA::setup(L.a, m0, p.M, lda(p), w, lane, wm * WTM, 0, p.A, p.K);
+        OB::setup(L.b, n0, p.N, ldb(p), w, lane, wn * WTN, A_REGION, p.B, p.K);
     }
 
-    // Buffer descriptors of one strip, rebased to the strip's first element so
-    // that every offset stays inside 31 bits.
+    // Where the copies of one strip read (per operand, DmaOperand::Strip).
     struct StripRes {
-        __amdgpu_buffer_rsrc_t a, b;
+        typename OA::Strip a;
+        typename OB::Strip b;
         int krem;  // valid k within the strip: [0, krem)
     };
 
     static __device__ __forceinline__ StripRes strip_res(const GemmParams& p, int m0, int n0,
-                                                         int strip)
+                                                         int strip, const Lane& L)
     {
         const int k0 = strip * BK;
         StripRes r;
-        r.a = OA::strip_rsrc(p.A, m0, p.M, lda(p), p.K, k0);
-        r.b = OB::strip_rsrc(p.B, n0, p.N, ldb(p), p.K, k0);
+        r.a = OA::strip(L.a, p.A, m0, p.M, lda(p), p.K, k0);
+        r.b = OB::strip(L.b, p.B, n0, p.N, ldb(p), p.K, k0);
         r.krem = p.K - k0;
         return r;
     }
@@ -338,7 +377,7 @@ struct DmaGemm {
                                                         int m0, int n0, int strip, int w,
                                                         u32 smem0)
     {
-        const StripRes r = strip_res(p, m0, n0, strip);
+        const StripRes r = strip_res(p, m0, n0, strip, L);
 #pragma unroll
         for (int d = 0; d < NCOPY; ++d)
             issue_copy<ST>(L, r, d, w, smem0);
@@ -431,7 +470,7 @@ struct DmaGemm {
             if constexpr (SLOT == 0) {
                 wait_copies_barrier<VM_AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
-                r = strip_res(p, m0, n0, t + NS - 1);
+                r = strip_res(p, m0, n0, t + NS - 1, L);
             }
             // strip t + NS - 1 into the stage strip t - 1 used: copy d of wave
             // W at slot cpos(d, W)
@@ -487,8 +526,8 @@ struct DmaGemm {
     {
         StripRes r, r1;
         if constexpr (NS == 2) {
-            r = strip_res(p, m0, n0, t + 2);
-            r1 = strip_res(p, m0, n0, t + 1);
+            r = strip_res(p, m0, n0, t + 2, L);
+            r1 = strip_res(p, m0, n0, t + 1, L);
         }
         slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
     }
@@ -583,7 +622,7 @@ struct DmaGemm {
         // of strip -1; strip 0 issues the rest)
         issue_copies<0>(L, p, m0, n0, 0, w, smem0);
         if constexpr (NS == 2) {
-            const StripRes r1 = strip_res(p, m0, n0, 1);
+            const StripRes r1 = strip_res(p, m0, n0, 1, L);
 #pragma unroll
             for (int d = 0; d < NCOPY; ++d)
                 if (((d * NW + w) * CSLOTS) / (NCOPY * NW) < STEPS)

@@ -152,7 +152,7 @@ struct DmaSp24 {
         }
         L.i_rd = CS ? I_REGION + ar * 32 + (((ar >> 3) & 1) << 4) : I_REGION + ar * 4;
         L.h16 = 16 * h;
-        OB::setup(L.b, n0, p.N, p.N, w, lane, wn * WTN, B_REGION);
+        OB::setup(L.b, n0, p.N, p.N, w, lane, wn * WTN, B_REGION, p.B, p.K);
     }
 
     // Resources of the tile's row band (values, metadata) for all of K, and
@@ -162,7 +162,7 @@ struct DmaSp24 {
         __amdgpu_buffer_rsrc_t a, i;
     };
     struct StripRes {
-        __amdgpu_buffer_rsrc_t b;
+        typename OB::Strip b;
         u32 ao, io;  // strip byte offsets in a row of values / metadata
         int krem;    // valid dense k within the strip
     };
@@ -189,7 +189,8 @@ struct DmaSp24 {
     {
         const int k0 = strip * BK;
         StripRes r;
-        r.b = OB::strip_rsrc(p.B, n0, p.N, p.N, p.K, k0);
+        r.b.rs = OB::strip_rsrc(p.B, n0, p.N, p.N, p.K, k0);
+        r.b.so = 0u;
         r.ao = (u32)k0;      // k0 / 2 values x 2 bytes
         r.io = (u32)(k0 / 8);
         r.krem = p.K - k0;
