@@ -518,18 +518,20 @@ struct DmaGemm {
     //     and no wave reads strip t's stage again.  The copies of strip t + 2
     //     go into that stage right away, spread over the last slab: they have
     //     a whole strip to land before the barrier of strip t + 1 waits for
-    //     them.
+    //     them.  `carry` holds strip t + 1's resources, computed by the strip
+    //     before as its t + 2; this strip computes t + 2's and leaves them
+    //     there for the next.
     template <int ST, int W>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[2],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
-                                                 int m0, int n0, int t, u32 smem0)
+                                                 int m0, int n0, int t, u32 smem0, StripRes& carry)
     {
-        StripRes r, r1;
-        if constexpr (NS == 2) {
+        StripRes r;
+        if constexpr (NS == 2)
             r = strip_res(p, m0, n0, t + 2, L);
-            r1 = strip_res(p, m0, n0, t + 1, L);
-        }
-        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
+        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r, carry);
+        if constexpr (NS == 2)
+            carry = r;
     }
 
     // The strip loop of wave W (the copy slots differ per wave).  The strip
@@ -541,15 +543,18 @@ struct DmaGemm {
                                                      const GemmParams& p, int m0, int n0, int KT,
                                                      u32 smem0)
     {
+        StripRes carry;
+        if constexpr (NS == 2)
+            carry = strip_res(p, m0, n0, 1, L);
         for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, F, L, sm, p, m0, n0, t, smem0);
-            strip<1, W>(acc, F, L, sm, p, m0, n0, t + 1, smem0);
+            strip<0, W>(acc, F, L, sm, p, m0, n0, t, smem0, carry);
+            strip<1, W>(acc, F, L, sm, p, m0, n0, t + 1, smem0, carry);
             if constexpr (NS > 2)
-                strip<2 % NS, W>(acc, F, L, sm, p, m0, n0, t + 2, smem0);
+                strip<2 % NS, W>(acc, F, L, sm, p, m0, n0, t + 2, smem0, carry);
             if constexpr (NS > 3)
-                strip<3 % NS, W>(acc, F, L, sm, p, m0, n0, t + 3, smem0);
+                strip<3 % NS, W>(acc, F, L, sm, p, m0, n0, t + 3, smem0, carry);
             if constexpr (NS > 4)
-                strip<4 % NS, W>(acc, F, L, sm, p, m0, n0, t + 4, smem0);
+                strip<4 % NS, W>(acc, F, L, sm, p, m0, n0, t + 4, smem0, carry);
         }
     }
 
