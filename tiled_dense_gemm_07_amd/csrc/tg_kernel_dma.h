@@ -315,6 +315,17 @@ struct DmaGemm {
     static constexpr int A_REGION = NS * A_STAGE;
     static constexpr int LDS_BYTES = NS * (A_STAGE + B_STAGE);
     static constexpr int NREAD = OA::NRD + OB::NRD;  // LDS reads per slab
+    // Fragment sets: a ring of RF, each slab reading the one PFD = RF - 1
+    // slabs ahead.  Two sets for most tiles; four for wave tiles of one or
+    // two MFMA blocks on rings of three or more stages and strips of four or
+    // more slabs, whose one or two MFMAs per slab would not cover the LDS
+    // read latency of the next slab.  (Two stages keep two sets: their
+    // barrier sits in the last slab, so no earlier slab may read the next
+    // strip.  With SL >= 4 the first reads of the next strip come after the
+    // barrier in slot 0.)
+    static constexpr int RF = (NS >= 3 && SL >= 4 && FM * FN <= 2) ? 4 : 2;
+    static constexpr int PFD = RF - 1;
+    static_assert((NS * SL) % RF == 0 && PFD < SL, "the fragment ring wraps with the stage cycle");
     static constexpr int NCOPY = OA::J + OB::J;      // copies per wave per strip
     static constexpr int VM_AHEAD = NS >= 3 ? (NS - 3) * NCOPY : 0;  // copies in flight at the barrier
 
@@ -408,27 +419,31 @@ struct DmaGemm {
                 0);
     }
 
-    // Reads of slab S + 1 of stage ST (or, for the last slab, slab 0 of the
-    // next stage NXT) into the fragment set the next slab uses.
+    // Reads of slab S + PFD of stage ST (past the strip's last slab: of the
+    // next stage NXT, which the barrier in slot 0 has published) into the
+    // ring set that slab uses.  Slab S of stage ST uses set (ST SL + S) % RF;
+    // NS SL is a multiple of RF, so the ring continues across strips.
     template <int ST, int NXT, int S>
-    static __device__ __forceinline__ void read_next(Frag (&F)[2], const Lane& L, lds_char* sm,
+    static __device__ __forceinline__ void read_next(Frag (&F)[RF], const Lane& L, lds_char* sm,
                                                      int i)
     {
-        if constexpr (S + 1 < SL)
-            read_one<ST, S + 1>(F[(S + 1) & 1], L, sm, i);
+        constexpr int T = S + PFD;
+        constexpr int SET = (ST * SL + T) % RF;
+        if constexpr (T < SL)
+            read_one<ST, T>(F[SET], L, sm, i);
         else
-            read_one<NXT, 0>(F[0], L, sm, i);
+            read_one<NXT, T - SL>(F[SET], L, sm, i);
     }
 
     // Step i of slab S: its MFMA, then (NS == 2, last slab, first step) the
     // barrier, then its read of the next slab's fragments.
     template <int ST, int NXT, int S, int I>
-    static __device__ __forceinline__ void slab_step(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+    static __device__ __forceinline__ void slab_step(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                      const Lane& L, lds_char* sm)
     {
         constexpr int NM = FM * FN;
         if constexpr (I < NM) {
-            mfma_one(acc, F[S & 1], I);
+            mfma_one(acc, F[(ST * SL + S) % RF], I);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (NS == 2 && S == SL - 1 && I == 0) {
@@ -459,7 +474,7 @@ struct DmaGemm {
     // Slot SLOT of a strip (stage ST) of wave W, then the following slots: the
     // recursion unrolls the strip at compile time whatever its length.
     template <int ST, int W, int SLOT>
-    static __device__ __forceinline__ void slots(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+    static __device__ __forceinline__ void slots(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
                                                  int m0, int n0, int t, u32 smem0, StripRes& r,
                                                  const StripRes& r1)
@@ -502,10 +517,10 @@ struct DmaGemm {
             slots<ST, W, SLOT + 1>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
     }
 
-    // One strip: SL slabs of FM x FN MFMAs; slab s uses fragment set F[s & 1]
-    // while the reads of the next slab fill the other set (the last slab reads
-    // slab 0 of strip t + 1 into F[0]).  Copies of strip t + NS - 1 go to the
-    // stage strip t - 1 used.
+    // One strip: SL slabs of FM x FN MFMAs; slab s uses one fragment set of
+    // the ring while its reads fill the set of slab s + PFD (past the last
+    // slab, the first slabs of strip t + 1).  Copies of strip t + NS - 1 go to
+    // the stage strip t - 1 used.
     //   NS >= 3: the barrier sits in slot 0 (after its MFMA and read): before
     //     it, strip t + 1's copies are waited for (at most the NCOPY x (NS - 3)
     //     younger ones stay in flight); after it, strip t + 1 is visible and the
@@ -522,7 +537,7 @@ struct DmaGemm {
     //     before as its t + 2; this strip computes t + 2's and leaves them
     //     there for the next.
     template <int ST, int W>
-    static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+    static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
                                                  int m0, int n0, int t, u32 smem0, StripRes& carry)
     {
@@ -538,7 +553,7 @@ struct DmaGemm {
     // count is rounded up to a multiple of NS: strips at or past KT copy only
     // out-of-range zeros, which add exactly nothing.
     template <int W>
-    static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], Frag (&F)[2],
+    static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                      const Lane& L, lds_char* sm,
                                                      const GemmParams& p, int m0, int n0, int KT,
                                                      u32 smem0)
@@ -642,10 +657,18 @@ struct DmaGemm {
         // strip 0 must be complete and visible before its first fragments are
         // read (NS == 2: wait for all)
         wait_copies_barrier<(NS == 2 ? 0 : NS - 2) * NCOPY>();
-        Frag F[2];
+        Frag F[RF];
 #pragma unroll
         for (int i = 0; i < NREAD; ++i)
             read_one<0, 0>(F[0], L, sm, i);
+        if constexpr (PFD > 1) {
+#pragma unroll
+            for (int i = 0; i < NREAD; ++i)
+                read_one<0, 1 % SL>(F[1], L, sm, i);
+#pragma unroll
+            for (int i = 0; i < NREAD; ++i)
+                read_one<0, 2 % SL>(F[2], L, sm, i);
+        }
 
         switch (w) {
         case 0:
