@@ -122,9 +122,10 @@ def dma_regs(bm, bn, bk, wgm, wgn) -> int:
     return wtm * wtn // 64 + 2 * (4 * fm + 4 * fn) + (2 * ja + jb + sl + fn + 10) + 24
 
 
-def dma_occupancy(bm, bn, nw) -> int:
-    """Waves per SIMD (DmaOcc): one for the largest tiles on four waves, else two."""
-    return 1 if bm * bn >= 256 * 128 and nw <= 4 else 2
+def dma_occupancy(bm, bn, nw, lds) -> int:
+    """Waves per SIMD (DmaOcc): one on four waves for the largest tiles and for
+    rings of more than half the LDS (no second workgroup fits), else two."""
+    return 1 if nw <= 4 and (bm * bn >= 256 * 128 or 2 * lds > LDS_BYTES) else 2
 
 
 def dma_candidates(dtype: int):
@@ -145,7 +146,7 @@ def dma_candidates(dtype: int):
                         lds = ns * (sa + sb)
                         if lds > LDS_BYTES:
                             continue
-                        occ = dma_occupancy(bm, bn, nw)
+                        occ = dma_occupancy(bm, bn, nw, lds)
                         regs = dma_regs(bm, bn, bk, wgm, wgn)
                         if regs > REGS_PER_LANE // occ:
                             continue

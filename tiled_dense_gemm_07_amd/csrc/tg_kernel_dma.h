@@ -709,19 +709,24 @@ struct DmaGemm {
     }
 };
 
-// Waves per SIMD the kernel is compiled for: one for the largest tiles on
-// four waves (all 512 registers of a lane available, 256 of them
-// accumulators), else two.
-template <int BM, int BN, int NW>
+// Waves per SIMD the kernel is compiled for: one on four waves for the
+// largest tiles (all 512 registers of a lane available, 256 of them
+// accumulators) and for rings of more than half the LDS (no second workgroup
+// fits beside them), else two.
+template <int BM, int BN, int NW, int LDS>
 struct DmaOcc {
-    static constexpr int value = (BM * BN >= 256 * 128 && NW <= 4) ? 1 : 2;
+    static constexpr int value =
+        (NW <= 4 && (BM * BN >= 256 * 128 || 2 * LDS > 160 * 1024)) ? 1 : 2;
 };
+
+template <int BM, int BN, int WGM, int WGN, int NS, int BK>
+using DmaOccOf = DmaOcc<BM, BN, WGM * WGN, NS * (BM + BN) * BK * 2>;
 
 template <int DT, bool TA, bool TB, int BM, int BN, int WGM, int WGN, int NS, int GROUP_M,
           int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(WGM * WGN * 64, WGM * WGN * 64),
-                          amdgpu_waves_per_eu(DmaOcc<BM, BN, WGM * WGN>::value,
-                                              DmaOcc<BM, BN, WGM * WGN>::value))) void
+                          amdgpu_waves_per_eu(DmaOccOf<BM, BN, WGM, WGN, NS, BK>::value,
+                                              DmaOccOf<BM, BN, WGM, WGN, NS, BK>::value))) void
 gemm_dma_kernel(GemmParams p)
 {
     const ClockStamp clk = stamp_begin(p);
