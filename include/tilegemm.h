@@ -28,9 +28,10 @@
  *     K == 0: C = epilogue(0) = 0; the operand pointers may be NULL then.
  *   - Accumulation is always fp32; the output is rounded to its type once,
  *     round-to-nearest-even (fp32 -> fp16 overflow gives +-inf).
- *   - Each operand must fit a 31-bit byte offset per tile row band: the library
- *     returns TG_ERR_BAD_SHAPE when 256 * K * element_size or
- *     64 * N * element_size exceeds 2^31 - 1 (and for M, N, K above 2^31 - 1).
+ *   - Each operand must fit a 31-bit byte offset per tile row band (up to 256
+ *     rows of a k-contiguous operand, up to 128 k-rows of an n-contiguous one):
+ *     the library returns TG_ERR_BAD_SHAPE when 256 * K * element_size or
+ *     128 * N * element_size exceeds 2^31 - 1 (and for M, N, K above 2^31 - 1).
  */
 #ifndef TILEGEMM_H
 #define TILEGEMM_H
@@ -100,7 +101,7 @@ tg_status tg_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A
  * LDS-DMA kernel; fp32: the register-staged kernel), any other call takes
  * element loads.
  * Errors: as tg_gemm; TG_ERR_BAD_LAYOUT (trans_a or trans_b not 0 or 1),
- *   TG_ERR_BAD_SHAPE also when trans_a and 64 * M * element_size exceeds
+ *   TG_ERR_BAD_SHAPE also when trans_a and 128 * M * element_size exceeds
  *   2^31 - 1.
  */
 tg_status tg_gemm_ex(int64_t M, int64_t N, int64_t K, tg_dtype dtype, const void* A, int trans_a,

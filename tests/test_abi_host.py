@@ -13,7 +13,7 @@ import re
 import numpy as np
 import pytest
 
-from tiled_dense_gemm_07_amd import binding
+from tiled_dense_gemm_07_amd import binding, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -55,6 +55,7 @@ def test_gemm_argument_errors(lib):
     assert g(4, 4, -1, 2, PA, PB, PC, 0, None) == SHAPE
     assert g(4, 4, 1 << 31, 2, PA, PB, PC, 0, None) == SHAPE
     assert g(4, 4, 1 << 23, 2, PA, PB, PC, 0, None) == SHAPE  # 256*K*2 > 2^31
+    assert g(4, 1 << 23, 4, 2, PA, PB, PC, 0, None) == SHAPE  # 128*N*2 > 2^31
     assert g(4, 4, 4, 3, PA, PB, PC, 0, None) == DTYPE
     assert g(4, 4, 4, -1, PA, PB, PC, 0, None) == DTYPE
     assert g(4, 4, 4, 2, PA, PB, PC, 2, None) == EPI
@@ -127,6 +128,7 @@ def test_gemm_ex_argument_errors(lib):
     assert g(4, 4, 4, 2, PA, 0, PB, -1, PC, 0, None) == BADL
     assert g(-1, 4, 4, 2, PA, 1, PB, 1, PC, 0, None) == SHAPE
     assert g(1 << 25, 4, 8, 2, PA, 1, PB, 0, PC, 0, None) == SHAPE  # 64 * M * 2 > 2^31
+    assert g(1 << 23, 4, 8, 2, PA, 1, PB, 0, PC, 0, None) == SHAPE  # 128 * M * 2 > 2^31
     assert g(4, 4, 4, 2, None, 1, PB, 0, PC, 0, None) == NULLP
     assert g(4, 4, 4, 2, PA, 1, PB, 0, PA + 4, 0, None) == ALIAS
     assert g(0, 4, 4, 2, None, 1, None, 1, None, 0, None) == OK
@@ -446,3 +448,25 @@ def test_tile_map_errors(lib):
     assert lib.tg_tile_map(0, 4, 1, p, p) == SHAPE
     assert lib.tg_tile_map(2, 2, 0, p, p) == SHAPE
     assert lib.tg_tile_map(2, 2, 1, None, p) == NULLP
+
+
+def test_hashed_ints_numpy_and_torch_agree():
+    """The index-hash generator used for multi-GiB operands: values in range,
+    roughly uniform, and the same on numpy arrays and torch tensors."""
+    import torch
+
+    r, c = np.arange(300)[:, None], np.arange(500)[None, :]
+    h = synth.hashed_ints(r, c, 7)
+    assert h.min() == -4 and h.max() == 4
+    counts = np.bincount((h + 4).ravel(), minlength=9)
+    assert counts.min() > 0.9 * h.size / 9 and counts.max() < 1.1 * h.size / 9
+    t = synth.hashed_ints(torch.arange(300)[:, None], torch.arange(500)[None, :], 7)
+    assert np.array_equal(t.numpy(), h)
+    assert not np.array_equal(synth.hashed_ints(r, c, 8), h)
+    # the largest indices an operand can have: int64 arrays give what Python's
+    # unbounded integers give, so no product wrapped
+    big = 0x7FFFFFFF
+    want = synth.hashed_ints(big, big, big)  # Python ints
+    got = synth.hashed_ints(np.array([[big]], dtype=np.int64), np.array([[big]], dtype=np.int64),
+                            big)
+    assert int(got[0, 0]) == want

@@ -434,7 +434,7 @@ tg_status check_shape(int64_t M, int64_t N, int64_t K, int esize)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return TG_ERR_BAD_SHAPE;
-    if (256 * K * esize > kMaxDim || 64 * N * esize > kMaxDim)
+    if (256 * K * esize > kMaxDim || 128 * N * esize > kMaxDim)
         return TG_ERR_BAD_SHAPE;
     if (tiles(M, 32) * tiles(N, 32) > kMaxDim)
         return TG_ERR_BAD_SHAPE;
@@ -569,7 +569,7 @@ tg_status gemm_impl(const Config* forced, int forced_index, int64_t M, int64_t N
     tg_status s = check_shape(M, N, K, es);
     if (s != TG_OK)
         return s;
-    if (trans_a && 64 * M * es > kMaxDim)
+    if (trans_a && 128 * M * es > kMaxDim)
         return TG_ERR_BAD_SHAPE;  // per-strip offsets of a [K][M] operand
     if (sk && sk->splits < 0)
         return TG_ERR_BAD_SHAPE;

@@ -12,6 +12,8 @@ page), so every workload here is synthetic:
 * floating inputs: numpy ``Generator(PCG64(seed)).standard_normal`` in float64,
   rounded to float32, then rounded (nearest-even) to the operand type;
 * integer inputs: uniform on {-4, ..., 4}, exact in every operand type;
+  operands of several GiB take the same range from a hash of (row, column,
+  seed) instead (:func:`hashed_ints`), so they can be filled on the device;
 * 4-bit weights: uniform bytes (so both nibbles are uniform on 0..15),
   E8M0 scale bytes 127 + uniform{-4..0}, i.e. scales 2^-4 .. 2^0;
 * MX-format activations: E2M1 as the weights; E4M3 codes uniform over the 254
@@ -47,6 +49,25 @@ def normal_f32(shape, seed: int) -> np.ndarray:
 def integers_f32(shape, seed: int, lo: int = -4, hi: int = 4) -> np.ndarray:
     """Uniform integers in [lo, hi] stored as float32 (exact)."""
     return rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def hashed_ints(r, c, seed: int, lo: int = -4, hi: int = 4):
+    """Integers in [lo, hi] as a function of (row, column, seed): a 32-bit
+    multiply / xor-shift mix of the index pair.
+
+    `r` and `c` are broadcastable int64 arrays: numpy arrays, or torch tensors
+    on any device (the same integer operators, so an operand of several GiB
+    can be filled on the device while the oracle side evaluates the rows or
+    columns it needs on the host).  Every product stays below 2^63.
+    """
+    m = 0xFFFFFFFF
+    x = (r * 0x3C6EF35F + c * 0x1B873593 + seed * 0x61C88647) & m
+    x = x ^ (x >> 16)
+    x = (x * 0x7FEB352D) & m
+    x = x ^ (x >> 15)
+    x = (x * 0x2C1B3C6D) & m
+    x = x ^ (x >> 16)
+    return x % (hi - lo + 1) + lo
 
 
 def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
