@@ -486,6 +486,75 @@ def test_transposed_misaligned_pointers(dtype):
         assert np.array_equal(to_host_bits(Ct, dtype), want), code
 
 
+def _hashed_device(rows: int, cols: int, seed: int, tdtype):
+    """[rows, cols] operand of synth.hashed_ints values, filled on the device."""
+    out = torch.empty((rows, cols), dtype=tdtype, device=DEV)
+    c = torch.arange(cols, device=DEV, dtype=torch.int64)[None, :]
+    step = max(1, (1 << 26) // cols)
+    for r0 in range(0, rows, step):
+        r = torch.arange(r0, min(rows, r0 + step), device=DEV, dtype=torch.int64)[:, None]
+        out[r0:r0 + r.shape[0]] = synth.hashed_ints(r, c, seed).to(tdtype)
+    return out
+
+
+# (M, N, K, trans_a, forced configurations).  Byte offsets inside the
+# n-contiguous operand (B stored [K][N], or A stored [K][M]) reach past 2^31:
+#  * 200 x 32768 x 32768: the band of the tiles at column 0 spans 2^31 bytes
+#    (resource rebuilt per k-strip); every other tile's band fits, read with
+#    scalar offsets up to 2^31 - 64 KiB;
+#  * 136 x 24568 x 45000 and A^T 32760 x 200 x 36000: no band fits (ragged
+#    in every dimension).
+WIDE = [(200, 32768, 32768, 0, ["64x64x64_w2x2_s4_g8_dma", "256x256x64_w2x4_s2_g4_dma"]),
+        (136, 24568, 45000, 0, ["128x128x64_w4x2_s4_g8_dma"]),
+        (32760, 200, 36000, 1, ["256x256x32_w2x2_s4_g4_dma_tn"])]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "%dx%dx%d_%s" % (
+    c[0], c[1], c[2], "tn" if c[3] else "nn"))
+def test_operand_offsets_past_31_bits(case):
+    """Operands of 2.1 to 2.4 GiB: whole columns (or rows) of C bitwise against
+    the oracle's product of the matching rows of A and columns of B."""
+    M, N, K, ta, forced = case
+    tdt = torch.bfloat16
+    sa, sb = 7001 + M, 7002 + N
+    say("wide operand %dx%dx%d ta=%d: filling" % (M, N, K, ta))
+    A_st = _hashed_device(K, M, sa, tdt) if ta else _hashed_device(M, K, sa, tdt)
+    Bt = _hashed_device(K, N, sb, tdt)
+    g = synth.rng(M + N + K)
+    if ta:  # every column of C at sampled rows
+        rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], g.integers(0, M, 24)]))
+        cols = np.arange(N)
+    else:  # every row of C at sampled columns, the first tile column whole
+        rows = np.arange(M)
+        cols = np.unique(np.concatenate([np.arange(0, 256), [N // 2 - 1, N // 2, N - 1],
+                                         np.arange(N - 136, N, 3), g.integers(0, N, 48)]))
+    kk = np.arange(K, dtype=np.int64)
+    if ta:
+        a_sub = synth.hashed_ints(kk[None, :], rows.astype(np.int64)[:, None], sa)
+    else:
+        a_sub = synth.hashed_ints(rows.astype(np.int64)[:, None], kk[None, :], sa)
+    b_sub = synth.hashed_ints(kk[:, None], cols.astype(np.int64)[None, :], sb)
+    a_bits = synth.to_storage(a_sub.astype(np.float32), BF16)
+    b_bits = synth.to_storage(b_sub.astype(np.float32), BF16)
+    want = oracle.encode(BF16, oracle.gemm_f64(a_bits, b_bits, BF16))
+    names = binding.list_configs(0, BF16)
+    runs = [None] + [names.index("gemm_bf16_" + f) for f in forced]
+    for idx in runs:
+        say("wide operand %dx%dx%d ta=%d config=%s" % (
+            M, N, K, ta, binding.query_config(0, M, N, K, BF16, bool(ta)) if idx is None
+            else names[idx]))
+        Ct = binding.gemm_ex(A_st, Bt, trans_a=ta, trans_b=False, config=idx)
+        torch.cuda.synchronize()
+        got = to_host_bits(Ct[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)],
+                           BF16)
+        diff = got != want
+        assert not diff.any(), "%d of %d sampled entries differ (first at %s)" % (
+            int(diff.sum()), diff.size, np.argwhere(diff)[0].tolist())
+        del Ct
+    del A_st, Bt
+    torch.cuda.empty_cache()
+
+
 def test_side_stream():
     """A call on a non-default stream is ordered on that stream."""
     M, N, K = 512, 512, 512

@@ -145,12 +145,15 @@ struct DmaOperand {
         int kk[KMAJ ? J : 1];  // KMAJ: k (within the strip) of the data each copy lane moves
         int lr;       // x-contiguous: the lane's k row within a copy (k = copy row + lr)
         u32 rd[KMAJ ? SL : FX];  // fragment read offsets (stage 0)
-        __amdgpu_buffer_rsrc_t band;  // KMAJ: the tile's rows over the whole K
+        __amdgpu_buffer_rsrc_t band;  // the tile's rows (KMAJ) or columns over the whole K
+        bool use_band;  // x-contiguous: the band's offsets fit 31 bits (KMAJ: always)
     };
-    // Where one strip's copies read: KMAJ, the tile's row band and the
-    // strip's byte offset in it (set up once per tile, so a strip costs one
-    // scalar multiply); x-contiguous, a resource rebased to the strip's first
-    // k row, so that offsets stay within 31 bits however large the operand.
+    // Where one strip's copies read: the tile's band (its rows over the whole
+    // K, or its columns over all K rows) and the strip's byte offset in it,
+    // set up once per tile, so a strip costs one scalar multiply.  An
+    // x-contiguous band spans K rows of the full matrix width; where that
+    // passes 31 bits of offset, each strip gets a resource rebased to its
+    // first k row instead (uniform per workgroup, decided at setup).
     struct Strip {
         __amdgpu_buffer_rsrc_t rs;
         u32 so;
@@ -166,8 +169,8 @@ struct DmaOperand {
                                                  int lane, int wx0, u32 region, const void* base,
                                                  int K)
     {
-        if constexpr (KMAJ)
-            L.band = strip_rsrc(base, x0, xtot, ld, K, 0);
+        L.band = strip_rsrc(base, x0, xtot, ld, K, 0);
+        L.use_band = KMAJ || (int64_t)(K - 1) * ld * 2 + (int64_t)(xtot - x0) * 2 < 0x7FFFFFFF;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int blk = w * J + j;
@@ -213,6 +216,7 @@ struct DmaOperand {
                              clamp_bytes(((int64_t)(K - k0 - 1) * ld + (xtot - x0)) * 2));
     }
 
+    template <bool BAND>
     static __device__ __forceinline__ Strip strip(const Lane& L, const void* base, int x0,
                                                   int xtot, int ld, int K, int k0)
     {
@@ -220,6 +224,9 @@ struct DmaOperand {
         if constexpr (KMAJ) {
             s.rs = L.band;
             s.so = (u32)k0 * 2u;
+        } else if constexpr (BAND) {
+            s.rs = L.band;
+            s.so = (u32)k0 * (u32)ld * 2u;
         } else {
             s.rs = strip_rsrc(base, x0, xtot, ld, K, k0);
             s.so = 0u;
@@ -233,10 +240,7 @@ struct DmaOperand {
     {
         const int kk = KMAJ ? L.kk[KMAJ ? d : 0] : (w * J + d) * RPB + L.lr;
         const u32 lds = region_lds + ST * STAGE + (w * J + d) * 1024;
-        if constexpr (KMAJ)
-            dma16_so(lds, kk < krem ? L.off[d] : kOob, sr.rs, sr.so);
-        else
-            dma16(lds, kk < krem ? L.off[d] : kOob, sr.rs);
+        dma16_so(lds, kk < krem ? L.off[d] : kOob, sr.rs, sr.so);
     }
 
     // LDS read i (0 .. NRD-1) of slab S of stage ST.
@@ -361,15 +365,29 @@ struct DmaGemm {
         int krem;  // valid k within the strip: [0, krem)
     };
 
+    // BAND: both operands read through their per-tile bands (decided per
+    // workgroup at setup; the loop is compiled for either case so that no
+    // strip branches on it).
+    template <bool BAND>
     static __device__ __forceinline__ StripRes strip_res(const GemmParams& p, int m0, int n0,
                                                          int strip, const Lane& L)
     {
         const int k0 = strip * BK;
         StripRes r;
-        r.a = OA::strip(L.a, p.A, m0, p.M, lda(p), p.K, k0);
-        r.b = OB::strip(L.b, p.B, n0, p.N, ldb(p), p.K, k0);
+        r.a = OA::template strip<BAND>(L.a, p.A, m0, p.M, lda(p), p.K, k0);
+        r.b = OB::template strip<BAND>(L.b, p.B, n0, p.N, ldb(p), p.K, k0);
         r.krem = p.K - k0;
         return r;
+    }
+    static __device__ __forceinline__ bool use_band(const Lane& L)
+    {
+        return L.a.use_band && L.b.use_band;
+    }
+    static __device__ __forceinline__ StripRes strip_res_any(const GemmParams& p, int m0, int n0,
+                                                             int strip, const Lane& L)
+    {
+        return use_band(L) ? strip_res<true>(p, m0, n0, strip, L)
+                           : strip_res<false>(p, m0, n0, strip, L);
     }
 
     // Copy d (0 .. NCOPY-1) of a strip into LDS stage ST: A's copies first.
@@ -388,7 +406,7 @@ struct DmaGemm {
                                                         int m0, int n0, int strip, int w,
                                                         u32 smem0)
     {
-        const StripRes r = strip_res(p, m0, n0, strip, L);
+        const StripRes r = strip_res_any(p, m0, n0, strip, L);
 #pragma unroll
         for (int d = 0; d < NCOPY; ++d)
             issue_copy<ST>(L, r, d, w, smem0);
@@ -473,7 +491,7 @@ struct DmaGemm {
 
     // Slot SLOT of a strip (stage ST) of wave W, then the following slots: the
     // recursion unrolls the strip at compile time whatever its length.
-    template <int ST, int W, int SLOT>
+    template <int ST, int W, int SLOT, bool BAND>
     static __device__ __forceinline__ void slots(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
                                                  int m0, int n0, int t, u32 smem0, StripRes& r,
@@ -485,7 +503,7 @@ struct DmaGemm {
             if constexpr (SLOT == 0) {
                 wait_copies_barrier<VM_AHEAD>();
                 __builtin_amdgcn_sched_barrier(0);
-                r = strip_res(p, m0, n0, t + NS - 1, L);
+                r = strip_res<BAND>(p, m0, n0, t + NS - 1, L);
             }
             // strip t + NS - 1 into the stage strip t - 1 used: copy d of wave
             // W at slot cpos(d, W)
@@ -514,7 +532,7 @@ struct DmaGemm {
             }
         }
         if constexpr (SLOT + 1 < SLOTS)
-            slots<ST, W, SLOT + 1>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
+            slots<ST, W, SLOT + 1, BAND>(acc, F, L, sm, p, m0, n0, t, smem0, r, r1);
     }
 
     // One strip: SL slabs of FM x FN MFMAs; slab s uses one fragment set of
@@ -536,15 +554,15 @@ struct DmaGemm {
     //     them.  `carry` holds strip t + 1's resources, computed by the strip
     //     before as its t + 2; this strip computes t + 2's and leaves them
     //     there for the next.
-    template <int ST, int W>
+    template <int ST, int W, bool BAND>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                  const Lane& L, lds_char* sm, const GemmParams& p,
                                                  int m0, int n0, int t, u32 smem0, StripRes& carry)
     {
         StripRes r;
         if constexpr (NS == 2)
-            r = strip_res(p, m0, n0, t + 2, L);
-        slots<ST, W, 0>(acc, F, L, sm, p, m0, n0, t, smem0, r, carry);
+            r = strip_res<BAND>(p, m0, n0, t + 2, L);
+        slots<ST, W, 0, BAND>(acc, F, L, sm, p, m0, n0, t, smem0, r, carry);
         if constexpr (NS == 2)
             carry = r;
     }
@@ -552,7 +570,7 @@ struct DmaGemm {
     // The strip loop of wave W (the copy slots differ per wave).  The strip
     // count is rounded up to a multiple of NS: strips at or past KT copy only
     // out-of-range zeros, which add exactly nothing.
-    template <int W>
+    template <int W, bool BAND>
     static __device__ __forceinline__ void main_loop(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
                                                      const Lane& L, lds_char* sm,
                                                      const GemmParams& p, int m0, int n0, int KT,
@@ -560,17 +578,29 @@ struct DmaGemm {
     {
         StripRes carry;
         if constexpr (NS == 2)
-            carry = strip_res(p, m0, n0, 1, L);
+            carry = strip_res<BAND>(p, m0, n0, 1, L);
         for (int t = 0; t < KT; t += NS) {
-            strip<0, W>(acc, F, L, sm, p, m0, n0, t, smem0, carry);
-            strip<1, W>(acc, F, L, sm, p, m0, n0, t + 1, smem0, carry);
+            strip<0, W, BAND>(acc, F, L, sm, p, m0, n0, t, smem0, carry);
+            strip<1, W, BAND>(acc, F, L, sm, p, m0, n0, t + 1, smem0, carry);
             if constexpr (NS > 2)
-                strip<2 % NS, W>(acc, F, L, sm, p, m0, n0, t + 2, smem0, carry);
+                strip<2 % NS, W, BAND>(acc, F, L, sm, p, m0, n0, t + 2, smem0, carry);
             if constexpr (NS > 3)
-                strip<3 % NS, W>(acc, F, L, sm, p, m0, n0, t + 3, smem0, carry);
+                strip<3 % NS, W, BAND>(acc, F, L, sm, p, m0, n0, t + 3, smem0, carry);
             if constexpr (NS > 4)
-                strip<4 % NS, W>(acc, F, L, sm, p, m0, n0, t + 4, smem0, carry);
+                strip<4 % NS, W, BAND>(acc, F, L, sm, p, m0, n0, t + 4, smem0, carry);
         }
+    }
+
+    template <int W>
+    static __device__ __forceinline__ void loop_for(f32x16 (&acc)[FM][FN], Frag (&F)[RF],
+                                                    const Lane& L, lds_char* sm,
+                                                    const GemmParams& p, int m0, int n0, int KT,
+                                                    u32 smem0)
+    {
+        if (use_band(L))
+            main_loop<W, true>(acc, F, L, sm, p, m0, n0, KT, smem0);
+        else
+            main_loop<W, false>(acc, F, L, sm, p, m0, n0, KT, smem0);
     }
 
     static __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN],
@@ -642,7 +672,7 @@ struct DmaGemm {
         // of strip -1; strip 0 issues the rest)
         issue_copies<0>(L, p, m0, n0, 0, w, smem0);
         if constexpr (NS == 2) {
-            const StripRes r1 = strip_res(p, m0, n0, 1, L);
+            const StripRes r1 = strip_res_any(p, m0, n0, 1, L);
 #pragma unroll
             for (int d = 0; d < NCOPY; ++d)
                 if (((d * NW + w) * CSLOTS) / (NCOPY * NW) < STEPS)
@@ -672,28 +702,28 @@ struct DmaGemm {
 
         switch (w) {
         case 0:
-            main_loop<0>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<0>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 1:
-            main_loop<1 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<1 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 2:
-            main_loop<2 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<2 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 3:
-            main_loop<3 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<3 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 4:
-            main_loop<4 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<4 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 5:
-            main_loop<5 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<5 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         case 6:
-            main_loop<6 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<6 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         default:
-            main_loop<7 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
+            loop_for<7 % NW>(acc, F, L, sm, p, m0, n0, KT, smem0);
             break;
         }
         // drain the copies of the strips past the end (all out of range)
