@@ -25,7 +25,8 @@
 //    metadata dwords of each row as two [BM][4] blocks (dword copies), B as
 //    [64 k][BN] (the dense kernel's x-contiguous operand, transposing reads);
 //  * per k-step a wave reads per 32-row block one ds_read_b128 of kept values
-//    and one ds_read_b32 of metadata (shifted by lane half), and per 32-column
+//    and its metadata dword (shifted by lane half: one ds_read_b32, or with CS
+//    one ds_read_b128 of four dwords every second strip), and per 32-column
 //    block the two slab fragments of B; one sparse MFMA per block pair;
 //  * one barrier per strip after its first MFMA; copies of strip t + 2 into
 //    the stage strip t - 1 used, spread over the strip;
@@ -243,8 +244,8 @@ struct DmaSp24 {
     // row block, then the B fragments (two slabs) per column block.  SP: the
     // strip's place in its metadata chunk and ib the chunk buffer's offset (CS).
     template <int ST, int Q, int SP>
-    static __device__ __forceinline__ void read_one(Frag& F, const Lane& L, lds_char* sm, int i,
-                                                    u32 ib)
+    static __device__ __forceinline__ void read_one(Frag& F, u32x4 (&meta)[FM], const Lane& L,
+                                                    lds_char* sm, int i, u32 ib)
     {
         typedef __attribute__((address_space(3))) u32 lds_u32;
         if (i < FM) {
@@ -252,10 +253,18 @@ struct DmaSp24 {
         } else if (i < 2 * FM) {
             const int fm = i - FM;
             if constexpr (CS) {
-                // row's half SP / 2, dword 2 (SP % 2) + Q of it
-                const u32 a = (L.i_rd ^ (u32)((SP >> 1) << 4)) + ib + (2 * (SP & 1) + Q) * 4 +
-                              fm * 32 * 32;
-                F.idx[fm] = *(const lds_u32*)(sm + a) >> L.h16;
+                // The row's 16-byte half SP / 2 of the chunk holds the
+                // metadata of strips SP & ~1 and SP | 1 (dword 2 (SP % 2) + Q).
+                // It is read whole at k-step 0 of an even place and kept for
+                // the four k-steps of the pair: rows 32 bytes apart with the
+                // half flipped by row bit 3 put a 16-lane pass of 16 rows on
+                // 16 different 16-byte bank groups, where dword reads of 32
+                // rows met two to a bank.
+                if constexpr (Q == 0 && (SP & 1) == 0) {
+                    const u32 a = (L.i_rd ^ (u32)((SP >> 1) << 4)) + ib + fm * 32 * 32;
+                    meta[fm] = *(const lds_u32x4*)(sm + a);
+                }
+                F.idx[fm] = meta[fm][2 * (SP & 1) + Q] >> L.h16;
             } else {
                 F.idx[fm] = *(const lds_u32*)(sm + L.i_rd + Q * BM * 4 + ST * I_STAGE +
                                               fm * 32 * 4) >>
@@ -308,6 +317,7 @@ struct DmaSp24 {
     // copies chunk c + 1.
     template <int ST, int W, int P = 0>
     static __device__ __forceinline__ void strip(f32x16 (&acc)[FM][FN], Frag& F0, Frag& F1,
+                                                 u32x4 (&meta)[FM],
                                                  const Lane& L, const Res& res, lds_char* sm,
                                                  const GemmParams& p, int n0, int t, u32 smem0)
     {
@@ -328,13 +338,13 @@ struct DmaSp24 {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rd = lo; rd < hi; ++rd)
-                    read_one<ST, 1, P>(F1, L, sm, rd, ib);
+                    read_one<ST, 1, P>(F1, meta, L, sm, rd, ib);
             } else {
                 mfma_one(acc, F1, i);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int rd = lo; rd < hi; ++rd)
-                    read_one<NXT, 0, PN>(F0, L, sm, rd, ibn);
+                    read_one<NXT, 0, PN>(F0, meta, L, sm, rd, ibn);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (slot == 0) {
@@ -376,46 +386,47 @@ struct DmaSp24 {
         issue_copies<1, W>(L, res, p, n0, 1, smem0);
         wait_copies_barrier<NCOPY>();  // chunk 0 and strip 0 landed and visible
         Frag F0, F1;
+        u32x4 meta[FM];  // CS: each row block's metadata for two strips (see read_one)
 #pragma unroll
         for (int i = 0; i < NRD; ++i)
-            read_one<0, 0, 0>(F0, L, sm, i, 0u);
+            read_one<0, 0, 0>(F0, meta, L, sm, i, 0u);
         if constexpr (CS) {
             // 12 strips (the stage and the place in the chunk both repeat),
             // then the 4 or 8 left (K % 256 == 0)
             int t = 0;
             for (; t + 12 <= KT; t += 12) {
-                strip<0, W, 0>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
-                strip<1, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
-                strip<2, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
-                strip<0, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 3, smem0);
-                strip<1, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 4, smem0);
-                strip<2, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 5, smem0);
-                strip<0, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 6, smem0);
-                strip<1, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 7, smem0);
-                strip<2, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 8, smem0);
-                strip<0, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 9, smem0);
-                strip<1, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 10, smem0);
-                strip<2, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 11, smem0);
+                strip<0, W, 0>(acc, F0, F1, meta, L, res, sm, p, n0, t, smem0);
+                strip<1, W, 1>(acc, F0, F1, meta, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W, 2>(acc, F0, F1, meta, L, res, sm, p, n0, t + 2, smem0);
+                strip<0, W, 3>(acc, F0, F1, meta, L, res, sm, p, n0, t + 3, smem0);
+                strip<1, W, 0>(acc, F0, F1, meta, L, res, sm, p, n0, t + 4, smem0);
+                strip<2, W, 1>(acc, F0, F1, meta, L, res, sm, p, n0, t + 5, smem0);
+                strip<0, W, 2>(acc, F0, F1, meta, L, res, sm, p, n0, t + 6, smem0);
+                strip<1, W, 3>(acc, F0, F1, meta, L, res, sm, p, n0, t + 7, smem0);
+                strip<2, W, 0>(acc, F0, F1, meta, L, res, sm, p, n0, t + 8, smem0);
+                strip<0, W, 1>(acc, F0, F1, meta, L, res, sm, p, n0, t + 9, smem0);
+                strip<1, W, 2>(acc, F0, F1, meta, L, res, sm, p, n0, t + 10, smem0);
+                strip<2, W, 3>(acc, F0, F1, meta, L, res, sm, p, n0, t + 11, smem0);
             }
             if (t + 4 <= KT) {
-                strip<0, W, 0>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
-                strip<1, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
-                strip<2, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
-                strip<0, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 3, smem0);
+                strip<0, W, 0>(acc, F0, F1, meta, L, res, sm, p, n0, t, smem0);
+                strip<1, W, 1>(acc, F0, F1, meta, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W, 2>(acc, F0, F1, meta, L, res, sm, p, n0, t + 2, smem0);
+                strip<0, W, 3>(acc, F0, F1, meta, L, res, sm, p, n0, t + 3, smem0);
                 if (t + 8 <= KT) {
-                    strip<1, W, 0>(acc, F0, F1, L, res, sm, p, n0, t + 4, smem0);
-                    strip<2, W, 1>(acc, F0, F1, L, res, sm, p, n0, t + 5, smem0);
-                    strip<0, W, 2>(acc, F0, F1, L, res, sm, p, n0, t + 6, smem0);
-                    strip<1, W, 3>(acc, F0, F1, L, res, sm, p, n0, t + 7, smem0);
+                    strip<1, W, 0>(acc, F0, F1, meta, L, res, sm, p, n0, t + 4, smem0);
+                    strip<2, W, 1>(acc, F0, F1, meta, L, res, sm, p, n0, t + 5, smem0);
+                    strip<0, W, 2>(acc, F0, F1, meta, L, res, sm, p, n0, t + 6, smem0);
+                    strip<1, W, 3>(acc, F0, F1, meta, L, res, sm, p, n0, t + 7, smem0);
                 }
             }
         } else {
             // The strip count is rounded up to a multiple of NS: strips at or
             // past KT copy only zeros, which add exactly nothing.
             for (int t = 0; t < KT; t += NS) {
-                strip<0, W>(acc, F0, F1, L, res, sm, p, n0, t, smem0);
-                strip<1, W>(acc, F0, F1, L, res, sm, p, n0, t + 1, smem0);
-                strip<2, W>(acc, F0, F1, L, res, sm, p, n0, t + 2, smem0);
+                strip<0, W>(acc, F0, F1, meta, L, res, sm, p, n0, t, smem0);
+                strip<1, W>(acc, F0, F1, meta, L, res, sm, p, n0, t + 1, smem0);
+                strip<2, W>(acc, F0, F1, meta, L, res, sm, p, n0, t + 2, smem0);
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
