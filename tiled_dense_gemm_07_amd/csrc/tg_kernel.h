@@ -313,6 +313,19 @@ struct GemmKernel {
     static constexpr int RED_BYTES = (KS - 1) * BM * BN * 4;
     static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
 
+    // Chunk swizzle of LDS row `row`.  Rows of 128 bytes take swz; rows of 16
+    // or more chunks start on the same bank, so the 16 lanes of a b128 read
+    // pass (16 consecutive rows at one logical chunk) need 16 different
+    // positions: the low four row bits, xor-ed with the next four so that the
+    // transposing stores (rows UW = 1, 2 or 4 apart at one chunk) spread too.
+    static __device__ __forceinline__ int sw(int row)
+    {
+        if constexpr (CPR >= 16)
+            return (row ^ (row >> 4)) & 15;
+        else
+            return swz(row);
+    }
+
     // Both operands sit in LDS k-contiguous ([rows][BK], 16-byte chunk
     // swizzle).  In global memory an operand is either k-contiguous (KOp: X
     // rows of K consecutive elements: A as [M][K], B stored [N][K]) or
@@ -367,7 +380,7 @@ struct GemmKernel {
                 const int q = tid + NT * i;
                 const int row = q / CPR;
                 const int c = q % CPR;
-                *(u32x4*)(S + row * ROWB + ((c ^ swz(row)) << 4)) = src[i];
+                *(u32x4*)(S + row * ROWB + ((c ^ sw(row)) << 4)) = src[i];
             }
         }
     };
@@ -459,7 +472,7 @@ struct GemmKernel {
                                   __builtin_amdgcn_perm(L[7][d], L[6][d], sel)};
                     }
                     const int n = nc * UW + j;
-                    *(u32x4*)(S + n * ROWB + ((kg ^ swz(n)) << 4)) = o;
+                    *(u32x4*)(S + n * ROWB + ((kg ^ sw(n)) << 4)) = o;
                 }
             }
         }
@@ -577,7 +590,7 @@ struct GemmKernel {
                     o[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 2));
                     o[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 3));
                     const int chunk = g * (CU / 8) + cc;
-                    *(u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4)) = o;
+                    *(u32x4*)(Bs + row * ROWB + ((chunk ^ sw(row)) << 4)) = o;
                 }
             }
         }
@@ -601,12 +614,12 @@ struct GemmKernel {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int row = wm * WTM + fm * 32 + lr;
-            F.a[fm] = *(const u32x4*)(As + row * ROWB + ((chunk ^ swz(row)) << 4));
+            F.a[fm] = *(const u32x4*)(As + row * ROWB + ((chunk ^ sw(row)) << 4));
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int row = wn * WTN + fn * 32 + lr;
-            F.b[fn] = *(const u32x4*)(Bs + row * ROWB + ((chunk ^ swz(row)) << 4));
+            F.b[fn] = *(const u32x4*)(Bs + row * ROWB + ((chunk ^ sw(row)) << 4));
         }
     }
 
