@@ -313,15 +313,17 @@ struct GemmKernel {
     static constexpr int RED_BYTES = (KS - 1) * BM * BN * 4;
     static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
 
-    // Chunk swizzle of LDS row `row`.  Rows of 128 bytes take swz; rows of 16
-    // or more chunks start on the same bank, so the 16 lanes of a b128 read
-    // pass (16 consecutive rows at one logical chunk) need 16 different
-    // positions: the low four row bits, xor-ed with the next four so that the
-    // transposing stores (rows UW = 1, 2 or 4 apart at one chunk) spread too.
+    // Chunk swizzle of LDS row `row`.  Rows of 128 bytes take swz.  Rows of
+    // 16 or more chunks all start on the same bank: a b128 read pass (16
+    // lanes, 256 bytes: 16 consecutive rows at one logical chunk) needs 16
+    // different positions, and a b128 write pass (8 lanes, 128 bytes: the
+    // transposing stores put rows UW = 1, 2, 4 or 8 apart at one chunk) 8
+    // different positions mod 8.  swz keeps the latter and row bit 3 adds
+    // the fourth bit for the former.
     static __device__ __forceinline__ int sw(int row)
     {
         if constexpr (CPR >= 16)
-            return (row ^ (row >> 4)) & 15;
+            return swz(row) | (row & 8);
         else
             return swz(row);
     }
