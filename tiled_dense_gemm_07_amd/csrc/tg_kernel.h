@@ -275,11 +275,16 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[FM][FN],
 }
 
 
-// E8M0 scale byte -> fp32 2^(E-127) (E = 0 is the fp32 subnormal 2^-127; 255 is NaN).
-__device__ __forceinline__ float e8m0_to_f32(u32 e)
+// Scale operand of the v_cvt_scalef32_pk_*_fp4 conversions for E8M0 byte e
+// (0 .. 255, the scale 2^(e - 127), 255 NaN).  Those instructions take the
+// scale from the exponent field of the fp32 they are given, so the byte
+// moved into that field serves as is: for every scale byte and every pair of
+// codes the results equal those for the decoded value (2^-127 as the fp32
+// subnormal for e = 0, a NaN for 255), bit for bit on the GPU, without the
+// two compares and selects the decoding takes.
+__device__ __forceinline__ float e8m0_cvt_scale(u32 e)
 {
-    u32 bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
-    return __builtin_bit_cast(float, bits);
+    return __builtin_bit_cast(float, e << 23);
 }
 
 // --------------------------------------------------------------------------
@@ -582,7 +587,7 @@ struct GemmKernel {
                 const int u = tid + NT * i;
                 const int row = u / UPR;
                 const int g = u % UPR;
-                const float sc = e8m0_to_f32(R.s[i]);
+                const float sc = e8m0_cvt_scale(R.s[i]);
 #pragma unroll
                 for (int cc = 0; cc < CU / 8; ++cc) {
                     const u32 packed = R.b[i][cc];  // 8 codes: k = 8cc .. 8cc+7 of this unit

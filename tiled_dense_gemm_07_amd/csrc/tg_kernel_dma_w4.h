@@ -367,7 +367,7 @@ struct DmaW4 {
     {
         const u32 packed = R.code[fn][j];
         const u32 sbyte = (sbytes >> (8 * (j >> 2))) & 0xFFu;  // 4 slabs per 32-k block
-        const float sc = e8m0_to_f32(sbyte);
+        const float sc = e8m0_cvt_scale(sbyte);
         u32x4 b;
         b[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 0));
         b[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, sc, 1));

@@ -188,7 +188,7 @@ struct GemvW4 {
                             const int blk = 4 * c + h;  // 32-k block of the round
                             const u32 e = (sc[q][blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
                             // a scale byte only multiplies codes of k < K (zeros past it)
-                            const float s = e8m0_to_f32(kr + 32 * blk < K ? e : 127u);
+                            const float s = e8m0_cvt_scale(kr + 32 * blk < K ? e : 127u);
                             const u32 packed = d[h];  // 8 codes: k = kr + 128 c + 32 h + 8 g ..
                             const u32x4 b = expand8(packed, s);
                             acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -248,7 +248,7 @@ struct GemvW4 {
                     for (int c = 0; c < 4; ++c) {
                         // a scale byte only multiplies codes of k < K (zeros past it)
                         const u32 e = (sc[q] >> (8 * c)) & 0xFFu;
-                        const float s = e8m0_to_f32(kq + 32 * c < K ? e : 127u);
+                        const float s = e8m0_cvt_scale(kq + 32 * c < K ? e : 127u);
 #pragma unroll
                         for (int h = 0; h < 4; ++h) {
                             const u32 packed = code[q][c][h];  // 8 codes: k = kq + 32c + 8h ..
