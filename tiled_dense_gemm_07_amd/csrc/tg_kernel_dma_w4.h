@@ -72,6 +72,14 @@ __device__ __forceinline__ void dma4(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t r
                  : "memory");
 }
 
+// The same with a wave-uniform byte offset added to every lane's address.
+__device__ __forceinline__ void dma4_so(u32 lds, u32 voff, __amdgpu_buffer_rsrc_t rs, u32 soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds),
+                 "v"(voff), "s"(rs), "s"(soff)
+                 : "memory");
+}
+
 template <int BM, int BN, int WGM, int WGN, int NS, int GROUP_M, int KS = 1, int SB = 1,
           int BK_ = 128>
 struct DmaW4 {
@@ -221,10 +229,11 @@ struct DmaW4 {
 
     // Byte offsets of one strip inside a row of A, of the codes and of the
     // scale bytes.  The buffer resources cover the tile's whole row bands
-    // (set up once, in Lane); the offsets are added to the lane offsets.
-    // Rows past M or N have kOob lane offsets, which stay out of range after
-    // the addition (offsets within a band stay below 2^31); strips past K
-    // copy kOob.
+    // (set up once, in Lane); the offsets are the copies' scalar offsets,
+    // added to the lane offsets by the address unit.  Rows past M or N have
+    // kOob lane offsets, which stay out of range with the offset added
+    // (offsets within a band stay below 2^31, so the sum cannot wrap);
+    // strips past K copy kOob.
     struct StripRes {
         u32 a, w, s;
         bool valid;
@@ -258,13 +267,16 @@ struct DmaW4 {
     static __device__ __forceinline__ void issue_copy(const Lane& L, const StripRes& r, int d,
                                                       u32 smem0)
     {
+        // the strip's byte offsets go in as the copies' scalar offsets, so a
+        // copy costs no vector address arithmetic
         if (d < JA)
-            dma16(smem0 + ST * A_STAGE + (W * JA + d) * 1024, r.valid ? L.a_off[d] + r.a : kOob, L.ra);
+            dma16_so(smem0 + ST * A_STAGE + (W * JA + d) * 1024, r.valid ? L.a_off[d] : kOob, L.ra,
+                     r.a);
         else if (d < JA + JW)
-            dma16(smem0 + W_REGION + ST * W_STAGE + (W * JW + d - JA) * 1024,
-                  r.valid ? L.w_off[d - JA] + r.w : kOob, L.rw);
+            dma16_so(smem0 + W_REGION + ST * W_STAGE + (W * JW + d - JA) * 1024,
+                     r.valid ? L.w_off[d - JA] : kOob, L.rw, r.w);
         else
-            dma4(smem0 + S_REGION + ST * S_STAGE + W * 256, r.valid ? L.s_off + r.s : kOob, L.rs);
+            dma4_so(smem0 + S_REGION + ST * S_STAGE + W * 256, r.valid ? L.s_off : kOob, L.rs, r.s);
     }
 
     template <int ST, int W>
